@@ -1,0 +1,90 @@
+// a7: gate-weighted combine of one pass.
+//
+// y[t] = sum over j ascending of gate[t,j] * out[row(t,j)] over the
+// assignments that have a row in this pass; a token with none gets 0.  This
+// is the combine back to token order of "MoE ring-of-experts: TC Pallas
+// ring all-gather for the combine backward + x_sorted remat save" (section
+// What), on one device a gather: every output row is written once, by one
+// wavefront, with a fixed summation order and no atomics.  Loads and stores
+// are 16 bytes per lane; accumulation is fp32.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(Dims d, PassArgs pa,
+                                                      const void* __restrict__ out,
+                                                      const int* __restrict__ row_of_assign,
+                                                      const float* __restrict__ gate, void* y) {
+  PassInfo pi = resolve_pass(pa);
+  if (!pi.active) return;
+  const int i = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (i >= pass_tokens(d, pi)) return;
+  const int t = pass_token(d, pi, i);
+  const int lane = lane_id();
+  // the token's rows and gates are wave-uniform (scalar loads)
+  const int* rows = row_of_assign + (size_t)t * d.k;
+  const float* gts = gate + (size_t)t * d.k;
+  if (BF16) {
+    const uint16_t* o = (const uint16_t*)out;
+    uint16_t* yr = (uint16_t*)y + (size_t)t * d.H;
+    for (int h = lane * 8; h < d.H; h += 512) {
+      float acc[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+      for (int j = 0; j < d.k; ++j) {
+        const int r = rows[j];
+        const float gj = gts[j];
+        if (r < 0) continue;
+        uint4 v = *(const uint4*)(o + (size_t)r * d.H + h);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(gj, __uint_as_float(w[q] << 16), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(gj, __uint_as_float(w[q] & 0xffff0000u), acc[2 * q + 1]);
+        }
+      }
+      uint4 outv;
+      outv.x = (uint32_t)f2bf(acc[0]) | ((uint32_t)f2bf(acc[1]) << 16);
+      outv.y = (uint32_t)f2bf(acc[2]) | ((uint32_t)f2bf(acc[3]) << 16);
+      outv.z = (uint32_t)f2bf(acc[4]) | ((uint32_t)f2bf(acc[5]) << 16);
+      outv.w = (uint32_t)f2bf(acc[6]) | ((uint32_t)f2bf(acc[7]) << 16);
+      *(uint4*)(yr + h) = outv;
+    }
+  } else {
+    const float* o = (const float*)out;
+    float* yr = (float*)y + (size_t)t * d.H;
+    for (int h = lane * 4; h < d.H; h += 256) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j = 0; j < d.k; ++j) {
+        const int r = rows[j];
+        const float gj = gts[j];
+        if (r < 0) continue;
+        float4 v = *(const float4*)(o + (size_t)r * d.H + h);
+        acc.x = fmaf(gj, v.x, acc.x);
+        acc.y = fmaf(gj, v.y, acc.y);
+        acc.z = fmaf(gj, v.z, acc.z);
+        acc.w = fmaf(gj, v.w, acc.w);
+      }
+      *(float4*)(yr + h) = acc;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Dims& d, const PassArgs& pa, const void* out,
+                          const int* row_of_assign, const float* gate, void* y,
+                          hipStream_t s) {
+  const int ntok = d.T / (pa.ovf != nullptr ? 1 : pa.n);
+  dim3 grid((ntok + 3) / 4), block(256);
+  if (d.bf16)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, s, d, pa, out, row_of_assign, gate, y);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, s, d, pa, out, row_of_assign, gate, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,99 @@
+// a1: router top-k and gates.
+//
+// The overflow check of "Support moe_dropless_fallback=layer on the ragged
+// all-to-all MoE path" (section How) works from the router's top-k.  One
+// wavefront owns one token: each lane holds E/64 logits in registers, and k
+// rounds of a wave-wide arg-max (butterfly over 64 lanes) pick the experts
+// in descending logit order, equal logits going to the lowest index.  The
+// key (value desc, index asc) is a total order over distinct indices, so
+// every lane ends each round with the same winner.
+#include "common.h"
+
+namespace moe {
+
+template <int VPL>
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T,
+                                                     int E, int k, int gate,
+                                                     int* __restrict__ idx,
+                                                     float* __restrict__ gate_out) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  float v[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    int e = i * 64 + lane;
+    v[i] = e < E ? row[e] : 0.0f;
+  }
+  unsigned taken = 0;
+  float my_v = 0.0f;
+  int my_i = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = 0.0f;
+    int bi = 0x7fffffff;  // no candidate in this lane
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      int e = i * 64 + lane;
+      bool ok = e < E && !((taken >> i) & 1u);
+      // lanes scan their logits in ascending index: strict > keeps the
+      // lowest index among equal values
+      if (ok && (bi == 0x7fffffff || v[i] > bv)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      float ov = __shfl_xor(bv, off);
+      int oi = __shfl_xor(bi, off);
+      bool take;
+      if (oi == 0x7fffffff) take = false;
+      else if (bi == 0x7fffffff) take = true;
+      else take = (ov > bv) || (ov == bv && oi < bi);
+      if (take) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == r) {
+      my_v = bv;
+      my_i = bi;
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+  }
+  float g;
+  if (gate == MOE_GATE_SOFTMAX) {
+    float l0 = __shfl(my_v, 0);
+    float z = lane < k ? __expf(my_v - l0) : 0.0f;
+    float sum = z;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+    g = z / sum;
+  } else {
+    g = 1.0f / (1.0f + __expf(-my_v));
+  }
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = my_i;
+    gate_out[(size_t)t * k + lane] = g;
+  }
+}
+
+hipError_t launch_route(const Dims& d, const float* logits, int* idx, float* gate,
+                        hipStream_t s) {
+  dim3 grid((d.T + 3) / 4), block(256);
+  int vpl = (d.E + 63) / 64;
+  if (vpl <= 1)
+    hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, s, logits, d.T, d.E, d.k, d.gate, idx, gate);
+  else if (vpl <= 2)
+    hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, s, logits, d.T, d.E, d.k, d.gate, idx, gate);
+  else if (vpl <= 4)
+    hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, s, logits, d.T, d.E, d.k, d.gate, idx, gate);
+  else if (vpl <= 8)
+    hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, s, logits, d.T, d.E, d.k, d.gate, idx, gate);
+  else
+    hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, s, logits, d.T, d.E, d.k, d.gate, idx, gate);
+  return hipGetLastError();
+}
+
+}  // namespace moe

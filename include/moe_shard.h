@@ -1,0 +1,223 @@
+/*
+ * moe_shard.h -- C ABI of the one-shard expert-parallel MoE layer on MI355X.
+ *
+ * The layer follows three maxtext pull-request pages, cited by title and
+ * section:
+ *   [DRED]     "Moe dynamic redundancy" (automated code review comments on
+ *              rerouting, dedup truncation and the duplication planner);
+ *   [FALLBACK] "Support moe_dropless_fallback=layer on the ragged all-to-all
+ *              MoE path" (sections Why, How, Shortcomings, Tests);
+ *   [RING]     "MoE ring-of-experts: TC Pallas ring all-gather for the
+ *              combine backward + x_sorted remat save" (section What).
+ *
+ * One GPU stands for one expert-parallel shard.  The all-to-all of the
+ * pages becomes local bucketing by virtual destination shard: counts and the
+ * overflow check cover every shard, while permute, grouped GEMM and combine
+ * run only for the resident shards [res_shard_lo, res_shard_hi).
+ *
+ * Conventions shared by every entry point:
+ *  - All array arguments are DEVICE pointers unless stated otherwise; the
+ *    problem struct and size outputs are host pointers.
+ *  - The caller owns every buffer.  The library allocates no device memory,
+ *    keeps no state between calls and is reentrant across streams.  Scratch
+ *    comes from the caller's workspace `ws` of `ws_bytes` bytes (256-byte
+ *    aligned), sized by moe_workspace_bytes / moe_layer_workspace_bytes.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it: nothing synchronises the host, so integer outputs
+ *    are valid once the stream reaches them.
+ *  - Errors: a negative moe_status, returned after validating every argument
+ *    on the host and before any launch.  A failed launch returns MOE_EHIP.
+ *    The library never truncates silently: too small a buffer is
+ *    MOE_ECAPACITY ([DRED], dedup truncation comment).
+ *  - Index arrays produced by moe_route are trusted by later calls; indices
+ *    outside [0, E) are skipped by the kernels (no out-of-bounds access) and
+ *    raise bit 0 of status[3].
+ *  - Layouts are row-major.  dtype MOE_BF16: x, weights, act, expert_out and
+ *    y are bfloat16 (fp32 accumulation; act, expert_out and y rounded to
+ *    nearest even); MOE_F32: all float32.  Logits and gates are float32.
+ *  - Weights are output-major with the reduction dimension contiguous:
+ *      w_gate, w_up [E_res, F, H],  w_down [E_res, H, F]
+ *    for the E_res = (res_shard_hi - res_shard_lo) * E/S resident experts,
+ *    resident expert i being global expert res_shard_lo*E/S + i.
+ *  - Slots: shard d owns slots [d*(E/S+B), (d+1)*(E/S+B)): its E/S home
+ *    experts in order, then B redundant slots ([DRED], rerouting comment:
+ *    the redundant slots are appended to the group sizes).  G = S*(E/S+B)
+ *    slots in all, G_res = (res_shard_hi-res_shard_lo)*(E/S+B) resident.
+ */
+#ifndef MOE_SHARD_H
+#define MOE_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,      /* a size, enum or pointer argument is invalid        */
+  MOE_EUNSUPPORTED = -2,/* valid problem this build does not run (see text)  */
+  MOE_ECAPACITY = -3,   /* a caller buffer or the workspace is too small      */
+  MOE_EHIP = -4         /* a HIP launch or copy failed                         */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Gate of the chosen experts.  SOFTMAX: softmax over the k chosen logits
+ * (renormalised top-k); SIGMOID: 1/(1+exp(-logit)), not normalised. */
+typedef enum { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 } moe_gate;
+
+/* How moe_layer_dropless_chunked handles the ragged buffer ([FALLBACK] How):
+ *  LAYER          overflow check; no overflow -> one capped pass, overflow ->
+ *                 one dropless pass per sequence chunk (decided on the device,
+ *                 the host never waits);
+ *  FORCE_DROPLESS one pass with the worst-case buffer (force_dropless);
+ *  CAPPED_ONLY    one capped pass that drops rows beyond the cap (the capped
+ *                 model the page's tests show diverging);
+ *  FORCE_CHUNKED  always the chunked dropless passes. */
+typedef enum {
+  MOE_MODE_LAYER = 0,
+  MOE_MODE_FORCE_DROPLESS = 1,
+  MOE_MODE_CAPPED_ONLY = 2,
+  MOE_MODE_FORCE_CHUNKED = 3
+} moe_mode;
+
+/* Statement of one layer call ([FALLBACK] Why/How: tokens, top-k, experts,
+ * EP shards, ragged buffer factor with -1 for no cap, sequence chunks;
+ * [DRED]: redundant slots per shard). */
+typedef struct {
+  int32_t tokens;          /* T = batch * seq_len                              */
+  int32_t seq_len;         /* L; chunks split every sequence, L % chunks == 0  */
+  int32_t hidden;          /* H                                                */
+  int32_t ffn;             /* F (SwiGLU inner size)                            */
+  int32_t num_experts;     /* E, global experts                                */
+  int32_t top_k;           /* k, 1 <= k <= min(E, 32)                          */
+  int32_t num_shards;      /* S virtual destination shards, E % S == 0         */
+  int32_t res_shard_lo;    /* resident shards [lo, hi), 0 <= lo < hi <= S      */
+  int32_t res_shard_hi;
+  float buffer_factor;     /* ragged_buffer_factor; <= 0 means no cap          */
+  int32_t num_chunks;      /* fallback chunks; 0 = ceil(S / factor)            */
+  int32_t gate;            /* moe_gate                                         */
+  int32_t dtype;           /* moe_dtype                                        */
+  int32_t dedup;           /* 1: one buffer row per (token, shard) ([DRED])    */
+  int32_t slots_per_shard; /* B redundant slots per shard                      */
+  int32_t num_replicas;    /* R replicas planned per call, R <= S*B; R > 0
+                              needs every shard resident (replica weights
+                              alias their home expert's weights)               */
+} moe_problem;
+
+/* Limits of this build (MOE_EUNSUPPORTED beyond them): E <= 1024,
+ * G <= 1024, T*k < 2^24.  MOE_BF16 also needs H % 256 == 0 and F % 128 == 0. */
+
+/* ---- sizes --------------------------------------------------------------- */
+
+/* Scratch bytes any single step call below may need. */
+int moe_workspace_bytes(const moe_problem* p, size_t* bytes);
+
+/* Row bounds of one pass: `num_chunks` chunks (1 = all tokens), capped or
+ * not.  *max_rows bounds the expert-sorted rows, *max_dedup_rows the dedup
+ * rows (0 without dedup).  Capped: every resident shard keeps at most cap =
+ * ceil(factor*T*k/S) buffer rows ([FALLBACK] Why); uncapped: the worst case
+ * T/n * min(k, E/S+B) rows per resident shard ([FALLBACK] How:
+ * force_dropless sizes for the worst case). */
+int moe_pass_max_rows(const moe_problem* p, int32_t num_chunks, int32_t capped,
+                      int64_t* max_rows, int64_t* max_dedup_rows);
+
+/* Workspace bytes of moe_layer_dropless_chunked in `mode` (all of its
+ * intermediate buffers, sized for the larger of the passes it may take). */
+int moe_layer_workspace_bytes(const moe_problem* p, int32_t mode, size_t* bytes);
+
+/* ---- the hot path -------------------------------------------------------- */
+
+/* a1. Router top-k ([FALLBACK] How: the check works "from the router's
+ * top-k").  logits [T,E] fp32 -> topk_idx [T,k] int32 in descending logit
+ * order, equal logits broken to the lowest index; topk_gate [T,k] fp32. */
+int moe_route(const moe_problem* p, const float* logits, int32_t* topk_idx,
+              float* topk_gate, void* stream);
+
+/* a2+a3. Counts, redundancy plan, reroute, capacity and overflow
+ * ([FALLBACK] How: _check_ragged_overflow; [DRED]: plan_expert_duplication
+ * with the has_candidate guard, tokens rerouted to the replicas).
+ * Outputs (device):
+ *   expert_counts [E]    assignments per expert;
+ *   slot_expert   [G]    global expert hosted by each slot, -1 = unused;
+ *   ndiv          [E]    assignments diverted to the expert's replica;
+ *   slot_of_assign[T*k]  slot of every assignment (the first ndiv[e]
+ *                        assignments of e in (t,j) order go to the replica);
+ *   shard_counts  [S]    rows each shard would receive (assignments, or
+ *                        distinct tokens with dedup);
+ *   status        [4]    cap (-1 = uncapped), overflow (0/1: some shard
+ *                        count > cap), max shard count, error bits.
+ * The required factor of [FALLBACK] Shortcomings is status[2] / (T*k/S). */
+int moe_count_overflow(const moe_problem* p, const int32_t* topk_idx,
+                       int32_t* expert_counts, int32_t* slot_expert, int32_t* ndiv,
+                       int32_t* slot_of_assign, int32_t* shard_counts, int32_t* status,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* a4+a5. Layout and permute of one pass: chunk `chunk` of `num_chunks`
+ * (token t = b*L + s is in chunk c when s*n/L == c; num_chunks 1 = all
+ * tokens), capped (rows past the cap of a resident shard's buffer are
+ * dropped) or not.  Rows are the pass's assignments on resident slots in
+ * stable (slot, t, j) order ([RING] What: the expert-sorted MoE input).
+ * Outputs (device):
+ *   group_offsets [G_res+1]  exclusive scan of the rows per resident slot;
+ *   row_of_assign [T*k]      row of each assignment of the pass, -1 if it is
+ *                            no row; entries of other tokens untouched;
+ *   sorted_assign [max_rows] flat assignment id t*k+j of each row;
+ *   x_sorted [max_rows, H]   x_sorted[n] = x[sorted_assign[n] / k];
+ *   with dedup ([DRED]: a token goes once to each destination shard and the
+ *   receiver re-expands it): dedup_offsets [S_res+1], dedup_token
+ *   [max_dedup_rows] (the distinct tokens of each resident shard in
+ *   ascending order, cut at the cap when capped), x_dedup [max_dedup_rows,H],
+ *   expand_idx [max_rows] (x_sorted[n] = x_dedup[expand_idx[n]]).  Without
+ *   dedup these four may be NULL.
+ * max_rows / max_dedup_rows must be at least moe_pass_max_rows' bounds. */
+int moe_permute(const moe_problem* p, int32_t num_chunks, int32_t chunk, int32_t capped,
+                const void* x, const int32_t* slot_of_assign,
+                int32_t* group_offsets, int32_t* row_of_assign, int32_t* sorted_assign,
+                int32_t* dedup_offsets, int32_t* dedup_token, int32_t* expand_idx,
+                void* x_dedup, void* x_sorted, int64_t max_rows, int64_t max_dedup_rows,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* a6. Grouped SwiGLU FFN over ragged groups ([DRED], rerouting comment: a
+ * grouped matmul over the local experts' group sizes).  Group g holds rows
+ * [group_offsets[g], group_offsets[g+1]) of x_sorted and runs the expert in
+ * resident slot g (slot_expert[res_shard_lo*(E/S+B) + g]; a replica slot
+ * uses its home expert's weights):
+ *   act[n]        = SiLU(x_sorted[n] Wg^T) * (x_sorted[n] Wu^T)   [max_rows,F]
+ *   expert_out[n] = act[n] Wd^T                                   [max_rows,H]
+ * SiLU(z) = z/(1+exp(-z)).  Rows past group_offsets[G_res] are untouched. */
+int moe_gmm_swiglu(const moe_problem* p, const void* x_sorted, const int32_t* group_offsets,
+                   const int32_t* slot_expert, const void* w_gate, const void* w_up,
+                   const void* w_down, void* act, void* expert_out, int64_t max_rows,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* a7. Gate-weighted combine of one pass: for every token t of the pass,
+ *   y[t] = sum over j ascending of topk_gate[t,j] * expert_out[row_of_assign[t*k+j]]
+ * over the assignments with a row (fp32 accumulation); 0 for a token with
+ * none (all its experts elsewhere or dropped).  Rows of other tokens of y
+ * are untouched. */
+int moe_combine(const moe_problem* p, int32_t num_chunks, int32_t chunk,
+                const void* expert_out, const int32_t* row_of_assign,
+                const float* topk_gate, void* y, void* stream);
+
+/* a8. The whole layer ([FALLBACK] How): route, counts, plan, capacity and
+ * overflow once, then the passes `mode` selects, writing y [T,H].  In LAYER
+ * mode the device picks between the capped pass and the num_chunks dropless
+ * chunk passes from the overflow flag, with no host synchronisation.
+ * info (device, may be NULL) receives [overflow, fallback_ran, cap, max
+ * shard count].  ws must hold moe_layer_workspace_bytes(p, mode). */
+int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x,
+                               const float* logits, const void* w_gate, const void* w_up,
+                               const void* w_down, void* y, int32_t* info,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Text of a status code (static storage). */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_SHARD_H */

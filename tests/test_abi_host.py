@@ -1,0 +1,118 @@
+"""Host-side checks of libmoe_shard.so (no GPU needed, no kernel launches).
+
+The library must load, export every function include/moe_shard.h declares,
+and reject invalid problems on the host with the documented status codes
+before touching the GPU.  Buffer bounds follow the pages' capacity rules.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _binding():
+    lib = os.path.join(ROOT, "grouped_gemm_shard_amd", "libmoe_shard.so")
+    if not os.path.exists(lib):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "gg_build", os.path.join(ROOT, "grouped_gemm_shard_amd", "build.py"))
+        m = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(m)
+        m.build()
+    import grouped_gemm_shard_amd as g
+    return g
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "moe_shard.h")).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(moe_\w+)\(", text, re.M)))
+
+
+def test_exports_match_header():
+    g = _binding()
+    decl = declared_functions()
+    assert sorted(g.EXPORTED) == decl
+    lib = ctypes.CDLL(g.lib_path)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def problem(**kw):
+    g = _binding()
+    base = dict(tokens=4096, seq_len=4096, hidden=1024, ffn=512, num_experts=32, top_k=4,
+                num_shards=8, res_lo=0, res_hi=8, factor=1.5, num_chunks=4)
+    base.update(kw)
+    return g.Problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tokens=0), -1), (dict(seq_len=1000), -1), (dict(num_experts=30), -1),
+    (dict(top_k=0), -1), (dict(top_k=33, num_experts=64), -2), (dict(res_lo=3, res_hi=3), -1),
+    (dict(res_hi=9), -1), (dict(num_chunks=3), -1), (dict(hidden=1000), -2),
+    (dict(ffn=100), -2), (dict(slots_per_shard=1, num_replicas=9), -1),
+    (dict(slots_per_shard=1, num_replicas=2, res_hi=4), -2),
+    (dict(num_experts=2048, num_shards=8), -2), (dict(factor=float("nan")), -1),
+    (dict(num_chunks=0, factor=1.5), -1),   # ceil(8 / 1.5) = 6 does not divide 4096
+])
+def test_invalid_problems_rejected(kw, status):
+    g = _binding()
+    with pytest.raises(g.MoeError) as ei:
+        g.layer_workspace_bytes(problem(**kw), g.MODE_LAYER)
+    assert ei.value.status == status
+
+
+def test_invalid_gate_and_mode():
+    g = _binding()
+    c = problem().c()
+    c.gate = 7
+    size = ctypes.c_size_t()
+    assert g.lib.moe_layer_workspace_bytes(ctypes.byref(c), 0, ctypes.byref(size)) == -1
+    assert g.lib.moe_layer_workspace_bytes(ctypes.byref(problem().c()), 9,
+                                           ctypes.byref(size)) == -1
+
+
+def test_null_pointers_rejected_before_launch():
+    g = _binding()
+    c = problem().c()
+    assert g.lib.moe_route(ctypes.byref(c), None, None, None, None) == -1
+    assert g.lib.moe_layer_dropless_chunked(ctypes.byref(c), 0, None, None, None, None, None,
+                                            None, None, None, 0, None) == -1
+    assert g.lib.moe_status_string(-3).decode() == "buffer or workspace too small"
+
+
+def test_pass_row_bounds():
+    g = _binding()
+    # Llama4-Maverick shard: cap = 2 * 32768 / 16 = 4096; a chunk of 4096
+    # tokens has a worst case of 4096 rows per shard, no more than the cap
+    # (the fallback page: the chunk buffer is no larger than the capped one).
+    mav = problem(tokens=32768, seq_len=8192, hidden=5120, ffn=8192, num_experts=128, top_k=1,
+                  num_shards=16, res_lo=0, res_hi=1, factor=2.0, num_chunks=8, gate="sigmoid")
+    assert g.pass_max_rows(mav, 8, 0) == (4096, 0)
+    assert g.pass_max_rows(mav, 1, 1) == (4096, 0)
+    assert g.pass_max_rows(mav, 1, 0) == (32768, 0)
+    # mid layer: capped 8 shards x 3072; a chunk of 1024 tokens x 4 rows
+    mid = problem()
+    assert g.pass_max_rows(mid, 1, 1) == (16384, 0)
+    assert g.pass_max_rows(mid, 4, 0) == (4096, 0)
+    # dedup: unique rows per shard bounded by the chunk's tokens and the cap
+    ded = problem(tokens=8192, seq_len=8192, hidden=7168, ffn=2048, num_experts=256, top_k=8,
+                  num_shards=16, res_lo=0, res_hi=16, factor=2.0, num_chunks=8, dedup=True,
+                  slots_per_shard=2, num_replicas=2)
+    assert g.pass_max_rows(ded, 1, 0) == (65536, 65536)
+    assert g.pass_max_rows(ded, 8, 0) == (8192, 8192)
+
+
+def test_layer_workspace_grows_with_uncapped_modes():
+    g = _binding()
+    p = problem()
+    capped = g.layer_workspace_bytes(p, g.MODE_CAPPED_ONLY)
+    dropless = g.layer_workspace_bytes(p, g.MODE_FORCE_DROPLESS)
+    chunked = g.layer_workspace_bytes(p, g.MODE_FORCE_CHUNKED)
+    layer = g.layer_workspace_bytes(p, g.MODE_LAYER)
+    assert chunked < capped <= dropless
+    assert layer == max(capped, chunked) or layer >= capped
+    assert g.workspace_bytes(p) > 0
