@@ -1,0 +1,274 @@
+"""Benchmark of the one-shard MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mid_bf16]
+
+A step is one call of the whole layer in LAYER mode (route, counts, plan,
+capacity and overflow check, then the capped pass or the chunked dropless
+fallback: permute, grouped SwiGLU GEMM, combine) on one batch of seeded
+synthetic input already resident in HBM.  The default workload is the mid
+bf16 layer (T=4096, H=1024, F=512, E=32, top-4, 8 virtual shards, Zipf-skewed
+routing that overflows buffer factor 1.5 and runs 4 dropless chunks).
+
+After the timed steps, the grouped GEMM, the permute and the combine of the
+same passes are timed one call at a time with HIP events on the stream they
+run on, to give achieved TFLOP/s and GB/s against MI355X peaks.  The CPU
+oracle is then timed on the host cores on the same inputs.  One JSON line is
+printed at the end.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import grouped_gemm_shard_amd as g  # noqa: E402
+import workloads  # noqa: E402
+
+METRIC = "MoE layer routed tokens/s; grouped-GEMM % MFMA peak; permute HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def pass_list(p, info):
+    """The passes LAYER mode took: chunks when the flag fired, else one
+    capped pass."""
+    if info[0]:
+        return [(p.num_chunks, c, 0) for c in range(p.num_chunks)]
+    return [(1, 0, 1)]
+
+
+def build_passes(p, w, inp, passes):
+    """Runs route / counts / permute through the step API and keeps each
+    pass's layout, so that single kernels can be timed on real data."""
+    T, k = w.tokens, w.top_k
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    g.moe_route(p, inp["logits"], idx, gate)
+    ws = torch.empty(g.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    i32 = lambda n: torch.empty(n, dtype=torch.int32, device="cuda")  # noqa: E731
+    cnt = dict(ec=i32(w.num_experts), se=i32(p.num_slots), nd=i32(w.num_experts),
+               soa=i32(T * k), sc=i32(w.num_shards), st=i32(4))
+    g.moe_count_overflow(p, idx, cnt["ec"], cnt["se"], cnt["nd"], cnt["soa"], cnt["sc"],
+                         cnt["st"], ws)
+    out = []
+    for (n, c, capped) in passes:
+        rows, drows = g.pass_max_rows(p, n, capped)
+        b = dict(n=n, c=c, capped=capped, rows=rows, ws=torch.empty_like(ws),
+                 go=i32(p.g_res + 1), roa=i32(T * k), sa=i32(rows),
+                 xs=torch.empty((rows, w.hidden), dtype=p.dtype, device="cuda"),
+                 act=torch.empty((rows, w.ffn), dtype=p.dtype, device="cuda"),
+                 out=torch.empty((rows, w.hidden), dtype=p.dtype, device="cuda"),
+                 y=torch.empty((T, w.hidden), dtype=p.dtype, device="cuda"))
+        if w.dedup:
+            b.update(do=i32(p.s_res + 1), dt=i32(drows), ex=i32(rows),
+                     xd=torch.empty((drows, w.hidden), dtype=p.dtype, device="cuda"))
+        else:
+            b.update(do=None, dt=None, ex=None, xd=None)
+        out.append(b)
+    return idx, gate, cnt, out
+
+
+def run_permute(p, inp, cnt, b):
+    g.moe_permute(p, b["n"], b["c"], b["capped"], inp["x"], cnt["soa"], b["go"], b["roa"],
+                  b["sa"], b["do"], b["dt"], b["ex"], b["xd"], b["xs"], b["ws"])
+
+
+def run_gmm(p, inp, cnt, b):
+    g.moe_gmm_swiglu(p, b["xs"], b["go"], cnt["se"], *inp["weights"], b["act"], b["out"],
+                     b["ws"])
+
+
+def run_combine(p, gate, b):
+    g.moe_combine(p, b["n"], b["c"], b["out"], b["roa"], gate, b["y"])
+
+
+def time_calls(fn, reps):
+    """Mean duration (s) of fn() over reps calls, HIP events on the current
+    stream (the stream every library call is enqueued on)."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    fn()
+    torch.cuda.synchronize()
+    for a, z in ev:
+        a.record(stream)
+        fn()
+        z.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(z) for a, z in ev) / reps / 1e3
+
+
+def kernel_figures(p, w, inp, info, reps):
+    passes = pass_list(p, info)
+    idx, gate, cnt, bufs = build_passes(p, w, inp, passes)
+    torch.cuda.synchronize()
+    es = 2 if w.bf16 else 4
+    rows = []
+    t_perm = t_gmm = t_comb = 0.0
+    for b in bufs:
+        t_perm += time_calls(lambda: run_permute(p, inp, cnt, b), reps)
+        t_gmm += time_calls(lambda: run_gmm(p, inp, cnt, b), reps)
+        t_comb += time_calls(lambda: run_combine(p, gate, b), reps)
+        rows.append(int(b["go"][-1].item()))
+    n_rows = sum(rows)
+    # algorithmic work per layer (all passes)
+    gemm_flops = 6.0 * n_rows * w.hidden * w.ffn
+    ec = cnt["ec"].cpu().numpy()
+    # weights streamed once per pass for every expert with rows in that pass
+    w_bytes = 0
+    for b in bufs:
+        go = b["go"].cpu().numpy()
+        se = cnt["se"].cpu().numpy()
+        used = set()
+        for q in range(p.g_res):
+            if go[q + 1] > go[q]:
+                used.add(int(se[w.res_lo * p.spd + q]))
+        w_bytes += len(used) * 3 * w.hidden * w.ffn * es
+    gemm_bytes = w_bytes + n_rows * (2 * w.hidden + 2 * w.ffn) * es
+    tokens_res = 0
+    for b in bufs:
+        roa = b["roa"].cpu().numpy().reshape(w.tokens, w.top_k)
+        toks = workloads_pass_tokens(w, b["n"], b["c"])
+        tokens_res += int(np.sum((roa[toks] >= 0).any(axis=1)))
+    perm_bytes = (tokens_res + n_rows) * w.hidden * es
+    comb_bytes = n_rows * w.hidden * es + w.tokens * w.hidden * es
+    del ec
+    return dict(rows=n_rows, t_gmm=t_gmm, t_perm=t_perm, t_comb=t_comb, gemm_flops=gemm_flops,
+                gemm_bytes=gemm_bytes, perm_bytes=perm_bytes, comb_bytes=comb_bytes)
+
+
+def workloads_pass_tokens(w, n, c):
+    lc = w.seq_len // n
+    b = np.arange(w.tokens // w.seq_len)[:, None] * w.seq_len
+    return (b + c * lc + np.arange(lc)[None, :]).ravel()
+
+
+def cpu_baseline(w, inp, budget_s):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=1)
+    except Exception:
+        threads = 1
+    op = oracle.Problem(**w.problem_kwargs())
+    args = (inp["logits"].cpu().numpy(), workloads.to_f64(inp["x"]),
+            *[workloads.to_f64(t) for t in inp["weights"]])
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.layer(op, oracle.MODE_LAYER, *args)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 5:
+            break
+    t = float(np.median(times))
+    return dict(value=w.tokens / t, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"whole {w.name} layer in LAYER mode, median of {len(times)} run(s), "
+                       f"{t:.2f} s each, float64 numpy")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mid_bf16", choices=sorted(workloads.CONFIGS))
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs one expert-parallel shard per "
+              "GPU and has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    w = workloads.CONFIGS[args.workload]
+    p = g.Problem(**w.problem_kwargs())
+    torch.cuda.set_device(0)
+    log(f"[bench] workload {w.name}: generating inputs")
+    inp = workloads.make_inputs(w, device="cuda")
+    run = g.LayerRunner(p, g.MODE_LAYER)
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        run(inp["x"], inp["logits"], *inp["weights"])
+    torch.cuda.synchronize()
+    info = run.info.cpu().tolist()
+    log(f"[bench] timing {args.steps} steps (overflow={info[0]} fallback={info[1]})")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run(inp["x"], inp["logits"], *inp["weights"])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) / args.steps * 1e3
+    tokens_s = w.tokens / (ms / 1e3)
+
+    log("[bench] per-kernel timing")
+    kf = kernel_figures(p, w, inp, info, args.kernel_reps)
+    peak_mm = PEAK_BF16_TFLOPS if w.bf16 else PEAK_FP32_TFLOPS
+    gemm_tflops = kf["gemm_flops"] / kf["t_gmm"] / 1e12
+    gemm_gbs = kf["gemm_bytes"] / kf["t_gmm"] / 1e9
+    ai = kf["gemm_flops"] / kf["gemm_bytes"]
+    gemm_bound = "mfma" if ai * PEAK_HBM_GBS / 1e3 >= peak_mm else "hbm"
+    perm_gbs = kf["perm_bytes"] / kf["t_perm"] / 1e9
+    comb_gbs = kf["comb_bytes"] / kf["t_comb"] / 1e9
+    if gemm_bound == "mfma":
+        roof = dict(bound="mfma", achieved=round(gemm_tflops, 2), peak=peak_mm, unit="TFLOP/s",
+                    frac=round(gemm_tflops / peak_mm, 4), traffic=None)
+    else:
+        roof = dict(bound="hbm", achieved=round(gemm_gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(gemm_gbs / PEAK_HBM_GBS, 4), traffic=None)
+    roof["kernel"] = "grouped SwiGLU GEMM (gate/up + down launches), per layer"
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(w, inp, args.cpu_budget)
+
+    res = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.bf16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.tokens, "hidden": w.hidden, "ffn": w.ffn,
+                   "experts": w.num_experts, "top_k": w.top_k, "shards": w.num_shards,
+                   "buffer_factor": w.factor, "chunks": w.num_chunks, "mode": "LAYER",
+                   "fallback_ran": int(info[1])},
+        "gemm": {"tflops": round(gemm_tflops, 2), "frac_mfma_peak": round(gemm_tflops / peak_mm, 4),
+                 "gbs": round(gemm_gbs, 1), "arith_intensity": round(ai, 1),
+                 "us_per_layer": round(kf["t_gmm"] * 1e6, 2), "rows": kf["rows"]},
+        "permute": {"gbs": round(perm_gbs, 1), "frac_hbm_peak": round(perm_gbs / PEAK_HBM_GBS, 4),
+                    "us_per_layer": round(kf["t_perm"] * 1e6, 2)},
+        "combine": {"gbs": round(comb_gbs, 1), "frac_hbm_peak": round(comb_gbs / PEAK_HBM_GBS, 4),
+                    "us_per_layer": round(kf["t_comb"] * 1e6, 2)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -3,8 +3,9 @@
 Argument marshalling only: every step of the layer runs in the library's
 HIP kernels.  Tensors are torch tensors on the GPU (torch provides device
 memory and the current stream); the names mirror the C ABI in
-include/moe_shard.h.  Importing fails loudly when the library has not been
-built (``python -m grouped_gemm_shard_amd.build``); there is no fallback.
+include/moe_shard.h.  The library is loaded on first use, and that use fails
+loudly when it has not been built (``python -m grouped_gemm_shard_amd.build``);
+there is no fallback.
 """
 
 from __future__ import annotations
@@ -129,11 +130,26 @@ def _load():
     return L
 
 
-lib = _load()
+_LIB = None
+
+
+def _lib():
+    """The loaded library (loaded on first use, so that the build module can
+    run before a library exists)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def __getattr__(name):
+    if name == "lib":
+        return _lib()
+    raise AttributeError(name)
 
 
 def status_string(status: int) -> str:
-    return lib.moe_status_string(status).decode()
+    return _lib().moe_status_string(status).decode()
 
 
 def _check(fn: str, status: int):
@@ -162,20 +178,20 @@ def _stream(stream):
 
 def workspace_bytes(p: Problem) -> int:
     out = ctypes.c_size_t()
-    _check("moe_workspace_bytes", lib.moe_workspace_bytes(ctypes.byref(p.c()), ctypes.byref(out)))
+    _check("moe_workspace_bytes", _lib().moe_workspace_bytes(ctypes.byref(p.c()), ctypes.byref(out)))
     return out.value
 
 
 def layer_workspace_bytes(p: Problem, mode: int) -> int:
     out = ctypes.c_size_t()
     _check("moe_layer_workspace_bytes",
-           lib.moe_layer_workspace_bytes(ctypes.byref(p.c()), mode, ctypes.byref(out)))
+           _lib().moe_layer_workspace_bytes(ctypes.byref(p.c()), mode, ctypes.byref(out)))
     return out.value
 
 
 def pass_max_rows(p: Problem, num_chunks: int, capped: int):
     r, u = ctypes.c_int64(), ctypes.c_int64()
-    _check("moe_pass_max_rows", lib.moe_pass_max_rows(ctypes.byref(p.c()), num_chunks, capped,
+    _check("moe_pass_max_rows", _lib().moe_pass_max_rows(ctypes.byref(p.c()), num_chunks, capped,
                                                       ctypes.byref(r), ctypes.byref(u)))
     return r.value, u.value
 
@@ -186,7 +202,7 @@ def _ws(ws):
 
 
 def moe_route(p: Problem, logits, topk_idx, topk_gate, stream=None):
-    _check("moe_route", lib.moe_route(ctypes.byref(p.c()), _ptr(logits, torch.float32, "logits"),
+    _check("moe_route", _lib().moe_route(ctypes.byref(p.c()), _ptr(logits, torch.float32, "logits"),
                                       _ptr(topk_idx, torch.int32, "topk_idx"),
                                       _ptr(topk_gate, torch.float32, "topk_gate"), _stream(stream)))
 
@@ -195,7 +211,7 @@ def moe_count_overflow(p: Problem, topk_idx, expert_counts, slot_expert, ndiv, s
                        shard_counts, status, ws, stream=None):
     w, nb = _ws(ws)
     i32 = torch.int32
-    _check("moe_count_overflow", lib.moe_count_overflow(
+    _check("moe_count_overflow", _lib().moe_count_overflow(
         ctypes.byref(p.c()), _ptr(topk_idx, i32, "topk_idx"),
         _ptr(expert_counts, i32, "expert_counts"), _ptr(slot_expert, i32, "slot_expert"),
         _ptr(ndiv, i32, "ndiv"), _ptr(slot_of_assign, i32, "slot_of_assign"),
@@ -210,7 +226,7 @@ def moe_permute(p: Problem, num_chunks, chunk, capped, x, slot_of_assign, group_
     i32 = torch.int32
     max_rows = x_sorted.shape[0]
     max_dedup = x_dedup.shape[0] if x_dedup is not None else 0
-    _check("moe_permute", lib.moe_permute(
+    _check("moe_permute", _lib().moe_permute(
         ctypes.byref(p.c()), num_chunks, chunk, capped, _ptr(x, p.dtype, "x"),
         _ptr(slot_of_assign, i32, "slot_of_assign"), _ptr(group_offsets, i32, "group_offsets"),
         _ptr(row_of_assign, i32, "row_of_assign"), _ptr(sorted_assign, i32, "sorted_assign"),
@@ -224,7 +240,7 @@ def moe_gmm_swiglu(p: Problem, x_sorted, group_offsets, slot_expert, w_gate, w_u
     w, nb = _ws(ws)
     i32 = torch.int32
     max_rows = min(x_sorted.shape[0], act.shape[0], expert_out.shape[0])
-    _check("moe_gmm_swiglu", lib.moe_gmm_swiglu(
+    _check("moe_gmm_swiglu", _lib().moe_gmm_swiglu(
         ctypes.byref(p.c()), _ptr(x_sorted, p.dtype, "x_sorted"),
         _ptr(group_offsets, i32, "group_offsets"), _ptr(slot_expert, i32, "slot_expert"),
         _ptr(w_gate, p.dtype, "w_gate"), _ptr(w_up, p.dtype, "w_up"),
@@ -234,7 +250,7 @@ def moe_gmm_swiglu(p: Problem, x_sorted, group_offsets, slot_expert, w_gate, w_u
 
 def moe_combine(p: Problem, num_chunks, chunk, expert_out, row_of_assign, topk_gate, y,
                 stream=None):
-    _check("moe_combine", lib.moe_combine(
+    _check("moe_combine", _lib().moe_combine(
         ctypes.byref(p.c()), num_chunks, chunk, _ptr(expert_out, p.dtype, "expert_out"),
         _ptr(row_of_assign, torch.int32, "row_of_assign"),
         _ptr(topk_gate, torch.float32, "topk_gate"), _ptr(y, p.dtype, "y"), _stream(stream)))
@@ -243,7 +259,7 @@ def moe_combine(p: Problem, num_chunks, chunk, expert_out, row_of_assign, topk_g
 def moe_layer_dropless_chunked(p: Problem, mode, x, logits, w_gate, w_up, w_down, y, info, ws,
                                stream=None):
     w, nb = _ws(ws)
-    _check("moe_layer_dropless_chunked", lib.moe_layer_dropless_chunked(
+    _check("moe_layer_dropless_chunked", _lib().moe_layer_dropless_chunked(
         ctypes.byref(p.c()), mode, _ptr(x, p.dtype, "x"), _ptr(logits, torch.float32, "logits"),
         _ptr(w_gate, p.dtype, "w_gate"), _ptr(w_up, p.dtype, "w_up"),
         _ptr(w_down, p.dtype, "w_down"), _ptr(y, p.dtype, "y"),

@@ -81,6 +81,9 @@ int make_dims(const moe_problem* p, Dims* d) {
   if (n == 0) n = f > 0.0 ? (int)ceil((double)d->S / f) : 1;
   if (n < 1 || n > d->L || d->L % n != 0) return MOE_EINVAL;
   d->n_default = n;
+  // tall tiles halve the operand traffic per flop where the reduction is
+  // long; short ones waste less on small groups
+  d->gemm_bm = d->H >= 2048 ? 256 : 128;
   return MOE_OK;
 }
 
@@ -194,8 +197,8 @@ int run_pass(const Dims& d, const PassArgs& pa, const void* x, const void* wg, c
                                 w.sorted_assign, w.dedup_offsets, w.dedup_token, w.expand_idx,
                                 w.x_dedup, w.x_sorted, s);
   if (e != hipSuccess) return MOE_EHIP;
-  e = launch_gmm(d, pa, w.x_sorted, w.group_offsets, pb.tile_off, w.slot_expert, wg, wu, wd,
-                 w.act, w.out, rows, nullptr, s);
+  e = launch_gmm(d, pa, w.x_sorted, w.group_offsets, pb.tile_off, pb.tile_group, w.slot_expert,
+                 wg, wu, wd, w.act, w.out, rows, nullptr, s);
   if (e != hipSuccess) return MOE_EHIP;
   e = launch_combine(d, pa, w.out, w.row_of_assign, w.topk_gate, y, s);
   return hip_status(e);
@@ -308,8 +311,9 @@ int moe_gmm_swiglu(const moe_problem* p, const void* x_sorted, const int32_t* gr
   if (max_rows >= (1ll << 31) / 2) return MOE_EUNSUPPORTED;
   if (ws_bytes < gmm_scratch_bytes(d)) return MOE_ECAPACITY;
   PassArgs pa{1, 0, 0, nullptr};
-  return hip_status(launch_gmm(d, pa, x_sorted, group_offsets, nullptr, slot_expert, w_gate, w_up,
-                               w_down, act, expert_out, max_rows, ws, (hipStream_t)stream));
+  return hip_status(launch_gmm(d, pa, x_sorted, group_offsets, nullptr, nullptr, slot_expert,
+                               w_gate, w_up, w_down, act, expert_out, max_rows, ws,
+                               (hipStream_t)stream));
 }
 
 int moe_combine(const moe_problem* p, int32_t num_chunks, int32_t chunk, const void* expert_out,

@@ -17,7 +17,7 @@ constexpr int kMaxSlots = 1024;     // G limit (keys of the slot sort)
 constexpr int kMaxExperts = 1024;   // E limit (route keeps E/64 logits per lane)
 constexpr int kMaxTopK = 32;        // one lane per chosen expert in route/combine
 constexpr int kSortBlocks = 64;     // blocks of the stable counting sort
-constexpr int kGemmBM = 128;        // rows per grouped-GEMM tile
+constexpr int kGemmBMMin = 128;     // smallest grouped-GEMM tile height
 
 // Problem dimensions, derived once on the host and passed by value.
 struct Dims {
@@ -33,6 +33,7 @@ struct Dims {
   int gate, bf16, dedup;
   int cap;       // ceil(factor*T*k/S), -1 when uncapped
   int n_default; // chunks of the fallback
+  int gemm_bm;   // grouped-GEMM tile height (128 or 256)
 };
 
 // One pass of the permute / GEMM / combine sequence.  Static passes carry
@@ -87,6 +88,19 @@ __device__ __forceinline__ float bf2f(uint16_t h) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// accesses, not for its global loads, so prefetches stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Capacity of the m-tile -> group map: rows never exceed T*k.
+__host__ __device__ __forceinline__ int tile_map_len(const Dims& d) {
+  return (int)(((long long)d.T * d.k) / kGemmBMMin) + d.G_res + 1;
+}
+
 __device__ __forceinline__ unsigned long long lanemask_lt() {
   int l = lane_id();
   return l == 0 ? 0ull : (~0ull >> (64 - l));
@@ -114,7 +128,8 @@ struct PassBuffers {
   int* bh_dedup;       // [kSortBlocks * S_res]
   int* kept;           // [G_res] kept rows per slot
   int* dedup_kept;     // [S_res]
-  int* tile_off;       // [G_res + 1] m-tiles (kGemmBM) prefix
+  int* tile_off;       // [G_res + 1] m-tile prefix (tile height gemm_bm)
+  int* tile_group;     // [tile_map_len] group of every m-tile
   int* meta;           // [8]: rows, dedup rows, ...
 };
 size_t pass_scratch_bytes(const Dims& d);
@@ -126,10 +141,12 @@ hipError_t launch_permute(const Dims& d, const PassArgs& pa, const void* x,
                           int* dedup_offsets, int* dedup_token, int* expand_idx,
                           void* x_dedup, void* x_sorted, hipStream_t s);
 
-// Grouped GEMM.  tile_off may be null: it is then computed into scratch.
+// Grouped GEMM.  tile_off / tile_group may be null: they are then computed
+// into scratch from group_offsets.
 size_t gmm_scratch_bytes(const Dims& d);
 hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const void* x_sorted,
-                      const int* group_offsets, const int* tile_off, const int* slot_expert,
+                      const int* group_offsets, const int* tile_off, const int* tile_group,
+                      const int* slot_expert,
                       const void* wg, const void* wu, const void* wd, void* act, void* out,
                       int64_t max_rows, void* scratch, hipStream_t s);
 

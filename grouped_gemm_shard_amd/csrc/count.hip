@@ -138,8 +138,8 @@ __global__ __launch_bounds__(64) void reroute_rank_kernel(Dims d, const int* __r
 }
 
 __global__ __launch_bounds__(1024) void reroute_scan_kernel(int K, int* bh) {
-  int q = threadIdx.x;
-  if (q < K) scan_key_over_blocks(bh, K, q);
+  __shared__ int totals[kMaxSlots];
+  scan_keys_over_blocks(bh, K, totals);
 }
 
 // slot_of_assign: home slot, or the replica slot for the first ndiv[e]

@@ -6,31 +6,41 @@
 // FFN itself is SwiGLU: act = SiLU(x Wg^T) * (x Wu^T), out = act Wd^T.
 //
 // bf16 path: two launches per pass.
-//  * GEMM1 (x_sorted [N,H] against Wg and Wu [F,H]): a 128-row tile computes
-//    128 act columns as 128 gate + 128 up columns held side by side in one
-//    256-row weight tile, so the SwiGLU epilogue finds the gate and up value
-//    of an element in the same lane and register.
-//  * GEMM2 (act [N,F] against Wd [H,F]): a 128 x 256 output tile.
+//  * GEMM1 (x_sorted [N,H] against Wg and Wu [F,H]): a tile computes 128 act
+//    columns as 128 gate + 128 up columns held side by side in one 256-row
+//    weight tile, so the SwiGLU epilogue finds the gate and up value of an
+//    element in the same lane and register.
+//  * GEMM2 (act [N,F] against Wd [H,F]): a BM x 256 output tile.
 // Both use v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  256 threads =
-// 4 waves in a 2 x 2 grid, each wave a 64 x 128 slice = 2 x 4 MFMA tiles.
-// K advances 64 per step through double-buffered LDS (rows padded to 72
-// bf16 so that the 16-byte fragment reads of 32 consecutive rows spread
-// over the banks); the next step's global loads are in flight while the
-// current step's MFMAs run.
+// 4 waves in a 2 x 2 grid, each wave a (BM/2) x 128 slice of 32 x 32 MFMA
+// tiles.
 //
-// Tiles: every group owns ceil(rows/128) m-tiles (an exclusive scan over
-// groups, computed with the layout), so empty groups cost nothing; a block
-// finds its group by binary search over the scan.
+// Operands go from HBM straight into LDS (buffer_load ... lds, 16 bytes per
+// lane, no staging registers) through a ring of NST stages of BK columns, so
+// NST-1 stages of loads are in flight while one is multiplied: the loads of
+// a weight-streaming GEMM need far more bytes in flight per CU than one
+// stage gives.  Two shapes:
+//   BM=128, BK=64, 3 stages (147 KB LDS): small groups, weight streaming;
+//   BM=256, BK=32, 4 stages (128 KB LDS): long reductions, half the operand
+//   traffic per flop.
+// In LDS each row of a stage holds BK bf16 as 16-byte chunks whose order is
+// XOR-permuted by row, so the fragment reads of 8 or 16 consecutive rows at
+// one chunk hit distinct banks.  Rows of A past the group read as zero (the
+// buffer's byte range ends at the group), and their results are not stored.
+//
+// Tiles: every group owns ceil(rows/BM) m-tiles (an exclusive scan over
+// groups, with an m-tile -> group map, computed with the layout), so empty
+// groups cost nothing.  Logical tile L = nt * m_tiles + mt: neighbours share
+// a weight panel.  Workgroups are dispatched round-robin over the 8 XCDs,
+// so each XCD is given a contiguous range of L and its L2 serves the panel
+// to all of that range's m-tiles.
 #include "common.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int BM = kGemmBM;  // 128
-constexpr int BNB = 256;     // weight rows per tile
-constexpr int BK = 64;
-constexpr int LDK = BK + 8;  // padded LDS row (bf16 elements)
+constexpr int BNB = 256;  // weight rows per tile
 
 struct GemmParams {
   const uint16_t* A;
@@ -40,132 +50,179 @@ struct GemmParams {
   uint16_t* C;
   const int* group_offsets;
   const int* tile_off;
+  const int* tile_group;
   const int* slot_expert;
   int G, K, Nout, lo_slot, e_base, e_res, n_ntiles;
   long long max_rows;
   PassArgs pa;
 };
 
-template <bool SWIGLU>
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  // raw buffer: loads at offsets >= bytes return zero
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Chunk permutation of LDS row `row`: distinct for the rows a fragment read
+// services together, with 32 or with 64 banks.
+template <int BK>
+__device__ __forceinline__ int swz(int row) {
+  if (BK == 64) return ((row >> 1) ^ ((row & 1) << 2)) & 7;
+  return ((row >> 1) ^ (row >> 3)) & 3;
+}
+
+// Waits until at most N of this wave's loads are outstanding, then joins
+// the workgroup barrier.  The memory clobber keeps the compiler from moving
+// LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Starts the loads of K step `step` into its ring stage: each wave-wide
+// load fills RPI consecutive rows (1 KB) of the stage.
+template <int BM, int BK, int NST, bool SWIGLU>
+__device__ __forceinline__ void gmm_issue(char* smem, int step, int w,
+                                          __amdgpu_buffer_rsrc_t ra_r, __amdgpu_buffer_rsrc_t rb0,
+                                          __amdgpu_buffer_rsrc_t rb1,
+                                          const int (&a_off)[BM / (1024 / (BK * 2)) / 4],
+                                          const int (&b_off)[BNB / (1024 / (BK * 2)) / 4]) {
+  constexpr int RB = BK * 2, RPI = 1024 / RB;
+  constexpr int AI = BM / RPI / 4, BI = BNB / RPI / 4;
+  constexpr int SA = BM * RB, SS = (BM + BNB) * RB;
+  char* st = smem + (step % NST) * SS;
+  const int kb = step * BK * 2;
+#pragma unroll
+  for (int i = 0; i < AI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_r, (lds_void*)(st + (i * 4 + w) * RPI * RB), 16,
+                                             a_off[i], kb, 0, 0);
+#pragma unroll
+  for (int i = 0; i < BI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(SWIGLU && i >= BI / 2 ? rb1 : rb0,
+                                             (lds_void*)(st + SA + (i * 4 + w) * RPI * RB), 16,
+                                             b_off[i], kb, 0, 0);
+}
+
+template <int BM, int BK, int NST, bool SWIGLU>
 __global__ __launch_bounds__(256, 1) void gmm_bf16_kernel(GemmParams P) {
+  constexpr int RB = BK * 2;          // LDS bytes per row of a stage
+  constexpr int CPR = BK / 8;         // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;      // rows one wave-wide load fills
+  constexpr int AI = BM / RPI / 4;    // A loads per wave per stage
+  constexpr int BI = BNB / RPI / 4;   // B loads per wave per stage
+  constexpr int LPS = AI + BI;
+  constexpr int SA = BM * RB, SS = (BM + BNB) * RB;
+  constexpr int MI = BM / 64;         // 32-row MFMA tiles per wave
+  static_assert(NST >= 2 && NST <= 4, "stages");
+
   PassInfo pi = resolve_pass(P.pa);
   if (!pi.active) return;
   const int total_mt = P.tile_off[P.G];
   if (P.group_offsets[P.G] > P.max_rows) return;  // malformed offsets: touch nothing
-  const int mt = blockIdx.x / P.n_ntiles;
-  const int nt = blockIdx.x - mt * P.n_ntiles;
-  if (mt >= total_mt) return;
-  int lo = 0, hi = P.G;
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (P.tile_off[mid] <= mt) lo = mid;
-    else hi = mid;
-  }
-  const int g = lo;
+  const int total = total_mt * P.n_ntiles;
+  const int per_xcd = (total + 7) >> 3;
+  const int bid = blockIdx.x;
+  if ((bid >> 3) >= per_xcd) return;
+  const int L = (bid & 7) * per_xcd + (bid >> 3);
+  if (L >= total) return;
+  const int nt = L / total_mt;
+  const int mt = L - nt * total_mt;
+  const int g = P.tile_group[mt];
+  const int gend = P.group_offsets[g + 1];
   const int row0 = P.group_offsets[g] + (mt - P.tile_off[g]) * BM;
-  const int rows = min(BM, P.group_offsets[g + 1] - row0);
+  if (row0 < 0 || row0 >= gend || gend > P.max_rows) return;
+  const int rows = min(BM, gend - row0);
   const int e = P.slot_expert[P.lo_slot + g] - P.e_base;
   if (e < 0 || e >= P.e_res) return;  // rows in a slot that hosts no resident expert
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BNB * LDK];
+  __shared__ __attribute__((aligned(1024))) char smem[NST * SS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
+  const int K = P.K;
+  const int KT = K / BK;
 
-  const uint16_t* a_src[4];
-  int a_dst[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int c = tid + i * 256, r = c >> 3, kc = c & 7;
-    int rr = r < rows ? r : rows - 1;  // rows past the group repeat its last row
-    a_src[i] = P.A + (size_t)(row0 + rr) * P.K + kc * 8;
-    a_dst[i] = r * LDK + kc * 8;
+  const __amdgpu_buffer_rsrc_t ra_r =
+      make_rsrc(P.A + (size_t)row0 * K, (unsigned)rows * K * 2);
+  __amdgpu_buffer_rsrc_t rb0, rb1;
+  if (SWIGLU) {
+    rb0 = make_rsrc(P.B0 + (size_t)e * P.b_stride + (size_t)nt * 128 * K, 128u * K * 2);
+    rb1 = make_rsrc(P.B1 + (size_t)e * P.b_stride + (size_t)nt * 128 * K, 128u * K * 2);
+  } else {
+    rb0 = make_rsrc(P.B0 + (size_t)e * P.b_stride + (size_t)nt * 256 * K, 256u * K * 2);
+    rb1 = rb0;
   }
-  const uint16_t* b_src[8];
-  int b_dst[8];
+  // global byte offsets of this lane's chunk in each of its loads
+  int a_off[AI], b_off[BI];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int c = tid + i * 256, r = c >> 3, kc = c & 7;
-    const uint16_t* base;
-    int wr;
-    if (SWIGLU) {
-      base = r < 128 ? P.B0 : P.B1;
-      wr = nt * 128 + (r & 127);
-    } else {
-      base = P.B0;
-      wr = nt * 256 + r;
-    }
-    b_src[i] = base + (size_t)e * P.b_stride + (size_t)wr * P.K + kc * 8;
-    b_dst[i] = r * LDK + kc * 8;
+  for (int i = 0; i < AI; ++i) {
+    int row = (i * 4 + w) * RPI + lane / CPR;
+    a_off[i] = row * K * 2 + (((lane % CPR) ^ swz<BK>(row)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    int row = (i * 4 + w) * RPI + lane / CPR;
+    int wr = SWIGLU ? (row & 127) : row;
+    b_off[i] = wr * K * 2 + (((lane % CPR) ^ swz<BK>(row)) << 4);
   }
 
-  uint4 ra[4], rb[8];
-  floatx16 acc[2][4];
+  // fragment read offsets (bytes within a stage) for chunk kc of each row
+  int a_row[MI], b_row[4];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < MI; ++mi) a_row[mi] = wm * (BM / 2) + mi * 32 + (lane & 31);
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni)
+    b_row[ni] = (SWIGLU ? ((ni >> 1) * 128 + wn * 64 + (ni & 1) * 32) : (wn * 128 + ni * 32)) +
+                (lane & 31);
+
+  floatx16 acc[MI][4];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.0f;
 
-  const int KT = P.K / BK;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ra[i] = *(const uint4*)(a_src[i]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) rb[i] = *(const uint4*)(b_src[i]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *(uint4*)&As[0][a_dst[i]] = ra[i];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) *(uint4*)&Bs[0][b_dst[i]] = rb[i];
-  __syncthreads();
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < KT) gmm_issue<BM, BK, NST, SWIGLU>(smem, s, w, ra_r, rb0, rb1, a_off, b_off);
 
   for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      const int k0 = (kt + 1) * BK;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ra[i] = *(const uint4*)(a_src[i] + k0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) rb[i] = *(const uint4*)(b_src[i] + k0);
-    }
-    const uint16_t* as = As[buf];
-    const uint16_t* bs = Bs[buf];
+    const int ahead = min(KT - 1 - kt, NST - 2);  // stages allowed to stay in flight
+    if (ahead >= 2) vm_wait_barrier<2 * LPS>();
+    else if (ahead == 1) vm_wait_barrier<LPS>();
+    else vm_wait_barrier<0>();
+    if (kt + NST - 1 < KT)
+      gmm_issue<BM, BK, NST, SWIGLU>(smem, kt + NST - 1, w, ra_r, rb0, rb1, a_off, b_off);
+    const char* sa = smem + (kt % NST) * SS;
+    const char* sb = sa + SA;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const int kof = ks * 16 + (lane >> 5) * 8;
-      bf16x8 a[2], b[4];
+      const int kc = ks * 2 + (lane >> 5);
+      bf16x8 a[MI], b[4];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        a[mi] = *(const bf16x8*)&as[(wm * 64 + mi * 32 + (lane & 31)) * LDK + kof];
+      for (int mi = 0; mi < MI; ++mi)
+        a[mi] = *(const bf16x8*)(sa + a_row[mi] * RB + ((kc ^ swz<BK>(a_row[mi])) << 4));
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        int brow = SWIGLU ? ((ni >> 1) * 128 + wn * 64 + (ni & 1) * 32) : (wn * 128 + ni * 32);
-        b[ni] = *(const bf16x8*)&bs[(brow + (lane & 31)) * LDK + kof];
-      }
+      for (int ni = 0; ni < 4; ++ni)
+        b[ni] = *(const bf16x8*)(sb + b_row[ni] * RB + ((kc ^ swz<BK>(b_row[ni])) << 4));
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
     }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *(uint4*)&As[buf ^ 1][a_dst[i]] = ra[i];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) *(uint4*)&Bs[buf ^ 1][b_dst[i]] = rb[i];
-    }
-    __syncthreads();
   }
 
   // 32x32 accumulator layout: register q of a lane holds row
   // (q/4)*8 + (lane/32)*4 + q%4, column lane%32.
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
+  for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int lr = wm * 64 + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+      const int lr = wm * (BM / 2) + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
       if (lr >= rows) continue;
       uint16_t* crow = P.C + (size_t)(row0 + lr) * P.Nout;
       if (SWIGLU) {
@@ -229,15 +286,29 @@ __global__ __launch_bounds__(256) void gmm_f32_kernel(F32Params P) {
   }
 }
 
-// m-tile offsets from group offsets (standalone grouped GEMM calls).
-__global__ __launch_bounds__(1024) void tile_schedule_kernel(int G, const int* group_offsets,
-                                                             int* tile_off, PassArgs pa) {
+// m-tile offsets and the m-tile -> group map from group offsets (standalone
+// grouped GEMM calls).  Offsets that are not a non-decreasing sequence
+// within [0, min(max_rows, T*k)] give no tiles at all.
+__global__ __launch_bounds__(1024) void tile_schedule_kernel(int G, int bm, int limit,
+                                                             const int* group_offsets,
+                                                             int* tile_off, int* tile_group,
+                                                             PassArgs pa) {
   PassInfo pi = resolve_pass(pa);
   if (!pi.active) return;
   __shared__ int tmp[16];
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   int g = threadIdx.x;
-  int v = g < G ? (group_offsets[g + 1] - group_offsets[g] + BM - 1) / BM : 0;
+  int v = 0;
+  if (g < G) {
+    int a = group_offsets[g], b = group_offsets[g + 1];
+    if (a < 0 || b < a || b > limit) bad = 1;
+    v = (b - a + bm - 1) / bm;
+  }
+  __syncthreads();
+  if (bad) v = 0;
   int x = v;
   for (int off = 1; off < 64; off <<= 1) {
     int y = __shfl_up(x, off);
@@ -255,57 +326,83 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(int G, const int* g
   }
   __syncthreads();
   int ex = (w > 0 ? tmp[w - 1] : 0) + x - v;
-  if (g < G) tile_off[g] = ex;
+  if (g < G) {
+    tile_off[g] = ex;
+    for (int m = 0; m < v; ++m) tile_group[ex + m] = g;
+  }
   if (g == 0) tile_off[G] = tmp[nw - 1];
+}
+
+template <int BM, int BK, int NST>
+void launch_bf16(const Dims& d, const PassArgs& pa, const void* x_sorted,
+                 const int* group_offsets, const int* toff, const int* tgroup,
+                 const int* slot_expert, const void* wg, const void* wu, const void* wd,
+                 void* act, void* out, int64_t max_rows, hipStream_t s) {
+  const long long mt_ub = (max_rows + BM - 1) / BM + d.G_res;
+  GemmParams p1;
+  p1.A = (const uint16_t*)x_sorted;
+  p1.B0 = (const uint16_t*)wg;
+  p1.B1 = (const uint16_t*)wu;
+  p1.b_stride = (size_t)d.F * d.H;
+  p1.C = (uint16_t*)act;
+  p1.group_offsets = group_offsets;
+  p1.tile_off = toff;
+  p1.tile_group = tgroup;
+  p1.slot_expert = slot_expert;
+  p1.G = d.G_res;
+  p1.K = d.H;
+  p1.Nout = d.F;
+  p1.lo_slot = d.lo_slot;
+  p1.e_base = d.e_base;
+  p1.e_res = d.S_res * d.El;
+  p1.max_rows = max_rows;
+  p1.n_ntiles = d.F / 128;
+  p1.pa = pa;
+  const long long g1 = (mt_ub * p1.n_ntiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, true>), dim3((unsigned)g1), dim3(256), 0, s, p1);
+  GemmParams p2 = p1;
+  p2.A = (const uint16_t*)act;
+  p2.B0 = (const uint16_t*)wd;
+  p2.B1 = nullptr;
+  p2.b_stride = (size_t)d.H * d.F;
+  p2.C = (uint16_t*)out;
+  p2.K = d.F;
+  p2.Nout = d.H;
+  p2.n_ntiles = d.H / 256;
+  const long long g2 = (mt_ub * p2.n_ntiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, false>), dim3((unsigned)g2), dim3(256), 0, s, p2);
 }
 
 }  // namespace
 
-size_t gmm_scratch_bytes(const Dims& d) { return ((size_t)(d.G_res + 1) * 4 + 255) / 256 * 256; }
+size_t gmm_scratch_bytes(const Dims& d) {
+  return ((size_t)(d.G_res + 1) * 4 + 255) / 256 * 256 +
+         ((size_t)tile_map_len(d) * 4 + 255) / 256 * 256;
+}
 
 hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const void* x_sorted,
-                      const int* group_offsets, const int* tile_off, const int* slot_expert,
-                      const void* wg, const void* wu, const void* wd, void* act, void* out,
-                      int64_t max_rows, void* scratch, hipStream_t s) {
+                      const int* group_offsets, const int* tile_off, const int* tile_group,
+                      const int* slot_expert, const void* wg, const void* wu, const void* wd,
+                      void* act, void* out, int64_t max_rows, void* scratch, hipStream_t s) {
   if (d.bf16) {
-    int* toff = (int*)tile_off;
-    if (toff == nullptr) {
-      toff = (int*)scratch;
-      hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, d.G_res, group_offsets,
-                         toff, pa);
+    const int* toff = tile_off;
+    const int* tgroup = tile_group;
+    if (toff == nullptr || tgroup == nullptr) {
+      int* t0 = (int*)scratch;
+      int* t1 = (int*)((char*)scratch + ((size_t)(d.G_res + 1) * 4 + 255) / 256 * 256);
+      long long lim = (long long)d.T * d.k;
+      if (max_rows < lim) lim = max_rows;
+      hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, d.G_res, d.gemm_bm,
+                         (int)lim, group_offsets, t0, t1, pa);
+      toff = t0;
+      tgroup = t1;
     }
-    const long long mt_ub = (max_rows + BM - 1) / BM + d.G_res;
-    GemmParams p1;
-    p1.A = (const uint16_t*)x_sorted;
-    p1.B0 = (const uint16_t*)wg;
-    p1.B1 = (const uint16_t*)wu;
-    p1.b_stride = (size_t)d.F * d.H;
-    p1.C = (uint16_t*)act;
-    p1.group_offsets = group_offsets;
-    p1.tile_off = toff;
-    p1.slot_expert = slot_expert;
-    p1.G = d.G_res;
-    p1.K = d.H;
-    p1.Nout = d.F;
-    p1.lo_slot = d.lo_slot;
-    p1.e_base = d.e_base;
-    p1.e_res = d.S_res * d.El;
-    p1.max_rows = max_rows;
-    p1.n_ntiles = d.F / 128;
-    p1.pa = pa;
-    hipLaunchKernelGGL(gmm_bf16_kernel<true>, dim3((unsigned)(mt_ub * p1.n_ntiles)), dim3(256), 0,
-                       s, p1);
-    GemmParams p2 = p1;
-    p2.A = (const uint16_t*)act;
-    p2.B0 = (const uint16_t*)wd;
-    p2.B1 = nullptr;
-    p2.b_stride = (size_t)d.H * d.F;
-    p2.C = (uint16_t*)out;
-    p2.K = d.F;
-    p2.Nout = d.H;
-    p2.n_ntiles = d.H / 256;
-    hipLaunchKernelGGL(gmm_bf16_kernel<false>, dim3((unsigned)(mt_ub * p2.n_ntiles)), dim3(256),
-                       0, s, p2);
+    if (d.gemm_bm == 256)
+      launch_bf16<256, 32, 4>(d, pa, x_sorted, group_offsets, toff, tgroup, slot_expert, wg, wu, wd, act,
+                       out, max_rows, s);
+    else
+      launch_bf16<128, 64, 3>(d, pa, x_sorted, group_offsets, toff, tgroup, slot_expert, wg, wu, wd, act,
+                       out, max_rows, s);
   } else {
     F32Params p1;
     p1.A = (const float*)x_sorted;

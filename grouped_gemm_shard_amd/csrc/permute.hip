@@ -110,17 +110,22 @@ __global__ __launch_bounds__(64) void pass_local_kernel(Dims d, PassArgs pa,
 __global__ __launch_bounds__(1024) void pass_scan_kernel(Dims d, PassArgs pa, int which,
                                                          int* bh_slot, int* bh_dedup, int* kept,
                                                          int* group_offsets, int* tile_off,
-                                                         int* dedup_kept, int* dedup_offsets,
-                                                         int* meta) {
+                                                         int* tile_group, int* dedup_kept,
+                                                         int* dedup_offsets, int* meta) {
   PassInfo pi = resolve_pass(pa);
   if (!pi.active) return;
   __shared__ int tmp[16];
   __shared__ int excl[kMaxSlots];
+  __shared__ int totals[kMaxSlots];
+  __shared__ int dtotals[kMaxSlots];
   const bool capped = pi.capped && d.cap >= 0;
   const int g = threadIdx.x;
+  if (which & 1) scan_keys_over_blocks(bh_slot, d.G_res, totals);
+  if (which & 2) scan_keys_over_blocks(bh_dedup, d.S_res, dtotals);
+  __syncthreads();
   if (which & 1) {
     const bool own = g < d.G_res;
-    int tot = own ? scan_key_over_blocks(bh_slot, d.G_res, g) : 0;
+    int tot = own ? totals[g] : 0;
     int all;
     int ex = block_exscan_1024(tot, tmp, &all);
     if (own) excl[g] = ex;
@@ -136,8 +141,12 @@ __global__ __launch_bounds__(1024) void pass_scan_kernel(Dims d, PassArgs pa, in
     int off = block_exscan_1024(own ? kp : 0, tmp, &nrows);
     if (own) group_offsets[g] = off;
     int ntiles;
-    int toff = block_exscan_1024(own ? (kp + kGemmBM - 1) / kGemmBM : 0, tmp, &ntiles);
-    if (own) tile_off[g] = toff;
+    const int tiles = own ? (kp + d.gemm_bm - 1) / d.gemm_bm : 0;
+    int toff = block_exscan_1024(tiles, tmp, &ntiles);
+    if (own) {
+      tile_off[g] = toff;
+      for (int m = 0; m < tiles; ++m) tile_group[toff + m] = g;
+    }
     if (g == 0) {
       group_offsets[d.G_res] = nrows;
       tile_off[d.G_res] = ntiles;
@@ -146,7 +155,7 @@ __global__ __launch_bounds__(1024) void pass_scan_kernel(Dims d, PassArgs pa, in
   }
   if (which & 2) {
     const bool own = g < d.S_res;
-    int u = own ? scan_key_over_blocks(bh_dedup, d.S_res, g) : 0;
+    int u = own ? dtotals[g] : 0;
     int ku = capped ? min(u, d.cap) : u;
     if (own) dedup_kept[g] = ku;
     int nu;
@@ -256,7 +265,8 @@ size_t pass_scratch_bytes(const Dims& d) {
   size_t n = (size_t)d.T * d.k;
   return al256(n * 4) * 2 + al256((size_t)kSortBlocks * d.G_res * 4) +
          al256((size_t)kSortBlocks * d.S_res * 4) + al256((size_t)d.G_res * 4) +
-         al256((size_t)d.S_res * 4) + al256((size_t)(d.G_res + 1) * 4) + al256(8 * 4);
+         al256((size_t)d.S_res * 4) + al256((size_t)(d.G_res + 1) * 4) +
+         al256((size_t)tile_map_len(d) * 4) + al256(8 * 4);
 }
 
 PassBuffers carve_pass(const Dims& d, void* scratch) {
@@ -270,6 +280,7 @@ PassBuffers carve_pass(const Dims& d, void* scratch) {
   b.kept = (int*)p;            p += al256((size_t)d.G_res * 4);
   b.dedup_kept = (int*)p;      p += al256((size_t)d.S_res * 4);
   b.tile_off = (int*)p;        p += al256((size_t)(d.G_res + 1) * 4);
+  b.tile_group = (int*)p;      p += al256((size_t)tile_map_len(d) * 4);
   b.meta = (int*)p;
   return b;
 }
@@ -290,24 +301,24 @@ hipError_t launch_permute(const Dims& d, const PassArgs& pa, const void* x,
     hipLaunchKernelGGL(pass_local_kernel<1>, lg, lb, 0, s, d, pa, soa, pb.skey, pb.dkey,
                        pb.bh_slot, pb.bh_dedup, 0);
     hipLaunchKernelGGL(pass_scan_kernel, one, sb, 0, s, d, pa, 1, pb.bh_slot, pb.bh_dedup,
-                       pb.kept, group_offsets, pb.tile_off, pb.dedup_kept, dedup_offsets,
+                       pb.kept, group_offsets, pb.tile_off, pb.tile_group, pb.dedup_kept, dedup_offsets,
                        pb.meta);
   } else if (!two_round) {
     hipLaunchKernelGGL(pass_local_kernel<3>, lg, lb, 0, s, d, pa, soa, pb.skey, pb.dkey,
                        pb.bh_slot, pb.bh_dedup, 0);
     hipLaunchKernelGGL(pass_scan_kernel, one, sb, 0, s, d, pa, 3, pb.bh_slot, pb.bh_dedup,
-                       pb.kept, group_offsets, pb.tile_off, pb.dedup_kept, dedup_offsets,
+                       pb.kept, group_offsets, pb.tile_off, pb.tile_group, pb.dedup_kept, dedup_offsets,
                        pb.meta);
   } else {
     hipLaunchKernelGGL(pass_local_kernel<2>, lg, lb, 0, s, d, pa, soa, pb.skey, pb.dkey,
                        pb.bh_slot, pb.bh_dedup, 0);
     hipLaunchKernelGGL(pass_scan_kernel, one, sb, 0, s, d, pa, 2, pb.bh_slot, pb.bh_dedup,
-                       pb.kept, group_offsets, pb.tile_off, pb.dedup_kept, dedup_offsets,
+                       pb.kept, group_offsets, pb.tile_off, pb.tile_group, pb.dedup_kept, dedup_offsets,
                        pb.meta);
     hipLaunchKernelGGL(pass_local_kernel<1>, lg, lb, 0, s, d, pa, soa, pb.skey, pb.dkey,
                        pb.bh_slot, pb.bh_dedup, 1);
     hipLaunchKernelGGL(pass_scan_kernel, one, sb, 0, s, d, pa, 1, pb.bh_slot, pb.bh_dedup,
-                       pb.kept, group_offsets, pb.tile_off, pb.dedup_kept, dedup_offsets,
+                       pb.kept, group_offsets, pb.tile_off, pb.tile_group, pb.dedup_kept, dedup_offsets,
                        pb.meta);
   }
   const dim3 cg((nmax + 3) / 4), cb(256);

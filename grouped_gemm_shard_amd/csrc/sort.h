@@ -90,19 +90,24 @@ __device__ __forceinline__ int block_exscan_1024(int v, int* tmp, int* total) {
   return prefix + x - v;
 }
 
-// Turns the block counts of one key into exclusive block bases (in place)
-// and returns the key's total.
-__device__ __forceinline__ int scan_key_over_blocks(int* bh, int K, int key) {
-  int vals[kSortBlocks];
+// Turns the block counts of keys [0, K) into exclusive block bases (in
+// place) and writes each key's total to totals[key] (LDS).  One wavefront
+// per key, one lane per sort block (kSortBlocks == 64).  Contains no
+// barrier; the caller synchronises before reading totals.
+__device__ __forceinline__ void scan_keys_over_blocks(int* bh, int K, int* totals) {
+  static_assert(kSortBlocks == 64, "one lane per sort block");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int key = w; key < K; key += nw) {
+    int v = bh[lane * K + key];
+    int x = v;
 #pragma unroll
-  for (int b = 0; b < kSortBlocks; ++b) vals[b] = bh[b * K + key];
-  int acc = 0;
-#pragma unroll
-  for (int b = 0; b < kSortBlocks; ++b) {
-    bh[b * K + key] = acc;
-    acc += vals[b];
+    for (int off = 1; off < 64; off <<= 1) {
+      int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    bh[lane * K + key] = x - v;
+    if (lane == 63) totals[key] = x;
   }
-  return acc;
 }
 
 }  // namespace moe

@@ -31,6 +31,9 @@ MEDIUM = {
                                                        seq_len=1024, hidden=1024, ffn=2048),
     "dedup_small": CONFIGS["dedup_redundant"].scaled(name="dedup_small", tokens=512,
                                                      seq_len=512, hidden=256, ffn=128),
+    # hidden >= 2048 selects the 256-row GEMM tile
+    "maverick_mid": CONFIGS["maverick_shard"].scaled(name="maverick_mid", tokens=2048,
+                                                     seq_len=512, hidden=2048, ffn=1024),
 }
 SMALL_CASES = {"tiny_fp32": CONFIGS["tiny_fp32"], "mid_bf16": CONFIGS["mid_bf16"], **MEDIUM}
 
