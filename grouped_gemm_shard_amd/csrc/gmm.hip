@@ -42,6 +42,14 @@ namespace {
 
 constexpr int BNB = 256;  // weight rows per tile
 
+// Tile shapes <BM, BK, stages, waves> for long reductions and for the rest.
+#ifndef MOE_GEMM_BIG
+#define MOE_GEMM_BIG 256, 64, 2, 8
+#endif
+#ifndef MOE_GEMM_SMALL
+#define MOE_GEMM_SMALL 128, 64, 3, 8
+#endif
+
 struct GemmParams {
   const uint16_t* A;
   const uint16_t* B0;  // gate weights (GEMM1) or down weights (GEMM2)
@@ -65,56 +73,86 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
                                            0x00020000);
 }
 
-// Chunk permutation of LDS row `row`: distinct for the rows a fragment read
-// services together, with 32 or with 64 banks.
+// Chunk permutation of LDS row `row`: the fragment reads of consecutive
+// rows at one logical chunk land on distinct banks (both permutations were
+// measured free of LDS bank conflicts on gfx950 with SQ_LDS_BANK_CONFLICT).
 template <int BK>
 __device__ __forceinline__ int swz(int row) {
   if (BK == 64) return ((row >> 1) ^ ((row & 1) << 2)) & 7;
-  return ((row >> 1) ^ (row >> 3)) & 3;
+  return (row >> 2) & 3;
 }
 
-// Waits until at most N of this wave's loads are outstanding, then joins
-// the workgroup barrier.  The memory clobber keeps the compiler from moving
-// LDS accesses across it.
+// Waits until at most N of this wave's global->LDS loads are outstanding
+// and all of its LDS reads have returned, then joins the workgroup barrier:
+// after it, every wave's loads of the awaited stage have landed and no wave
+// still reads the buffer the next loads overwrite.  The memory clobber keeps
+// the compiler from moving LDS accesses across it.
 template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // Starts the loads of K step `step` into its ring stage: each wave-wide
 // load fills RPI consecutive rows (1 KB) of the stage.
-template <int BM, int BK, int NST, bool SWIGLU>
+template <int BM, int BK, int NST, bool SWIGLU, int NW>
 __device__ __forceinline__ void gmm_issue(char* smem, int step, int w,
                                           __amdgpu_buffer_rsrc_t ra_r, __amdgpu_buffer_rsrc_t rb0,
                                           __amdgpu_buffer_rsrc_t rb1,
-                                          const int (&a_off)[BM / (1024 / (BK * 2)) / 4],
-                                          const int (&b_off)[BNB / (1024 / (BK * 2)) / 4]) {
+                                          const int (&a_off)[BM / (1024 / (BK * 2)) / NW],
+                                          const int (&b_off)[BNB / (1024 / (BK * 2)) / NW]) {
   constexpr int RB = BK * 2, RPI = 1024 / RB;
-  constexpr int AI = BM / RPI / 4, BI = BNB / RPI / 4;
+  constexpr int AI = BM / RPI / NW, BI = BNB / RPI / NW;
   constexpr int SA = BM * RB, SS = (BM + BNB) * RB;
   char* st = smem + (step % NST) * SS;
   const int kb = step * BK * 2;
 #pragma unroll
   for (int i = 0; i < AI; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_r, (lds_void*)(st + (i * 4 + w) * RPI * RB), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_r, (lds_void*)(st + (i * NW + w) * RPI * RB), 16,
                                              a_off[i], kb, 0, 0);
 #pragma unroll
   for (int i = 0; i < BI; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(SWIGLU && i >= BI / 2 ? rb1 : rb0,
-                                             (lds_void*)(st + SA + (i * 4 + w) * RPI * RB), 16,
+                                             (lds_void*)(st + SA + (i * NW + w) * RPI * RB), 16,
                                              b_off[i], kb, 0, 0);
 }
 
-template <int BM, int BK, int NST, bool SWIGLU>
-__global__ __launch_bounds__(256, 1) void gmm_bf16_kernel(GemmParams P) {
+// Reads the A and B fragments of K slice ks (16 columns) of one stage.
+template <int BK, int MI>
+__device__ __forceinline__ void gmm_frags(const char* sa, const char* sb, const int (&a_row)[MI],
+                                          const int (&b_row)[4], int lane, int ks,
+                                          bf16x8 (&a)[MI], bf16x8 (&b)[4]) {
+  constexpr int RB = BK * 2;
+  const int kc = ks * 2 + (lane >> 5);
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+    a[mi] = *(const bf16x8*)(sa + a_row[mi] * RB + ((kc ^ swz<BK>(a_row[mi])) << 4));
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni)
+    b[ni] = *(const bf16x8*)(sb + b_row[ni] * RB + ((kc ^ swz<BK>(b_row[ni])) << 4));
+}
+
+template <int MI>
+__device__ __forceinline__ void gmm_mma(const bf16x8 (&a)[MI], const bf16x8 (&b)[4],
+                                        floatx16 (&acc)[MI][4]) {
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+}
+
+template <int BM, int BK, int NST, bool SWIGLU, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   constexpr int RB = BK * 2;          // LDS bytes per row of a stage
   constexpr int CPR = BK / 8;         // 16-byte chunks per row
   constexpr int RPI = 1024 / RB;      // rows one wave-wide load fills
-  constexpr int AI = BM / RPI / 4;    // A loads per wave per stage
-  constexpr int BI = BNB / RPI / 4;   // B loads per wave per stage
+  constexpr int AI = BM / RPI / NW;   // A loads per wave per stage
+  constexpr int BI = BNB / RPI / NW;  // B loads per wave per stage
   constexpr int LPS = AI + BI;
   constexpr int SA = BM * RB, SS = (BM + BNB) * RB;
-  constexpr int MI = BM / 64;         // 32-row MFMA tiles per wave
+  constexpr int WM = BM / (NW / 2);   // rows per wave (waves form (NW/2) x 2)
+  constexpr int MI = WM / 32;         // 32-row MFMA tiles per wave
+  static_assert(AI >= 1 && BI >= 2 && MI >= 1, "tile shape");
   static_assert(NST >= 2 && NST <= 4, "stages");
 
   PassInfo pi = resolve_pass(P.pa);
@@ -158,12 +196,12 @@ __global__ __launch_bounds__(256, 1) void gmm_bf16_kernel(GemmParams P) {
   int a_off[AI], b_off[BI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    int row = (i * 4 + w) * RPI + lane / CPR;
+    int row = (i * NW + w) * RPI + lane / CPR;
     a_off[i] = row * K * 2 + (((lane % CPR) ^ swz<BK>(row)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
-    int row = (i * 4 + w) * RPI + lane / CPR;
+    int row = (i * NW + w) * RPI + lane / CPR;
     int wr = SWIGLU ? (row & 127) : row;
     b_off[i] = wr * K * 2 + (((lane % CPR) ^ swz<BK>(row)) << 4);
   }
@@ -171,7 +209,7 @@ __global__ __launch_bounds__(256, 1) void gmm_bf16_kernel(GemmParams P) {
   // fragment read offsets (bytes within a stage) for chunk kc of each row
   int a_row[MI], b_row[4];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) a_row[mi] = wm * (BM / 2) + mi * 32 + (lane & 31);
+  for (int mi = 0; mi < MI; ++mi) a_row[mi] = wm * WM + mi * 32 + (lane & 31);
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni)
     b_row[ni] = (SWIGLU ? ((ni >> 1) * 128 + wn * 64 + (ni & 1) * 32) : (wn * 128 + ni * 32)) +
@@ -187,34 +225,35 @@ __global__ __launch_bounds__(256, 1) void gmm_bf16_kernel(GemmParams P) {
 
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
-    if (s < KT) gmm_issue<BM, BK, NST, SWIGLU>(smem, s, w, ra_r, rb0, rb1, a_off, b_off);
+    if (s < KT) gmm_issue<BM, BK, NST, SWIGLU, NW>(smem, s, w, ra_r, rb0, rb1, a_off, b_off);
 
+  // Software pipeline across K steps: the last slice's fragments are read
+  // before the barrier, and its MFMAs are issued after it, overlapping the
+  // first fragment reads of the next stage.
+  constexpr int NS = BK / 16;  // K slices per step
+  static_assert(NS % 2 == 0, "the pending last slice lives in fragment set 1");
+  bf16x8 a[2][MI], b[2][4];
   for (int kt = 0; kt < KT; ++kt) {
     const int ahead = min(KT - 1 - kt, NST - 2);  // stages allowed to stay in flight
     if (ahead >= 2) vm_wait_barrier<2 * LPS>();
     else if (ahead == 1) vm_wait_barrier<LPS>();
     else vm_wait_barrier<0>();
     if (kt + NST - 1 < KT)
-      gmm_issue<BM, BK, NST, SWIGLU>(smem, kt + NST - 1, w, ra_r, rb0, rb1, a_off, b_off);
+      gmm_issue<BM, BK, NST, SWIGLU, NW>(smem, kt + NST - 1, w, ra_r, rb0, rb1, a_off, b_off);
     const char* sa = smem + (kt % NST) * SS;
     const char* sb = sa + SA;
+    // slice 0 of this step goes to set 0; slice NS-1 of the previous step
+    // is still pending in set 1
+    gmm_frags<BK, MI>(sa, sb, a_row, b_row, lane, 0, a[0], b[0]);
+    if (kt > 0) gmm_mma<MI>(a[1], b[1], acc);  // last slice of the previous step
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int kc = ks * 2 + (lane >> 5);
-      bf16x8 a[MI], b[4];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        a[mi] = *(const bf16x8*)(sa + a_row[mi] * RB + ((kc ^ swz<BK>(a_row[mi])) << 4));
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        b[ni] = *(const bf16x8*)(sb + b_row[ni] * RB + ((kc ^ swz<BK>(b_row[ni])) << 4));
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    for (int ks = 0; ks < NS - 1; ++ks) {
+      const int cur = ks & 1;
+      gmm_frags<BK, MI>(sa, sb, a_row, b_row, lane, ks + 1, a[cur ^ 1], b[cur ^ 1]);
+      gmm_mma<MI>(a[cur], b[cur], acc);
     }
   }
+  gmm_mma<MI>(a[(NS - 1) & 1], b[(NS - 1) & 1], acc);
 
   // 32x32 accumulator layout: register q of a lane holds row
   // (q/4)*8 + (lane/32)*4 + q%4, column lane%32.
@@ -222,7 +261,7 @@ __global__ __launch_bounds__(256, 1) void gmm_bf16_kernel(GemmParams P) {
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int lr = wm * (BM / 2) + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+      const int lr = wm * WM + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
       if (lr >= rows) continue;
       uint16_t* crow = P.C + (size_t)(row0 + lr) * P.Nout;
       if (SWIGLU) {
@@ -333,7 +372,7 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(int G, int bm, int 
   if (g == 0) tile_off[G] = tmp[nw - 1];
 }
 
-template <int BM, int BK, int NST>
+template <int BM, int BK, int NST, int NW>
 void launch_bf16(const Dims& d, const PassArgs& pa, const void* x_sorted,
                  const int* group_offsets, const int* toff, const int* tgroup,
                  const int* slot_expert, const void* wg, const void* wu, const void* wd,
@@ -359,7 +398,7 @@ void launch_bf16(const Dims& d, const PassArgs& pa, const void* x_sorted,
   p1.n_ntiles = d.F / 128;
   p1.pa = pa;
   const long long g1 = (mt_ub * p1.n_ntiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, true>), dim3((unsigned)g1), dim3(256), 0, s, p1);
+  hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, true, NW>), dim3((unsigned)g1), dim3(64 * NW), 0, s, p1);
   GemmParams p2 = p1;
   p2.A = (const uint16_t*)act;
   p2.B0 = (const uint16_t*)wd;
@@ -370,7 +409,7 @@ void launch_bf16(const Dims& d, const PassArgs& pa, const void* x_sorted,
   p2.Nout = d.H;
   p2.n_ntiles = d.H / 256;
   const long long g2 = (mt_ub * p2.n_ntiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, false>), dim3((unsigned)g2), dim3(256), 0, s, p2);
+  hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, false, NW>), dim3((unsigned)g2), dim3(64 * NW), 0, s, p2);
 }
 
 }  // namespace
@@ -398,10 +437,10 @@ hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const void* x_sorted,
       tgroup = t1;
     }
     if (d.gemm_bm == 256)
-      launch_bf16<256, 32, 4>(d, pa, x_sorted, group_offsets, toff, tgroup, slot_expert, wg, wu, wd, act,
+      launch_bf16<MOE_GEMM_BIG>(d, pa, x_sorted, group_offsets, toff, tgroup, slot_expert, wg, wu, wd, act,
                        out, max_rows, s);
     else
-      launch_bf16<128, 64, 3>(d, pa, x_sorted, group_offsets, toff, tgroup, slot_expert, wg, wu, wd, act,
+      launch_bf16<MOE_GEMM_SMALL>(d, pa, x_sorted, group_offsets, toff, tgroup, slot_expert, wg, wu, wd, act,
                        out, max_rows, s);
   } else {
     F32Params p1;
