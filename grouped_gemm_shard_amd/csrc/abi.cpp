@@ -121,8 +121,59 @@ void layer_bounds(const Dims& d, int mode, int64_t* rows, int64_t* drows) {
   *drows = u1 > u2 ? u1 : u2;
 }
 
+// The layout set of a single static pass (chunk c of n, capped or not).
+LayoutSet single_layout(int n, int c, int capped) {
+  LayoutSet ls;
+  memset(&ls, 0, sizeof(ls));
+  if (n == 1) {
+    ls.has_single = 1;
+    ls.single_capped = capped;
+  } else {
+    ls.n_chunks = n;
+    ls.chunk_lo = c;
+    ls.chunk_cnt = 1;
+    ls.chunk_capped = capped;
+  }
+  return ls;
+}
+
+// The passes of a layer call in `mode`.  LAYER with a cap: the single pass
+// (layout 0) or the dropless chunks (layouts 1..n), chosen on the device by
+// the overflow flag.  Without overflow no shard exceeds the cap, so the
+// single pass keeps every row and is laid out uncapped.
+LayoutSet layer_layout(const Dims& d, int mode, const int* ovf) {
+  LayoutSet ls;
+  memset(&ls, 0, sizeof(ls));
+  const int n = d.n_default;
+  switch (mode) {
+    case MOE_MODE_LAYER:
+      ls.has_single = 1;
+      if (d.cap >= 0) {
+        ls.n_chunks = n;
+        ls.chunk_cnt = n;
+        ls.ovf = ovf;
+      }
+      break;
+    case MOE_MODE_FORCE_DROPLESS: ls.has_single = 1; break;
+    case MOE_MODE_CAPPED_ONLY: ls.has_single = 1; ls.single_capped = 1; break;
+    default: ls.n_chunks = n; ls.chunk_cnt = n; break;
+  }
+  return ls;
+}
+
+// Static pass arguments of layout j.
+PassArgs static_pass(const Dims& d, const LayoutSet& ls, int j) {
+  PassArgs pa;
+  size_t e0;
+  layout_pass(d, ls, j, &pa.n, &pa.c, &pa.capped, &e0);
+  pa.ovf = nullptr;
+  pa.j = j;
+  return pa;
+}
+
 size_t step_scratch(const Dims& d) {
-  size_t a = count_scratch_bytes(d), b = pass_scratch_bytes(d), c = gmm_scratch_bytes(d);
+  size_t a = count_scratch_bytes(d), b = layout_scratch_bytes(d, single_layout(1, 0, 1)),
+         c = gmm_scratch_bytes(d);
   size_t m = a > b ? a : b;
   return m > c ? m : c;
 }
@@ -138,21 +189,14 @@ struct LayerWs {
   int* shard_counts;
   int* status;
   void* count_scratch;
-  void* pass_scratch;
-  int* group_offsets;
-  int* row_of_assign;
-  int* sorted_assign;
-  int* dedup_offsets;
-  int* dedup_token;
-  int* expand_idx;
+  void* layout_scratch;
   void* x_dedup;
-  void* x_sorted;
   void* act;
   void* out;
   size_t bytes;
 };
 
-LayerWs carve_layer(const Dims& d, int64_t rows, int64_t drows, char* base) {
+LayerWs carve_layer(const Dims& d, const LayoutSet& ls, int64_t rows, int64_t drows, char* base) {
   LayerWs w;
   size_t off = 0;
   auto take = [&](size_t b) {
@@ -171,15 +215,8 @@ LayerWs carve_layer(const Dims& d, int64_t rows, int64_t drows, char* base) {
   w.shard_counts = (int*)take((size_t)d.S * 4);
   w.status = (int*)take(4 * 4);
   w.count_scratch = take(count_scratch_bytes(d));
-  w.pass_scratch = take(pass_scratch_bytes(d));
-  w.group_offsets = (int*)take((size_t)(d.G_res + 1) * 4);
-  w.row_of_assign = (int*)take(tk * 4);
-  w.sorted_assign = (int*)take((size_t)rows * 4);
-  w.dedup_offsets = (int*)take((size_t)(d.S_res + 1) * 4);
-  w.dedup_token = (int*)take((size_t)drows * 4);
-  w.expand_idx = (int*)take((size_t)rows * 4);
-  w.x_dedup = take((size_t)drows * d.H * es);
-  w.x_sorted = take((size_t)rows * d.H * es);
+  w.layout_scratch = take(layout_scratch_bytes(d, ls));
+  w.x_dedup = take(d.dedup ? (size_t)drows * d.H * es : 0);
   w.act = take((size_t)rows * d.F * es);
   w.out = take((size_t)rows * d.H * es);
   w.bytes = off;
@@ -190,17 +227,47 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP
 
 bool misaligned(const void* p, size_t a) { return ((uintptr_t)p) % a != 0; }
 
-int run_pass(const Dims& d, const PassArgs& pa, const void* x, const void* wg, const void* wu,
-             const void* wd, void* y, const LayerWs& w, int64_t rows, hipStream_t s) {
-  PassBuffers pb = carve_pass(d, w.pass_scratch);
-  hipError_t e = launch_permute(d, pa, x, w.slot_of_assign, pb, w.group_offsets, w.row_of_assign,
-                                w.sorted_assign, w.dedup_offsets, w.dedup_token, w.expand_idx,
-                                w.x_dedup, w.x_sorted, s);
+// The GEMMs address their bf16 operands through 32-bit buffer offsets.
+bool fits_rsrc(const Dims& d, int64_t rows, int64_t drows) {
+  if (!d.bf16) return true;
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t wide = d.H > d.F ? d.H : d.F;
+  return (int64_t)d.T * d.H * 2 < lim && rows * wide * 2 < lim && drows * d.H * 2 < lim;
+}
+
+// One pass of the layer: with dedup the pass's distinct tokens are copied
+// once per shard (the dedup buffer) and GEMM1 re-expands them through
+// expand_idx; without, GEMM1 gathers its rows from x through sorted_assign.
+// Then the combine of the pass's tokens.
+int run_pass(const Dims& d, const PassArgs& pa, const LayoutSet& ls, const LayoutBuffers& lb,
+             const void* x, const void* wg, const void* wu, const void* wd, void* y,
+             const LayerWs& w, int64_t rows, int64_t drows, hipStream_t s) {
+  const long long tk = (long long)d.T * d.k;
+  const int es = d.bf16 ? 2 : 4;
+  GemmPass gp;
+  if (d.dedup) {
+    hipError_t e = launch_gather_rows(lb.meta + 1, kLayoutMeta, lb.dedup_token, tk, 1, x,
+                                      w.x_dedup, d.H * es, d.T, drows, pa, s);
+    if (e != hipSuccess) return MOE_EHIP;
+    gp.a_src = w.x_dedup;
+    gp.a_src_rows = (int)drows;
+    gp.a_index = lb.expand_idx;
+    gp.a_div = 1;
+  } else {
+    gp.a_src = x;
+    gp.a_src_rows = d.T;
+    gp.a_index = lb.sorted_assign;
+    gp.a_div = d.k;
+  }
+  gp.a_index_stride = tk;
+  gp.group_offsets = lb.group_offsets;
+  gp.tile_off = lb.tile_off;
+  gp.tile_group = lb.tile_group;
+  gp.go_stride = d.G_res + 1;
+  gp.tg_stride = tile_map_len(d);
+  hipError_t e = launch_gmm(d, pa, gp, w.slot_expert, wg, wu, wd, w.act, w.out, rows, nullptr, s);
   if (e != hipSuccess) return MOE_EHIP;
-  e = launch_gmm(d, pa, w.x_sorted, w.group_offsets, pb.tile_off, pb.tile_group, w.slot_expert,
-                 wg, wu, wd, w.act, w.out, rows, nullptr, s);
-  if (e != hipSuccess) return MOE_EHIP;
-  e = launch_combine(d, pa, w.out, w.row_of_assign, w.topk_gate, y, s);
+  e = launch_combine(d, pa, ls, w.out, lb.row_of_assign, tk, rows, w.topk_gate, y, s);
   return hip_status(e);
 }
 
@@ -236,7 +303,7 @@ int moe_layer_workspace_bytes(const moe_problem* p, int32_t mode, size_t* bytes)
     return MOE_EINVAL;
   int64_t rows, drows;
   layer_bounds(d, mode, &rows, &drows);
-  *bytes = carve_layer(d, rows, drows, nullptr).bytes;
+  *bytes = carve_layer(d, layer_layout(d, mode, nullptr), rows, drows, nullptr).bytes;
   return MOE_OK;
 }
 
@@ -287,12 +354,35 @@ int moe_permute(const moe_problem* p, int32_t num_chunks, int32_t chunk, int32_t
   int64_t rb, ub;
   pass_bounds(d, num_chunks, capped, &rb, &ub);
   if (max_rows < rb || (d.dedup && max_dedup_rows < ub)) return MOE_ECAPACITY;
-  if (ws_bytes < pass_scratch_bytes(d)) return MOE_ECAPACITY;
-  PassArgs pa{num_chunks, chunk, capped, nullptr};
-  PassBuffers pb = carve_pass(d, ws);
-  return hip_status(launch_permute(d, pa, x, slot_of_assign, pb, group_offsets, row_of_assign,
-                                   sorted_assign, dedup_offsets, dedup_token, expand_idx, x_dedup,
-                                   x_sorted, (hipStream_t)stream));
+  const LayoutSet ls = single_layout(num_chunks, chunk, capped);
+  if (ws_bytes < layout_scratch_bytes(d, ls)) return MOE_ECAPACITY;
+  if (max_rows >= (1ll << 31) || max_dedup_rows >= (1ll << 31)) return MOE_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  // the layout writes the caller's arrays directly; the rest stays in ws
+  LayoutBuffers lb = carve_layout(d, ls, ws);
+  lb.group_offsets = group_offsets;
+  lb.row_of_assign = row_of_assign;
+  lb.sorted_assign = sorted_assign;
+  if (d.dedup) {
+    lb.dedup_offsets = dedup_offsets;
+    lb.dedup_token = dedup_token;
+    lb.expand_idx = expand_idx;
+  }
+  hipError_t e = launch_layout(d, ls, slot_of_assign, lb, s);
+  if (e != hipSuccess) return MOE_EHIP;
+  const int row_bytes = d.H * (d.bf16 ? 2 : 4);
+  const PassArgs pa{num_chunks, chunk, capped, nullptr, 0};
+  if (d.dedup) {
+    e = launch_gather_rows(lb.meta + 1, kLayoutMeta, dedup_token, 0, 1, x, x_dedup, row_bytes,
+                           d.T, max_dedup_rows, pa, s);
+    if (e != hipSuccess) return MOE_EHIP;
+    e = launch_gather_rows(lb.meta, kLayoutMeta, expand_idx, 0, 1, x_dedup, x_sorted, row_bytes,
+                           (int)max_dedup_rows, max_rows, pa, s);
+  } else {
+    e = launch_gather_rows(lb.meta, kLayoutMeta, sorted_assign, 0, d.k, x, x_sorted, row_bytes,
+                           d.T, max_rows, pa, s);
+  }
+  return hip_status(e);
 }
 
 int moe_gmm_swiglu(const moe_problem* p, const void* x_sorted, const int32_t* group_offsets,
@@ -310,10 +400,16 @@ int moe_gmm_swiglu(const moe_problem* p, const void* x_sorted, const int32_t* gr
     return MOE_EINVAL;
   if (max_rows >= (1ll << 31) / 2) return MOE_EUNSUPPORTED;
   if (ws_bytes < gmm_scratch_bytes(d)) return MOE_ECAPACITY;
-  PassArgs pa{1, 0, 0, nullptr};
-  return hip_status(launch_gmm(d, pa, x_sorted, group_offsets, nullptr, nullptr, slot_expert,
-                               w_gate, w_up, w_down, act, expert_out, max_rows, ws,
-                               (hipStream_t)stream));
+  if (!fits_rsrc(d, max_rows, 0)) return MOE_EUNSUPPORTED;
+  PassArgs pa{1, 0, 0, nullptr, 0};
+  GemmPass gp;
+  memset(&gp, 0, sizeof(gp));
+  gp.a_src = x_sorted;
+  gp.a_src_rows = (int)max_rows;
+  gp.a_div = 1;
+  gp.group_offsets = group_offsets;
+  return hip_status(launch_gmm(d, pa, gp, slot_expert, w_gate, w_up, w_down, act, expert_out,
+                               max_rows, ws, (hipStream_t)stream));
 }
 
 int moe_combine(const moe_problem* p, int32_t num_chunks, int32_t chunk, const void* expert_out,
@@ -325,9 +421,10 @@ int moe_combine(const moe_problem* p, int32_t num_chunks, int32_t chunk, const v
     return MOE_EINVAL;
   if (!expert_out || !row_of_assign || !topk_gate || !y) return MOE_EINVAL;
   if (misaligned(expert_out, 16) || misaligned(y, 16)) return MOE_EINVAL;
-  PassArgs pa{num_chunks, chunk, 0, nullptr};
-  return hip_status(
-      launch_combine(d, pa, expert_out, row_of_assign, topk_gate, y, (hipStream_t)stream));
+  PassArgs pa{num_chunks, chunk, 0, nullptr, 0};
+  const LayoutSet ls = single_layout(num_chunks, chunk, 0);
+  return hip_status(launch_combine(d, pa, ls, expert_out, row_of_assign, 0, INT64_MAX, topk_gate,
+                                   y, (hipStream_t)stream));
 }
 
 int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x,
@@ -344,8 +441,12 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
     return MOE_EINVAL;
   int64_t rows, drows;
   layer_bounds(d, mode, &rows, &drows);
-  LayerWs w = carve_layer(d, rows, drows, (char*)ws);
-  if (ws_bytes < w.bytes) return MOE_ECAPACITY;
+  if (!fits_rsrc(d, rows, drows)) return MOE_EUNSUPPORTED;
+  LayerWs w0 = carve_layer(d, layer_layout(d, mode, nullptr), rows, drows, nullptr);
+  if (ws_bytes < w0.bytes) return MOE_ECAPACITY;
+  // status[1] (the overflow flag) lives in the workspace
+  LayerWs w = carve_layer(d, layer_layout(d, mode, nullptr), rows, drows, (char*)ws);
+  const LayoutSet ls = layer_layout(d, mode, w.status + 1);
   hipStream_t s = (hipStream_t)stream;
 
   hipError_t e = launch_route(d, logits, w.topk_idx, w.topk_gate, s);
@@ -353,26 +454,24 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
   e = launch_count(d, w.topk_idx, w.expert_counts, w.slot_expert, w.ndiv, w.slot_of_assign,
                    w.shard_counts, w.status, w.count_scratch, info, mode, s);
   if (e != hipSuccess) return MOE_EHIP;
+  const LayoutBuffers lb = carve_layout(d, ls, w.layout_scratch);
+  e = launch_layout(d, ls, w.slot_of_assign, lb, s);
+  if (e != hipSuccess) return MOE_EHIP;
 
   const int n = d.n_default;
-  if (mode == MOE_MODE_LAYER && d.cap >= 0) {
-    // the device decides: capped pass 0 alone, or n dropless chunks
+  if (ls.ovf != nullptr) {
+    // the device decides: the single pass alone, or n dropless chunks
     for (int c = 0; c < n; ++c) {
-      PassArgs pa{n, c, 1, w.status + 1};
-      st = run_pass(d, pa, x, w_gate, w_up, w_down, y, w, rows, s);
-      if (st != MOE_OK) return st;
-    }
-  } else if (mode == MOE_MODE_FORCE_CHUNKED) {
-    for (int c = 0; c < n; ++c) {
-      PassArgs pa{n, c, 0, nullptr};
-      st = run_pass(d, pa, x, w_gate, w_up, w_down, y, w, rows, s);
+      PassArgs pa{n, c, 0, ls.ovf, 0};
+      st = run_pass(d, pa, ls, lb, x, w_gate, w_up, w_down, y, w, rows, drows, s);
       if (st != MOE_OK) return st;
     }
   } else {
-    int capped = (mode == MOE_MODE_CAPPED_ONLY) ? 1 : 0;
-    PassArgs pa{1, 0, capped, nullptr};
-    st = run_pass(d, pa, x, w_gate, w_up, w_down, y, w, rows, s);
-    if (st != MOE_OK) return st;
+    for (int j = 0; j < layout_num_passes(ls); ++j) {
+      const PassArgs pa = static_pass(d, ls, j);
+      st = run_pass(d, pa, ls, lb, x, w_gate, w_up, w_down, y, w, rows, drows, s);
+      if (st != MOE_OK) return st;
+    }
   }
   return MOE_OK;
 }

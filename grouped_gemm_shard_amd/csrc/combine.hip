@@ -14,12 +14,14 @@ namespace moe {
 namespace {
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void combine_kernel(Dims d, PassArgs pa,
+__global__ __launch_bounds__(256) void combine_kernel(Dims d, PassArgs pa, LayoutSet ls,
                                                       const void* __restrict__ out,
                                                       const int* __restrict__ row_of_assign,
+                                                      long long roa_stride, long long max_rows,
                                                       const float* __restrict__ gate, void* y) {
   PassInfo pi = resolve_pass(pa);
   if (!pi.active) return;
+  row_of_assign += (size_t)layout_set_of(ls, pi.j) * roa_stride;
   const int i = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (i >= pass_tokens(d, pi)) return;
   const int t = pass_token(d, pi, i);
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(256) void combine_kernel(Dims d, PassArgs pa,
       for (int j = 0; j < d.k; ++j) {
         const int r = rows[j];
         const float gj = gts[j];
-        if (r < 0) continue;
+        if (r < 0 || r >= max_rows) continue;
         uint4 v = *(const uint4*)(o + (size_t)r * d.H + h);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(256) void combine_kernel(Dims d, PassArgs pa,
       for (int j = 0; j < d.k; ++j) {
         const int r = rows[j];
         const float gj = gts[j];
-        if (r < 0) continue;
+        if (r < 0 || r >= max_rows) continue;
         float4 v = *(const float4*)(o + (size_t)r * d.H + h);
         acc.x = fmaf(gj, v.x, acc.x);
         acc.y = fmaf(gj, v.y, acc.y);
@@ -75,15 +77,17 @@ __global__ __launch_bounds__(256) void combine_kernel(Dims d, PassArgs pa,
 
 }  // namespace
 
-hipError_t launch_combine(const Dims& d, const PassArgs& pa, const void* out,
-                          const int* row_of_assign, const float* gate, void* y,
-                          hipStream_t s) {
+hipError_t launch_combine(const Dims& d, const PassArgs& pa, const LayoutSet& ls, const void* out,
+                          const int* row_of_assign, long long roa_stride, int64_t max_rows,
+                          const float* gate, void* y, hipStream_t s) {
   const int ntok = d.T / (pa.ovf != nullptr ? 1 : pa.n);
   dim3 grid((ntok + 3) / 4), block(256);
   if (d.bf16)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, s, d, pa, out, row_of_assign, gate, y);
+    hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, s, d, pa, ls, out, row_of_assign,
+                       roa_stride, (long long)max_rows, gate, y);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, s, d, pa, out, row_of_assign, gate, y);
+    hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, s, d, pa, ls, out, row_of_assign,
+                       roa_stride, (long long)max_rows, gate, y);
   return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@ constexpr int kMaxExperts = 1024;   // E limit (route keeps E/64 logits per lane
 constexpr int kMaxTopK = 32;        // one lane per chosen expert in route/combine
 constexpr int kSortBlocks = 64;     // blocks of the stable counting sort
 constexpr int kGemmBMMin = 128;     // smallest grouped-GEMM tile height
+constexpr int kMaxChunks = 64;      // sequence chunks of the fallback
 
 // Problem dimensions, derived once on the host and passed by value.
 struct Dims {
@@ -36,32 +37,91 @@ struct Dims {
   int gemm_bm;   // grouped-GEMM tile height (128 or 256)
 };
 
-// One pass of the permute / GEMM / combine sequence.  Static passes carry
-// (n, c, capped) directly.  A dynamic pass (ovf != nullptr) is one of the
-// LAYER-mode passes: when *ovf is set it is chunk c of n, dropless; else
-// pass 0 covers every token with the capped buffer and passes c > 0 are
-// inactive.  Every kernel of a pass resolves this itself, so the host never
-// waits for the overflow flag.
+// One pass of the GEMM / combine sequence.  Static passes carry (n, c,
+// capped) and the index j of their layout directly.  A dynamic pass
+// (ovf != nullptr) is one of the LAYER-mode pass slots: when *ovf is set it
+// is chunk c of n (layout 1 + c), else slot 0 runs the single pass over all
+// tokens (layout 0) and slots c > 0 are inactive.  Every kernel of a pass
+// resolves this itself, so the host never waits for the overflow flag.
 struct PassArgs {
   int n, c, capped;
   const int* ovf;
+  int j;
 };
 
 struct PassInfo {
-  int active, n, c, capped;
+  int active, n, c, capped, j;
 };
 
 __device__ __forceinline__ PassInfo resolve_pass(const PassArgs& a) {
   PassInfo p;
   if (a.ovf == nullptr) {
-    p.active = 1; p.n = a.n; p.c = a.c; p.capped = a.capped;
+    p.active = 1; p.n = a.n; p.c = a.c; p.capped = a.capped; p.j = a.j;
   } else if (*a.ovf != 0) {
-    p.active = 1; p.n = a.n; p.c = a.c; p.capped = 0;
+    p.active = 1; p.n = a.n; p.c = a.c; p.capped = 0; p.j = 1 + a.c;
   } else {
-    p.active = (a.c == 0); p.n = 1; p.c = 0; p.capped = 1;
+    p.active = (a.c == 0); p.n = 1; p.c = 0; p.capped = 0; p.j = 0;
   }
   return p;
 }
+
+// The passes whose layouts are computed together: an optional single pass
+// over all tokens, then chunk passes [chunk_lo, chunk_lo + chunk_cnt) of a
+// split of every sequence into n_chunks.  Layout j: 0 is the single pass
+// when there is one, the chunk passes follow in order.  The single pass's
+// rows use one row_of_assign array ("set" 0) and the chunk passes share the
+// next one (their tokens are disjoint).  With `ovf` set (a LAYER-mode call)
+// the device computes only the layouts the flag selects: the single pass
+// when *ovf == 0, the chunk passes otherwise.
+struct LayoutSet {
+  int has_single, single_capped;
+  int n_chunks, chunk_lo, chunk_cnt, chunk_capped;
+  const int* ovf;
+};
+
+__device__ __forceinline__ bool layout_live(const LayoutSet& ls, int j) {
+  if (ls.ovf == nullptr) return true;
+  return (ls.has_single && j == 0) ? (*ls.ovf == 0) : (*ls.ovf != 0);
+}
+
+__host__ __device__ __forceinline__ int layout_num_passes(const LayoutSet& ls) {
+  return ls.has_single + ls.chunk_cnt;
+}
+__host__ __device__ __forceinline__ int layout_num_sets(const LayoutSet& ls) {
+  return ls.has_single + (ls.chunk_cnt > 0 ? 1 : 0);
+}
+__host__ __device__ __forceinline__ int layout_set_of(const LayoutSet& ls, int j) {
+  return (ls.has_single && j == 0) ? 0 : ls.has_single;
+}
+// Geometry of layout j; its rows and elements start at j * T*k in the
+// per-element arrays (each layout gets room for all T*k assignments).
+__host__ __device__ __forceinline__ void layout_pass(const Dims& d, const LayoutSet& ls, int j,
+                                                     int* n, int* c, int* capped, size_t* e0) {
+  if (ls.has_single && j == 0) {
+    *n = 1; *c = 0; *capped = ls.single_capped;
+  } else {
+    *n = ls.n_chunks; *c = ls.chunk_lo + (j - ls.has_single); *capped = ls.chunk_capped;
+  }
+  *e0 = (size_t)j * d.T * d.k;
+}
+__host__ __device__ __forceinline__ size_t layout_row_base(const Dims& d, const LayoutSet& ls, int j) {
+  return (size_t)j * d.T * d.k;
+}
+__host__ __device__ __forceinline__ size_t layout_dedup_base(const Dims& d, const LayoutSet& ls,
+                                                             int j) {
+  return (size_t)j * d.T * d.k;
+}
+__host__ __device__ __forceinline__ size_t layout_total_elems(const Dims& d, const LayoutSet& ls) {
+  return (size_t)layout_num_passes(ls) * d.T * d.k;
+}
+__host__ __device__ __forceinline__ size_t layout_total_dedup(const Dims& d, const LayoutSet& ls) {
+  return d.dedup ? layout_total_elems(d, ls) : 1;
+}
+__host__ __device__ __forceinline__ int layout_min_chunks(const LayoutSet& ls) {
+  return ls.has_single ? 1 : ls.n_chunks;
+}
+
+constexpr int kLayoutMeta = 8;  // per layout: [0] rows, [1] dedup rows
 
 // Token of the i-th position of a pass: chunk c of n holds s in
 // [c*L/n, (c+1)*L/n) of every sequence b, in ascending t = b*L + s.
@@ -120,38 +180,62 @@ hipError_t launch_count(const Dims& d, const int* idx, int* expert_counts, int* 
                         int* ndiv, int* slot_of_assign, int* shard_counts, int* status,
                         void* scratch, int* info_out, int info_mode, hipStream_t s);
 
-// Per-pass layout state carved from the workspace.
-struct PassBuffers {
-  unsigned* skey;      // [T*k] packed slot key / local rank
-  unsigned* dkey;      // [T*k] packed dedup key / local rank
-  int* bh_slot;        // [kSortBlocks * G_res] block counts -> bases
-  int* bh_dedup;       // [kSortBlocks * S_res]
-  int* kept;           // [G_res] kept rows per slot
-  int* dedup_kept;     // [S_res]
-  int* tile_off;       // [G_res + 1] m-tile prefix (tile height gemm_bm)
-  int* tile_group;     // [tile_map_len] group of every m-tile
-  int* meta;           // [8]: rows, dedup rows, ...
+// Layout state of every pass of a LayoutSet (arrays are per layout j with
+// the strides used by the kernels below).
+struct LayoutBuffers {
+  unsigned* skey;       // [elems] packed slot key / local rank
+  unsigned* dkey;       // [elems] packed dedup key / local rank
+  int* bh_slot;         // [np][kSortBlocks][G_res] block counts -> bases
+  int* bh_dedup;        // [np][kSortBlocks][S_res]
+  int* kept;            // [np][G_res] kept rows per slot
+  int* dedup_kept;      // [np][S_res]
+  int* group_offsets;   // [np][G_res + 1]
+  int* tile_off;        // [np][G_res + 1] m-tile prefix (tile height gemm_bm)
+  int* tile_group;      // [np][tile_map_len] group of every m-tile
+  int* dedup_offsets;   // [np][S_res + 1]
+  int* meta;            // [np][kLayoutMeta]
+  int* row_of_assign;   // [sets][T*k]
+  int* sorted_assign;   // [elems] rows of layout j start at its first element
+  int* expand_idx;      // [elems]
+  int* dedup_token;     // [elems] (dedup only)
 };
-size_t pass_scratch_bytes(const Dims& d);
-PassBuffers carve_pass(const Dims& d, void* scratch);
+size_t layout_scratch_bytes(const Dims& d, const LayoutSet& ls);
+LayoutBuffers carve_layout(const Dims& d, const LayoutSet& ls, void* scratch);
+hipError_t launch_layout(const Dims& d, const LayoutSet& ls, const int* slot_of_assign,
+                         const LayoutBuffers& lb, hipStream_t s);
 
-hipError_t launch_permute(const Dims& d, const PassArgs& pa, const void* x,
-                          const int* slot_of_assign, const PassBuffers& pb,
-                          int* group_offsets, int* row_of_assign, int* sorted_assign,
-                          int* dedup_offsets, int* dedup_token, int* expand_idx,
-                          void* x_dedup, void* x_sorted, hipStream_t s);
+// dst[r] = src[index[r] / div] for r < *count, per pass: count, index are
+// base pointers advanced by count_stride / index_stride per layout j.
+hipError_t launch_gather_rows(const int* count, int count_stride, const int* index,
+                              long long index_stride, int div, const void* src, void* dst,
+                              int row_bytes, int src_rows, int64_t max_rows, const PassArgs& pa,
+                              hipStream_t s);
 
-// Grouped GEMM.  tile_off / tile_group may be null: they are then computed
-// into scratch from group_offsets.
+// Grouped GEMM of one pass.  GEMM1 reads its rows through a_index when it
+// is non-null (row n of the pass = src[a_index[n] / a_div]), else rows are
+// contiguous in x_sorted.  Per-pass arrays advance by the given strides per
+// layout j; tile_off / tile_group may be null, and are then computed into
+// scratch from group_offsets.
+struct GemmPass {
+  const void* a_src;      // GEMM1 row source: x, x_dedup or x_sorted
+  int a_src_rows;         // rows of a_src (bounds of the gather)
+  const int* a_index;     // per-row source index or null
+  long long a_index_stride;
+  int a_div;
+  const int* group_offsets;
+  const int* tile_off;
+  const int* tile_group;
+  int go_stride, tg_stride;
+};
 size_t gmm_scratch_bytes(const Dims& d);
-hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const void* x_sorted,
-                      const int* group_offsets, const int* tile_off, const int* tile_group,
-                      const int* slot_expert,
-                      const void* wg, const void* wu, const void* wd, void* act, void* out,
-                      int64_t max_rows, void* scratch, hipStream_t s);
+hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const GemmPass& gp,
+                      const int* slot_expert, const void* wg, const void* wu, const void* wd,
+                      void* act, void* out, int64_t max_rows, void* scratch, hipStream_t s);
 
-hipError_t launch_combine(const Dims& d, const PassArgs& pa, const void* out,
-                          const int* row_of_assign, const float* gate, void* y,
-                          hipStream_t s);
+// Combine of one pass; row_of_assign advances by roa_stride per row_of_assign
+// set of the pass's layout.  Rows at or past max_rows are treated as absent.
+hipError_t launch_combine(const Dims& d, const PassArgs& pa, const LayoutSet& ls, const void* out,
+                          const int* row_of_assign, long long roa_stride, int64_t max_rows,
+                          const float* gate, void* y, hipStream_t s);
 
 }  // namespace moe

@@ -51,14 +51,18 @@ constexpr int BNB = 256;  // weight rows per tile
 #endif
 
 struct GemmParams {
-  const uint16_t* A;
-  const uint16_t* B0;  // gate weights (GEMM1) or down weights (GEMM2)
-  const uint16_t* B1;  // up weights (GEMM1)
-  size_t b_stride;     // elements per expert
+  const uint16_t* A;       // row source (whole array; rows past a group read as zero)
+  const int* a_index;      // row n of the pass = A row a_index[n] / a_div, or n when null
+  long long a_index_stride;
+  int a_div, a_rows;       // a_rows: rows of A (its byte range)
+  const uint16_t* B0;      // gate weights (GEMM1) or down weights (GEMM2)
+  const uint16_t* B1;      // up weights (GEMM1)
+  size_t b_stride;         // elements per expert
   uint16_t* C;
   const int* group_offsets;
   const int* tile_off;
   const int* tile_group;
+  int go_stride, tg_stride;  // per layout j
   const int* slot_expert;
   int G, K, Nout, lo_slot, e_base, e_res, n_ntiles;
   long long max_rows;
@@ -157,8 +161,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
 
   PassInfo pi = resolve_pass(P.pa);
   if (!pi.active) return;
-  const int total_mt = P.tile_off[P.G];
-  if (P.group_offsets[P.G] > P.max_rows) return;  // malformed offsets: touch nothing
+  const int* group_offsets = P.group_offsets + (size_t)pi.j * P.go_stride;
+  const int* tile_off = P.tile_off + (size_t)pi.j * P.go_stride;
+  const int* tile_group = P.tile_group + (size_t)pi.j * P.tg_stride;
+  const int total_mt = tile_off[P.G];
+  if (group_offsets[P.G] > P.max_rows) return;  // malformed offsets: touch nothing
   const int total = total_mt * P.n_ntiles;
   const int per_xcd = (total + 7) >> 3;
   const int bid = blockIdx.x;
@@ -167,9 +174,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   if (L >= total) return;
   const int nt = L / total_mt;
   const int mt = L - nt * total_mt;
-  const int g = P.tile_group[mt];
-  const int gend = P.group_offsets[g + 1];
-  const int row0 = P.group_offsets[g] + (mt - P.tile_off[g]) * BM;
+  const int g = tile_group[mt];
+  const int gend = group_offsets[g + 1];
+  const int row0 = group_offsets[g] + (mt - tile_off[g]) * BM;
   if (row0 < 0 || row0 >= gend || gend > P.max_rows) return;
   const int rows = min(BM, gend - row0);
   const int e = P.slot_expert[P.lo_slot + g] - P.e_base;
@@ -182,8 +189,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   const int K = P.K;
   const int KT = K / BK;
 
-  const __amdgpu_buffer_rsrc_t ra_r =
-      make_rsrc(P.A + (size_t)row0 * K, (unsigned)rows * K * 2);
+  // A as one raw buffer over its whole source; each lane's rows come from
+  // the row index (gathered rows) or are the pass rows themselves.  Rows
+  // past the group get an offset beyond the buffer and read as zero.
+  const __amdgpu_buffer_rsrc_t ra_r = make_rsrc(P.A, (unsigned)P.a_rows * K * 2);
+  const int* aidx = P.a_index ? P.a_index + (size_t)pi.j * P.a_index_stride : nullptr;
   __amdgpu_buffer_rsrc_t rb0, rb1;
   if (SWIGLU) {
     rb0 = make_rsrc(P.B0 + (size_t)e * P.b_stride + (size_t)nt * 128 * K, 128u * K * 2);
@@ -197,7 +207,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
     int row = (i * NW + w) * RPI + lane / CPR;
-    a_off[i] = row * K * 2 + (((lane % CPR) ^ swz<BK>(row)) << 4);
+    int src = -1;
+    if (row < rows) src = aidx ? aidx[row0 + row] / P.a_div : row0 + row;
+    a_off[i] = (src >= 0 && src < P.a_rows)
+                   ? src * K * 2 + (((lane % CPR) ^ swz<BK>(row)) << 4)
+                   : (int)0x80000000;
   }
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
@@ -283,11 +297,15 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
 // fp32 path (the tiny fp32 workload): one thread per output element.
 struct F32Params {
   const float* A;
+  const int* a_index;
+  long long a_index_stride;
+  int a_div, a_rows;
   const float* B0;
   const float* B1;
   size_t b_stride;
   float* C;
   const int* group_offsets;
+  int go_stride;
   const int* slot_expert;
   int G, K, Nout, lo_slot, e_base, e_res;
   long long max_rows;
@@ -298,18 +316,21 @@ template <bool SWIGLU>
 __global__ __launch_bounds__(256) void gmm_f32_kernel(F32Params P) {
   PassInfo pi = resolve_pass(P.pa);
   if (!pi.active) return;
+  const int* go = P.group_offsets + (size_t)pi.j * P.go_stride;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int row = (int)(idx / P.Nout), col = (int)(idx - (long long)row * P.Nout);
-  if (row >= P.group_offsets[P.G] || P.group_offsets[P.G] > P.max_rows) return;
+  if (row >= go[P.G] || go[P.G] > P.max_rows) return;
   int lo = 0, hi = P.G;
   while (hi - lo > 1) {
     int mid = (lo + hi) >> 1;
-    if (P.group_offsets[mid] <= row) lo = mid;
+    if (go[mid] <= row) lo = mid;
     else hi = mid;
   }
   const int e = P.slot_expert[P.lo_slot + lo] - P.e_base;
   if (e < 0 || e >= P.e_res) return;
-  const float* a = P.A + (size_t)row * P.K;
+  const int src = P.a_index ? P.a_index[(size_t)pi.j * P.a_index_stride + row] / P.a_div : row;
+  if (src < 0 || src >= P.a_rows) return;
+  const float* a = P.A + (size_t)src * P.K;
   const float* w0 = P.B0 + (size_t)e * P.b_stride + (size_t)col * P.K;
   float s0 = 0.0f, s1 = 0.0f;
   if (SWIGLU) {
@@ -373,20 +394,26 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(int G, int bm, int 
 }
 
 template <int BM, int BK, int NST, int NW>
-void launch_bf16(const Dims& d, const PassArgs& pa, const void* x_sorted,
-                 const int* group_offsets, const int* toff, const int* tgroup,
-                 const int* slot_expert, const void* wg, const void* wu, const void* wd,
-                 void* act, void* out, int64_t max_rows, hipStream_t s) {
+void launch_bf16(const Dims& d, const PassArgs& pa, const GemmPass& gp, const int* toff,
+                 const int* tgroup, int go_stride, int tg_stride, const int* slot_expert,
+                 const void* wg, const void* wu, const void* wd, void* act, void* out,
+                 int64_t max_rows, hipStream_t s) {
   const long long mt_ub = (max_rows + BM - 1) / BM + d.G_res;
   GemmParams p1;
-  p1.A = (const uint16_t*)x_sorted;
+  p1.A = (const uint16_t*)gp.a_src;
+  p1.a_index = gp.a_index;
+  p1.a_index_stride = gp.a_index_stride;
+  p1.a_div = gp.a_div;
+  p1.a_rows = gp.a_src_rows;
   p1.B0 = (const uint16_t*)wg;
   p1.B1 = (const uint16_t*)wu;
   p1.b_stride = (size_t)d.F * d.H;
   p1.C = (uint16_t*)act;
-  p1.group_offsets = group_offsets;
+  p1.group_offsets = gp.group_offsets;
   p1.tile_off = toff;
   p1.tile_group = tgroup;
+  p1.go_stride = go_stride;
+  p1.tg_stride = tg_stride;
   p1.slot_expert = slot_expert;
   p1.G = d.G_res;
   p1.K = d.H;
@@ -401,6 +428,10 @@ void launch_bf16(const Dims& d, const PassArgs& pa, const void* x_sorted,
   hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, true, NW>), dim3((unsigned)g1), dim3(64 * NW), 0, s, p1);
   GemmParams p2 = p1;
   p2.A = (const uint16_t*)act;
+  p2.a_index = nullptr;
+  p2.a_index_stride = 0;
+  p2.a_div = 1;
+  p2.a_rows = (int)max_rows;
   p2.B0 = (const uint16_t*)wd;
   p2.B1 = nullptr;
   p2.b_stride = (size_t)d.H * d.F;
@@ -419,37 +450,44 @@ size_t gmm_scratch_bytes(const Dims& d) {
          ((size_t)tile_map_len(d) * 4 + 255) / 256 * 256;
 }
 
-hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const void* x_sorted,
-                      const int* group_offsets, const int* tile_off, const int* tile_group,
+hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const GemmPass& gp,
                       const int* slot_expert, const void* wg, const void* wu, const void* wd,
                       void* act, void* out, int64_t max_rows, void* scratch, hipStream_t s) {
   if (d.bf16) {
-    const int* toff = tile_off;
-    const int* tgroup = tile_group;
+    const int* toff = gp.tile_off;
+    const int* tgroup = gp.tile_group;
+    int go_stride = gp.go_stride, tg_stride = gp.tg_stride;
     if (toff == nullptr || tgroup == nullptr) {
       int* t0 = (int*)scratch;
       int* t1 = (int*)((char*)scratch + ((size_t)(d.G_res + 1) * 4 + 255) / 256 * 256);
       long long lim = (long long)d.T * d.k;
       if (max_rows < lim) lim = max_rows;
       hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, d.G_res, d.gemm_bm,
-                         (int)lim, group_offsets, t0, t1, pa);
+                         (int)lim, gp.group_offsets, t0, t1, pa);
       toff = t0;
       tgroup = t1;
+      go_stride = 0;
+      tg_stride = 0;
     }
     if (d.gemm_bm == 256)
-      launch_bf16<MOE_GEMM_BIG>(d, pa, x_sorted, group_offsets, toff, tgroup, slot_expert, wg, wu, wd, act,
-                       out, max_rows, s);
+      launch_bf16<MOE_GEMM_BIG>(d, pa, gp, toff, tgroup, go_stride, tg_stride, slot_expert, wg,
+                                wu, wd, act, out, max_rows, s);
     else
-      launch_bf16<MOE_GEMM_SMALL>(d, pa, x_sorted, group_offsets, toff, tgroup, slot_expert, wg, wu, wd, act,
-                       out, max_rows, s);
+      launch_bf16<MOE_GEMM_SMALL>(d, pa, gp, toff, tgroup, go_stride, tg_stride, slot_expert, wg,
+                                  wu, wd, act, out, max_rows, s);
   } else {
     F32Params p1;
-    p1.A = (const float*)x_sorted;
+    p1.A = (const float*)gp.a_src;
+    p1.a_index = gp.a_index;
+    p1.a_index_stride = gp.a_index_stride;
+    p1.a_div = gp.a_div;
+    p1.a_rows = gp.a_src_rows;
     p1.B0 = (const float*)wg;
     p1.B1 = (const float*)wu;
     p1.b_stride = (size_t)d.F * d.H;
     p1.C = (float*)act;
-    p1.group_offsets = group_offsets;
+    p1.group_offsets = gp.group_offsets;
+    p1.go_stride = gp.go_stride;
     p1.slot_expert = slot_expert;
     p1.G = d.G_res;
     p1.K = d.H;
@@ -464,6 +502,10 @@ hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const void* x_sorted,
                        p1);
     F32Params p2 = p1;
     p2.A = (const float*)act;
+    p2.a_index = nullptr;
+    p2.a_index_stride = 0;
+    p2.a_div = 1;
+    p2.a_rows = (int)max_rows;
     p2.B0 = (const float*)wd;
     p2.B1 = nullptr;
     p2.b_stride = (size_t)d.H * d.F;

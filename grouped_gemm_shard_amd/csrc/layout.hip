@@ -1,0 +1,377 @@
+// a4 + a5: layouts of the passes and the permute.
+//
+// Rows of a pass are its assignments on resident slots in stable (slot, t,
+// j) order: the expert-sorted MoE input ("MoE ring-of-experts: TC Pallas
+// ring all-gather for the combine backward + x_sorted remat save", section
+// What).  With a capped buffer each resident shard keeps its first `cap`
+// rows ("Support moe_dropless_fallback=layer on the ragged all-to-all MoE
+// path", section Why: rows beyond the cap are dropped).  With dedup a token
+// is stored once per destination shard and re-expanded ("Moe dynamic
+// redundancy", code review: dedup and expand_indices), and the buffer is
+// never truncated below the exact count (the same review's truncation
+// comment).
+//
+// The layouts of every pass a call may take (the single pass and each
+// sequence chunk) are computed together, before any pass runs, in three
+// launches: local ranks (one wave per sort block and pass), one scan block
+// per pass (bases, group offsets, kept rows, GEMM tile schedule), and the
+// placement of every element (sorted_assign, row_of_assign, dedup lists,
+// expand indices).  Row copies are separate: the dedup buffer of a pass and,
+// for the standalone permute, x_sorted, one wavefront per row with 16-byte
+// loads and stores.
+#include "sort.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ int slot_key(const Dims& d, int s) {
+  return (s >= d.lo_slot && s < d.lo_slot + d.G_res) ? s - d.lo_slot : -1;
+}
+
+// First assignment j' <= j of the token on the same shard as slot s.
+__device__ __forceinline__ int first_on_shard(const Dims& d, const int* row, int j, int s) {
+  int sh = s / d.spd;
+  for (int jj = 0; jj < j; ++jj) {
+    int s2 = row[jj];
+    if (s2 >= 0 && s2 / d.spd == sh) return jj;
+  }
+  return j;
+}
+
+// Dedup key: local resident shard of the token's first assignment on it.
+__device__ __forceinline__ int dedup_key(const Dims& d, const int* row, int j) {
+  int s = row[j];
+  if (slot_key(d, s) < 0) return -1;
+  if (first_on_shard(d, row, j, s) != j) return -1;
+  return s / d.spd - d.res_lo;
+}
+
+struct PassGeom {
+  int n, c, capped, nelem, blk;
+  size_t e0;  // first element of the pass in the per-element arrays
+};
+
+__device__ __forceinline__ PassGeom pass_geom(const Dims& d, const LayoutSet& ls, int j) {
+  PassGeom g;
+  layout_pass(d, ls, j, &g.n, &g.c, &g.capped, &g.e0);
+  g.nelem = (d.T / g.n) * d.k;
+  g.blk = sort_block_len(g.nelem);
+  return g;
+}
+
+__device__ __forceinline__ int elem_token(const Dims& d, const PassGeom& g, int e) {
+  int i = e / d.k;
+  int lc = d.L / g.n;
+  int b = i / lc;
+  return b * d.L + g.c * lc + (i - b * lc);
+}
+
+// Rank of pass element e (relative to its dedup shard), from the packed
+// local rank and the block base.
+__device__ __forceinline__ int dedup_rank(const Dims& d, const LayoutBuffers& lb, const PassGeom& g,
+                                          int j, int e, int* key_out) {
+  unsigned v = lb.dkey[g.e0 + e];
+  int kd = packed_key(v);
+  *key_out = kd;
+  return lb.bh_dedup[((size_t)j * kSortBlocks + e / g.blk) * d.S_res + kd] + packed_rank(v);
+}
+
+template <int WHICH>  // bit 0: slot keys, bit 1: dedup keys
+__global__ __launch_bounds__(64) void layout_local_kernel(Dims d, LayoutSet ls,
+                                                          const int* __restrict__ soa,
+                                                          LayoutBuffers lb, int drop_check) {
+  __shared__ int run_s[kMaxSlots];
+  __shared__ int run_d[kMaxSlots];
+  const int j = blockIdx.y;
+  if (!layout_live(ls, j)) return;
+  const PassGeom g = pass_geom(d, ls, j);
+  const int e0 = blockIdx.x * g.blk, e1 = min(g.nelem, e0 + g.blk);
+  const int nb_s = key_bits(d.G_res), nb_d = key_bits(d.S_res);
+  for (int q = threadIdx.x; q < d.G_res; q += 64) run_s[q] = 0;
+  for (int q = threadIdx.x; q < d.S_res; q += 64) run_d[q] = 0;
+  __syncthreads();
+  for (int base = e0; base < e1; base += 64) {
+    const int e = base + lane_id();
+    const bool in = e < e1;
+    int jj = 0;
+    const int* row = soa;
+    if (in) {
+      jj = e % d.k;
+      row = soa + (size_t)elem_token(d, g, e) * d.k;
+    }
+    if (WHICH & 1) {
+      int ks = in ? slot_key(d, row[jj]) : -1;
+      if (drop_check && g.capped && ks >= 0) {
+        // the token was cut from this shard's dedup buffer: drop the row
+        int jr = first_on_shard(d, row, jj, row[jj]);
+        int kd;
+        int r = dedup_rank(d, lb, g, j, e - jj + jr, &kd);
+        if (r >= d.cap) ks = -1;
+      }
+      int r = wave_rank_step(ks, nb_s, run_s);
+      if (in) lb.skey[g.e0 + e] = pack_key(ks, r);
+    }
+    if (WHICH & 2) {
+      int kd = in ? dedup_key(d, row, jj) : -1;
+      int r = wave_rank_step(kd, nb_d, run_d);
+      if (in) lb.dkey[g.e0 + e] = pack_key(kd, r);
+    }
+  }
+  __syncthreads();
+  if (WHICH & 1)
+    for (int q = threadIdx.x; q < d.G_res; q += 64)
+      lb.bh_slot[((size_t)j * kSortBlocks + blockIdx.x) * d.G_res + q] = run_s[q];
+  if (WHICH & 2)
+    for (int q = threadIdx.x; q < d.S_res; q += 64)
+      lb.bh_dedup[((size_t)j * kSortBlocks + blockIdx.x) * d.S_res + q] = run_d[q];
+}
+
+// One block per pass.  Slot part: block bases, rows per slot, kept rows
+// (without dedup, a capped shard keeps the first `cap` rows of its bucket,
+// i.e. a prefix of each slot), group offsets, GEMM m-tile offsets and the
+// m-tile -> group map.  Dedup part: distinct tokens per shard, cut at the
+// cap when capped, and their offsets.
+__global__ __launch_bounds__(1024) void layout_scan_kernel(Dims d, LayoutSet ls, int which,
+                                                           LayoutBuffers lb) {
+  __shared__ int tmp[16];
+  __shared__ int excl[kMaxSlots];
+  __shared__ int totals[kMaxSlots];
+  __shared__ int dtotals[kMaxSlots];
+  const int j = blockIdx.x;
+  if (!layout_live(ls, j)) return;
+  const PassGeom pg = pass_geom(d, ls, j);
+  const bool capped = pg.capped && d.cap >= 0;
+  const int g = threadIdx.x;
+  int* bh_s = lb.bh_slot + (size_t)j * kSortBlocks * d.G_res;
+  int* bh_d = lb.bh_dedup + (size_t)j * kSortBlocks * d.S_res;
+  if (which & 1) scan_keys_over_blocks(bh_s, d.G_res, totals);
+  if (which & 2) scan_keys_over_blocks(bh_d, d.S_res, dtotals);
+  __syncthreads();
+  int* meta = lb.meta + (size_t)j * kLayoutMeta;
+  if (which & 1) {
+    int* kept = lb.kept + (size_t)j * d.G_res;
+    int* go = lb.group_offsets + (size_t)j * (d.G_res + 1);
+    int* toff = lb.tile_off + (size_t)j * (d.G_res + 1);
+    int* tgrp = lb.tile_group + (size_t)j * tile_map_len(d);
+    const bool own = g < d.G_res;
+    int tot = own ? totals[g] : 0;
+    int all;
+    int ex = block_exscan_1024(tot, tmp, &all);
+    if (own) excl[g] = ex;
+    __syncthreads();
+    int kp = tot;
+    if (own && capped && !d.dedup) {
+      int first = ((g + d.lo_slot) / d.spd) * d.spd - d.lo_slot;
+      int bstart = ex - excl[first];
+      kp = min(max(d.cap - bstart, 0), tot);
+    }
+    if (own) kept[g] = kp;
+    int nrows;
+    int off = block_exscan_1024(own ? kp : 0, tmp, &nrows);
+    if (own) go[g] = off;
+    int ntiles;
+    const int tiles = own ? (kp + d.gemm_bm - 1) / d.gemm_bm : 0;
+    int to = block_exscan_1024(tiles, tmp, &ntiles);
+    if (own) {
+      toff[g] = to;
+      for (int m = 0; m < tiles; ++m) tgrp[to + m] = g;
+    }
+    if (g == 0) {
+      go[d.G_res] = nrows;
+      toff[d.G_res] = ntiles;
+      meta[0] = nrows;
+    }
+  }
+  if (which & 2) {
+    int* dkept = lb.dedup_kept + (size_t)j * d.S_res;
+    int* doff = lb.dedup_offsets + (size_t)j * (d.S_res + 1);
+    const bool own = g < d.S_res;
+    int u = own ? dtotals[g] : 0;
+    int ku = capped ? min(u, d.cap) : u;
+    if (own) dkept[g] = ku;
+    int nu;
+    int off = block_exscan_1024(own ? ku : 0, tmp, &nu);
+    if (own) doff[g] = off;
+    if (g == 0) {
+      doff[d.S_res] = nu;
+      meta[1] = nu;
+    }
+  }
+}
+
+// Places every element of every pass: row_of_assign, sorted_assign and, with
+// dedup, the dedup token lists and the expand indices.
+__global__ __launch_bounds__(256) void layout_place_kernel(Dims d, LayoutSet ls,
+                                                           const int* __restrict__ soa,
+                                                           LayoutBuffers lb) {
+  const int j = blockIdx.y;
+  if (!layout_live(ls, j)) return;
+  const PassGeom g = pass_geom(d, ls, j);
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= g.nelem) return;
+  const int jj = e % d.k;
+  const int t = elem_token(d, g, e);
+  const int a = t * d.k + jj;
+  const size_t srow = layout_row_base(d, ls, j);
+  int* roa = lb.row_of_assign + (size_t)layout_set_of(ls, j) * ((size_t)d.T * d.k);
+  if (d.dedup) {
+    unsigned vd = lb.dkey[g.e0 + e];
+    int kd = packed_key(vd);
+    if (kd >= 0) {
+      int r = lb.bh_dedup[((size_t)j * kSortBlocks + e / g.blk) * d.S_res + kd] + packed_rank(vd);
+      if (r < lb.dedup_kept[(size_t)j * d.S_res + kd])
+        lb.dedup_token[layout_dedup_base(d, ls, j) + lb.dedup_offsets[(size_t)j * (d.S_res + 1) + kd] + r] = t;
+    }
+  }
+  unsigned v = lb.skey[g.e0 + e];
+  int ks = packed_key(v);
+  int pos = -1;
+  if (ks >= 0) {
+    int r = lb.bh_slot[((size_t)j * kSortBlocks + e / g.blk) * d.G_res + ks] + packed_rank(v);
+    if (r < lb.kept[(size_t)j * d.G_res + ks]) pos = lb.group_offsets[(size_t)j * (d.G_res + 1) + ks] + r;
+  }
+  roa[a] = pos;
+  if (pos < 0) return;
+  lb.sorted_assign[srow + pos] = a;
+  if (d.dedup) {
+    const int* row = soa + (size_t)t * d.k;
+    int jr = first_on_shard(d, row, jj, row[jj]);
+    int kd;
+    int r = dedup_rank(d, lb, g, j, e - jj + jr, &kd);
+    lb.expand_idx[srow + pos] = lb.dedup_offsets[(size_t)j * (d.S_res + 1) + kd] + r;
+  }
+}
+
+// Copies one row of `nbytes` (a multiple of 16) with the whole wavefront.
+__device__ __forceinline__ void wave_copy_row(char* __restrict__ dst, const char* __restrict__ src,
+                                              int nbytes) {
+  int off = lane_id() * 16;
+  for (; off + 3 * 1024 < nbytes; off += 4 * 1024) {
+    uint4 v0 = *(const uint4*)(src + off);
+    uint4 v1 = *(const uint4*)(src + off + 1024);
+    uint4 v2 = *(const uint4*)(src + off + 2048);
+    uint4 v3 = *(const uint4*)(src + off + 3072);
+    *(uint4*)(dst + off) = v0;
+    *(uint4*)(dst + off + 1024) = v1;
+    *(uint4*)(dst + off + 2048) = v2;
+    *(uint4*)(dst + off + 3072) = v3;
+  }
+  for (; off < nbytes; off += 1024) *(uint4*)(dst + off) = *(const uint4*)(src + off);
+}
+
+// dst[r] = src[index[r] / div] for r < count (count read on the device),
+// one wavefront per row; count and index belong to the pass's layout j.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const int* __restrict__ count,
+                                                          int count_stride,
+                                                          const int* __restrict__ index,
+                                                          long long index_stride, int div,
+                                                          const char* __restrict__ src,
+                                                          char* __restrict__ dst, int row_bytes,
+                                                          int src_rows, long long max_rows,
+                                                          PassArgs pa) {
+  PassInfo pi = resolve_pass(pa);
+  if (!pi.active) return;
+  const int r = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int cnt = count[(size_t)pi.j * count_stride];
+  if (r >= cnt || r >= max_rows) return;
+  const int s = index[(size_t)pi.j * index_stride + r] / div;
+  if (s < 0 || s >= src_rows) return;
+  wave_copy_row(dst + (size_t)r * row_bytes, src + (size_t)s * row_bytes, row_bytes);
+}
+
+inline size_t al256(size_t b) { return (b + 255) / 256 * 256; }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Buffers and launches
+// ---------------------------------------------------------------------------
+
+size_t layout_scratch_bytes(const Dims& d, const LayoutSet& ls) {
+  const int np = layout_num_passes(ls);
+  const size_t tk = (size_t)d.T * d.k;
+  const size_t elems = layout_total_elems(d, ls);
+  size_t b = 0;
+  b += al256(elems * 4) * 2;                                     // skey, dkey
+  b += al256((size_t)np * kSortBlocks * d.G_res * 4);            // bh_slot
+  b += al256((size_t)np * kSortBlocks * d.S_res * 4);            // bh_dedup
+  b += al256((size_t)np * d.G_res * 4);                          // kept
+  b += al256((size_t)np * d.S_res * 4);                          // dedup_kept
+  b += al256((size_t)np * (d.G_res + 1) * 4) * 2;                // group_offsets, tile_off
+  b += al256((size_t)np * tile_map_len(d) * 4);                  // tile_group
+  b += al256((size_t)np * (d.S_res + 1) * 4);                    // dedup_offsets
+  b += al256((size_t)np * kLayoutMeta * 4);                      // meta
+  b += al256((size_t)layout_num_sets(ls) * tk * 4);              // row_of_assign
+  b += al256(elems * 4) * 2;                                     // sorted_assign, expand_idx
+  b += al256(layout_total_dedup(d, ls) * 4);                     // dedup_token
+  return b;
+}
+
+LayoutBuffers carve_layout(const Dims& d, const LayoutSet& ls, void* scratch) {
+  const int np = layout_num_passes(ls);
+  const size_t tk = (size_t)d.T * d.k;
+  const size_t elems = layout_total_elems(d, ls);
+  char* p = (char*)scratch;
+  LayoutBuffers lb;
+  auto take = [&](size_t bytes) {
+    char* q = p;
+    p += al256(bytes);
+    return q;
+  };
+  lb.skey = (unsigned*)take(elems * 4);
+  lb.dkey = (unsigned*)take(elems * 4);
+  lb.bh_slot = (int*)take((size_t)np * kSortBlocks * d.G_res * 4);
+  lb.bh_dedup = (int*)take((size_t)np * kSortBlocks * d.S_res * 4);
+  lb.kept = (int*)take((size_t)np * d.G_res * 4);
+  lb.dedup_kept = (int*)take((size_t)np * d.S_res * 4);
+  lb.group_offsets = (int*)take((size_t)np * (d.G_res + 1) * 4);
+  lb.tile_off = (int*)take((size_t)np * (d.G_res + 1) * 4);
+  lb.tile_group = (int*)take((size_t)np * tile_map_len(d) * 4);
+  lb.dedup_offsets = (int*)take((size_t)np * (d.S_res + 1) * 4);
+  lb.meta = (int*)take((size_t)np * kLayoutMeta * 4);
+  lb.row_of_assign = (int*)take((size_t)layout_num_sets(ls) * tk * 4);
+  lb.sorted_assign = (int*)take(elems * 4);
+  lb.expand_idx = (int*)take(elems * 4);
+  lb.dedup_token = (int*)take(layout_total_dedup(d, ls) * 4);
+  return lb;
+}
+
+hipError_t launch_layout(const Dims& d, const LayoutSet& ls, const int* soa,
+                         const LayoutBuffers& lb, hipStream_t s) {
+  const int np = layout_num_passes(ls);
+  const dim3 lb64(64), lgrid(kSortBlocks, np), sb(1024), sgrid(np);
+  // Static capped + dedup: the cut of each shard's dedup buffer decides which
+  // rows drop, so the dedup ranks are scanned before the slot keys.
+  const bool two_round = d.dedup && d.cap >= 0 &&
+                         ((ls.has_single && ls.single_capped) || (ls.chunk_cnt && ls.chunk_capped));
+  if (!d.dedup) {
+    hipLaunchKernelGGL(layout_local_kernel<1>, lgrid, lb64, 0, s, d, ls, soa, lb, 0);
+    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 1, lb);
+  } else if (!two_round) {
+    hipLaunchKernelGGL(layout_local_kernel<3>, lgrid, lb64, 0, s, d, ls, soa, lb, 0);
+    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 3, lb);
+  } else {
+    hipLaunchKernelGGL(layout_local_kernel<2>, lgrid, lb64, 0, s, d, ls, soa, lb, 0);
+    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 2, lb);
+    hipLaunchKernelGGL(layout_local_kernel<1>, lgrid, lb64, 0, s, d, ls, soa, lb, 1);
+    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 1, lb);
+  }
+  const int maxe = (d.T / layout_min_chunks(ls)) * d.k;
+  hipLaunchKernelGGL(layout_place_kernel, dim3((maxe + 255) / 256, np), dim3(256), 0, s, d, ls,
+                     soa, lb);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const int* count, int count_stride, const int* index,
+                              long long index_stride, int div, const void* src, void* dst,
+                              int row_bytes, int src_rows, int64_t max_rows, const PassArgs& pa,
+                              hipStream_t s) {
+  if (max_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)((max_rows + 3) / 4)), dim3(256), 0, s,
+                     count, count_stride, index, index_stride, div, (const char*)src, (char*)dst,
+                     row_bytes, src_rows, (long long)max_rows, pa);
+  return hipGetLastError();
+}
+
+}  // namespace moe
