@@ -524,24 +524,34 @@ def layer_plain_tokens(p: Problem, logits, x, w_gate, w_up, w_down, tokens):
     assignments on resident shards.  Dedup, rerouting and chunking do not
     change it ([FALLBACK] Tests: the fallback matches the dropless model;
     [DRED]: a replica computes its home expert's function).  Used at full
-    sizes on a sample of tokens."""
+    sizes on a sample of tokens; each expert's weights are read once
+    (w_gate[e] etc. may be lazy accessors)."""
     idx, gates = route(logits, p.top_k, p.gate)
     counts = expert_counts(idx, p.num_experts)
     slot_expert, ndiv, replica_slot = plan_redundancy(counts, p)
     slot = assign_slots(idx, p, ndiv, replica_slot)
     k, spd = p.top_k, p.spd
+    tokens = [int(t) for t in tokens]
+    by_expert = {}
+    for t in tokens:
+        for j in range(k):
+            s = int(slot[t, j])
+            if p.res_lo <= s // spd < p.res_hi:
+                e = int(slot_expert[s]) - p.res_lo * p.e_loc
+                by_expert.setdefault(e, []).append((t, j))
+    o = {}
+    for e in sorted(by_expert):
+        pairs = by_expert[e]
+        rows = np.stack([np.asarray(x[t], dtype=np.float64) for (t, _) in pairs])
+        _, out = expert_ffn(rows, w_gate[e], w_up[e], w_down[e], p.bf16)
+        for r, tj in enumerate(pairs):
+            o[tj] = out[r]
     y = np.zeros((len(tokens), p.hidden), dtype=np.float64)
-    xs = np.asarray(x)
     for i, t in enumerate(tokens):
         acc = np.zeros(p.hidden, dtype=np.float64)
         for j in range(k):
-            s = int(slot[t, j])
-            if not (p.res_lo <= s // spd < p.res_hi):
-                continue
-            e = int(slot_expert[s]) - p.res_lo * p.e_loc
-            _, o = expert_ffn(np.asarray(xs[t:t + 1], dtype=np.float64),
-                              w_gate[e], w_up[e], w_down[e], p.bf16)
-            acc = acc + gates[t, j] * o[0]
+            if (t, j) in o:
+                acc = acc + gates[t, j] * o[(t, j)]
         y[i] = acc
     if p.bf16:
         y = round_bf16(y)
