@@ -4,10 +4,12 @@
 
 A step is one call of the whole layer in LAYER mode (route, counts, plan,
 capacity and overflow check, then the capped pass or the chunked dropless
-fallback: permute, grouped SwiGLU GEMM, combine) on one batch of seeded
-synthetic input already resident in HBM.  The default workload is the mid
-bf16 layer (T=4096, H=1024, F=512, E=32, top-4, 8 virtual shards, Zipf-skewed
-routing that overflows buffer factor 1.5 and runs 4 dropless chunks).
+fallback: layout, grouped SwiGLU GEMM gathering its rows, combine) on one
+batch of seeded synthetic input already resident in HBM.  The default
+workload is the mid bf16 layer (T=4096, H=1024, F=512, E=32, top-4, 8
+virtual shards, Zipf-skewed routing that overflows buffer factor 1.5 and
+runs the 4-chunk dropless fallback; the capped buffer of the 8 resident
+shards holds all 4 chunks, so they run as one pass).
 
 After the timed steps, the grouped GEMM, the permute and the combine of the
 same passes are timed one call at a time with HIP events on the stream they
@@ -63,10 +65,15 @@ def log(*a):
 
 
 def pass_list(p, info):
-    """The passes LAYER mode took: chunks when the flag fired, else one
-    capped pass."""
+    """The passes LAYER mode took, as (chunks, chunk, capped) of the step API:
+    when the flag fired, the dropless chunks q at a time (q consecutive
+    chunks of n are chunk b of n/q), else the one capped pass."""
     if info[0]:
-        return [(p.num_chunks, c, 0) for c in range(p.num_chunks)]
+        n = p.num_chunks
+        q = g.layer_chunks_per_pass(p, g.MODE_LAYER)
+        if n % q:
+            q = 1
+        return [(n // q, b, 0) for b in range(n // q)]
     return [(1, 0, 1)]
 
 
@@ -287,7 +294,8 @@ def main():
         "config": {"workload": w.name, "tokens": w.tokens, "hidden": w.hidden, "ffn": w.ffn,
                    "experts": w.num_experts, "top_k": w.top_k, "shards": w.num_shards,
                    "buffer_factor": w.factor, "chunks": w.num_chunks, "mode": "LAYER",
-                   "fallback_ran": int(info[1])},
+                   "fallback_ran": int(info[1]),
+                   "chunks_per_pass": g.layer_chunks_per_pass(p, g.MODE_LAYER)},
         "gemm": {"tflops": round(gemm_tflops, 2), "frac_mfma_peak": round(gemm_tflops / peak_mm, 4),
                  "gbs": round(gemm_gbs, 1), "arith_intensity": round(ai, 1),
                  "us_per_layer": round(kf["t_gmm"] * 1e6, 2), "rows": kf["rows"]},

@@ -30,6 +30,7 @@ MODE_LAYER, MODE_FORCE_DROPLESS, MODE_CAPPED_ONLY, MODE_FORCE_CHUNKED = 0, 1, 2,
 GATES = {"softmax": 0, "sigmoid": 1}
 
 EXPORTED = ["moe_workspace_bytes", "moe_pass_max_rows", "moe_layer_workspace_bytes",
+            "moe_layer_chunks_per_pass",
             "moe_route", "moe_count_overflow", "moe_permute", "moe_gmm_swiglu",
             "moe_combine", "moe_layer_dropless_chunked", "moe_status_string"]
 
@@ -113,6 +114,7 @@ def _load():
         "moe_workspace_bytes": [P, ctypes.POINTER(sz)],
         "moe_pass_max_rows": [P, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)],
         "moe_layer_workspace_bytes": [P, i32, ctypes.POINTER(sz)],
+        "moe_layer_chunks_per_pass": [P, i32, ctypes.POINTER(i32)],
         "moe_route": [P, vp, vp, vp, vp],
         "moe_count_overflow": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_permute": [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp,
@@ -186,6 +188,13 @@ def layer_workspace_bytes(p: Problem, mode: int) -> int:
     out = ctypes.c_size_t()
     _check("moe_layer_workspace_bytes",
            _lib().moe_layer_workspace_bytes(ctypes.byref(p.c()), mode, ctypes.byref(out)))
+    return out.value
+
+
+def layer_chunks_per_pass(p: Problem, mode: int) -> int:
+    out = ctypes.c_int32()
+    _check("moe_layer_chunks_per_pass",
+           _lib().moe_layer_chunks_per_pass(ctypes.byref(p.c()), mode, ctypes.byref(out)))
     return out.value
 
 

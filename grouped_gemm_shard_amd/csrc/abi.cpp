@@ -87,9 +87,10 @@ int make_dims(const moe_problem* p, Dims* d) {
   return MOE_OK;
 }
 
-// Row bounds of a pass of n chunks, capped or not.
-void pass_bounds(const Dims& d, int n, int capped, int64_t* rows, int64_t* drows) {
-  const int64_t tc = d.T / n;
+// Row bounds of a pass over a window of lw positions of every sequence,
+// capped or not.
+void window_bounds(const Dims& d, int lw, int capped, int64_t* rows, int64_t* drows) {
+  const int64_t tc = (int64_t)(d.T / d.L) * lw;
   const int64_t per_tok = d.k < d.spd ? d.k : d.spd;  // a token's rows on one shard
   int64_t r = tc * d.k;
   int64_t u = d.dedup ? tc * d.S_res : 0;
@@ -103,6 +104,11 @@ void pass_bounds(const Dims& d, int n, int capped, int64_t* rows, int64_t* drows
   }
   *rows = r;
   *drows = u;
+}
+
+// Row bounds of chunk passes of n chunks.
+void pass_bounds(const Dims& d, int n, int capped, int64_t* rows, int64_t* drows) {
+  window_bounds(d, d.L / n, capped, rows, drows);
 }
 
 // The passes a layer call in `mode` may take, as bounds.
@@ -122,57 +128,73 @@ void layer_bounds(const Dims& d, int mode, int64_t* rows, int64_t* drows) {
 }
 
 // The layout set of a single static pass (chunk c of n, capped or not).
-LayoutSet single_layout(int n, int c, int capped) {
+LayoutSet single_layout(const Dims& d, int n, int c, int capped) {
   LayoutSet ls;
   memset(&ls, 0, sizeof(ls));
   if (n == 1) {
     ls.has_single = 1;
     ls.single_capped = capped;
   } else {
-    ls.n_chunks = n;
-    ls.chunk_lo = c;
-    ls.chunk_cnt = 1;
-    ls.chunk_capped = capped;
+    ls.win = d.L / n;
+    ls.w_lo = c;
+    ls.w_cnt = 1;
+    ls.w_capped = capped;
   }
   return ls;
 }
 
+// Chunks of the dropless fallback that run as one pass: the most
+// consecutive chunks whose worst-case rows still fit the buffers sized for
+// the call (rows, drows), so that running them together never needs more
+// memory than the capped buffer.  Their tokens are disjoint and every row
+// of the grouped GEMM is computed independently of the others, so y is the
+// same as chunk by chunk.
+int chunk_batch(const Dims& d, int64_t rows, int64_t drows) {
+  const int n = d.n_default, lc = d.L / n;
+  int q = 1;
+  for (int cand = 2; cand <= n; ++cand) {
+    int64_t r, u;
+    window_bounds(d, cand * lc, 0, &r, &u);
+    if (r > rows || u > drows) break;
+    q = cand;
+  }
+  return q;
+}
+
 // The passes of a layer call in `mode`.  LAYER with a cap: the single pass
-// (layout 0) or the dropless chunks (layouts 1..n), chosen on the device by
-// the overflow flag.  Without overflow no shard exceeds the cap, so the
-// single pass keeps every row and is laid out uncapped.
-LayoutSet layer_layout(const Dims& d, int mode, const int* ovf) {
+// (layout 0) or the dropless chunks in batches of q (layouts 1..), chosen on
+// the device by the overflow flag.  Without overflow no shard exceeds the
+// cap, so the single pass keeps every row and is laid out uncapped.
+LayoutSet layer_layout(const Dims& d, int mode, int q, const int* ovf) {
   LayoutSet ls;
   memset(&ls, 0, sizeof(ls));
   const int n = d.n_default;
+  ls.win = (d.L / n) * q;
   switch (mode) {
     case MOE_MODE_LAYER:
       ls.has_single = 1;
       if (d.cap >= 0) {
-        ls.n_chunks = n;
-        ls.chunk_cnt = n;
+        ls.w_cnt = (n + q - 1) / q;
         ls.ovf = ovf;
       }
       break;
     case MOE_MODE_FORCE_DROPLESS: ls.has_single = 1; break;
     case MOE_MODE_CAPPED_ONLY: ls.has_single = 1; ls.single_capped = 1; break;
-    default: ls.n_chunks = n; ls.chunk_cnt = n; break;
+    default: ls.w_cnt = (n + q - 1) / q; break;
   }
   return ls;
 }
 
 // Static pass arguments of layout j.
 PassArgs static_pass(const Dims& d, const LayoutSet& ls, int j) {
-  PassArgs pa;
+  int s0, lw, capped;
   size_t e0;
-  layout_pass(d, ls, j, &pa.n, &pa.c, &pa.capped, &e0);
-  pa.ovf = nullptr;
-  pa.j = j;
-  return pa;
+  layout_pass(d, ls, j, &s0, &lw, &capped, &e0);
+  return static_pass_args(s0, lw, capped, j, d.L);
 }
 
 size_t step_scratch(const Dims& d) {
-  size_t a = count_scratch_bytes(d), b = layout_scratch_bytes(d, single_layout(1, 0, 1)),
+  size_t a = count_scratch_bytes(d), b = layout_scratch_bytes(d, single_layout(d, 1, 0, 1)),
          c = gmm_scratch_bytes(d);
   size_t m = a > b ? a : b;
   return m > c ? m : c;
@@ -303,7 +325,20 @@ int moe_layer_workspace_bytes(const moe_problem* p, int32_t mode, size_t* bytes)
     return MOE_EINVAL;
   int64_t rows, drows;
   layer_bounds(d, mode, &rows, &drows);
-  *bytes = carve_layer(d, layer_layout(d, mode, nullptr), rows, drows, nullptr).bytes;
+  const int q = chunk_batch(d, rows, drows);
+  *bytes = carve_layer(d, layer_layout(d, mode, q, nullptr), rows, drows, nullptr).bytes;
+  return MOE_OK;
+}
+
+int moe_layer_chunks_per_pass(const moe_problem* p, int32_t mode, int32_t* chunks) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (chunks == nullptr || mode < MOE_MODE_LAYER || mode > MOE_MODE_FORCE_CHUNKED)
+    return MOE_EINVAL;
+  int64_t rows, drows;
+  layer_bounds(d, mode, &rows, &drows);
+  *chunks = chunk_batch(d, rows, drows);
   return MOE_OK;
 }
 
@@ -354,7 +389,7 @@ int moe_permute(const moe_problem* p, int32_t num_chunks, int32_t chunk, int32_t
   int64_t rb, ub;
   pass_bounds(d, num_chunks, capped, &rb, &ub);
   if (max_rows < rb || (d.dedup && max_dedup_rows < ub)) return MOE_ECAPACITY;
-  const LayoutSet ls = single_layout(num_chunks, chunk, capped);
+  const LayoutSet ls = single_layout(d, num_chunks, chunk, capped);
   if (ws_bytes < layout_scratch_bytes(d, ls)) return MOE_ECAPACITY;
   if (max_rows >= (1ll << 31) || max_dedup_rows >= (1ll << 31)) return MOE_EUNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
@@ -371,7 +406,8 @@ int moe_permute(const moe_problem* p, int32_t num_chunks, int32_t chunk, int32_t
   hipError_t e = launch_layout(d, ls, slot_of_assign, lb, s);
   if (e != hipSuccess) return MOE_EHIP;
   const int row_bytes = d.H * (d.bf16 ? 2 : 4);
-  const PassArgs pa{num_chunks, chunk, capped, nullptr, 0};
+  const int lc = d.L / num_chunks;
+  const PassArgs pa = static_pass_args(chunk * lc, lc, capped, 0, d.L);
   if (d.dedup) {
     e = launch_gather_rows(lb.meta + 1, kLayoutMeta, dedup_token, 0, 1, x, x_dedup, row_bytes,
                            d.T, max_dedup_rows, pa, s);
@@ -401,7 +437,7 @@ int moe_gmm_swiglu(const moe_problem* p, const void* x_sorted, const int32_t* gr
   if (max_rows >= (1ll << 31) / 2) return MOE_EUNSUPPORTED;
   if (ws_bytes < gmm_scratch_bytes(d)) return MOE_ECAPACITY;
   if (!fits_rsrc(d, max_rows, 0)) return MOE_EUNSUPPORTED;
-  PassArgs pa{1, 0, 0, nullptr, 0};
+  const PassArgs pa = static_pass_args(0, d.L, 0, 0, d.L);
   GemmPass gp;
   memset(&gp, 0, sizeof(gp));
   gp.a_src = x_sorted;
@@ -421,8 +457,9 @@ int moe_combine(const moe_problem* p, int32_t num_chunks, int32_t chunk, const v
     return MOE_EINVAL;
   if (!expert_out || !row_of_assign || !topk_gate || !y) return MOE_EINVAL;
   if (misaligned(expert_out, 16) || misaligned(y, 16)) return MOE_EINVAL;
-  PassArgs pa{num_chunks, chunk, 0, nullptr, 0};
-  const LayoutSet ls = single_layout(num_chunks, chunk, 0);
+  const int lc = d.L / num_chunks;
+  const PassArgs pa = static_pass_args(chunk * lc, lc, 0, 0, d.L);
+  const LayoutSet ls = single_layout(d, num_chunks, chunk, 0);
   return hip_status(launch_combine(d, pa, ls, expert_out, row_of_assign, 0, INT64_MAX, topk_gate,
                                    y, (hipStream_t)stream));
 }
@@ -442,11 +479,12 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
   int64_t rows, drows;
   layer_bounds(d, mode, &rows, &drows);
   if (!fits_rsrc(d, rows, drows)) return MOE_EUNSUPPORTED;
-  LayerWs w0 = carve_layer(d, layer_layout(d, mode, nullptr), rows, drows, nullptr);
+  const int q = chunk_batch(d, rows, drows);
+  LayerWs w0 = carve_layer(d, layer_layout(d, mode, q, nullptr), rows, drows, nullptr);
   if (ws_bytes < w0.bytes) return MOE_ECAPACITY;
   // status[1] (the overflow flag) lives in the workspace
-  LayerWs w = carve_layer(d, layer_layout(d, mode, nullptr), rows, drows, (char*)ws);
-  const LayoutSet ls = layer_layout(d, mode, w.status + 1);
+  LayerWs w = carve_layer(d, layer_layout(d, mode, q, nullptr), rows, drows, (char*)ws);
+  const LayoutSet ls = layer_layout(d, mode, q, w.status + 1);
   hipStream_t s = (hipStream_t)stream;
 
   hipError_t e = launch_route(d, logits, w.topk_idx, w.topk_gate, s);
@@ -458,11 +496,13 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
   e = launch_layout(d, ls, w.slot_of_assign, lb, s);
   if (e != hipSuccess) return MOE_EHIP;
 
-  const int n = d.n_default;
   if (ls.ovf != nullptr) {
-    // the device decides: the single pass alone, or n dropless chunks
-    for (int c = 0; c < n; ++c) {
-      PassArgs pa{n, c, 0, ls.ovf, 0};
+    // the device decides: the single pass alone, or the batches of dropless
+    // chunks
+    for (int b = 0; b < ls.w_cnt; ++b) {
+      const int s0 = b * ls.win;
+      PassArgs pa = static_pass_args(s0, ls.win < d.L - s0 ? ls.win : d.L - s0, 0, b, d.L);
+      pa.ovf = ls.ovf;
       st = run_pass(d, pa, ls, lb, x, w_gate, w_up, w_down, y, w, rows, drows, s);
       if (st != MOE_OK) return st;
     }

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void combine_kernel(Dims d, PassArgs pa, Layou
 hipError_t launch_combine(const Dims& d, const PassArgs& pa, const LayoutSet& ls, const void* out,
                           const int* row_of_assign, long long roa_stride, int64_t max_rows,
                           const float* gate, void* y, hipStream_t s) {
-  const int ntok = d.T / (pa.ovf != nullptr ? 1 : pa.n);
+  const int ntok = pa.ovf != nullptr ? d.T : (d.T / d.L) * pa.lw;
   dim3 grid((ntok + 3) / 4), block(256);
   if (d.bf16)
     hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, s, d, pa, ls, out, row_of_assign,

@@ -37,45 +37,55 @@ struct Dims {
   int gemm_bm;   // grouped-GEMM tile height (128 or 256)
 };
 
-// One pass of the GEMM / combine sequence.  Static passes carry (n, c,
-// capped) and the index j of their layout directly.  A dynamic pass
-// (ovf != nullptr) is one of the LAYER-mode pass slots: when *ovf is set it
-// is chunk c of n (layout 1 + c), else slot 0 runs the single pass over all
-// tokens (layout 0) and slots c > 0 are inactive.  Every kernel of a pass
-// resolves this itself, so the host never waits for the overflow flag.
+// A pass covers the window [s0, s0 + lw) of every sequence: token t = b*L + s
+// belongs to it when s0 <= s < s0 + lw.  The single pass over all tokens is
+// (0, L), chunk c of n is (c*L/n, L/n), and a batch of q consecutive chunks
+// is the window (c*L/n, q*L/n).  Static passes (ovf == nullptr) carry their
+// window and the index j of their layout.  A dynamic pass is slot j of a
+// LAYER-mode call: when *ovf is set it is batch j of the dropless chunks
+// (layout 1 + j, window as given), else slot 0 runs the single pass
+// (layout 0, window (0, L)) and the other slots are inactive.  Every kernel
+// of a pass resolves this itself, so the host never waits for the flag.
 struct PassArgs {
-  int n, c, capped;
+  int s0, lw, capped;
   const int* ovf;
   int j;
+  int L;  // sequence length (window of the single pass)
 };
 
 struct PassInfo {
-  int active, n, c, capped, j;
+  int active, s0, lw, capped, j;
 };
+
+__host__ __device__ __forceinline__ PassArgs static_pass_args(int s0, int lw, int capped, int j,
+                                                              int L) {
+  PassArgs a;
+  a.s0 = s0; a.lw = lw; a.capped = capped; a.ovf = nullptr; a.j = j; a.L = L;
+  return a;
+}
 
 __device__ __forceinline__ PassInfo resolve_pass(const PassArgs& a) {
   PassInfo p;
   if (a.ovf == nullptr) {
-    p.active = 1; p.n = a.n; p.c = a.c; p.capped = a.capped; p.j = a.j;
+    p.active = 1; p.s0 = a.s0; p.lw = a.lw; p.capped = a.capped; p.j = a.j;
   } else if (*a.ovf != 0) {
-    p.active = 1; p.n = a.n; p.c = a.c; p.capped = 0; p.j = 1 + a.c;
+    p.active = 1; p.s0 = a.s0; p.lw = a.lw; p.capped = 0; p.j = 1 + a.j;
   } else {
-    p.active = (a.c == 0); p.n = 1; p.c = 0; p.capped = 0; p.j = 0;
+    p.active = (a.j == 0); p.s0 = 0; p.lw = a.L; p.capped = 0; p.j = 0;
   }
   return p;
 }
 
 // The passes whose layouts are computed together: an optional single pass
-// over all tokens, then chunk passes [chunk_lo, chunk_lo + chunk_cnt) of a
-// split of every sequence into n_chunks.  Layout j: 0 is the single pass
-// when there is one, the chunk passes follow in order.  The single pass's
-// rows use one row_of_assign array ("set" 0) and the chunk passes share the
-// next one (their tokens are disjoint).  With `ovf` set (a LAYER-mode call)
-// the device computes only the layouts the flag selects: the single pass
-// when *ovf == 0, the chunk passes otherwise.
+// over all tokens (layout 0), then windows w_lo .. w_lo + w_cnt - 1 of
+// width `win` (the last one clipped at L), in order.  The single pass's
+// rows use one row_of_assign array ("set" 0) and the windows share the next
+// one (their tokens are disjoint).  With `ovf` set (a LAYER-mode call) the
+// device computes only the layouts the flag selects: the single pass when
+// *ovf == 0, the windows otherwise.
 struct LayoutSet {
   int has_single, single_capped;
-  int n_chunks, chunk_lo, chunk_cnt, chunk_capped;
+  int win, w_lo, w_cnt, w_capped;
   const int* ovf;
 };
 
@@ -85,22 +95,25 @@ __device__ __forceinline__ bool layout_live(const LayoutSet& ls, int j) {
 }
 
 __host__ __device__ __forceinline__ int layout_num_passes(const LayoutSet& ls) {
-  return ls.has_single + ls.chunk_cnt;
+  return ls.has_single + ls.w_cnt;
 }
 __host__ __device__ __forceinline__ int layout_num_sets(const LayoutSet& ls) {
-  return ls.has_single + (ls.chunk_cnt > 0 ? 1 : 0);
+  return ls.has_single + (ls.w_cnt > 0 ? 1 : 0);
 }
 __host__ __device__ __forceinline__ int layout_set_of(const LayoutSet& ls, int j) {
   return (ls.has_single && j == 0) ? 0 : ls.has_single;
 }
-// Geometry of layout j; its rows and elements start at j * T*k in the
+// Window of layout j; its rows and elements start at j * T*k in the
 // per-element arrays (each layout gets room for all T*k assignments).
 __host__ __device__ __forceinline__ void layout_pass(const Dims& d, const LayoutSet& ls, int j,
-                                                     int* n, int* c, int* capped, size_t* e0) {
+                                                     int* s0, int* lw, int* capped, size_t* e0) {
   if (ls.has_single && j == 0) {
-    *n = 1; *c = 0; *capped = ls.single_capped;
+    *s0 = 0; *lw = d.L; *capped = ls.single_capped;
   } else {
-    *n = ls.n_chunks; *c = ls.chunk_lo + (j - ls.has_single); *capped = ls.chunk_capped;
+    const int w0 = (ls.w_lo + (j - ls.has_single)) * ls.win;
+    *s0 = w0;
+    *lw = ls.win < d.L - w0 ? ls.win : d.L - w0;
+    *capped = ls.w_capped;
   }
   *e0 = (size_t)j * d.T * d.k;
 }
@@ -117,22 +130,26 @@ __host__ __device__ __forceinline__ size_t layout_total_elems(const Dims& d, con
 __host__ __device__ __forceinline__ size_t layout_total_dedup(const Dims& d, const LayoutSet& ls) {
   return d.dedup ? layout_total_elems(d, ls) : 1;
 }
-__host__ __device__ __forceinline__ int layout_min_chunks(const LayoutSet& ls) {
-  return ls.has_single ? 1 : ls.n_chunks;
+// Widest window of the set.
+__host__ __device__ __forceinline__ int layout_max_lw(const Dims& d, const LayoutSet& ls) {
+  if (ls.has_single) return d.L;
+  return ls.win < d.L ? ls.win : d.L;
 }
 
 constexpr int kLayoutMeta = 8;  // per layout: [0] rows, [1] dedup rows
 
-// Token of the i-th position of a pass: chunk c of n holds s in
-// [c*L/n, (c+1)*L/n) of every sequence b, in ascending t = b*L + s.
+// Token of the i-th position of a pass, in ascending t = b*L + s.
+__host__ __device__ __forceinline__ int window_token(int L, int s0, int lw, int i) {
+  int b = i / lw;
+  return b * L + s0 + (i - b * lw);
+}
+
 __device__ __forceinline__ int pass_token(const Dims& d, const PassInfo& p, int i) {
-  int lc = d.L / p.n;
-  int b = i / lc;
-  return b * d.L + p.c * lc + (i - b * lc);
+  return window_token(d.L, p.s0, p.lw, i);
 }
 
 __device__ __forceinline__ int pass_tokens(const Dims& d, const PassInfo& p) {
-  return d.T / p.n;
+  return (d.T / d.L) * p.lw;
 }
 
 // float -> bfloat16 bits, round to nearest even (finite inputs).

@@ -48,23 +48,20 @@ __device__ __forceinline__ int dedup_key(const Dims& d, const int* row, int j) {
 }
 
 struct PassGeom {
-  int n, c, capped, nelem, blk;
+  int s0, lw, capped, nelem, blk;
   size_t e0;  // first element of the pass in the per-element arrays
 };
 
 __device__ __forceinline__ PassGeom pass_geom(const Dims& d, const LayoutSet& ls, int j) {
   PassGeom g;
-  layout_pass(d, ls, j, &g.n, &g.c, &g.capped, &g.e0);
-  g.nelem = (d.T / g.n) * d.k;
+  layout_pass(d, ls, j, &g.s0, &g.lw, &g.capped, &g.e0);
+  g.nelem = (d.T / d.L) * g.lw * d.k;
   g.blk = sort_block_len(g.nelem);
   return g;
 }
 
 __device__ __forceinline__ int elem_token(const Dims& d, const PassGeom& g, int e) {
-  int i = e / d.k;
-  int lc = d.L / g.n;
-  int b = i / lc;
-  return b * d.L + g.c * lc + (i - b * lc);
+  return window_token(d.L, g.s0, g.lw, e / d.k);
 }
 
 // Rank of pass element e (relative to its dedup shard), from the packed
@@ -344,7 +341,7 @@ hipError_t launch_layout(const Dims& d, const LayoutSet& ls, const int* soa,
   // Static capped + dedup: the cut of each shard's dedup buffer decides which
   // rows drop, so the dedup ranks are scanned before the slot keys.
   const bool two_round = d.dedup && d.cap >= 0 &&
-                         ((ls.has_single && ls.single_capped) || (ls.chunk_cnt && ls.chunk_capped));
+                         ((ls.has_single && ls.single_capped) || (ls.w_cnt && ls.w_capped));
   if (!d.dedup) {
     hipLaunchKernelGGL(layout_local_kernel<1>, lgrid, lb64, 0, s, d, ls, soa, lb, 0);
     hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 1, lb);
@@ -357,7 +354,7 @@ hipError_t launch_layout(const Dims& d, const LayoutSet& ls, const int* soa,
     hipLaunchKernelGGL(layout_local_kernel<1>, lgrid, lb64, 0, s, d, ls, soa, lb, 1);
     hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 1, lb);
   }
-  const int maxe = (d.T / layout_min_chunks(ls)) * d.k;
+  const int maxe = (d.T / d.L) * layout_max_lw(d, ls) * d.k;
   hipLaunchKernelGGL(layout_place_kernel, dim3((maxe + 255) / 256, np), dim3(256), 0, s, d, ls,
                      soa, lb);
   return hipGetLastError();

@@ -128,6 +128,15 @@ int moe_pass_max_rows(const moe_problem* p, int32_t num_chunks, int32_t capped,
  * intermediate buffers, sized for the larger of the passes it may take). */
 int moe_layer_workspace_bytes(const moe_problem* p, int32_t mode, size_t* bytes);
 
+/* Chunks of the dropless fallback that moe_layer_dropless_chunked runs as
+ * one pass in `mode`: the most consecutive chunks whose worst-case rows fit
+ * the buffers the call is sized for, so running them together never needs
+ * more memory than the capped buffer ([FALLBACK] How: a chunk's worst-case
+ * buffer is no larger than the capped one, so peak HBM does not grow).  The
+ * tokens of the chunks are disjoint and every grouped-GEMM row is computed
+ * on its own, so y is the same as chunk by chunk.  1 = one chunk per pass. */
+int moe_layer_chunks_per_pass(const moe_problem* p, int32_t mode, int32_t* chunks);
+
 /* ---- the hot path -------------------------------------------------------- */
 
 /* a1. Router top-k ([FALLBACK] How: the check works "from the router's
@@ -205,7 +214,8 @@ int moe_combine(const moe_problem* p, int32_t num_chunks, int32_t chunk,
 /* a8. The whole layer ([FALLBACK] How): route, counts, plan, capacity and
  * overflow once, then the passes `mode` selects, writing y [T,H].  In LAYER
  * mode the device picks between the capped pass and the num_chunks dropless
- * chunk passes from the overflow flag, with no host synchronisation.
+ * chunks (moe_layer_chunks_per_pass of them per pass) from the overflow
+ * flag, with no host synchronisation.
  * info (device, may be NULL) receives [overflow, fallback_ran, cap, max
  * shard count].  ws must hold moe_layer_workspace_bytes(p, mode). */
 int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x,
