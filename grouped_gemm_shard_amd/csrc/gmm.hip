@@ -6,34 +6,34 @@
 // FFN itself is SwiGLU: act = SiLU(x Wg^T) * (x Wu^T), out = act Wd^T.
 //
 // bf16 path: two launches per pass.
-//  * GEMM1 (x_sorted [N,H] against Wg and Wu [F,H]): a tile computes 128 act
-//    columns as 128 gate + 128 up columns held side by side in one 256-row
-//    weight tile, so the SwiGLU epilogue finds the gate and up value of an
-//    element in the same lane and register.
+//  * GEMM1 (A rows against Wg and Wu [F,H]): a tile computes 128 act columns
+//    as 128 gate + 128 up columns held side by side in one 256-row weight
+//    tile, so the SwiGLU epilogue finds the gate and up value of an element
+//    in the same lane and register.  A rows are gathered through the pass's
+//    row index (from x, or from the dedup buffer), so the layer never
+//    writes a permuted copy of x.
 //  * GEMM2 (act [N,F] against Wd [H,F]): a BM x 256 output tile.
-// Both use v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  256 threads =
-// 4 waves in a 2 x 2 grid, each wave a (BM/2) x 128 slice of 32 x 32 MFMA
+// Both use v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  512 threads =
+// 8 waves in a 4 x 2 grid, each wave a (BM/4) x 128 slice of 32 x 32 MFMA
 // tiles.
 //
 // Operands go from HBM straight into LDS (buffer_load ... lds, 16 bytes per
-// lane, no staging registers) through a ring of NST stages of BK columns, so
-// NST-1 stages of loads are in flight while one is multiplied: the loads of
-// a weight-streaming GEMM need far more bytes in flight per CU than one
-// stage gives.  Two shapes:
-//   BM=128, BK=64, 3 stages (147 KB LDS): small groups, weight streaming;
-//   BM=256, BK=32, 4 stages (128 KB LDS): long reductions, half the operand
-//   traffic per flop.
-// In LDS each row of a stage holds BK bf16 as 16-byte chunks whose order is
-// XOR-permuted by row, so the fragment reads of 8 or 16 consecutive rows at
-// one chunk hit distinct banks.  Rows of A past the group read as zero (the
-// buffer's byte range ends at the group), and their results are not stored.
+// lane, no staging registers) through a ring of NST stages of BK = 64
+// columns, so NST-1 stages of loads are in flight while one is multiplied.
+// Two shapes: BM=256 with 2 stages (128 KB LDS) for long reductions, where
+// the taller tile halves the operand traffic per flop, and BM=128 with 3
+// stages (144 KB) otherwise.  In LDS each 128-byte row holds its 16-byte
+// chunks XOR-permuted by row, so the fragment reads of consecutive rows at
+// one chunk hit distinct banks.  Rows of A past the group read as zero (an
+// offset past the buffer's byte range) and their results are not stored.
 //
 // Tiles: every group owns ceil(rows/BM) m-tiles (an exclusive scan over
 // groups, with an m-tile -> group map, computed with the layout), so empty
-// groups cost nothing.  Logical tile L = nt * m_tiles + mt: neighbours share
-// a weight panel.  Workgroups are dispatched round-robin over the 8 XCDs,
-// so each XCD is given a contiguous range of L and its L2 serves the panel
-// to all of that range's m-tiles.
+// groups cost nothing.  A group's tiles are ordered in bands of up to GM
+// m-tiles, n-tile by n-tile.  Workgroups are dispatched round-robin over the
+// 8 XCDs, and each XCD is given a contiguous range of that order, so the
+// blocks an XCD runs together cover a few m-tiles by a few n-tiles of one
+// expert and share both operand panels in its L2.
 #include "common.h"
 
 namespace moe {
@@ -41,6 +41,7 @@ namespace moe {
 namespace {
 
 constexpr int BNB = 256;  // weight rows per tile
+constexpr int GM = 8;     // m-tiles per band of the tile order
 
 // Tile shapes <BM, BK, stages, waves> for long reductions and for the rest.
 #ifndef MOE_GEMM_BIG
@@ -172,11 +173,22 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   if ((bid >> 3) >= per_xcd) return;
   const int L = (bid & 7) * per_xcd + (bid >> 3);
   if (L >= total) return;
-  const int nt = L / total_mt;
-  const int mt = L - nt * total_mt;
-  const int g = tile_group[mt];
+  // Tiles of group g are L in [tile_off[g], tile_off[g+1]) * n_ntiles, in
+  // bands of up to GM m-tiles: a band's tiles go n-tile by n-tile, so the
+  // blocks an XCD runs together cover a few m-tiles by a few n-tiles of one
+  // expert and share both operand panels in that XCD's L2.
+  const int g = tile_group[L / P.n_ntiles];
+  if (g < 0 || g >= P.G) return;
+  const int t0 = tile_off[g];
+  const int mt_g = tile_off[g + 1] - t0;
+  int r = L - t0 * P.n_ntiles;
+  const int band = r / (GM * P.n_ntiles);
+  const int gm = min(GM, mt_g - band * GM);
+  r -= band * GM * P.n_ntiles;
+  const int nt = r / gm;
+  const int ml = band * GM + (r - nt * gm);
   const int gend = group_offsets[g + 1];
-  const int row0 = group_offsets[g] + (mt - tile_off[g]) * BM;
+  const int row0 = group_offsets[g] + ml * BM;
   if (row0 < 0 || row0 >= gend || gend > P.max_rows) return;
   const int rows = min(BM, gend - row0);
   const int e = P.slot_expert[P.lo_slot + g] - P.e_base;
