@@ -34,6 +34,10 @@ MEDIUM = {
     # hidden >= 2048 selects the 256-row GEMM tile
     "maverick_mid": CONFIGS["maverick_shard"].scaled(name="maverick_mid", tokens=2048,
                                                      seq_len=512, hidden=2048, ffn=1024),
+    # F >= 4096: the grouped GEMM splits each pass into two stream-parallel
+    # halves of m-tiles
+    "maverick_wide": CONFIGS["maverick_shard"].scaled(name="maverick_wide", tokens=1024,
+                                                      seq_len=256, hidden=256, ffn=4096),
 }
 SMALL_CASES = {"tiny_fp32": CONFIGS["tiny_fp32"], "mid_bf16": CONFIGS["mid_bf16"], **MEDIUM}
 
