@@ -348,7 +348,7 @@ int moe_route(const moe_problem* p, const float* logits, int32_t* topk_idx, floa
   int st = make_dims(p, &d);
   if (st != MOE_OK) return st;
   if (!logits || !topk_idx || !topk_gate) return MOE_EINVAL;
-  return hip_status(launch_route(d, logits, topk_idx, topk_gate, (hipStream_t)stream));
+  return hip_status(launch_route(d, logits, topk_idx, topk_gate, nullptr, (hipStream_t)stream));
 }
 
 int moe_count_overflow(const moe_problem* p, const int32_t* topk_idx, int32_t* expert_counts,
@@ -364,7 +364,7 @@ int moe_count_overflow(const moe_problem* p, const int32_t* topk_idx, int32_t* e
   if (misaligned(ws, 256)) return MOE_EINVAL;
   if (ws_bytes < count_scratch_bytes(d)) return MOE_ECAPACITY;
   return hip_status(launch_count(d, topk_idx, expert_counts, slot_expert, ndiv, slot_of_assign,
-                                 shard_counts, status, ws, nullptr, 0, (hipStream_t)stream));
+                                 shard_counts, status, ws, 0, nullptr, 0, (hipStream_t)stream));
 }
 
 int moe_permute(const moe_problem* p, int32_t num_chunks, int32_t chunk, int32_t capped,
@@ -403,7 +403,7 @@ int moe_permute(const moe_problem* p, int32_t num_chunks, int32_t chunk, int32_t
     lb.dedup_token = dedup_token;
     lb.expand_idx = expand_idx;
   }
-  hipError_t e = launch_layout(d, ls, slot_of_assign, lb, s);
+  hipError_t e = launch_layout(d, ls, slot_of_assign, 0, lb, s);
   if (e != hipSuccess) return MOE_EHIP;
   const int row_bytes = d.H * (d.bf16 ? 2 : 4);
   const int lc = d.L / num_chunks;
@@ -487,13 +487,18 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
   const LayoutSet ls = layer_layout(d, mode, q, w.status + 1);
   hipStream_t s = (hipStream_t)stream;
 
-  hipError_t e = launch_route(d, logits, w.topk_idx, w.topk_gate, s);
+  hipError_t e = launch_route(d, logits, w.topk_idx, w.topk_gate,
+                              count_hist_area(d, w.count_scratch), s);
   if (e != hipSuccess) return MOE_EHIP;
-  e = launch_count(d, w.topk_idx, w.expert_counts, w.slot_expert, w.ndiv, w.slot_of_assign,
-                   w.shard_counts, w.status, w.count_scratch, info, mode, s);
+  // without rerouting every assignment goes to its expert's home slot, so
+  // the layout reads the top-k directly
+  const bool reroute = d.R > 0 && d.B > 0;
+  e = launch_count(d, w.topk_idx, w.expert_counts, w.slot_expert, w.ndiv,
+                   reroute ? w.slot_of_assign : nullptr, w.shard_counts, w.status,
+                   w.count_scratch, 1, info, mode, s);
   if (e != hipSuccess) return MOE_EHIP;
   const LayoutBuffers lb = carve_layout(d, ls, w.layout_scratch);
-  e = launch_layout(d, ls, w.slot_of_assign, lb, s);
+  e = launch_layout(d, ls, reroute ? w.slot_of_assign : w.topk_idx, reroute ? 0 : 1, lb, s);
   if (e != hipSuccess) return MOE_EHIP;
 
   if (ls.ovf != nullptr) {

@@ -187,15 +187,32 @@ __device__ __forceinline__ unsigned long long lanemask_lt() {
 // Host-side launchers (defined in the .hip files).  Each returns hipError_t.
 // ---------------------------------------------------------------------------
 
-hipError_t launch_route(const Dims& d, const float* logits, int* idx, float* gate,
+// Rows of the per-block expert histograms the route step can leave for the
+// count step (one per route block).
+__host__ __device__ __forceinline__ int route_hist_blocks(const Dims& d) {
+  const int nb = (d.T + 15) / 16;  // 16 waves per block, a token per wave
+  return nb < 256 ? nb : 256;
+}
+
+// Router top-k.  With ph non-null (route_hist_blocks(d) x E ints) it also
+// leaves per-block expert histograms for launch_count.
+hipError_t launch_route(const Dims& d, const float* logits, int* idx, float* gate, int* ph,
                         hipStream_t s);
 
-// Scratch of the count step: kSortBlocks*R ints of block histograms and T*k
-// packed keys.
+// Scratch of the count step: per-block expert histograms and error flags,
+// and for rerouting kSortBlocks*R ints of block histograms and T*k packed
+// keys.
 size_t count_scratch_bytes(const Dims& d);
+// The per-block histogram area of the count scratch (route may fill it).
+int* count_hist_area(const Dims& d, void* scratch);
+// Counts, plan, slots, shard counts and the overflow check from the top-k.
+// hist_ready: the route step already left its histograms in the scratch.
+// Without rerouting (R == 0 or B == 0) slot_of_assign may be null: every
+// assignment then goes to its expert's home slot.
 hipError_t launch_count(const Dims& d, const int* idx, int* expert_counts, int* slot_expert,
                         int* ndiv, int* slot_of_assign, int* shard_counts, int* status,
-                        void* scratch, int* info_out, int info_mode, hipStream_t s);
+                        void* scratch, int hist_ready, int* info_out, int info_mode,
+                        hipStream_t s);
 
 // Layout state of every pass of a LayoutSet (arrays are per layout j with
 // the strides used by the kernels below).
@@ -218,7 +235,9 @@ struct LayoutBuffers {
 };
 size_t layout_scratch_bytes(const Dims& d, const LayoutSet& ls);
 LayoutBuffers carve_layout(const Dims& d, const LayoutSet& ls, void* scratch);
-hipError_t launch_layout(const Dims& d, const LayoutSet& ls, const int* slot_of_assign,
+// slots: slot_of_assign [T*k], or with home != 0 the top-k expert ids, each
+// assignment then going to its expert's home slot (no rerouting).
+hipError_t launch_layout(const Dims& d, const LayoutSet& ls, const int* slots, int home,
                          const LayoutBuffers& lb, hipStream_t s);
 
 // dst[r] = src[index[r] / div] for r < *count, per pass: count, index are

@@ -7,39 +7,81 @@
 // duplication plan with the has_candidate guard, and the rerouting of a
 // planned share of the overloaded expert's tokens to its replica slot).
 //
-// Counts are order-independent, so they use LDS histograms and integer
-// atomics; the reroute needs each assignment's rank among the assignments
-// of its expert, which comes from the stable counting sort in sort.h.
+// Counts are order-independent: per-block LDS histograms (left by the route
+// kernel in a layer call, else by hist_kernel) are summed by one workgroup.
+// Without rerouting, that workgroup also assigns the home slots, counts the
+// shards and checks overflow, so the whole step is one launch after route.
+// The reroute needs each assignment's rank among the assignments of its
+// expert, which comes from the stable counting sort in sort.h.
 #include "sort.h"
 
 namespace moe {
 
 namespace {
 
-__global__ void count_init_kernel(int* expert_counts, int E, int* shard_counts, int S,
-                                  int* status) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < E) expert_counts[i] = 0;
-  if (i < S) shard_counts[i] = 0;
-  if (i < 4) status[i] = 0;
-}
-
-__global__ __launch_bounds__(256) void count_experts_kernel(const int* __restrict__ idx, int n,
-                                                            int E, int* expert_counts,
-                                                            int* status) {
+// Per-block expert histograms of a caller-supplied top-k (row blockIdx of
+// ph) and a per-block flag for out-of-range expert ids.
+__global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ idx, int n, int E,
+                                                   int* __restrict__ ph, int* __restrict__ pbad) {
   __shared__ int hist[kMaxExperts];
+  __shared__ int bad;
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  if (threadIdx.x == 0) bad = 0;
   __syncthreads();
-  int bad = 0;
   for (int a = blockIdx.x * blockDim.x + threadIdx.x; a < n; a += gridDim.x * blockDim.x) {
     int e = idx[a];
     if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
     else bad = 1;
   }
-  if (bad) atomicOr(&status[3], 1);
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
-    if (hist[e]) atomicAdd(&expert_counts[e], hist[e]);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) ph[(size_t)blockIdx.x * E + e] = hist[e];
+  if (threadIdx.x == 0) pbad[blockIdx.x] = bad;
+}
+
+// Sums the per-block histograms into counts[E] (one thread per expert) and
+// ORs the blocks' bad-id flags (pbad may be null: no bad ids) into *bad_out.
+__device__ __forceinline__ void sum_hist(const Dims& d, const int* __restrict__ ph,
+                                         const int* __restrict__ pbad, int nb, int* counts,
+                                         int* bad_out) {
+  // blockDim / E partitions of the rows per expert, then a reduction in LDS
+  __shared__ int part[1024];
+  const int P = max(1, (int)blockDim.x / d.E);
+  const int e = threadIdx.x % d.E, q = threadIdx.x / d.E;
+  int acc = 0;
+  if (q < P) {
+#pragma unroll 4
+    for (int b = q; b < nb; b += P) acc += ph[(size_t)b * d.E + e];
+    part[q * d.E + e] = acc;
+  }
+  if (threadIdx.x == 0) {
+    int bad = 0;
+    if (pbad != nullptr)
+      for (int b = 0; b < nb; ++b) bad |= pbad[b];
+    *bad_out = bad;
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < d.E; x += blockDim.x) {
+    int sum = 0;
+    for (int qq = 0; qq < P; ++qq) sum += part[qq * d.E + x];
+    counts[x] = sum;
+  }
+  __syncthreads();
+}
+
+// Counts and status for the rerouting path: sums the histograms and clears
+// the shard counts and status words the later kernels accumulate into.
+__global__ __launch_bounds__(1024) void count_sum_kernel(Dims d, const int* __restrict__ ph,
+                                                         const int* __restrict__ pbad, int nb,
+                                                         int* expert_counts, int* shard_counts,
+                                                         int* status) {
+  __shared__ int bad;
+  sum_hist(d, ph, pbad, nb, expert_counts, &bad);
+  for (int s = threadIdx.x; s < d.S; s += blockDim.x) shard_counts[s] = 0;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    status[0] = status[1] = status[2] = 0;
+    status[3] = bad ? 1 : 0;
+  }
 }
 
 // The greedy plan, in one workgroup.  Loads are assignment counts per shard.
@@ -223,11 +265,108 @@ __global__ __launch_bounds__(1024) void finalize_kernel(Dims d, const int* __res
   }
 }
 
+__device__ __forceinline__ void write_status(const Dims& d, int mx, int bad, int* status,
+                                             int* info, int info_mode) {
+  int ovf = (d.cap >= 0 && mx > d.cap) ? 1 : 0;
+  status[0] = d.cap;
+  status[1] = ovf;
+  status[2] = mx;
+  status[3] = bad ? 1 : 0;
+  if (info != nullptr) {
+    int ran = info_mode == MOE_MODE_FORCE_CHUNKED ? 1 : (info_mode == MOE_MODE_LAYER ? ovf : 0);
+    info[0] = ovf;
+    info[1] = ran;
+    info[2] = d.cap;
+    info[3] = mx;
+  }
+}
+
+// The whole count step without rerouting, in one workgroup: expert counts
+// from the per-block histograms, home slots for every assignment, shard
+// counts (assignments per shard, or distinct tokens per shard with dedup)
+// and the overflow check.
+__global__ __launch_bounds__(1024) void count_fused_kernel(Dims d, const int* __restrict__ idx,
+                                                           const int* __restrict__ ph,
+                                                           const int* __restrict__ pbad, int nb,
+                                                           int* expert_counts, int* slot_expert,
+                                                           int* ndiv, int* slot_of_assign,
+                                                           int* shard_counts, int* status,
+                                                           int* info, int info_mode) {
+  __shared__ int counts[kMaxExperts];
+  __shared__ int load[kMaxSlots];
+  __shared__ int bad;
+  __shared__ int red[16];
+  sum_hist(d, ph, pbad, nb, counts, &bad);
+  for (int s = threadIdx.x; s < d.G; s += blockDim.x) {
+    int sh = s / d.spd, i = s - sh * d.spd;
+    slot_expert[s] = i < d.El ? sh * d.El + i : -1;
+  }
+  for (int sh = threadIdx.x; sh < d.S; sh += blockDim.x) load[sh] = 0;
+  __syncthreads();
+  for (int e = threadIdx.x; e < d.E; e += blockDim.x) {
+    expert_counts[e] = counts[e];
+    ndiv[e] = 0;
+  }
+  const int n = d.T * d.k;
+  if (slot_of_assign != nullptr) {
+#pragma unroll 4
+    for (int a = threadIdx.x; a < n; a += blockDim.x) {
+      int e = idx[a];
+      slot_of_assign[a] = (e >= 0 && e < d.E) ? home_slot(d, e) : -1;
+    }
+  }
+  if (!d.dedup) {
+    for (int sh = threadIdx.x; sh < d.S; sh += blockDim.x) {
+      int acc = 0;
+      for (int i = 0; i < d.El; ++i) acc += counts[sh * d.El + i];
+      load[sh] = acc;
+    }
+  } else {
+    // one buffer row per distinct (token, shard) pair, from the top-k
+    for (int t = threadIdx.x; t < d.T; t += blockDim.x) {
+      const int* row = idx + (size_t)t * d.k;
+      for (int j = 0; j < d.k; ++j) {
+        int e = row[j];
+        if (e < 0 || e >= d.E) continue;
+        int sh = e / d.El;
+        bool first = true;
+        for (int jj = 0; jj < j; ++jj) {
+          int e2 = row[jj];
+          if (e2 >= 0 && e2 < d.E && e2 / d.El == sh) first = false;
+        }
+        if (first) atomicAdd(&load[sh], 1);
+      }
+    }
+  }
+  __syncthreads();
+  int m = 0;
+  for (int sh = threadIdx.x; sh < d.S; sh += blockDim.x) {
+    shard_counts[sh] = load[sh];
+    m = max(m, load[sh]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int mx = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) mx = max(mx, red[w]);
+    write_status(d, mx, bad, status, info, info_mode);
+  }
+}
+
 }  // namespace
+
+inline size_t hist_bytes(const Dims& d) {
+  return (((size_t)route_hist_blocks(d) * d.E * 4 + 255) / 256) * 256 +
+         (((size_t)route_hist_blocks(d) * 4 + 255) / 256) * 256;
+}
+
+int* count_hist_area(const Dims& d, void* scratch) { return (int*)scratch; }
 
 size_t count_scratch_bytes(const Dims& d) {
   size_t n = (size_t)d.T * d.k;
-  size_t bytes = 0;
+  size_t bytes = hist_bytes(d);
   bytes += ((n * sizeof(unsigned) + 255) / 256) * 256;                          // keys
   bytes += (((size_t)kSortBlocks * (d.R > 0 ? d.R : 1) * 4 + 255) / 256) * 256;  // bh
   bytes += (((size_t)d.E * 4 + 255) / 256) * 256;                               // replica
@@ -237,9 +376,13 @@ size_t count_scratch_bytes(const Dims& d) {
 
 hipError_t launch_count(const Dims& d, const int* idx, int* expert_counts, int* slot_expert,
                         int* ndiv, int* slot_of_assign, int* shard_counts, int* status,
-                        void* scratch, int* info, int info_mode, hipStream_t st) {
+                        void* scratch, int hist_ready, int* info, int info_mode, hipStream_t st) {
   size_t n = (size_t)d.T * d.k;
+  const int nb = route_hist_blocks(d);
   char* p = (char*)scratch;
+  int* ph = (int*)p;
+  int* pbad = (int*)(p + (((size_t)nb * d.E * 4 + 255) / 256) * 256);
+  p += hist_bytes(d);
   unsigned* keys = (unsigned*)p;
   p += ((n * sizeof(unsigned) + 255) / 256) * 256;
   int* bh = (int*)p;
@@ -248,23 +391,30 @@ hipError_t launch_count(const Dims& d, const int* idx, int* expert_counts, int* 
   p += (((size_t)d.E * 4 + 255) / 256) * 256;
   int* dup_id = (int*)p;
 
-  int m = d.E > d.S ? d.E : d.S;
-  hipLaunchKernelGGL(count_init_kernel, dim3((m + 255) / 256), dim3(256), 0, st, expert_counts,
-                     d.E, shard_counts, d.S, status);
+  if (hist_ready) {
+    // the route step wrote the histograms; its expert ids are all in range
+    pbad = nullptr;
+  } else {
+    hipLaunchKernelGGL(hist_kernel, dim3(nb), dim3(256), 0, st, idx, (int)n, d.E, ph, pbad);
+  }
+  const bool reroute = d.R > 0 && d.B > 0;
+  if (!reroute) {
+    hipLaunchKernelGGL(count_fused_kernel, dim3(1), dim3(1024), 0, st, d, idx, ph, pbad, nb,
+                       expert_counts, slot_expert, ndiv, slot_of_assign, shard_counts, status,
+                       info, info_mode);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(count_sum_kernel, dim3(1), dim3(1024), 0, st, d, ph, pbad, nb,
+                     expert_counts, shard_counts, status);
   int nblk = (int)((n + 255) / 256);
   if (nblk > 1024) nblk = 1024;
-  hipLaunchKernelGGL(count_experts_kernel, dim3(nblk), dim3(256), 0, st, idx, (int)n, d.E,
-                     expert_counts, status);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, st, d, expert_counts, slot_expert,
                      ndiv, replica, dup_id, shard_counts);
-  bool reroute = d.R > 0 && d.B > 0;
-  if (reroute) {
-    hipLaunchKernelGGL(reroute_rank_kernel, dim3(kSortBlocks), dim3(64), 0, st, d, idx, dup_id,
-                       keys, bh);
-    hipLaunchKernelGGL(reroute_scan_kernel, dim3(1), dim3(1024), 0, st, d.R, bh);
-  }
+  hipLaunchKernelGGL(reroute_rank_kernel, dim3(kSortBlocks), dim3(64), 0, st, d, idx, dup_id,
+                     keys, bh);
+  hipLaunchKernelGGL(reroute_scan_kernel, dim3(1), dim3(1024), 0, st, d.R, bh);
   hipLaunchKernelGGL(assign_slots_kernel, dim3(nblk), dim3(256), 0, st, d, idx, ndiv, replica,
-                     reroute ? keys : nullptr, bh, slot_of_assign);
+                     keys, bh, slot_of_assign);
   if (d.dedup) {
     int tb = (d.T + 255) / 256;
     if (tb > 1024) tb = 1024;

@@ -29,21 +29,33 @@ __device__ __forceinline__ int slot_key(const Dims& d, int s) {
   return (s >= d.lo_slot && s < d.lo_slot + d.G_res) ? s - d.lo_slot : -1;
 }
 
+// Slot of assignment j of a token whose row starts at `row`: the row holds
+// slots, or (home != 0: nothing was rerouted) expert ids, whose slot is the
+// expert's home slot.
+__device__ __forceinline__ int slot_at(const Dims& d, const int* row, int home, int j) {
+  const int v = row[j];
+  if (!home) return v;
+  if (v < 0 || v >= d.E) return -1;
+  const int sh = v / d.El;
+  return sh * d.spd + (v - sh * d.El);
+}
+
 // First assignment j' <= j of the token on the same shard as slot s.
-__device__ __forceinline__ int first_on_shard(const Dims& d, const int* row, int j, int s) {
+__device__ __forceinline__ int first_on_shard(const Dims& d, const int* row, int home, int j,
+                                              int s) {
   int sh = s / d.spd;
   for (int jj = 0; jj < j; ++jj) {
-    int s2 = row[jj];
+    int s2 = slot_at(d, row, home, jj);
     if (s2 >= 0 && s2 / d.spd == sh) return jj;
   }
   return j;
 }
 
 // Dedup key: local resident shard of the token's first assignment on it.
-__device__ __forceinline__ int dedup_key(const Dims& d, const int* row, int j) {
-  int s = row[j];
+__device__ __forceinline__ int dedup_key(const Dims& d, const int* row, int home, int j) {
+  int s = slot_at(d, row, home, j);
   if (slot_key(d, s) < 0) return -1;
-  if (first_on_shard(d, row, j, s) != j) return -1;
+  if (first_on_shard(d, row, home, j, s) != j) return -1;
   return s / d.spd - d.res_lo;
 }
 
@@ -77,7 +89,8 @@ __device__ __forceinline__ int dedup_rank(const Dims& d, const LayoutBuffers& lb
 template <int WHICH>  // bit 0: slot keys, bit 1: dedup keys
 __global__ __launch_bounds__(64) void layout_local_kernel(Dims d, LayoutSet ls,
                                                           const int* __restrict__ soa,
-                                                          LayoutBuffers lb, int drop_check) {
+                                                          int home, LayoutBuffers lb,
+                                                          int drop_check) {
   __shared__ int run_s[kMaxSlots];
   __shared__ int run_d[kMaxSlots];
   const int j = blockIdx.y;
@@ -98,10 +111,11 @@ __global__ __launch_bounds__(64) void layout_local_kernel(Dims d, LayoutSet ls,
       row = soa + (size_t)elem_token(d, g, e) * d.k;
     }
     if (WHICH & 1) {
-      int ks = in ? slot_key(d, row[jj]) : -1;
+      const int sl = in ? slot_at(d, row, home, jj) : -1;
+      int ks = in ? slot_key(d, sl) : -1;
       if (drop_check && g.capped && ks >= 0) {
         // the token was cut from this shard's dedup buffer: drop the row
-        int jr = first_on_shard(d, row, jj, row[jj]);
+        int jr = first_on_shard(d, row, home, jj, sl);
         int kd;
         int r = dedup_rank(d, lb, g, j, e - jj + jr, &kd);
         if (r >= d.cap) ks = -1;
@@ -110,7 +124,7 @@ __global__ __launch_bounds__(64) void layout_local_kernel(Dims d, LayoutSet ls,
       if (in) lb.skey[g.e0 + e] = pack_key(ks, r);
     }
     if (WHICH & 2) {
-      int kd = in ? dedup_key(d, row, jj) : -1;
+      int kd = in ? dedup_key(d, row, home, jj) : -1;
       int r = wave_rank_step(kd, nb_d, run_d);
       if (in) lb.dkey[g.e0 + e] = pack_key(kd, r);
     }
@@ -201,7 +215,7 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(Dims d, LayoutSet ls,
 // dedup, the dedup token lists and the expand indices.
 __global__ __launch_bounds__(256) void layout_place_kernel(Dims d, LayoutSet ls,
                                                            const int* __restrict__ soa,
-                                                           LayoutBuffers lb) {
+                                                           int home, LayoutBuffers lb) {
   const int j = blockIdx.y;
   if (!layout_live(ls, j)) return;
   const PassGeom g = pass_geom(d, ls, j);
@@ -233,7 +247,7 @@ __global__ __launch_bounds__(256) void layout_place_kernel(Dims d, LayoutSet ls,
   lb.sorted_assign[srow + pos] = a;
   if (d.dedup) {
     const int* row = soa + (size_t)t * d.k;
-    int jr = first_on_shard(d, row, jj, row[jj]);
+    int jr = first_on_shard(d, row, home, jj, slot_at(d, row, home, jj));
     int kd;
     int r = dedup_rank(d, lb, g, j, e - jj + jr, &kd);
     lb.expand_idx[srow + pos] = lb.dedup_offsets[(size_t)j * (d.S_res + 1) + kd] + r;
@@ -334,7 +348,7 @@ LayoutBuffers carve_layout(const Dims& d, const LayoutSet& ls, void* scratch) {
   return lb;
 }
 
-hipError_t launch_layout(const Dims& d, const LayoutSet& ls, const int* soa,
+hipError_t launch_layout(const Dims& d, const LayoutSet& ls, const int* soa, int home,
                          const LayoutBuffers& lb, hipStream_t s) {
   const int np = layout_num_passes(ls);
   const dim3 lb64(64), lgrid(kSortBlocks, np), sb(1024), sgrid(np);
@@ -343,20 +357,20 @@ hipError_t launch_layout(const Dims& d, const LayoutSet& ls, const int* soa,
   const bool two_round = d.dedup && d.cap >= 0 &&
                          ((ls.has_single && ls.single_capped) || (ls.w_cnt && ls.w_capped));
   if (!d.dedup) {
-    hipLaunchKernelGGL(layout_local_kernel<1>, lgrid, lb64, 0, s, d, ls, soa, lb, 0);
+    hipLaunchKernelGGL(layout_local_kernel<1>, lgrid, lb64, 0, s, d, ls, soa, home, lb, 0);
     hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 1, lb);
   } else if (!two_round) {
-    hipLaunchKernelGGL(layout_local_kernel<3>, lgrid, lb64, 0, s, d, ls, soa, lb, 0);
+    hipLaunchKernelGGL(layout_local_kernel<3>, lgrid, lb64, 0, s, d, ls, soa, home, lb, 0);
     hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 3, lb);
   } else {
-    hipLaunchKernelGGL(layout_local_kernel<2>, lgrid, lb64, 0, s, d, ls, soa, lb, 0);
+    hipLaunchKernelGGL(layout_local_kernel<2>, lgrid, lb64, 0, s, d, ls, soa, home, lb, 0);
     hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 2, lb);
-    hipLaunchKernelGGL(layout_local_kernel<1>, lgrid, lb64, 0, s, d, ls, soa, lb, 1);
+    hipLaunchKernelGGL(layout_local_kernel<1>, lgrid, lb64, 0, s, d, ls, soa, home, lb, 1);
     hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 1, lb);
   }
   const int maxe = (d.T / d.L) * layout_max_lw(d, ls) * d.k;
   hipLaunchKernelGGL(layout_place_kernel, dim3((maxe + 255) / 256, np), dim3(256), 0, s, d, ls,
-                     soa, lb);
+                     soa, home, lb);
   return hipGetLastError();
 }
 
