@@ -46,8 +46,8 @@ PEAK_HBM_GBS = 8000.0
 # holds only for the kernel source it was measured on (sha256 of gmm.hip);
 # for any other source or workload the traffic is reported as null.
 GEMM_TRAFFIC = {"workload": "mid_bf16",
-                "gmm_src_sha256": "2f5ef55f2b9622189af119887ac096cb9d20e9cdd7c5709b134ec871866ec33c",
-                "bytes_per_layer": 663222109}
+                "gmm_src_sha256": "dbce7c77d32d3b2900be3af27e07e7d1fab4da617044c74dbd016b310576c566",
+                "bytes_per_layer": 292102544}
 
 
 def recorded_gemm_traffic(workload):
