@@ -13,6 +13,35 @@ namespace moe {
 
 namespace {
 
+// One token's output columns [h, h + 8) in bf16: the KC row loads of a
+// batch of KC assignments are issued together, then accumulated in j order.
+template <int KC>
+__device__ __forceinline__ void combine_bf16_cols(const uint16_t* __restrict__ o, const int* rows,
+                                                  const float* gts, int j0, int k, int H,
+                                                  long long max_rows, int h, float (&acc)[8]) {
+  uint4 v[KC];
+  float gj[KC];
+  bool ok[KC];
+#pragma unroll
+  for (int u = 0; u < KC; ++u) {
+    const int j = j0 + u;
+    const int r = j < k ? rows[j] : -1;
+    ok[u] = r >= 0 && r < max_rows;
+    gj[u] = j < k ? gts[j] : 0.0f;
+    if (ok[u]) v[u] = *(const uint4*)(o + (size_t)r * H + h);
+  }
+#pragma unroll
+  for (int u = 0; u < KC; ++u) {
+    if (!ok[u]) continue;
+    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] = fmaf(gj[u], __uint_as_float(w[q] << 16), acc[2 * q]);
+      acc[2 * q + 1] = fmaf(gj[u], __uint_as_float(w[q] & 0xffff0000u), acc[2 * q + 1]);
+    }
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(Dims d, PassArgs pa, LayoutSet ls,
                                                       const void* __restrict__ out,
@@ -36,18 +65,9 @@ __global__ __launch_bounds__(256) void combine_kernel(Dims d, PassArgs pa, Layou
       float acc[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-      for (int j = 0; j < d.k; ++j) {
-        const int r = rows[j];
-        const float gj = gts[j];
-        if (r < 0 || r >= max_rows) continue;
-        uint4 v = *(const uint4*)(o + (size_t)r * d.H + h);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = fmaf(gj, __uint_as_float(w[q] << 16), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(gj, __uint_as_float(w[q] & 0xffff0000u), acc[2 * q + 1]);
-        }
-      }
+      // assignments in ascending j, four row loads in flight at a time
+      for (int j0 = 0; j0 < d.k; j0 += 4)
+        combine_bf16_cols<4>(o, rows, gts, j0, d.k, d.H, max_rows, h, acc);
       uint4 outv;
       outv.x = (uint32_t)f2bf(acc[0]) | ((uint32_t)f2bf(acc[1]) << 16);
       outv.y = (uint32_t)f2bf(acc[2]) | ((uint32_t)f2bf(acc[3]) << 16);

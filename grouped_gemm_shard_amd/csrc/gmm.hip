@@ -14,8 +14,8 @@
 //    writes a permuted copy of x.
 //  * GEMM2 (act [N,F] against Wd [H,F]): a BM x 256 output tile.
 // Both use v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  512 threads =
-// 8 waves in a 4 x 2 grid, each wave a (BM/4) x 128 slice of 32 x 32 MFMA
-// tiles.
+// 8 waves, in a 4 x 2 grid (256-row tiles: 64 x 128 per wave) or a 2 x 4
+// grid (128-row tiles: 64 x 64 per wave) of 32 x 32 MFMA tiles.
 //
 // Operands go from HBM straight into LDS (buffer_load ... lds, 16 bytes per
 // lane, no staging registers) through a ring of NST stages of BK = 64
@@ -45,12 +45,15 @@ namespace {
 constexpr int BNB = 256;  // weight rows per tile
 constexpr int GM = 8;     // m-tiles per band of the tile order
 
-// Tile shapes <BM, BK, stages, waves> for long reductions and for the rest.
+// Tile shapes <BM, BK, stages, waves, waves along N> for long reductions and
+// for the rest.  The 128-row tile uses a 2 x 4 wave grid (64 x 64 per wave):
+// 4 fragment reads per 4 MFMAs instead of 5 with 4 x 2, which keeps its LDS
+// reads within the MFMA time of a K step.
 #ifndef MOE_GEMM_BIG
-#define MOE_GEMM_BIG 256, 64, 2, 8
+#define MOE_GEMM_BIG 256, 64, 2, 8, 2
 #endif
 #ifndef MOE_GEMM_SMALL
-#define MOE_GEMM_SMALL 128, 64, 3, 8
+#define MOE_GEMM_SMALL 128, 64, 3, 8, 4
 #endif
 
 struct GemmParams {
@@ -125,31 +128,31 @@ __device__ __forceinline__ void gmm_issue(char* smem, int step, int w,
 }
 
 // Reads the A and B fragments of K slice ks (16 columns) of one stage.
-template <int BK, int MI>
+template <int BK, int MI, int NI>
 __device__ __forceinline__ void gmm_frags(const char* sa, const char* sb, const int (&a_row)[MI],
-                                          const int (&b_row)[4], int lane, int ks,
-                                          bf16x8 (&a)[MI], bf16x8 (&b)[4]) {
+                                          const int (&b_row)[NI], int lane, int ks,
+                                          bf16x8 (&a)[MI], bf16x8 (&b)[NI]) {
   constexpr int RB = BK * 2;
   const int kc = ks * 2 + (lane >> 5);
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
     a[mi] = *(const bf16x8*)(sa + a_row[mi] * RB + ((kc ^ swz<BK>(a_row[mi])) << 4));
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni)
+  for (int ni = 0; ni < NI; ++ni)
     b[ni] = *(const bf16x8*)(sb + b_row[ni] * RB + ((kc ^ swz<BK>(b_row[ni])) << 4));
 }
 
-template <int MI>
-__device__ __forceinline__ void gmm_mma(const bf16x8 (&a)[MI], const bf16x8 (&b)[4],
-                                        floatx16 (&acc)[MI][4]) {
+template <int MI, int NI>
+__device__ __forceinline__ void gmm_mma(const bf16x8 (&a)[MI], const bf16x8 (&b)[NI],
+                                        floatx16 (&acc)[MI][NI]) {
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < NI; ++ni)
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
 }
 
-template <int BM, int BK, int NST, bool SWIGLU, int NW>
+template <int BM, int BK, int NST, bool SWIGLU, int NW, int NWN>
 __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   constexpr int RB = BK * 2;          // LDS bytes per row of a stage
   constexpr int CPR = BK / 8;         // 16-byte chunks per row
@@ -158,8 +161,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   constexpr int BI = BNB / RPI / NW;  // B loads per wave per stage
   constexpr int LPS = AI + BI;
   constexpr int SA = BM * RB, SS = (BM + BNB) * RB;
-  constexpr int WM = BM / (NW / 2);   // rows per wave (waves form (NW/2) x 2)
-  constexpr int MI = WM / 32;         // 32-row MFMA tiles per wave
+  constexpr int WM = BM / (NW / NWN);  // rows per wave (waves form (NW/NWN) x NWN)
+  constexpr int MI = WM / 32;          // 32-row MFMA tiles per wave
+  constexpr int NI = BNB / NWN / 32;   // 32-column MFMA tiles per wave
+  static_assert(NI >= 2 && NI % 2 == 0, "a SwiGLU wave pairs gate and up tiles");
   static_assert(AI >= 1 && BI >= 2 && MI >= 1, "tile shape");
   static_assert(NST >= 2 && NST <= 4, "stages");
 
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   __shared__ __attribute__((aligned(1024))) char smem[NST * SS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / NWN, wn = w % NWN;
   const int K = P.K;
   const int KT = K / BK;
 
@@ -236,19 +241,22 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   }
 
   // fragment read offsets (bytes within a stage) for chunk kc of each row
-  int a_row[MI], b_row[4];
+  int a_row[MI], b_row[NI];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) a_row[mi] = wm * WM + mi * 32 + (lane & 31);
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni)
-    b_row[ni] = (SWIGLU ? ((ni >> 1) * 128 + wn * 64 + (ni & 1) * 32) : (wn * 128 + ni * 32)) +
+  // SwiGLU: the wave's gate tiles are its first NI/2, the up tiles of the
+  // same act columns its last NI/2 (weight rows 128 + the gate rows)
+  for (int ni = 0; ni < NI; ++ni)
+    b_row[ni] = (SWIGLU ? ((ni / (NI / 2)) * 128 + wn * (128 / NWN) + (ni % (NI / 2)) * 32)
+                        : (wn * (BNB / NWN) + ni * 32)) +
                 (lane & 31);
 
-  floatx16 acc[MI][4];
+  floatx16 acc[MI][NI];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.0f;
 
@@ -261,7 +269,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   // first fragment reads of the next stage.
   constexpr int NS = BK / 16;  // K slices per step
   static_assert(NS % 2 == 0, "the pending last slice lives in fragment set 1");
-  bf16x8 a[2][MI], b[2][4];
+  bf16x8 a[2][MI], b[2][NI];
   for (int kt = 0; kt < KT; ++kt) {
     const int ahead = min(KT - 1 - kt, NST - 2);  // stages allowed to stay in flight
     if (ahead >= 2) vm_wait_barrier<2 * LPS>();
@@ -273,17 +281,26 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
     const char* sb = sa + SA;
     // slice 0 of this step goes to set 0; slice NS-1 of the previous step
     // is still pending in set 1
-    gmm_frags<BK, MI>(sa, sb, a_row, b_row, lane, 0, a[0], b[0]);
-    if (kt > 0) gmm_mma<MI>(a[1], b[1], acc);  // last slice of the previous step
+    gmm_frags<BK, MI, NI>(sa, sb, a_row, b_row, lane, 0, a[0], b[0]);
+    if (kt > 0) gmm_mma<MI, NI>(a[1], b[1], acc);  // last slice of the previous step
 #pragma unroll
     for (int ks = 0; ks < NS - 1; ++ks) {
       const int cur = ks & 1;
-      gmm_frags<BK, MI>(sa, sb, a_row, b_row, lane, ks + 1, a[cur ^ 1], b[cur ^ 1]);
-      gmm_mma<MI>(a[cur], b[cur], acc);
+      gmm_frags<BK, MI, NI>(sa, sb, a_row, b_row, lane, ks + 1, a[cur ^ 1], b[cur ^ 1]);
+      gmm_mma<MI, NI>(a[cur], b[cur], acc);
     }
   }
-  gmm_mma<MI>(a[(NS - 1) & 1], b[(NS - 1) & 1], acc);
+  gmm_mma<MI, NI>(a[(NS - 1) & 1], b[(NS - 1) & 1], acc);
 
+  // Epilogue through LDS: the ring is free once every wave has read its last
+  // stage, so the tile is written there in bf16 and then stored as whole
+  // 16-byte row chunks (instead of 2-byte stores scattered over rows).
+  constexpr int OUTC = SWIGLU ? 128 : BNB;           // output columns of the tile
+  constexpr int ROWB = OUTC * 2;                      // bytes per output row
+  constexpr int PAD = BM * (ROWB + 16) <= NST * SS ? 16 : 0;  // keeps row r and r+4 apart
+  constexpr int STRIDE = ROWB + PAD;
+  static_assert(BM * STRIDE <= NST * SS, "output tile fits the ring");
+  __syncthreads();
   // 32x32 accumulator layout: register q of a lane holds row
   // (q/4)*8 + (lane/32)*4 + q%4, column lane%32.
 #pragma unroll
@@ -291,21 +308,32 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int lr = wm * WM + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-      if (lr >= rows) continue;
-      uint16_t* crow = P.C + (size_t)(row0 + lr) * P.Nout;
+      uint16_t* orow = (uint16_t*)(smem + lr * STRIDE);
       if (SWIGLU) {
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          float gv = acc[mi][ni][q], uv = acc[mi][ni + 2][q];
-          float av = gv / (1.0f + __expf(-gv)) * uv;
-          crow[nt * 128 + wn * 64 + ni * 32 + (lane & 31)] = f2bf(av);
+        for (int ni = 0; ni < NI / 2; ++ni) {
+          const float gv = acc[mi][ni][q], uv = acc[mi][ni + NI / 2][q];
+          // SiLU(g) * u with the hardware reciprocal (~1 ulp)
+          const float av = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+          orow[wn * (128 / NWN) + ni * 32 + (lane & 31)] = f2bf(av);
         }
       } else {
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          crow[nt * 256 + wn * 128 + ni * 32 + (lane & 31)] = f2bf(acc[mi][ni][q]);
+        for (int ni = 0; ni < NI; ++ni)
+          orow[wn * (BNB / NWN) + ni * 32 + (lane & 31)] = f2bf(acc[mi][ni][q]);
       }
     }
+  }
+  __syncthreads();
+  constexpr int CPRO = ROWB / 16;                 // 16-byte chunks per output row
+  constexpr int RPIO = (64 * NW) / CPRO;          // rows per pass of the block
+  static_assert((64 * NW) % CPRO == 0 && BM % RPIO == 0, "store passes");
+  uint16_t* cbase = P.C + (size_t)row0 * P.Nout + (size_t)nt * OUTC;
+#pragma unroll
+  for (int it = 0; it < BM / RPIO; ++it) {
+    const int r = it * RPIO + tid / CPRO, ch = tid % CPRO;
+    if (r < rows)
+      *(uint4*)(cbase + (size_t)r * P.Nout + ch * 8) = *(const uint4*)(smem + r * STRIDE + ch * 16);
   }
 }
 
@@ -437,7 +465,7 @@ std::mutex& side_mutex() {
   return mu;
 }
 
-template <int BM, int BK, int NST, int NW>
+template <int BM, int BK, int NST, int NW, int NWN>
 hipError_t launch_bf16(const Dims& d, const PassArgs& pa, const GemmPass& gp, const int* toff,
                        const int* tgroup, int go_stride, int tg_stride, const int* slot_expert,
                        const void* wg, const void* wu, const void* wd, void* act, void* out,
@@ -505,9 +533,9 @@ hipError_t launch_bf16(const Dims& d, const PassArgs& pa, const GemmPass& gp, co
     hipStream_t st = part == 0 ? s : ss->s;
     p1.part = p2.part = part;
     p1.parts = p2.parts = parts;
-    hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, true, NW>), dim3((unsigned)g1),
+    hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, true, NW, NWN>), dim3((unsigned)g1),
                        dim3(64 * NW), 0, st, p1);
-    hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, false, NW>), dim3((unsigned)g2),
+    hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, false, NW, NWN>), dim3((unsigned)g2),
                        dim3(64 * NW), 0, st, p2);
   }
   if (parts == 2) {
