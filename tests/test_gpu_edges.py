@@ -1,0 +1,70 @@
+"""GPU parity on degenerate and boundary problems, the whole layer in every
+mode against the float64 oracle (info bit-exact, y within the layer's
+tolerance, and the dropless, chunked and LAYER results bitwise equal).
+
+The cases sit at the edges the method allows: every token choosing every
+expert (k = E), one expert per shard with only some shards resident, a
+fallback whose chunks hold one position of each sequence, a single token,
+heavy capped drops, and the fp32 path with dedup and redundant slots.
+"""
+
+import pytest
+import torch
+
+import oracle
+import workloads
+from moe_cases import binding_problem, check_close, host, ints, oracle_problem, say
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.Workload
+EDGES = {
+    # k = E: every token is routed to every expert
+    "all_experts": W("all_experts", tokens=64, seq_len=64, hidden=256, ffn=128, num_experts=4,
+                     top_k=4, num_shards=2, res_lo=0, res_hi=2, factor=2.0, num_chunks=2),
+    # one expert per shard, shards 2..4 resident, skewed sigmoid routing
+    "one_per_shard": W("one_per_shard", tokens=256, seq_len=64, hidden=256, ffn=256,
+                       num_experts=8, top_k=2, num_shards=8, res_lo=2, res_hi=5, factor=1.0,
+                       num_chunks=4, gate="sigmoid", zipf=1.0),
+    # chunks of one position per sequence (32 chunks of 2 tokens)
+    "chunk_per_position": W("chunk_per_position", tokens=64, seq_len=32, hidden=256, ffn=128,
+                            num_experts=8, top_k=2, num_shards=4, res_lo=0, res_hi=4,
+                            factor=0.5, num_chunks=32, zipf=1.2),
+    # a single token
+    "single_token": W("single_token", tokens=1, seq_len=1, hidden=256, ffn=128, num_experts=8,
+                      top_k=2, num_shards=4, res_lo=0, res_hi=4, factor=2.0, num_chunks=1),
+    # a cap of a quarter of the balanced load: most rows drop when capped
+    "capped_drops": W("capped_drops", tokens=256, seq_len=256, hidden=256, ffn=128,
+                      num_experts=16, top_k=2, num_shards=4, res_lo=0, res_hi=4, factor=0.25,
+                      num_chunks=4, zipf=1.0),
+    # fp32 with dedup and two redundant slots
+    "fp32_dedup_redundant": W("fp32_dedup_redundant", tokens=128, seq_len=128, hidden=64,
+                              ffn=64, num_experts=8, top_k=3, num_shards=4, res_lo=0, res_hi=4,
+                              factor=1.0, num_chunks=2, bf16=False, dedup=True,
+                              slots_per_shard=1, num_replicas=2, zipf=1.5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGES))
+def test_edge_layer_all_modes(name):
+    import grouped_gemm_shard_amd as g
+    w = EDGES[name]
+    p, op = binding_problem(w), oracle_problem(w)
+    inp = workloads.make_inputs(w, device="cuda")
+    logits, x = inp["logits"].cpu().numpy(), host(inp["x"])
+    ws = [host(t) for t in inp["weights"]]
+    ys = {}
+    for mode in (g.MODE_LAYER, g.MODE_FORCE_DROPLESS, g.MODE_CAPPED_ONLY, g.MODE_FORCE_CHUNKED):
+        say(f"[edge] {name} mode={mode}")
+        run = g.LayerRunner(p, mode)
+        y = run(inp["x"], inp["logits"], *inp["weights"]).clone()
+        info = ints(run.info)
+        want = oracle.layer(op, mode, logits, x, *ws)
+        torch.cuda.synchronize()
+        cap = -1 if want["cap"] is None else want["cap"]
+        assert info.tolist() == [int(want["overflow"]), int(want["fallback_ran"]), cap,
+                                 int(want["shard_counts"].max())], name
+        check_close(host(y), want["y"], f"y {name} mode {mode}")
+        ys[mode] = y
+    assert torch.equal(ys[g.MODE_FORCE_DROPLESS], ys[g.MODE_FORCE_CHUNKED])
+    assert torch.equal(ys[g.MODE_LAYER], ys[g.MODE_FORCE_DROPLESS])
