@@ -13,13 +13,16 @@ namespace moe {
 
 namespace {
 
-// One token's output columns [h, h + 8) in bf16: the KC row loads of a
-// batch of KC assignments are issued together, then accumulated in j order.
-template <int KC>
+// Output columns [h + u*512, h + u*512 + 8) of one token, u < HU, in bf16:
+// the row loads of a batch of KC assignments for all HU column groups are
+// issued together, then accumulated in ascending j (the summation order of
+// every column stays j = 0, 1, ..., k-1).
+template <int KC, int HU>
 __device__ __forceinline__ void combine_bf16_cols(const uint16_t* __restrict__ o, const int* rows,
                                                   const float* gts, int j0, int k, int H,
-                                                  long long max_rows, int h, float (&acc)[8]) {
-  uint4 v[KC];
+                                                  long long max_rows, int h,
+                                                  float (&acc)[HU][8]) {
+  uint4 v[KC][HU];
   float gj[KC];
   bool ok[KC];
 #pragma unroll
@@ -28,16 +31,22 @@ __device__ __forceinline__ void combine_bf16_cols(const uint16_t* __restrict__ o
     const int r = j < k ? rows[j] : -1;
     ok[u] = r >= 0 && r < max_rows;
     gj[u] = j < k ? gts[j] : 0.0f;
-    if (ok[u]) v[u] = *(const uint4*)(o + (size_t)r * H + h);
+#pragma unroll
+    for (int c = 0; c < HU; ++c)
+      if (ok[u] && h + c * 512 < H) v[u][c] = *(const uint4*)(o + (size_t)r * H + h + c * 512);
   }
 #pragma unroll
   for (int u = 0; u < KC; ++u) {
     if (!ok[u]) continue;
-    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] = fmaf(gj[u], __uint_as_float(w[q] << 16), acc[2 * q]);
-      acc[2 * q + 1] = fmaf(gj[u], __uint_as_float(w[q] & 0xffff0000u), acc[2 * q + 1]);
+    for (int c = 0; c < HU; ++c) {
+      if (h + c * 512 >= H) continue;
+      const uint32_t w[4] = {v[u][c].x, v[u][c].y, v[u][c].z, v[u][c].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[c][2 * q] = fmaf(gj[u], __uint_as_float(w[q] << 16), acc[c][2 * q]);
+        acc[c][2 * q + 1] = fmaf(gj[u], __uint_as_float(w[q] & 0xffff0000u), acc[c][2 * q + 1]);
+      }
     }
   }
 }
@@ -61,19 +70,26 @@ __global__ __launch_bounds__(256) void combine_kernel(Dims d, PassArgs pa, Layou
   if (BF16) {
     const uint16_t* o = (const uint16_t*)out;
     uint16_t* yr = (uint16_t*)y + (size_t)t * d.H;
-    for (int h = lane * 8; h < d.H; h += 512) {
-      float acc[8];
+    constexpr int HU = 4;  // column groups of 512 per pass over the assignments
+    for (int h = lane * 8; h < d.H; h += 512 * HU) {
+      float acc[HU][8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-      // assignments in ascending j, four row loads in flight at a time
-      for (int j0 = 0; j0 < d.k; j0 += 4)
-        combine_bf16_cols<4>(o, rows, gts, j0, d.k, d.H, max_rows, h, acc);
-      uint4 outv;
-      outv.x = (uint32_t)f2bf(acc[0]) | ((uint32_t)f2bf(acc[1]) << 16);
-      outv.y = (uint32_t)f2bf(acc[2]) | ((uint32_t)f2bf(acc[3]) << 16);
-      outv.z = (uint32_t)f2bf(acc[4]) | ((uint32_t)f2bf(acc[5]) << 16);
-      outv.w = (uint32_t)f2bf(acc[6]) | ((uint32_t)f2bf(acc[7]) << 16);
-      *(uint4*)(yr + h) = outv;
+      for (int c = 0; c < HU; ++c)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[c][q] = 0.0f;
+      // assignments in ascending j, two at a time: 2 x HU row loads in flight
+      for (int j0 = 0; j0 < d.k; j0 += 2)
+        combine_bf16_cols<2, HU>(o, rows, gts, j0, d.k, d.H, max_rows, h, acc);
+#pragma unroll
+      for (int c = 0; c < HU; ++c) {
+        if (h + c * 512 >= d.H) continue;
+        uint4 outv;
+        outv.x = (uint32_t)f2bf(acc[c][0]) | ((uint32_t)f2bf(acc[c][1]) << 16);
+        outv.y = (uint32_t)f2bf(acc[c][2]) | ((uint32_t)f2bf(acc[c][3]) << 16);
+        outv.z = (uint32_t)f2bf(acc[c][4]) | ((uint32_t)f2bf(acc[c][5]) << 16);
+        outv.w = (uint32_t)f2bf(acc[c][6]) | ((uint32_t)f2bf(acc[c][7]) << 16);
+        *(uint4*)(yr + h + c * 512) = outv;
+      }
     }
   } else {
     const float* o = (const float*)out;
