@@ -29,11 +29,14 @@
 //
 // Tiles: every group owns ceil(rows/BM) m-tiles (an exclusive scan over
 // groups, with an m-tile -> group map, computed with the layout), so empty
-// groups cost nothing.  A group's tiles are ordered in bands of up to GM
-// m-tiles, n-tile by n-tile.  Workgroups are dispatched round-robin over the
-// 8 XCDs, and each XCD is given a contiguous range of that order, so the
-// blocks an XCD runs together cover a few m-tiles by a few n-tiles of one
-// expert and share both operand panels in its L2.
+// groups cost nothing.  With BM = 256, a group's last m-tile runs as a
+// 128-row tile when it holds at most 128 rows.  Tiles are ordered in bands
+// of up to GM m-tiles, n-tile by n-tile.  Workgroups are dispatched
+// round-robin over the 8 XCDs; each round of CU-count blocks covers a run of
+// that order and each XCD a contiguous eighth of the run, so the blocks an
+// XCD runs together cover a few m-tiles by a few n-tiles of one expert and
+// share both operand panels in its L2, and every XCD gets the same share of
+// tall and short tiles.
 #include <mutex>
 
 #include "common.h"
@@ -55,6 +58,10 @@ constexpr int GM = 8;     // m-tiles per band of the tile order
 #ifndef MOE_GEMM_SMALL
 #define MOE_GEMM_SMALL 128, 64, 3, 8, 4
 #endif
+constexpr int shape_rows(int bm, int, int, int, int) { return bm; }
+constexpr int shape_ring(int bm, int bk, int nst, int, int) { return nst * (bm + BNB) * bk * 2; }
+constexpr int kSmallBM = shape_rows(MOE_GEMM_SMALL);
+constexpr int kSmallRing = shape_ring(MOE_GEMM_SMALL);
 
 struct GemmParams {
   const uint16_t* A;       // row source (whole array; rows past a group read as zero)
@@ -71,6 +78,7 @@ struct GemmParams {
   int go_stride, tg_stride;  // per layout j
   const int* slot_expert;
   int G, K, Nout, lo_slot, e_base, e_res, n_ntiles;
+  int round_blocks;        // blocks per round of the tile order (a multiple of 8)
   int part, parts;         // this launch covers m-tiles [M*part/parts, M*(part+1)/parts)
   long long max_rows;
   PassArgs pa;
@@ -152,8 +160,12 @@ __device__ __forceinline__ void gmm_mma(const bf16x8 (&a)[MI], const bf16x8 (&b)
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
 }
 
-template <int BM, int BK, int NST, bool SWIGLU, int NW, int NWN>
-__global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
+// One BM x 256 tile (GEMM1: BM x 128 act columns) of group rows
+// [row0, row0 + rows), rows <= BM, of weight n-tile nt of local expert e;
+// smem holds at least NST * (BM + 256) * BK * 2 bytes.
+template <int BM, int BK, int NST, int NW, int NWN, bool SWIGLU>
+__device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const int* aidx,
+                                         int row0, int rows, int nt, int e) {
   constexpr int RB = BK * 2;          // LDS bytes per row of a stage
   constexpr int CPR = BK / 8;         // 16-byte chunks per row
   constexpr int RPI = 1024 / RB;      // rows one wave-wide load fills
@@ -168,41 +180,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   static_assert(AI >= 1 && BI >= 2 && MI >= 1, "tile shape");
   static_assert(NST >= 2 && NST <= 4, "stages");
 
-  PassInfo pi = resolve_pass(P.pa);
-  if (!pi.active) return;
-  const int* group_offsets = P.group_offsets + (size_t)pi.j * P.go_stride;
-  const int* tile_off = P.tile_off + (size_t)pi.j * P.go_stride;
-  const int* tile_group = P.tile_group + (size_t)pi.j * P.tg_stride;
-  const int total_mt = tile_off[P.G];
-  if (group_offsets[P.G] > P.max_rows || total_mt < 0) return;  // malformed: touch nothing
-  // this launch's part of the m-tiles
-  const int m0 = (int)(((long long)total_mt * P.part) / P.parts);
-  const int mx = (int)(((long long)total_mt * (P.part + 1)) / P.parts) - m0;
-  const int total = mx * P.n_ntiles;
-  const int per_xcd = (total + 7) >> 3;
-  const int bid = blockIdx.x;
-  if ((bid >> 3) >= per_xcd) return;
-  const int L = (bid & 7) * per_xcd + (bid >> 3);
-  if (L >= total) return;
-  // The part's tiles go in bands of up to GM m-tiles, n-tile by n-tile, so
-  // the blocks an XCD runs together cover a few m-tiles by a few n-tiles and
-  // share both operand panels in that XCD's L2.
-  const int band = L / (GM * P.n_ntiles);
-  const int gm = min(GM, mx - band * GM);
-  const int r = L - band * GM * P.n_ntiles;
-  const int nt = r / gm;
-  const int m = m0 + band * GM + (r - nt * gm);
-  const int g = tile_group[m];
-  if (g < 0 || g >= P.G) return;
-  const int ml = m - tile_off[g];
-  const int gend = group_offsets[g + 1];
-  const int row0 = group_offsets[g] + ml * BM;
-  if (row0 < 0 || row0 >= gend || gend > P.max_rows) return;
-  const int rows = min(BM, gend - row0);
-  const int e = P.slot_expert[P.lo_slot + g] - P.e_base;
-  if (e < 0 || e >= P.e_res) return;  // rows in a slot that hosts no resident expert
-
-  __shared__ __attribute__((aligned(1024))) char smem[NST * SS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / NWN, wn = w % NWN;
@@ -213,7 +190,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   // the row index (gathered rows) or are the pass rows themselves.  Rows
   // past the group get an offset beyond the buffer and read as zero.
   const __amdgpu_buffer_rsrc_t ra_r = make_rsrc(P.A, (unsigned)P.a_rows * K * 2);
-  const int* aidx = P.a_index ? P.a_index + (size_t)pi.j * P.a_index_stride : nullptr;
   __amdgpu_buffer_rsrc_t rb0, rb1;
   if (SWIGLU) {
     rb0 = make_rsrc(P.B0 + (size_t)e * P.b_stride + (size_t)nt * 128 * K, 128u * K * 2);
@@ -335,6 +311,64 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
     if (r < rows)
       *(uint4*)(cbase + (size_t)r * P.Nout + ch * 8) = *(const uint4*)(smem + r * STRIDE + ch * 16);
   }
+}
+
+template <int BM, int BK, int NST, bool SWIGLU, int NW, int NWN>
+__global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
+  // one ring for either tile shape the kernel may run
+  constexpr int RING = NST * (BM + BNB) * BK * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[RING > kSmallRing ? RING : kSmallRing];
+  PassInfo pi = resolve_pass(P.pa);
+  if (!pi.active) return;
+  const int* group_offsets = P.group_offsets + (size_t)pi.j * P.go_stride;
+  const int* tile_off = P.tile_off + (size_t)pi.j * P.go_stride;
+  const int* tile_group = P.tile_group + (size_t)pi.j * P.tg_stride;
+  const int total_mt = tile_off[P.G];
+  if (group_offsets[P.G] > P.max_rows || total_mt < 0) return;  // malformed: touch nothing
+  // this launch's part of the m-tiles
+  const int m0 = (int)(((long long)total_mt * P.part) / P.parts);
+  const int mx = (int)(((long long)total_mt * (P.part + 1)) / P.parts) - m0;
+  const int total = mx * P.n_ntiles;
+  // Blocks go round-robin over the 8 XCDs (block b to XCD b % 8).  Each
+  // round of round_blocks blocks covers that many consecutive tiles of the
+  // order (the last round what is left), and XCD x takes the x-th eighth of
+  // the round: every XCD gets an equal share of every part of the order
+  // (tiles differ in height, so a split of the whole order into eighths
+  // would leave some XCDs the heavy groups), and the tiles it runs together
+  // are neighbours in the order.
+  const int nb = P.round_blocks;
+  const int bid = blockIdx.x;
+  const int rbase = (bid / nb) * nb;
+  const int rs = min(nb, total - rbase);  // tiles in this round
+  if (rs <= 0) return;
+  const int x = bid & 7, slot = (bid - rbase) >> 3;
+  const int L = rbase + (x * rs >> 3) + slot;
+  if (L >= rbase + ((x + 1) * rs >> 3)) return;
+  // The part's tiles go in bands of up to GM m-tiles, n-tile by n-tile, so
+  // neighbouring tiles cover a few m-tiles by a few n-tiles and share both
+  // operand panels in an XCD's L2.
+  const int band = L / (GM * P.n_ntiles);
+  const int gm = min(GM, mx - band * GM);
+  const int r = L - band * GM * P.n_ntiles;
+  const int nt = r / gm;
+  const int m = m0 + band * GM + (r - nt * gm);
+  const int g = tile_group[m];
+  if (g < 0 || g >= P.G) return;
+  const int ml = m - tile_off[g];
+  const int gend = group_offsets[g + 1];
+  const int row0 = group_offsets[g] + ml * BM;
+  if (row0 < 0 || row0 >= gend || gend > P.max_rows) return;
+  const int rows = min(BM, gend - row0);
+  const int e = P.slot_expert[P.lo_slot + g] - P.e_base;
+  if (e < 0 || e >= P.e_res) return;  // rows in a slot that hosts no resident expert
+  const int* aidx = P.a_index ? P.a_index + (size_t)pi.j * P.a_index_stride : nullptr;
+  // A group's last tile with at most 128 rows runs as a 128-row tile: the
+  // same place in the tile order (so it shares the expert's weight panels
+  // in L2 with the group's other tiles), half the MFMA work.
+  if (BM > kSmallBM && rows <= kSmallBM)
+    gmm_tile<MOE_GEMM_SMALL, SWIGLU>(P, smem, aidx, row0, rows, nt, e);
+  else
+    gmm_tile<BM, BK, NST, NW, NWN, SWIGLU>(P, smem, aidx, row0, rows, nt, e);
 }
 
 // fp32 path (the tiny fp32 workload): one thread per output element.
@@ -465,6 +499,24 @@ std::mutex& side_mutex() {
   return mu;
 }
 
+// Compute units of the current device rounded down to a multiple of 8 (the
+// XCDs): the blocks per round of the tile order.
+int round_blocks() {
+  static int cus[64] = {0};
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 8)
+      n = 256;
+    cus[dev] = n / 8 * 8;
+  }
+  return cus[dev];
+}
+
 template <int BM, int BK, int NST, int NW, int NWN>
 hipError_t launch_bf16(const Dims& d, const PassArgs& pa, const GemmPass& gp, const int* toff,
                        const int* tgroup, int go_stride, int tg_stride, const int* slot_expert,
@@ -520,8 +572,10 @@ hipError_t launch_bf16(const Dims& d, const PassArgs& pa, const GemmPass& gp, co
   SideStream* ss = d.F >= 4096 ? side_stream() : nullptr;
   const int parts = ss ? 2 : 1;
   const long long mt_part = (mt_ub + parts - 1) / parts + 1;
-  const long long g1 = (mt_part * p1.n_ntiles + 7) / 8 * 8;
-  const long long g2 = (mt_part * p2.n_ntiles + 7) / 8 * 8;
+  const int nb = round_blocks();
+  p1.round_blocks = p2.round_blocks = nb;
+  const long long g1 = (mt_part * p1.n_ntiles + nb - 1) / nb * nb;
+  const long long g2 = (mt_part * p2.n_ntiles + nb - 1) / nb * nb;
   std::unique_lock<std::mutex> lock(side_mutex(), std::defer_lock);
   if (parts == 2) {
     lock.lock();
