@@ -31,7 +31,8 @@ MEDIUM = {
                                                        seq_len=1024, hidden=1024, ffn=2048),
     "dedup_small": CONFIGS["dedup_redundant"].scaled(name="dedup_small", tokens=512,
                                                      seq_len=512, hidden=256, ffn=128),
-    # hidden >= 2048 selects the 256-row GEMM tile
+    # hidden >= 2048 selects 256-row GEMM tiles (a group's last tile of at
+    # most 128 rows runs as a 128-row tile)
     "maverick_mid": CONFIGS["maverick_shard"].scaled(name="maverick_mid", tokens=2048,
                                                      seq_len=512, hidden=2048, ffn=1024),
     # F >= 4096: the grouped GEMM splits each pass into two stream-parallel
