@@ -18,25 +18,28 @@
 // grid (128-row tiles: 64 x 64 per wave) of 32 x 32 MFMA tiles.
 //
 // Operands go from HBM straight into LDS (buffer_load ... lds, 16 bytes per
-// lane, no staging registers) through a ring of NST stages of BK = 64
-// columns, so NST-1 stages of loads are in flight while one is multiplied.
-// Two shapes: BM=256 with 2 stages (128 KB LDS) for long reductions, where
-// the taller tile halves the operand traffic per flop, and BM=128 with 3
-// stages (144 KB) otherwise.  In LDS each 128-byte row holds its 16-byte
-// chunks XOR-permuted by row, so the fragment reads of consecutive rows at
-// one chunk hit distinct banks.  Rows of A past the group read as zero (an
-// offset past the buffer's byte range) and their results are not stored.
+// lane, no staging registers) through a ring of NST stages of BK columns,
+// so NST-1 stages of loads are in flight while one is multiplied.  Shapes:
+// BM=256, BK=64, 2 stages (128 KB LDS) for long reductions (H >= 2048),
+// where the taller tile halves the operand traffic per flop; otherwise
+// BM=128, BK=32, 3 stages (72 KB), so two workgroups share a CU and one's
+// tile set-up, first loads and epilogue overlap the other's MFMAs.  A
+// 256-row kernel runs a group's short last tile as BM=128, BK=64, 3 stages.
+// In LDS the 16-byte chunks of each row are XOR-permuted by row, so the
+// fragment reads of consecutive rows at one chunk hit distinct banks.  Rows
+// of A past the group read as zero (an offset past the buffer's byte range)
+// and their results are not stored.
 //
 // Tiles: every group owns ceil(rows/BM) m-tiles (an exclusive scan over
 // groups, with an m-tile -> group map, computed with the layout), so empty
 // groups cost nothing.  With BM = 256, a group's last m-tile runs as a
 // 128-row tile when it holds at most 128 rows.  Tiles are ordered in bands
 // of up to GM m-tiles, n-tile by n-tile.  Workgroups are dispatched
-// round-robin over the 8 XCDs; each round of CU-count blocks covers a run of
-// that order and each XCD a contiguous eighth of the run, so the blocks an
-// XCD runs together cover a few m-tiles by a few n-tiles of one expert and
-// share both operand panels in its L2, and every XCD gets the same share of
-// tall and short tiles.
+// round-robin over the 8 XCDs; each round of as many blocks as the chip
+// holds at once covers a run of that order and each XCD a contiguous eighth
+// of the run, so the blocks an XCD runs together cover a few m-tiles by a
+// few n-tiles of one expert and share both operand panels in its L2, and
+// every XCD gets the same share of tall and short tiles.
 #include <mutex>
 
 #include "common.h"
@@ -48,20 +51,25 @@ namespace {
 constexpr int BNB = 256;  // weight rows per tile
 constexpr int GM = 8;     // m-tiles per band of the tile order
 
-// Tile shapes <BM, BK, stages, waves, waves along N> for long reductions and
-// for the rest.  The 128-row tile uses a 2 x 4 wave grid (64 x 64 per wave):
-// 4 fragment reads per 4 MFMAs instead of 5 with 4 x 2, which keeps its LDS
-// reads within the MFMA time of a K step.
+// Tile shapes <BM, BK, stages, waves, waves along N>: BIG for long
+// reductions, SMALL for the rest, and REM, the 128-row shape a BIG kernel
+// runs for a group's last tile of at most 128 rows (same wave count as BIG).
+// REM uses a 2 x 4 wave grid (64 x 64 per wave): 4 fragment reads per 4
+// MFMAs instead of 5 with 4 x 2.
 #ifndef MOE_GEMM_BIG
 #define MOE_GEMM_BIG 256, 64, 2, 8, 2
 #endif
 #ifndef MOE_GEMM_SMALL
-#define MOE_GEMM_SMALL 128, 64, 3, 8, 4
+#define MOE_GEMM_SMALL 128, 32, 3, 8, 4
+#endif
+#ifndef MOE_GEMM_REM
+#define MOE_GEMM_REM 128, 64, 3, 8, 4
 #endif
 constexpr int shape_rows(int bm, int, int, int, int) { return bm; }
+constexpr int shape_waves(int, int, int, int nw, int) { return nw; }
 constexpr int shape_ring(int bm, int bk, int nst, int, int) { return nst * (bm + BNB) * bk * 2; }
-constexpr int kSmallBM = shape_rows(MOE_GEMM_SMALL);
-constexpr int kSmallRing = shape_ring(MOE_GEMM_SMALL);
+constexpr int kRemBM = shape_rows(MOE_GEMM_REM);
+constexpr int kRemRing = shape_ring(MOE_GEMM_REM);
 
 struct GemmParams {
   const uint16_t* A;       // row source (whole array; rows past a group read as zero)
@@ -78,7 +86,8 @@ struct GemmParams {
   int go_stride, tg_stride;  // per layout j
   const int* slot_expert;
   int G, K, Nout, lo_slot, e_base, e_res, n_ntiles;
-  int round_blocks;        // blocks per round of the tile order (a multiple of 8)
+  int round_blocks;        // blocks per round of the tile order (a multiple of 8):
+                           // the blocks resident on the chip at once
   int part, parts;         // this launch covers m-tiles [M*part/parts, M*(part+1)/parts)
   long long max_rows;
   PassArgs pa;
@@ -316,8 +325,10 @@ __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const 
 template <int BM, int BK, int NST, bool SWIGLU, int NW, int NWN>
 __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   // one ring for either tile shape the kernel may run
+  constexpr bool HAS_REM = BM > kRemBM;
   constexpr int RING = NST * (BM + BNB) * BK * 2;
-  __shared__ __attribute__((aligned(1024))) char smem[RING > kSmallRing ? RING : kSmallRing];
+  static_assert(!HAS_REM || shape_waves(MOE_GEMM_REM) == NW, "REM runs in the same block");
+  __shared__ __attribute__((aligned(1024))) char smem[HAS_REM && kRemRing > RING ? kRemRing : RING];
   PassInfo pi = resolve_pass(P.pa);
   if (!pi.active) return;
   const int* group_offsets = P.group_offsets + (size_t)pi.j * P.go_stride;
@@ -365,8 +376,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   // A group's last tile with at most 128 rows runs as a 128-row tile: the
   // same place in the tile order (so it shares the expert's weight panels
   // in L2 with the group's other tiles), half the MFMA work.
-  if (BM > kSmallBM && rows <= kSmallBM)
-    gmm_tile<MOE_GEMM_SMALL, SWIGLU>(P, smem, aidx, row0, rows, nt, e);
+  if (HAS_REM && rows <= kRemBM)
+    gmm_tile<MOE_GEMM_REM, SWIGLU>(P, smem, aidx, row0, rows, nt, e);
   else
     gmm_tile<BM, BK, NST, NW, NWN, SWIGLU>(P, smem, aidx, row0, rows, nt, e);
 }
@@ -517,6 +528,25 @@ int round_blocks() {
   return cus[dev];
 }
 
+// Workgroups of one tile shape that fit on a CU at once (the GEMM1 kernel).
+template <int BM, int BK, int NST, int NW, int NWN>
+int resident_blocks() {
+  static int occ[64] = {0};
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (occ[dev] == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(gmm_bf16_kernel<BM, BK, NST, true, NW, NWN>),
+            64 * NW, 0) != hipSuccess || n < 1)
+      n = 1;
+    occ[dev] = n;
+  }
+  return occ[dev];
+}
+
 template <int BM, int BK, int NST, int NW, int NWN>
 hipError_t launch_bf16(const Dims& d, const PassArgs& pa, const GemmPass& gp, const int* toff,
                        const int* tgroup, int go_stride, int tg_stride, const int* slot_expert,
@@ -572,7 +602,7 @@ hipError_t launch_bf16(const Dims& d, const PassArgs& pa, const GemmPass& gp, co
   SideStream* ss = d.F >= 4096 ? side_stream() : nullptr;
   const int parts = ss ? 2 : 1;
   const long long mt_part = (mt_ub + parts - 1) / parts + 1;
-  const int nb = round_blocks();
+  const int nb = round_blocks() * resident_blocks<BM, BK, NST, NW, NWN>();
   p1.round_blocks = p2.round_blocks = nb;
   const long long g1 = (mt_part * p1.n_ntiles + nb - 1) / nb * nb;
   const long long g2 = (mt_part * p2.n_ntiles + nb - 1) / nb * nb;
