@@ -42,12 +42,12 @@ PEAK_HBM_GBS = 8000.0
 
 # HBM traffic of the grouped GEMM (both launches) per mid_bf16 layer, from two
 # rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by what the counters
-# read for a plain 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  It
+# read for a plain 1 GiB device copy (FETCH_SIZE x1.9999, WRITE_SIZE x1.0).  It
 # holds only for the kernel source it was measured on (sha256 of gmm.hip);
 # for any other source or workload the traffic is reported as null.
 GEMM_TRAFFIC = {"workload": "mid_bf16",
-                "gmm_src_sha256": "dbce7c77d32d3b2900be3af27e07e7d1fab4da617044c74dbd016b310576c566",
-                "bytes_per_layer": 292102544}
+                "gmm_src_sha256": "aab40b7b9c13480c019feae46cc84b2883a6ee1ca76196aa049b0efeb82b2ac3",
+                "bytes_per_layer": 238202196}
 
 
 def recorded_gemm_traffic(workload):
