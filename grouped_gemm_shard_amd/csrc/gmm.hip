@@ -41,6 +41,7 @@
 // few n-tiles of one expert and share both operand panels in its L2, and
 // every XCD gets the same share of tall and short tiles.
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 
@@ -144,26 +145,29 @@ __device__ __forceinline__ void gmm_issue(char* smem, int step, int w,
                                              b_off[i], kb, 0, 0);
 }
 
-// Reads the A and B fragments of K slice ks (16 columns) of one stage.
-template <int BK, int MI, int NI>
+// Reads the A and B fragments of K slice ks (16 columns) of one stage, for
+// the wave's first LV 32-row MFMA tiles (the rest hold only rows past the
+// group).
+template <int BK, int MI, int NI, int LV>
 __device__ __forceinline__ void gmm_frags(const char* sa, const char* sb, const int (&a_row)[MI],
                                           const int (&b_row)[NI], int lane, int ks,
                                           bf16x8 (&a)[MI], bf16x8 (&b)[NI]) {
+  if (LV == 0) return;
   constexpr int RB = BK * 2;
   const int kc = ks * 2 + (lane >> 5);
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+  for (int mi = 0; mi < LV; ++mi)
     a[mi] = *(const bf16x8*)(sa + a_row[mi] * RB + ((kc ^ swz<BK>(a_row[mi])) << 4));
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni)
     b[ni] = *(const bf16x8*)(sb + b_row[ni] * RB + ((kc ^ swz<BK>(b_row[ni])) << 4));
 }
 
-template <int MI, int NI>
+template <int MI, int NI, int LV>
 __device__ __forceinline__ void gmm_mma(const bf16x8 (&a)[MI], const bf16x8 (&b)[NI],
                                         floatx16 (&acc)[MI][NI]) {
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+  for (int mi = 0; mi < LV; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
@@ -251,31 +255,44 @@ __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const 
 
   // Software pipeline across K steps: the last slice's fragments are read
   // before the barrier, and its MFMAs are issued after it, overlapping the
-  // first fragment reads of the next stage.
+  // first fragment reads of the next stage.  A wave multiplies only its
+  // 32-row MFMA tiles that hold rows of the group (LV of them); padding rows
+  // cost it no fragment reads and no MFMAs, so on a short tile the other
+  // wave of each SIMD has the matrix pipe to itself.  Every wave still
+  // issues its share of the loads and joins every barrier.
   constexpr int NS = BK / 16;  // K slices per step
   static_assert(NS % 2 == 0, "the pending last slice lives in fragment set 1");
+  static_assert(MI <= 2, "live-tile dispatch covers MI <= 2");
   bf16x8 a[2][MI], b[2][NI];
-  for (int kt = 0; kt < KT; ++kt) {
-    const int ahead = min(KT - 1 - kt, NST - 2);  // stages allowed to stay in flight
-    if (ahead >= 2) vm_wait_barrier<2 * LPS>();
-    else if (ahead == 1) vm_wait_barrier<LPS>();
-    else vm_wait_barrier<0>();
-    if (kt + NST - 1 < KT)
-      gmm_issue<BM, BK, NST, SWIGLU, NW>(smem, kt + NST - 1, w, ra_r, rb0, rb1, a_off, b_off);
-    const char* sa = smem + (kt % NST) * SS;
-    const char* sb = sa + SA;
-    // slice 0 of this step goes to set 0; slice NS-1 of the previous step
-    // is still pending in set 1
-    gmm_frags<BK, MI, NI>(sa, sb, a_row, b_row, lane, 0, a[0], b[0]);
-    if (kt > 0) gmm_mma<MI, NI>(a[1], b[1], acc);  // last slice of the previous step
+  auto kloop = [&](auto live_c) {
+    constexpr int LV = decltype(live_c)::value;
+    for (int kt = 0; kt < KT; ++kt) {
+      const int ahead = min(KT - 1 - kt, NST - 2);  // stages allowed to stay in flight
+      if (ahead >= 2) vm_wait_barrier<2 * LPS>();
+      else if (ahead == 1) vm_wait_barrier<LPS>();
+      else vm_wait_barrier<0>();
+      if (kt + NST - 1 < KT)
+        gmm_issue<BM, BK, NST, SWIGLU, NW>(smem, kt + NST - 1, w, ra_r, rb0, rb1, a_off, b_off);
+      const char* sa = smem + (kt % NST) * SS;
+      const char* sb = sa + SA;
+      // slice 0 of this step goes to set 0; slice NS-1 of the previous step
+      // is still pending in set 1
+      gmm_frags<BK, MI, NI, LV>(sa, sb, a_row, b_row, lane, 0, a[0], b[0]);
+      if (kt > 0) gmm_mma<MI, NI, LV>(a[1], b[1], acc);  // last slice of the previous step
 #pragma unroll
-    for (int ks = 0; ks < NS - 1; ++ks) {
-      const int cur = ks & 1;
-      gmm_frags<BK, MI, NI>(sa, sb, a_row, b_row, lane, ks + 1, a[cur ^ 1], b[cur ^ 1]);
-      gmm_mma<MI, NI>(a[cur], b[cur], acc);
+      for (int ks = 0; ks < NS - 1; ++ks) {
+        const int cur = ks & 1;
+        gmm_frags<BK, MI, NI, LV>(sa, sb, a_row, b_row, lane, ks + 1, a[cur ^ 1], b[cur ^ 1]);
+        gmm_mma<MI, NI, LV>(a[cur], b[cur], acc);
+      }
     }
-  }
-  gmm_mma<MI, NI>(a[(NS - 1) & 1], b[(NS - 1) & 1], acc);
+    gmm_mma<MI, NI, LV>(a[(NS - 1) & 1], b[(NS - 1) & 1], acc);
+  };
+  // 32-row MFMA tiles of this wave that hold rows of the group (wave-uniform)
+  const int live = __builtin_amdgcn_readfirstlane(min(MI, max(0, (rows - wm * WM + 31) / 32)));
+  if (live >= MI) kloop(std::integral_constant<int, MI>{});
+  else if (live == 1) kloop(std::integral_constant<int, (MI > 1 ? 1 : MI)>{});
+  else kloop(std::integral_constant<int, 0>{});
 
   // Epilogue through LDS: the ring is free once every wave has read its last
   // stage, so the tile is written there in bf16 and then stored as whole
