@@ -212,11 +212,19 @@ struct LayerWs {
   int* status;
   void* count_scratch;
   void* layout_scratch;
-  void* x_dedup;
-  void* act;
-  void* out;
+  // per-pass buffers, two sets when passes alternate between two streams
+  void* x_dedup[2];
+  void* act[2];
+  void* out[2];
   size_t bytes;
 };
+
+// Pass slots a layer call enqueues: with the device-side choice (LAYER with
+// a cap) one per chunk batch, the first also standing for the single pass;
+// otherwise one per layout.
+int layer_pass_slots(const LayoutSet& ls) {
+  return (ls.has_single && ls.w_cnt > 0) ? ls.w_cnt : layout_num_passes(ls);
+}
 
 LayerWs carve_layer(const Dims& d, const LayoutSet& ls, int64_t rows, int64_t drows, char* base) {
   LayerWs w;
@@ -238,9 +246,13 @@ LayerWs carve_layer(const Dims& d, const LayoutSet& ls, int64_t rows, int64_t dr
   w.status = (int*)take(4 * 4);
   w.count_scratch = take(count_scratch_bytes(d));
   w.layout_scratch = take(layout_scratch_bytes(d, ls));
-  w.x_dedup = take(d.dedup ? (size_t)drows * d.H * es : 0);
-  w.act = take((size_t)rows * d.F * es);
-  w.out = take((size_t)rows * d.H * es);
+  const int sets = layer_pass_slots(ls) >= 2 ? 2 : 1;
+  for (int i = 0; i < 2; ++i) {
+    const bool own = i < sets;
+    w.x_dedup[i] = own ? take(d.dedup ? (size_t)drows * d.H * es : 0) : nullptr;
+    w.act[i] = own ? take((size_t)rows * d.F * es) : nullptr;
+    w.out[i] = own ? take((size_t)rows * d.H * es) : nullptr;
+  }
   w.bytes = off;
   return w;
 }
@@ -263,15 +275,16 @@ bool fits_rsrc(const Dims& d, int64_t rows, int64_t drows) {
 // Then the combine of the pass's tokens.
 int run_pass(const Dims& d, const PassArgs& pa, const LayoutSet& ls, const LayoutBuffers& lb,
              const void* x, const void* wg, const void* wu, const void* wd, void* y,
-             const LayerWs& w, int64_t rows, int64_t drows, hipStream_t s) {
+             const LayerWs& w, int set, bool split_ok, int64_t rows, int64_t drows,
+             hipStream_t s) {
   const long long tk = (long long)d.T * d.k;
   const int es = d.bf16 ? 2 : 4;
   GemmPass gp;
   if (d.dedup) {
     hipError_t e = launch_gather_rows(lb.meta + 1, kLayoutMeta, lb.dedup_token, tk, 1, x,
-                                      w.x_dedup, d.H * es, d.T, drows, pa, s);
+                                      w.x_dedup[set], d.H * es, d.T, drows, pa, s);
     if (e != hipSuccess) return MOE_EHIP;
-    gp.a_src = w.x_dedup;
+    gp.a_src = w.x_dedup[set];
     gp.a_src_rows = (int)drows;
     gp.a_index = lb.expand_idx;
     gp.a_div = 1;
@@ -287,9 +300,11 @@ int run_pass(const Dims& d, const PassArgs& pa, const LayoutSet& ls, const Layou
   gp.tile_group = lb.tile_group;
   gp.go_stride = d.G_res + 1;
   gp.tg_stride = tile_map_len(d);
-  hipError_t e = launch_gmm(d, pa, gp, w.slot_expert, wg, wu, wd, w.act, w.out, rows, nullptr, s);
+  gp.split_ok = split_ok;
+  hipError_t e = launch_gmm(d, pa, gp, w.slot_expert, wg, wu, wd, w.act[set], w.out[set], rows,
+                            nullptr, s);
   if (e != hipSuccess) return MOE_EHIP;
-  e = launch_combine(d, pa, ls, w.out, lb.row_of_assign, tk, rows, w.topk_gate, y, s);
+  e = launch_combine(d, pa, ls, w.out[set], lb.row_of_assign, tk, rows, w.topk_gate, y, s);
   return hip_status(e);
 }
 
@@ -444,6 +459,7 @@ int moe_gmm_swiglu(const moe_problem* p, const void* x_sorted, const int32_t* gr
   gp.a_src_rows = (int)max_rows;
   gp.a_div = 1;
   gp.group_offsets = group_offsets;
+  gp.split_ok = true;
   return hip_status(launch_gmm(d, pa, gp, slot_expert, w_gate, w_up, w_down, act, expert_out,
                                max_rows, ws, (hipStream_t)stream));
 }
@@ -501,24 +517,44 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
   e = launch_layout(d, ls, reroute ? w.slot_of_assign : w.topk_idx, reroute ? 0 : 1, lb, s);
   if (e != hipSuccess) return MOE_EHIP;
 
-  if (ls.ovf != nullptr) {
-    // the device decides: the single pass alone, or the batches of dropless
-    // chunks
-    for (int b = 0; b < ls.w_cnt; ++b) {
-      const int s0 = b * ls.win;
-      PassArgs pa = static_pass_args(s0, ls.win < d.L - s0 ? ls.win : d.L - s0, 0, b, d.L);
-      pa.ovf = ls.ovf;
-      st = run_pass(d, pa, ls, lb, x, w_gate, w_up, w_down, y, w, rows, drows, s);
-      if (st != MOE_OK) return st;
-    }
-  } else {
-    for (int j = 0; j < layout_num_passes(ls); ++j) {
-      const PassArgs pa = static_pass(d, ls, j);
-      st = run_pass(d, pa, ls, lb, x, w_gate, w_up, w_down, y, w, rows, drows, s);
-      if (st != MOE_OK) return st;
-    }
+  // With two or more passes they alternate between the caller's stream and
+  // the side stream, each stream with its own buffer set: the passes have
+  // disjoint tokens and read the layout only, so one pass's GEMM tail and
+  // combine overlap the next pass's work.  A buffer set is reused only by
+  // the next pass on the same stream, which stream order puts after it.
+  const int slots = layer_pass_slots(ls);
+  SideStream* ss = slots >= 2 ? side_stream() : nullptr;
+  std::unique_lock<std::mutex> lock(side_mutex(), std::defer_lock);
+  if (ss != nullptr) {
+    lock.lock();
+    e = hipEventRecord(ss->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+    if (e != hipSuccess) return MOE_EHIP;
   }
-  return MOE_OK;
+  for (int b = 0; b < slots && st == MOE_OK; ++b) {
+    const int set = ss != nullptr ? (b & 1) : 0;
+    hipStream_t sb = set ? ss->s : s;
+    PassArgs pa;
+    if (ls.ovf != nullptr) {
+      // the device decides: the single pass alone, or the batches of
+      // dropless chunks
+      const int s0 = b * ls.win;
+      pa = static_pass_args(s0, ls.win < d.L - s0 ? ls.win : d.L - s0, 0, b, d.L);
+      pa.ovf = ls.ovf;
+    } else {
+      pa = static_pass(d, ls, b);
+    }
+    st = run_pass(d, pa, ls, lb, x, w_gate, w_up, w_down, y, w, set, ss == nullptr, rows, drows,
+                  sb);
+  }
+  if (ss != nullptr) {
+    // join even after a failed launch, so the caller's stream never runs
+    // ahead of work already on the side stream
+    e = hipEventRecord(ss->join, ss->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, ss->join, 0);
+    if (e != hipSuccess && st == MOE_OK) st = MOE_EHIP;
+  }
+  return st;
 }
 
 const char* moe_status_string(int status) {

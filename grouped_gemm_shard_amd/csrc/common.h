@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -262,8 +263,21 @@ struct GemmPass {
   const int* tile_off;
   const int* tile_group;
   int go_stride, tg_stride;
+  bool split_ok;          // long-F passes may split their m-tiles over the side stream
 };
 size_t gmm_scratch_bytes(const Dims& d);
+
+// A second stream per device (default priority), with the events that fork
+// work onto it from a caller's stream and join it back.  Whoever enqueues
+// work on it holds side_mutex() from the fork to the join, so concurrent
+// callers cannot interleave their fork/join records.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ok = false;
+};
+SideStream* side_stream();
+std::mutex& side_mutex();
 hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const GemmPass& gp,
                       const int* slot_expert, const void* wg, const void* wu, const void* wd,
                       void* act, void* out, int64_t max_rows, void* scratch, hipStream_t s);

@@ -498,35 +498,6 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(int G, int bm, int 
   if (g == 0) tile_off[G] = tmp[nw - 1];
 }
 
-// A second stream per device for the second half of a pass's m-tiles, and
-// the events that fork it from and join it back to the caller's stream.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool ok = false;
-};
-
-SideStream* side_stream() {
-  static SideStream side[64];
-  static std::mutex mu;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  SideStream& ss = side[dev];
-  if (!ss.ok) {
-    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) return nullptr;
-    ss.ok = true;
-  }
-  return &ss;
-}
-
-std::mutex& side_mutex() {
-  static std::mutex mu;
-  return mu;
-}
-
 // Compute units of the current device rounded down to a multiple of 8 (the
 // XCDs): the blocks per round of the tile order.
 int round_blocks() {
@@ -616,7 +587,7 @@ hipError_t launch_bf16(const Dims& d, const PassArgs& pa, const GemmPass& gp, co
   // half's work instead of idling the chip.  (Measured on MI355X: 8% faster
   // on the Llama4-Maverick-shaped shard; with short GEMM2 reductions the
   // second queue costs more than it saves.)
-  SideStream* ss = d.F >= 4096 ? side_stream() : nullptr;
+  SideStream* ss = gp.split_ok && d.F >= 4096 ? side_stream() : nullptr;
   const int parts = ss ? 2 : 1;
   const long long mt_part = (mt_ub + parts - 1) / parts + 1;
   const int nb = round_blocks() * resident_blocks<BM, BK, NST, NW, NWN>();
@@ -648,6 +619,30 @@ hipError_t launch_bf16(const Dims& d, const PassArgs& pa, const GemmPass& gp, co
 }
 
 }  // namespace
+
+SideStream* side_stream() {
+  static SideStream side[64];
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  SideStream& ss = side[dev];
+  if (!ss.ok) {
+    if (ss.s == nullptr && hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess)
+      return nullptr;
+    if (ss.fork == nullptr && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess)
+      return nullptr;
+    if (ss.join == nullptr && hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      return nullptr;
+    ss.ok = true;
+  }
+  return &ss;
+}
+
+std::mutex& side_mutex() {
+  static std::mutex mu;
+  return mu;
+}
 
 size_t gmm_scratch_bytes(const Dims& d) {
   return ((size_t)(d.G_res + 1) * 4 + 255) / 256 * 256 +
