@@ -18,13 +18,19 @@
  * Conventions shared by every entry point:
  *  - All array arguments are DEVICE pointers unless stated otherwise; the
  *    problem struct and size outputs are host pointers.
- *  - The caller owns every buffer.  The library allocates no device memory,
- *    keeps no state between calls and is reentrant across streams.  Scratch
+ *  - The caller owns every buffer.  The library allocates no device memory
+ *    and is reentrant across streams; the only state it keeps is one side
+ *    stream and two events per device, created on first use.  Scratch
  *    comes from the caller's workspace `ws` of `ws_bytes` bytes (256-byte
  *    aligned), sized by moe_workspace_bytes / moe_layer_workspace_bytes.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
- *    enqueues work on it: nothing synchronises the host, so integer outputs
- *    are valid once the stream reaches them.
+ *    enqueues work: nothing synchronises the host, so integer outputs are
+ *    valid once the stream reaches them.  moe_gmm_swiglu with F >= 4096 and
+ *    moe_layer_dropless_chunked with two or more passes put part of their
+ *    work on the side stream, forked from `stream` and joined back to it by
+ *    events inside the call, so everything is complete when `stream` reaches
+ *    the point after the call.  Concurrent calls on one device serialise
+ *    only that enqueue (a mutex), not their GPU work.
  *  - Errors: a negative moe_status, returned after validating every argument
  *    on the host and before any launch.  A failed launch returns MOE_EHIP.
  *    The library never truncates silently: too small a buffer is
