@@ -418,7 +418,7 @@ int moe_permute(const moe_problem* p, int32_t num_chunks, int32_t chunk, int32_t
     lb.dedup_token = dedup_token;
     lb.expand_idx = expand_idx;
   }
-  hipError_t e = launch_layout(d, ls, slot_of_assign, 0, lb, s);
+  hipError_t e = launch_layout(d, ls, slot_of_assign, 0, lb, nullptr, s);
   if (e != hipSuccess) return MOE_EHIP;
   const int row_bytes = d.H * (d.bf16 ? 2 : 4);
   const int lc = d.L / num_chunks;
@@ -507,15 +507,24 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
                               count_hist_area(d, w.count_scratch), s);
   if (e != hipSuccess) return MOE_EHIP;
   // without rerouting every assignment goes to its expert's home slot, so
-  // the layout reads the top-k directly
+  // the layout reads the top-k directly; without dedup either, the count
+  // step runs inside the layout's scan launch
   const bool reroute = d.R > 0 && d.B > 0;
-  e = launch_count(d, w.topk_idx, w.expert_counts, w.slot_expert, w.ndiv,
-                   reroute ? w.slot_of_assign : nullptr, w.shard_counts, w.status,
-                   w.count_scratch, 1, info, mode, s);
-  if (e != hipSuccess) return MOE_EHIP;
   const LayoutBuffers lb = carve_layout(d, ls, w.layout_scratch);
-  e = launch_layout(d, ls, reroute ? w.slot_of_assign : w.topk_idx, reroute ? 0 : 1, lb, s);
-  if (e != hipSuccess) return MOE_EHIP;
+  if (!reroute && !d.dedup) {
+    const CountArgs c = layer_count_args(d, w.topk_idx, w.expert_counts, w.slot_expert, w.ndiv,
+                                         w.shard_counts, w.status, w.count_scratch, info, mode);
+    e = launch_layout(d, ls, w.topk_idx, 1, lb, &c, s);
+    if (e != hipSuccess) return MOE_EHIP;
+  } else {
+    e = launch_count(d, w.topk_idx, w.expert_counts, w.slot_expert, w.ndiv,
+                     reroute ? w.slot_of_assign : nullptr, w.shard_counts, w.status,
+                     w.count_scratch, 1, info, mode, s);
+    if (e != hipSuccess) return MOE_EHIP;
+    e = launch_layout(d, ls, reroute ? w.slot_of_assign : w.topk_idx, reroute ? 0 : 1, lb,
+                      nullptr, s);
+    if (e != hipSuccess) return MOE_EHIP;
+  }
 
   // With two or more passes they alternate between the caller's stream and
   // the side stream, each stream with its own buffer set: the passes have

@@ -215,6 +215,29 @@ hipError_t launch_count(const Dims& d, const int* idx, int* expert_counts, int* 
                         void* scratch, int hist_ready, int* info_out, int info_mode,
                         hipStream_t s);
 
+// Arguments of the count step without rerouting (one workgroup): the top-k,
+// per-block expert histograms ph [nb][E] (pbad: per-block bad-id flags, or
+// null), and its outputs.
+struct CountArgs {
+  const int* idx;
+  const int* ph;
+  const int* pbad;
+  int nb;
+  int* expert_counts;
+  int* slot_expert;
+  int* ndiv;
+  int* slot_of_assign;  // may be null
+  int* shard_counts;
+  int* status;
+  int* info;            // may be null
+  int info_mode;
+};
+// The CountArgs of a layer call whose route step left its histograms in the
+// count scratch.
+CountArgs layer_count_args(const Dims& d, const int* idx, int* expert_counts, int* slot_expert,
+                           int* ndiv, int* shard_counts, int* status, void* scratch, int* info,
+                           int info_mode);
+
 // Layout state of every pass of a LayoutSet (arrays are per layout j with
 // the strides used by the kernels below).
 struct LayoutBuffers {
@@ -238,8 +261,12 @@ size_t layout_scratch_bytes(const Dims& d, const LayoutSet& ls);
 LayoutBuffers carve_layout(const Dims& d, const LayoutSet& ls, void* scratch);
 // slots: slot_of_assign [T*k], or with home != 0 the top-k expert ids, each
 // assignment then going to its expert's home slot (no rerouting).
+// cnt (no rerouting, no dedup; may be null): the count step runs inside the
+// layout, in one extra workgroup of the scan kernel, and the local ranks and
+// scans cover every candidate pass, so the layout does not wait for the
+// overflow flag (only the placement reads it).
 hipError_t launch_layout(const Dims& d, const LayoutSet& ls, const int* slots, int home,
-                         const LayoutBuffers& lb, hipStream_t s);
+                         const LayoutBuffers& lb, const CountArgs* cnt, hipStream_t s);
 
 // dst[r] = src[index[r] / div] for r < *count, per pass: count, index are
 // base pointers advanced by count_stride / index_stride per layout j.

@@ -19,6 +19,9 @@
 // expand indices).  Row copies are separate: the dedup buffer of a pass and,
 // for the standalone permute, x_sorted, one wavefront per row with 16-byte
 // loads and stores.
+#include <string.h>
+
+#include "count_body.h"
 #include "sort.h"
 
 namespace moe {
@@ -144,12 +147,17 @@ __global__ __launch_bounds__(64) void layout_local_kernel(Dims d, LayoutSet ls,
 // m-tile -> group map.  Dedup part: distinct tokens per shard, cut at the
 // cap when capped, and their offsets.
 __global__ __launch_bounds__(1024) void layout_scan_kernel(Dims d, LayoutSet ls, int which,
-                                                           LayoutBuffers lb) {
+                                                           LayoutBuffers lb, CountArgs cnt,
+                                                           int has_count) {
   __shared__ int tmp[16];
   __shared__ int excl[kMaxSlots];
   __shared__ int totals[kMaxSlots];
   __shared__ int dtotals[kMaxSlots];
   const int j = blockIdx.x;
+  if (has_count && j == layout_num_passes(ls)) {
+    count_fused_body(d, cnt);  // the extra workgroup
+    return;
+  }
   if (!layout_live(ls, j)) return;
   const PassGeom pg = pass_geom(d, ls, j);
   const bool capped = pg.capped && d.cap >= 0;
@@ -349,24 +357,39 @@ LayoutBuffers carve_layout(const Dims& d, const LayoutSet& ls, void* scratch) {
 }
 
 hipError_t launch_layout(const Dims& d, const LayoutSet& ls, const int* soa, int home,
-                         const LayoutBuffers& lb, hipStream_t s) {
+                         const LayoutBuffers& lb, const CountArgs* cnt, hipStream_t s) {
   const int np = layout_num_passes(ls);
   const dim3 lb64(64), lgrid(kSortBlocks, np), sb(1024), sgrid(np);
+  if (cnt != nullptr) {
+    if (d.dedup || !home) return hipErrorInvalidValue;
+    // every candidate pass is laid out (liveness would need the flag the
+    // count workgroup is still computing); the placement skips dead ones
+    LayoutSet all = ls;
+    all.ovf = nullptr;
+    hipLaunchKernelGGL(layout_local_kernel<1>, lgrid, lb64, 0, s, d, all, soa, home, lb, 0);
+    hipLaunchKernelGGL(layout_scan_kernel, dim3(np + 1), sb, 0, s, d, all, 1, lb, *cnt, 1);
+    const int maxe = (d.T / d.L) * layout_max_lw(d, ls) * d.k;
+    hipLaunchKernelGGL(layout_place_kernel, dim3((maxe + 255) / 256, np), dim3(256), 0, s, d, ls,
+                       soa, home, lb);
+    return hipGetLastError();
+  }
+  CountArgs none;
+  memset(&none, 0, sizeof(none));
   // Static capped + dedup: the cut of each shard's dedup buffer decides which
   // rows drop, so the dedup ranks are scanned before the slot keys.
   const bool two_round = d.dedup && d.cap >= 0 &&
                          ((ls.has_single && ls.single_capped) || (ls.w_cnt && ls.w_capped));
   if (!d.dedup) {
     hipLaunchKernelGGL(layout_local_kernel<1>, lgrid, lb64, 0, s, d, ls, soa, home, lb, 0);
-    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 1, lb);
+    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 1, lb, none, 0);
   } else if (!two_round) {
     hipLaunchKernelGGL(layout_local_kernel<3>, lgrid, lb64, 0, s, d, ls, soa, home, lb, 0);
-    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 3, lb);
+    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 3, lb, none, 0);
   } else {
     hipLaunchKernelGGL(layout_local_kernel<2>, lgrid, lb64, 0, s, d, ls, soa, home, lb, 0);
-    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 2, lb);
+    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 2, lb, none, 0);
     hipLaunchKernelGGL(layout_local_kernel<1>, lgrid, lb64, 0, s, d, ls, soa, home, lb, 1);
-    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 1, lb);
+    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 1, lb, none, 0);
   }
   const int maxe = (d.T / d.L) * layout_max_lw(d, ls) * d.k;
   hipLaunchKernelGGL(layout_place_kernel, dim3((maxe + 255) / 256, np), dim3(256), 0, s, d, ls,
