@@ -507,11 +507,11 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
                               count_hist_area(d, w.count_scratch), s);
   if (e != hipSuccess) return MOE_EHIP;
   // without rerouting every assignment goes to its expert's home slot, so
-  // the layout reads the top-k directly; without dedup either, the count
-  // step runs inside the layout's scan launch
+  // the layout reads the top-k directly; when the layout fuses its scan and
+  // placement, the count step runs inside that launch too
   const bool reroute = d.R > 0 && d.B > 0;
   const LayoutBuffers lb = carve_layout(d, ls, w.layout_scratch);
-  if (!reroute && !d.dedup) {
+  if (!reroute && layout_fused(d)) {
     const CountArgs c = layer_count_args(d, w.topk_idx, w.expert_counts, w.slot_expert, w.ndiv,
                                          w.shard_counts, w.status, w.count_scratch, info, mode);
     e = launch_layout(d, ls, w.topk_idx, 1, lb, &c, s);

@@ -261,10 +261,14 @@ size_t layout_scratch_bytes(const Dims& d, const LayoutSet& ls);
 LayoutBuffers carve_layout(const Dims& d, const LayoutSet& ls, void* scratch);
 // slots: slot_of_assign [T*k], or with home != 0 the top-k expert ids, each
 // assignment then going to its expert's home slot (no rerouting).
-// cnt (no rerouting, no dedup; may be null): the count step runs inside the
-// layout, in one extra workgroup of the scan kernel, and the local ranks and
-// scans cover every candidate pass, so the layout does not wait for the
-// overflow flag (only the placement reads it).
+// Layouts without dedup and with at most kFusedBases / kSortBlocks resident
+// slots take two launches: local ranks, then scan and placement together.
+constexpr int kFusedBases = 8192;
+bool layout_fused(const Dims& d);
+// cnt (no rerouting, and layout_fused; may be null otherwise): the count
+// step runs inside the layout, in one extra workgroup of the scan/place
+// launch, and every candidate pass is laid out, so the layout does not wait
+// for the overflow flag.
 hipError_t launch_layout(const Dims& d, const LayoutSet& ls, const int* slots, int home,
                          const LayoutBuffers& lb, const CountArgs* cnt, hipStream_t s);
 

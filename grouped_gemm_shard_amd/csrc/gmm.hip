@@ -173,6 +173,17 @@ __device__ __forceinline__ void gmm_mma(const bf16x8 (&a)[MI], const bf16x8 (&b)
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
 }
 
+// Calls f(std::integral_constant<int, min(live, L)>) for live >= 0.
+template <int L, class F>
+__device__ __forceinline__ void live_dispatch(int live, F& f) {
+  if constexpr (L == 0) {
+    f(std::integral_constant<int, 0>{});
+  } else {
+    if (live >= L) f(std::integral_constant<int, L>{});
+    else live_dispatch<L - 1>(live, f);
+  }
+}
+
 // One BM x 256 tile (GEMM1: BM x 128 act columns) of group rows
 // [row0, row0 + rows), rows <= BM, of weight n-tile nt of local expert e;
 // smem holds at least NST * (BM + 256) * BK * 2 bytes.
@@ -262,7 +273,6 @@ __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const 
   // issues its share of the loads and joins every barrier.
   constexpr int NS = BK / 16;  // K slices per step
   static_assert(NS % 2 == 0, "the pending last slice lives in fragment set 1");
-  static_assert(MI <= 2, "live-tile dispatch covers MI <= 2");
   bf16x8 a[2][MI], b[2][NI];
   auto kloop = [&](auto live_c) {
     constexpr int LV = decltype(live_c)::value;
@@ -290,9 +300,7 @@ __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const 
   };
   // 32-row MFMA tiles of this wave that hold rows of the group (wave-uniform)
   const int live = __builtin_amdgcn_readfirstlane(min(MI, max(0, (rows - wm * WM + 31) / 32)));
-  if (live >= MI) kloop(std::integral_constant<int, MI>{});
-  else if (live == 1) kloop(std::integral_constant<int, (MI > 1 ? 1 : MI)>{});
-  else kloop(std::integral_constant<int, 0>{});
+  live_dispatch<MI>(live, kloop);
 
   // Epilogue through LDS: the ring is free once every wave has read its last
   // stage, so the tile is written there in bf16 and then stored as whole

@@ -141,23 +141,69 @@ __global__ __launch_bounds__(64) void layout_local_kernel(Dims d, LayoutSet ls,
       lb.bh_dedup[((size_t)j * kSortBlocks + blockIdx.x) * d.S_res + q] = run_d[q];
 }
 
+// Slot part of pass j's scan, from the rows per slot in totals (LDS): rows
+// kept per slot (without dedup, a capped shard keeps the first `cap` rows of
+// its bucket, i.e. a prefix of each slot), group offsets and the GEMM m-tile
+// schedule.  With `write` they go to the pass's layout buffers; kept rows
+// and offsets also go to kept_l / go_l (LDS) when those are set.  Every
+// thread of the 1024-thread block calls it (it holds barriers).
+__device__ __forceinline__ void slot_scan(const Dims& d, int j, bool capped, const int* totals,
+                                          int* excl, int* tmp, bool write,
+                                          const LayoutBuffers& lb, int* kept_l, int* go_l) {
+  const int g = threadIdx.x;
+  int* kept = lb.kept + (size_t)j * d.G_res;
+  int* go = lb.group_offsets + (size_t)j * (d.G_res + 1);
+  int* toff = lb.tile_off + (size_t)j * (d.G_res + 1);
+  int* tgrp = lb.tile_group + (size_t)j * tile_map_len(d);
+  const bool own = g < d.G_res;
+  int tot = own ? totals[g] : 0;
+  int all;
+  int ex = block_exscan_1024(tot, tmp, &all);
+  if (own) excl[g] = ex;
+  __syncthreads();
+  int kp = tot;
+  if (own && capped && !d.dedup) {
+    int first = ((g + d.lo_slot) / d.spd) * d.spd - d.lo_slot;
+    int bstart = ex - excl[first];
+    kp = min(max(d.cap - bstart, 0), tot);
+  }
+  int nrows;
+  int off = block_exscan_1024(own ? kp : 0, tmp, &nrows);
+  if (own && kept_l != nullptr) {
+    kept_l[g] = kp;
+    go_l[g] = off;
+  }
+  if (!write) return;
+  if (own) {
+    kept[g] = kp;
+    go[g] = off;
+  }
+  int ntiles;
+  const int tiles = own ? (kp + d.gemm_bm - 1) / d.gemm_bm : 0;
+  int to = block_exscan_1024(tiles, tmp, &ntiles);
+  if (own) {
+    toff[g] = to;
+    for (int m = 0; m < tiles; ++m) tgrp[to + m] = g;
+  }
+  if (g == 0) {
+    go[d.G_res] = nrows;
+    toff[d.G_res] = ntiles;
+    lb.meta[(size_t)j * kLayoutMeta] = nrows;
+  }
+}
+
 // One block per pass.  Slot part: block bases, rows per slot, kept rows
 // (without dedup, a capped shard keeps the first `cap` rows of its bucket,
 // i.e. a prefix of each slot), group offsets, GEMM m-tile offsets and the
 // m-tile -> group map.  Dedup part: distinct tokens per shard, cut at the
 // cap when capped, and their offsets.
 __global__ __launch_bounds__(1024) void layout_scan_kernel(Dims d, LayoutSet ls, int which,
-                                                           LayoutBuffers lb, CountArgs cnt,
-                                                           int has_count) {
+                                                           LayoutBuffers lb) {
   __shared__ int tmp[16];
   __shared__ int excl[kMaxSlots];
   __shared__ int totals[kMaxSlots];
   __shared__ int dtotals[kMaxSlots];
   const int j = blockIdx.x;
-  if (has_count && j == layout_num_passes(ls)) {
-    count_fused_body(d, cnt);  // the extra workgroup
-    return;
-  }
   if (!layout_live(ls, j)) return;
   const PassGeom pg = pass_geom(d, ls, j);
   const bool capped = pg.capped && d.cap >= 0;
@@ -168,40 +214,7 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(Dims d, LayoutSet ls,
   if (which & 2) scan_keys_over_blocks(bh_d, d.S_res, dtotals);
   __syncthreads();
   int* meta = lb.meta + (size_t)j * kLayoutMeta;
-  if (which & 1) {
-    int* kept = lb.kept + (size_t)j * d.G_res;
-    int* go = lb.group_offsets + (size_t)j * (d.G_res + 1);
-    int* toff = lb.tile_off + (size_t)j * (d.G_res + 1);
-    int* tgrp = lb.tile_group + (size_t)j * tile_map_len(d);
-    const bool own = g < d.G_res;
-    int tot = own ? totals[g] : 0;
-    int all;
-    int ex = block_exscan_1024(tot, tmp, &all);
-    if (own) excl[g] = ex;
-    __syncthreads();
-    int kp = tot;
-    if (own && capped && !d.dedup) {
-      int first = ((g + d.lo_slot) / d.spd) * d.spd - d.lo_slot;
-      int bstart = ex - excl[first];
-      kp = min(max(d.cap - bstart, 0), tot);
-    }
-    if (own) kept[g] = kp;
-    int nrows;
-    int off = block_exscan_1024(own ? kp : 0, tmp, &nrows);
-    if (own) go[g] = off;
-    int ntiles;
-    const int tiles = own ? (kp + d.gemm_bm - 1) / d.gemm_bm : 0;
-    int to = block_exscan_1024(tiles, tmp, &ntiles);
-    if (own) {
-      toff[g] = to;
-      for (int m = 0; m < tiles; ++m) tgrp[to + m] = g;
-    }
-    if (g == 0) {
-      go[d.G_res] = nrows;
-      toff[d.G_res] = ntiles;
-      meta[0] = nrows;
-    }
-  }
+  if (which & 1) slot_scan(d, j, capped, totals, excl, tmp, true, lb, nullptr, nullptr);
   if (which & 2) {
     int* dkept = lb.dedup_kept + (size_t)j * d.S_res;
     int* doff = lb.dedup_offsets + (size_t)j * (d.S_res + 1);
@@ -217,6 +230,64 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(Dims d, LayoutSet ls,
       meta[1] = nu;
     }
   }
+}
+
+// Scan and placement in one launch (no dedup, kSortBlocks * G_res <=
+// kFusedBases): every 1024-thread workgroup of pass j recomputes the pass's
+// scan in LDS (per-key block bases, kept rows, group offsets) from the local
+// counts and places its 1024 elements; workgroup 0 of the pass also writes
+// the scan's results for the GEMM and the combine.  With has_count, row
+// np of the grid runs the count step in its first workgroup.
+__global__ __launch_bounds__(1024) void layout_scan_place_kernel(Dims d, LayoutSet ls,
+                                                                 LayoutBuffers lb, CountArgs cnt,
+                                                                 int has_count) {
+  __shared__ int bases[kFusedBases];
+  __shared__ int tmp[16];
+  __shared__ int excl[kMaxSlots];
+  __shared__ int totals[kMaxSlots];
+  __shared__ int kept_l[kMaxSlots];
+  __shared__ int go_l[kMaxSlots];
+  const int j = blockIdx.y;
+  if (has_count && j == layout_num_passes(ls)) {
+    if (blockIdx.x == 0) count_fused_body(d, cnt);
+    return;
+  }
+  if (!layout_live(ls, j)) return;
+  const PassGeom g = pass_geom(d, ls, j);
+  if (blockIdx.x > 0 && blockIdx.x * 1024 >= g.nelem) return;  // block-uniform
+  const int G = d.G_res;
+  // per-key exclusive bases over the sort blocks: one wave per key, one lane
+  // per block
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int* bh = lb.bh_slot + (size_t)j * kSortBlocks * G;
+  for (int key = w; key < G; key += 16) {
+    const int v = bh[lane * G + key];
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    bases[lane * G + key] = x - v;
+    if (lane == 63) totals[key] = x;
+  }
+  __syncthreads();
+  slot_scan(d, j, g.capped && d.cap >= 0, totals, excl, tmp, blockIdx.x == 0, lb, kept_l, go_l);
+  __syncthreads();
+  const int e = blockIdx.x * 1024 + threadIdx.x;
+  if (e >= g.nelem) return;
+  const int jj = e % d.k;
+  const int t = elem_token(d, g, e);
+  const int a = t * d.k + jj;
+  const unsigned v = lb.skey[g.e0 + e];
+  const int ks = packed_key(v);
+  int pos = -1;
+  if (ks >= 0) {
+    const int r = bases[(e / g.blk) * G + ks] + packed_rank(v);
+    if (r < kept_l[ks]) pos = go_l[ks] + r;
+  }
+  lb.row_of_assign[(size_t)layout_set_of(ls, j) * ((size_t)d.T * d.k) + a] = pos;
+  if (pos >= 0) lb.sorted_assign[layout_row_base(d, ls, j) + pos] = a;
 }
 
 // Places every element of every pass: row_of_assign, sorted_assign and, with
@@ -356,42 +427,45 @@ LayoutBuffers carve_layout(const Dims& d, const LayoutSet& ls, void* scratch) {
   return lb;
 }
 
+bool layout_fused(const Dims& d) {
+  return !d.dedup && d.G_res * kSortBlocks <= kFusedBases;
+}
+
 hipError_t launch_layout(const Dims& d, const LayoutSet& ls, const int* soa, int home,
                          const LayoutBuffers& lb, const CountArgs* cnt, hipStream_t s) {
   const int np = layout_num_passes(ls);
   const dim3 lb64(64), lgrid(kSortBlocks, np), sb(1024), sgrid(np);
-  if (cnt != nullptr) {
-    if (d.dedup || !home) return hipErrorInvalidValue;
-    // every candidate pass is laid out (liveness would need the flag the
-    // count workgroup is still computing); the placement skips dead ones
-    LayoutSet all = ls;
-    all.ovf = nullptr;
-    hipLaunchKernelGGL(layout_local_kernel<1>, lgrid, lb64, 0, s, d, all, soa, home, lb, 0);
-    hipLaunchKernelGGL(layout_scan_kernel, dim3(np + 1), sb, 0, s, d, all, 1, lb, *cnt, 1);
-    const int maxe = (d.T / d.L) * layout_max_lw(d, ls) * d.k;
-    hipLaunchKernelGGL(layout_place_kernel, dim3((maxe + 255) / 256, np), dim3(256), 0, s, d, ls,
-                       soa, home, lb);
+  const int maxe = (d.T / d.L) * layout_max_lw(d, ls) * d.k;
+  if (layout_fused(d)) {
+    // with the count step inside, every candidate pass is laid out
+    // (liveness would need the flag the count workgroup is computing)
+    CountArgs none;
+    memset(&none, 0, sizeof(none));
+    LayoutSet lsl = ls;
+    if (cnt != nullptr) lsl.ovf = nullptr;
+    const int pb = (maxe + 1023) / 1024 > 0 ? (maxe + 1023) / 1024 : 1;
+    hipLaunchKernelGGL(layout_local_kernel<1>, lgrid, lb64, 0, s, d, lsl, soa, home, lb, 0);
+    hipLaunchKernelGGL(layout_scan_place_kernel, dim3(pb, np + (cnt != nullptr ? 1 : 0)), sb, 0,
+                       s, d, lsl, lb, cnt != nullptr ? *cnt : none, cnt != nullptr ? 1 : 0);
     return hipGetLastError();
   }
-  CountArgs none;
-  memset(&none, 0, sizeof(none));
+  if (cnt != nullptr) return hipErrorInvalidValue;
   // Static capped + dedup: the cut of each shard's dedup buffer decides which
   // rows drop, so the dedup ranks are scanned before the slot keys.
   const bool two_round = d.dedup && d.cap >= 0 &&
                          ((ls.has_single && ls.single_capped) || (ls.w_cnt && ls.w_capped));
   if (!d.dedup) {
     hipLaunchKernelGGL(layout_local_kernel<1>, lgrid, lb64, 0, s, d, ls, soa, home, lb, 0);
-    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 1, lb, none, 0);
+    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 1, lb);
   } else if (!two_round) {
     hipLaunchKernelGGL(layout_local_kernel<3>, lgrid, lb64, 0, s, d, ls, soa, home, lb, 0);
-    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 3, lb, none, 0);
+    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 3, lb);
   } else {
     hipLaunchKernelGGL(layout_local_kernel<2>, lgrid, lb64, 0, s, d, ls, soa, home, lb, 0);
-    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 2, lb, none, 0);
+    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 2, lb);
     hipLaunchKernelGGL(layout_local_kernel<1>, lgrid, lb64, 0, s, d, ls, soa, home, lb, 1);
-    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 1, lb, none, 0);
+    hipLaunchKernelGGL(layout_scan_kernel, sgrid, sb, 0, s, d, ls, 1, lb);
   }
-  const int maxe = (d.T / d.L) * layout_max_lw(d, ls) * d.k;
   hipLaunchKernelGGL(layout_place_kernel, dim3((maxe + 255) / 256, np), dim3(256), 0, s, d, ls,
                      soa, home, lb);
   return hipGetLastError();
