@@ -12,13 +12,15 @@
 // comment).
 //
 // The layouts of every pass a call may take (the single pass and each
-// sequence chunk) are computed together, before any pass runs, in three
-// launches: local ranks (one wave per sort block and pass), one scan block
-// per pass (bases, group offsets, kept rows, GEMM tile schedule), and the
-// placement of every element (sorted_assign, row_of_assign, dedup lists,
-// expand indices).  Row copies are separate: the dedup buffer of a pass and,
-// for the standalone permute, x_sorted, one wavefront per row with 16-byte
-// loads and stores.
+// sequence chunk) are computed together, before any pass runs: local ranks
+// (one wave per sort block and pass), the scan (bases, group offsets, kept
+// rows, GEMM tile schedule) and the placement of every element
+// (sorted_assign, row_of_assign, dedup lists, expand indices).  Without
+// dedup, scan and placement share one launch: each placement workgroup
+// recomputes its pass's scan in LDS; with dedup they are separate launches
+// (one scan block per pass).  Row copies are separate: the dedup buffer of a
+// pass and, for the standalone permute, x_sorted, one wavefront per row with
+// 16-byte loads and stores.
 #include <string.h>
 
 #include "count_body.h"
