@@ -51,6 +51,33 @@ __device__ __forceinline__ void combine_bf16_cols(const uint16_t* __restrict__ o
   }
 }
 
+// One token's output row in bf16: column groups of 512 per pass over the
+// assignments, KC assignments' loads in flight at a time.
+template <int KC, int HU>
+__device__ __forceinline__ void combine_bf16_token(const uint16_t* __restrict__ o, const int* rows,
+                                                   const float* gts, int k, int H,
+                                                   long long max_rows, uint16_t* yr, int lane) {
+  for (int h = lane * 8; h < H; h += 512 * HU) {
+    float acc[HU][8];
+#pragma unroll
+    for (int c = 0; c < HU; ++c)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[c][q] = 0.0f;
+    // assignments in ascending j, KC at a time: KC x HU row loads in flight
+    for (int j0 = 0; j0 < k; j0 += KC) combine_bf16_cols<KC, HU>(o, rows, gts, j0, k, H, max_rows, h, acc);
+#pragma unroll
+    for (int c = 0; c < HU; ++c) {
+      if (h + c * 512 >= H) continue;
+      uint4 outv;
+      outv.x = (uint32_t)f2bf(acc[c][0]) | ((uint32_t)f2bf(acc[c][1]) << 16);
+      outv.y = (uint32_t)f2bf(acc[c][2]) | ((uint32_t)f2bf(acc[c][3]) << 16);
+      outv.z = (uint32_t)f2bf(acc[c][4]) | ((uint32_t)f2bf(acc[c][5]) << 16);
+      outv.w = (uint32_t)f2bf(acc[c][6]) | ((uint32_t)f2bf(acc[c][7]) << 16);
+      *(uint4*)(yr + h + c * 512) = outv;
+    }
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(Dims d, PassArgs pa, LayoutSet ls,
                                                       const void* __restrict__ out,
@@ -70,27 +97,12 @@ __global__ __launch_bounds__(256) void combine_kernel(Dims d, PassArgs pa, Layou
   if (BF16) {
     const uint16_t* o = (const uint16_t*)out;
     uint16_t* yr = (uint16_t*)y + (size_t)t * d.H;
-    constexpr int HU = 4;  // column groups of 512 per pass over the assignments
-    for (int h = lane * 8; h < d.H; h += 512 * HU) {
-      float acc[HU][8];
-#pragma unroll
-      for (int c = 0; c < HU; ++c)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc[c][q] = 0.0f;
-      // assignments in ascending j, two at a time: 2 x HU row loads in flight
-      for (int j0 = 0; j0 < d.k; j0 += 2)
-        combine_bf16_cols<2, HU>(o, rows, gts, j0, d.k, d.H, max_rows, h, acc);
-#pragma unroll
-      for (int c = 0; c < HU; ++c) {
-        if (h + c * 512 >= d.H) continue;
-        uint4 outv;
-        outv.x = (uint32_t)f2bf(acc[c][0]) | ((uint32_t)f2bf(acc[c][1]) << 16);
-        outv.y = (uint32_t)f2bf(acc[c][2]) | ((uint32_t)f2bf(acc[c][3]) << 16);
-        outv.z = (uint32_t)f2bf(acc[c][4]) | ((uint32_t)f2bf(acc[c][5]) << 16);
-        outv.w = (uint32_t)f2bf(acc[c][6]) | ((uint32_t)f2bf(acc[c][7]) << 16);
-        *(uint4*)(yr + h + c * 512) = outv;
-      }
-    }
+    // rows of at most 1024 columns: all of a token's (up to 4) assignments
+    // in flight at once; wider rows: 4 column groups, 2 assignments
+    if (d.H <= 1024)
+      combine_bf16_token<4, 2>(o, rows, gts, d.k, d.H, max_rows, yr, lane);
+    else
+      combine_bf16_token<2, 4>(o, rows, gts, d.k, d.H, max_rows, yr, lane);
   } else {
     const float* o = (const float*)out;
     float* yr = (float*)y + (size_t)t * d.H;

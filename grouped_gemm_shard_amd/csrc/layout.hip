@@ -349,7 +349,15 @@ __device__ __forceinline__ void wave_copy_row(char* __restrict__ dst, const char
     *(uint4*)(dst + off + 2048) = v2;
     *(uint4*)(dst + off + 3072) = v3;
   }
-  for (; off < nbytes; off += 1024) *(uint4*)(dst + off) = *(const uint4*)(src + off);
+  // the rest (at most 3 chunks per lane): every load before the stores
+  const bool p0 = off < nbytes, p1 = off + 1024 < nbytes, p2 = off + 2048 < nbytes;
+  uint4 v0, v1, v2;
+  if (p0) v0 = *(const uint4*)(src + off);
+  if (p1) v1 = *(const uint4*)(src + off + 1024);
+  if (p2) v2 = *(const uint4*)(src + off + 2048);
+  if (p0) *(uint4*)(dst + off) = v0;
+  if (p1) *(uint4*)(dst + off + 1024) = v1;
+  if (p2) *(uint4*)(dst + off + 2048) = v2;
 }
 
 // dst[r] = src[index[r] / div] for r < count (count read on the device),
