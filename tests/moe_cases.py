@@ -31,6 +31,9 @@ MEDIUM = {
                                                        seq_len=1024, hidden=1024, ffn=2048),
     "dedup_small": CONFIGS["dedup_redundant"].scaled(name="dedup_small", tokens=512,
                                                      seq_len=512, hidden=256, ffn=128),
+    # the DeepSeek-V3 receive shape: 8 source sequences, shard 0 resident
+    "dsv3_ep8_small": CONFIGS["dsv3_ep8_receive"].scaled(name="dsv3_ep8_small", tokens=2048,
+                                                         seq_len=256, hidden=1024, ffn=512),
     # hidden >= 2048 selects 256-row GEMM tiles (a group's last tile of at
     # most 128 rows runs as a 128-row tile)
     "maverick_mid": CONFIGS["maverick_shard"].scaled(name="maverick_mid", tokens=2048,

@@ -24,7 +24,7 @@ from workloads import CONFIGS
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-FULL = ["dsv3_shard", "maverick_shard", "dedup_redundant"]
+FULL = ["dsv3_shard", "maverick_shard", "dedup_redundant", "dsv3_ep8_receive"]
 
 
 class LazyRows:

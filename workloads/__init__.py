@@ -91,13 +91,21 @@ CONFIGS = {
                                ffn=8192, num_experts=128, top_k=1, num_shards=16,
                                res_lo=0, res_hi=1, factor=2.0, num_chunks=8,
                                gate="sigmoid", zipf=1.3),
+    # The DeepSeek-V3 shard as it receives under 8-way expert parallelism:
+    # 8 sources (sequences) of 4096 tokens each route over all 256 experts,
+    # and this GPU runs shard 0 (experts 0..31) on the union of the rows the
+    # sources send it (~32.8k rows instead of ~4.1k from one source).
+    "dsv3_ep8_receive": Workload("dsv3_ep8_receive", tokens=32768, seq_len=4096, hidden=7168,
+                                 ffn=2048, num_experts=256, top_k=8, num_shards=8, res_lo=0,
+                                 res_hi=1, factor=2.0, num_chunks=4, gate="softmax"),
     "dedup_redundant": Workload("dedup_redundant", tokens=8192, seq_len=8192, hidden=7168,
                                 ffn=2048, num_experts=256, top_k=8, num_shards=16,
                                 res_lo=0, res_hi=16, factor=2.0, num_chunks=8,
                                 gate="softmax", dedup=True, slots_per_shard=2,
                                 num_replicas=2, zipf=1.2),
 }
-ORDER = ["tiny_fp32", "mid_bf16", "dsv3_shard", "maverick_shard", "dedup_redundant"]
+ORDER = ["tiny_fp32", "mid_bf16", "dsv3_shard", "maverick_shard", "dedup_redundant",
+         "dsv3_ep8_receive"]
 
 
 def _seed(seed: int, stream: int, index: int) -> int:
