@@ -18,8 +18,8 @@ pages, cited by title and section:
              backward + x_sorted remat save" (maxtext PR 4969), section What.
 
 Where the pages are silent (gate function, SwiGLU, dtypes, shapes) the
-oracle follows the workload statement that accompanies them; every such
-reading is listed in DESIGN.md.
+oracle follows the workload statement that accompanies them; each such
+reading is stated in the docstring of the function that makes it.
 
 Arithmetic is float64.  Where the GPU path stores bfloat16 (the SwiGLU
 activation, the expert output and the layer output) the oracle rounds its

@@ -34,7 +34,8 @@ __all__ = [
     "Problem", "round_bf16", "route", "expert_counts", "plan_redundancy",
     "assign_slots", "shard_counts", "capacity", "overflow", "required_factor",
     "default_num_chunks", "pass_tokens", "pass_layout", "permute", "permute_dedup", "expert_ffn",
-    "gmm_swiglu", "combine", "layer", "layer_plain", "layer_plain_tokens",
+    "gmm_swiglu", "combine", "combine_partial", "combine_from_partials", "layer", "layer_plain",
+    "layer_plain_tokens",
 ]
 
 MODE_LAYER = 0           # overflow check, capped pass or chunked dropless fallback
@@ -453,6 +454,72 @@ def combine(p: Problem, expert_out, row_of_assign, gates, tokens):
             if r >= 0:
                 acc = acc + gates[t, j] * expert_out[r]
         y[i] = acc
+    if p.bf16:
+        y = round_bf16(y)
+    return y
+
+
+# --------------------------------------------------------------------------
+# Return-path dedup: partial combine at the receiving shard, sum at the source
+# --------------------------------------------------------------------------
+#
+# The pages deduplicate the dispatch: a token goes once to each destination
+# shard and is re-expanded there ([DRED] code review: dedup and
+# expand_indices).  The return path applied the same way: the receiving
+# shard sums its own assignments of a token, gate-weighted, into one row per
+# (token, shard), and the token's source adds those rows.  Without rounding
+# this is the combine regrouped by shard; with bf16 storage the partial rows
+# (what would travel back) are rounded once more.
+
+
+def combine_partial(p: Problem, expert_out, row_of_assign, gates, slot, dedup_offsets,
+                    dedup_token):
+    """partial[u] for every dedup row u of a pass (token t on resident shard
+    d): the sum over j ascending, over the token's assignments whose slot
+    lies on shard d and that have a row in this pass, of g_tj * out[row(t, j)],
+    float64; rounded to bfloat16 with bf16 storage."""
+    k, spd = p.top_k, p.spd
+    slot = np.asarray(slot, dtype=np.int64)
+    u_total = int(dedup_offsets[-1])
+    partial = np.zeros((u_total, p.hidden), dtype=np.float64)
+    for i, d in enumerate(range(p.res_lo, p.res_hi)):
+        for u in range(int(dedup_offsets[i]), int(dedup_offsets[i + 1])):
+            t = int(dedup_token[u])
+            acc = np.zeros(p.hidden, dtype=np.float64)
+            for j in range(k):
+                r = int(row_of_assign[t * k + j])
+                if r >= 0 and int(slot[t, j]) // spd == d:
+                    acc = acc + gates[t, j] * expert_out[r]
+            partial[u] = acc
+    if p.bf16:
+        partial = round_bf16(partial)
+    return partial
+
+
+def combine_from_partials(p: Problem, partial, slot, dedup_offsets, dedup_token, tokens):
+    """Source side of the return-path dedup: y_t = the sum of the token's
+    partial rows, one per resident shard that kept the token, taken in the
+    order of the token's first assignment on each shard; 0 for a token with
+    none.  Rounded to bfloat16 with bf16 storage.  Returns y rows for
+    `tokens` in the given order."""
+    k, spd = p.top_k, p.spd
+    slot = np.asarray(slot, dtype=np.int64)
+    row_of = {}
+    for i, d in enumerate(range(p.res_lo, p.res_hi)):
+        for u in range(int(dedup_offsets[i]), int(dedup_offsets[i + 1])):
+            row_of[(d, int(dedup_token[u]))] = u
+    y = np.zeros((len(tokens), p.hidden), dtype=np.float64)
+    for n, t in enumerate(tokens):
+        t = int(t)
+        seen = set()
+        acc = np.zeros(p.hidden, dtype=np.float64)
+        for j in range(k):
+            d = int(slot[t, j]) // spd
+            if d in seen or (d, t) not in row_of:
+                continue
+            seen.add(d)
+            acc = acc + partial[row_of[(d, t)]]
+        y[n] = acc
     if p.bf16:
         y = round_bf16(y)
     return y
