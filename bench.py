@@ -173,8 +173,26 @@ def kernel_figures(p, w, inp, info, reps):
     perm_bytes = (tokens_res + n_rows) * w.hidden * es
     comb_bytes = n_rows * w.hidden * es + w.tokens * w.hidden * es
     del ec
-    return dict(rows=n_rows, t_gmm=t_gmm, t_perm=t_perm, t_comb=t_comb, gemm_flops=gemm_flops,
-                gemm_bytes=gemm_bytes, perm_bytes=perm_bytes, comb_bytes=comb_bytes)
+    fig = dict(rows=n_rows, t_gmm=t_gmm, t_perm=t_perm, t_comb=t_comb, gemm_flops=gemm_flops,
+               gemm_bytes=gemm_bytes, perm_bytes=perm_bytes, comb_bytes=comb_bytes)
+    if w.dedup:
+        # return-path dedup: partial rows at the receiving shard (reads every
+        # expert_out row once, writes one row per token and shard), then the
+        # sum at the source (reads the partial rows, writes y)
+        t_part = t_src = 0.0
+        u_rows = 0
+        for b in bufs:
+            part = torch.empty((b["dt"].shape[0], w.hidden), dtype=torch.float32, device="cuda")
+            y2 = torch.empty_like(b["y"])
+            t_part += time_calls(lambda: g.moe_combine_partial(
+                p, b["out"], b["roa"], gate, b["do"], b["dt"], b["ex"], part), reps)
+            t_src += time_calls(lambda: g.moe_combine_from_partials(
+                p, b["n"], b["c"], part, b["roa"], b["ex"], y2, b["rows"]), reps)
+            u_rows += int(b["do"][-1].item())
+        fig.update(u_rows=u_rows, t_part=t_part, t_src=t_src,
+                   part_bytes=n_rows * w.hidden * es + u_rows * w.hidden * 4,
+                   src_bytes=u_rows * w.hidden * 4 + w.tokens * w.hidden * es)
+    return fig
 
 
 def workloads_pass_tokens(w, n, c):
@@ -306,6 +324,13 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if "u_rows" in kf:
+        res["return_dedup"] = {
+            "rows_per_assignment": kf["rows"], "rows_per_token_shard": kf["u_rows"],
+            "partial_gbs": round(kf["part_bytes"] / kf["t_part"] / 1e9, 1),
+            "partial_us_per_layer": round(kf["t_part"] * 1e6, 2),
+            "source_sum_gbs": round(kf["src_bytes"] / kf["t_src"] / 1e9, 1),
+            "source_sum_us_per_layer": round(kf["t_src"] * 1e6, 2)}
     print(json.dumps(res), flush=True)
 
 

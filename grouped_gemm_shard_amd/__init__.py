@@ -21,8 +21,8 @@ __all__ = [
     "MODE_LAYER", "MODE_FORCE_DROPLESS", "MODE_CAPPED_ONLY", "MODE_FORCE_CHUNKED",
     "EXPORTED", "MoeError", "Problem", "lib", "lib_path", "workspace_bytes",
     "layer_workspace_bytes", "pass_max_rows", "moe_route", "moe_count_overflow",
-    "moe_permute", "moe_gmm_swiglu", "moe_combine", "moe_layer_dropless_chunked",
-    "status_string", "LayerRunner",
+    "moe_permute", "moe_gmm_swiglu", "moe_combine", "moe_combine_partial",
+    "moe_combine_from_partials", "moe_layer_dropless_chunked", "status_string", "LayerRunner",
 ]
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EHIP = 0, -1, -2, -3, -4
@@ -32,7 +32,8 @@ GATES = {"softmax": 0, "sigmoid": 1}
 EXPORTED = ["moe_workspace_bytes", "moe_pass_max_rows", "moe_layer_workspace_bytes",
             "moe_layer_chunks_per_pass",
             "moe_route", "moe_count_overflow", "moe_permute", "moe_gmm_swiglu",
-            "moe_combine", "moe_layer_dropless_chunked", "moe_status_string"]
+            "moe_combine", "moe_combine_partial", "moe_combine_from_partials",
+            "moe_layer_dropless_chunked", "moe_status_string"]
 
 lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_shard.so")
 
@@ -121,6 +122,8 @@ def _load():
                         sz, vp],
         "moe_gmm_swiglu": [P, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, sz, vp],
         "moe_combine": [P, i32, i32, vp, vp, vp, vp, vp],
+        "moe_combine_partial": [P, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp],
+        "moe_combine_from_partials": [P, i32, i32, vp, vp, vp, vp, i64, i64, vp],
         "moe_layer_dropless_chunked": [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
@@ -263,6 +266,33 @@ def moe_combine(p: Problem, num_chunks, chunk, expert_out, row_of_assign, topk_g
         ctypes.byref(p.c()), num_chunks, chunk, _ptr(expert_out, p.dtype, "expert_out"),
         _ptr(row_of_assign, torch.int32, "row_of_assign"),
         _ptr(topk_gate, torch.float32, "topk_gate"), _ptr(y, p.dtype, "y"), _stream(stream)))
+
+
+def moe_combine_partial(p: Problem, expert_out, row_of_assign, topk_gate, dedup_offsets,
+                        dedup_token, expand_idx, partial, stream=None):
+    """Return-path dedup, receiving side: one float32 partial row per (token,
+    shard).  max_rows / max_dedup_rows are the row counts of expert_out /
+    partial."""
+    _check("moe_combine_partial", _lib().moe_combine_partial(
+        ctypes.byref(p.c()), _ptr(expert_out, p.dtype, "expert_out"),
+        _ptr(row_of_assign, torch.int32, "row_of_assign"),
+        _ptr(topk_gate, torch.float32, "topk_gate"),
+        _ptr(dedup_offsets, torch.int32, "dedup_offsets"),
+        _ptr(dedup_token, torch.int32, "dedup_token"), _ptr(expand_idx, torch.int32, "expand_idx"),
+        _ptr(partial, torch.float32, "partial"), expert_out.shape[0], partial.shape[0],
+        _stream(stream)))
+
+
+def moe_combine_from_partials(p: Problem, num_chunks, chunk, partial, row_of_assign, expand_idx, y,
+                              max_rows, stream=None):
+    """Return-path dedup, source side: y of the chunk's tokens from the
+    partial rows.  max_rows is the row count behind row_of_assign (the length
+    of expand_idx)."""
+    _check("moe_combine_from_partials", _lib().moe_combine_from_partials(
+        ctypes.byref(p.c()), num_chunks, chunk, _ptr(partial, torch.float32, "partial"),
+        _ptr(row_of_assign, torch.int32, "row_of_assign"),
+        _ptr(expand_idx, torch.int32, "expand_idx"), _ptr(y, p.dtype, "y"), max_rows,
+        partial.shape[0], _stream(stream)))
 
 
 def moe_layer_dropless_chunked(p: Problem, mode, x, logits, w_gate, w_up, w_down, y, info, ws,

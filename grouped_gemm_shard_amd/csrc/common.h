@@ -315,6 +315,17 @@ hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const GemmPass& gp,
 
 // Combine of one pass; row_of_assign advances by roa_stride per row_of_assign
 // set of the pass's layout.  Rows at or past max_rows are treated as absent.
+// Return-path dedup: partial[u] for u < *u_count (one row per token and
+// resident shard; rows of expert_out at or past max_rows count as absent),
+// and y of the pass's tokens from those rows.
+hipError_t launch_combine_partial(const Dims& d, const int* u_count, const int* dedup_token,
+                                  const int* row_of_assign, const int* expand_idx,
+                                  const float* gate, const void* out, int64_t max_rows,
+                                  int64_t max_urows, void* partial, hipStream_t s);
+hipError_t launch_combine_from_partials(const Dims& d, const PassArgs& pa,
+                                        const int* row_of_assign, const int* expand_idx,
+                                        const void* partial, int64_t max_rows, int64_t max_urows,
+                                        void* y, hipStream_t s);
 hipError_t launch_combine(const Dims& d, const PassArgs& pa, const LayoutSet& ls, const void* out,
                           const int* row_of_assign, long long roa_stride, int64_t max_rows,
                           const float* gate, void* y, hipStream_t s);

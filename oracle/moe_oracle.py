@@ -467,9 +467,9 @@ def combine(p: Problem, expert_out, row_of_assign, gates, tokens):
 # shard and is re-expanded there ([DRED] code review: dedup and
 # expand_indices).  The return path applied the same way: the receiving
 # shard sums its own assignments of a token, gate-weighted, into one row per
-# (token, shard), and the token's source adds those rows.  Without rounding
-# this is the combine regrouped by shard; with bf16 storage the partial rows
-# (what would travel back) are rounded once more.
+# (token, shard), and the token's source adds those rows.  The partial rows
+# are not rounded to the activation dtype (float32 on the GPU): the sum is
+# the combine regrouped by shard, rounded once at the source.
 
 
 def combine_partial(p: Problem, expert_out, row_of_assign, gates, slot, dedup_offsets,
@@ -477,7 +477,7 @@ def combine_partial(p: Problem, expert_out, row_of_assign, gates, slot, dedup_of
     """partial[u] for every dedup row u of a pass (token t on resident shard
     d): the sum over j ascending, over the token's assignments whose slot
     lies on shard d and that have a row in this pass, of g_tj * out[row(t, j)],
-    float64; rounded to bfloat16 with bf16 storage."""
+    float64 and not rounded (whatever the storage of the activations)."""
     k, spd = p.top_k, p.spd
     slot = np.asarray(slot, dtype=np.int64)
     u_total = int(dedup_offsets[-1])
@@ -491,8 +491,6 @@ def combine_partial(p: Problem, expert_out, row_of_assign, gates, slot, dedup_of
                 if r >= 0 and int(slot[t, j]) // spd == d:
                     acc = acc + gates[t, j] * expert_out[r]
             partial[u] = acc
-    if p.bf16:
-        partial = round_bf16(partial)
     return partial
 
 

@@ -84,6 +84,31 @@ def test_null_pointers_rejected_before_launch():
     assert g.lib.moe_status_string(-3).decode() == "buffer or workspace too small"
 
 
+def test_return_path_dedup_entry_points_validate_on_the_host():
+    g = _binding()
+    fake = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    plain = problem().c()
+    dd = problem(dedup=True).c()
+    # without dedup there are no partial rows
+    assert g.lib.moe_combine_partial(ctypes.byref(plain), fake, fake, fake, fake, fake, fake, fake,
+                                     16, 16, None) == -1
+    assert g.lib.moe_combine_from_partials(ctypes.byref(plain), 1, 0, fake, fake, fake, fake, 16,
+                                           16, None) == -1
+    # null arrays, negative bounds, a chunk outside the chunk count
+    assert g.lib.moe_combine_partial(ctypes.byref(dd), None, fake, fake, fake, fake, fake, fake,
+                                     16, 16, None) == -1
+    assert g.lib.moe_combine_partial(ctypes.byref(dd), fake, fake, fake, fake, fake, fake, fake,
+                                     -1, 16, None) == -1
+    assert g.lib.moe_combine_from_partials(ctypes.byref(dd), 4, 4, fake, fake, fake, fake, 16, 16,
+                                           None) == -1
+    assert g.lib.moe_combine_from_partials(ctypes.byref(dd), 1, 0, fake, None, fake, fake, 16, 16,
+                                           None) == -1
+    # misaligned rows
+    odd = ctypes.c_void_p(258)
+    assert g.lib.moe_combine_partial(ctypes.byref(dd), odd, fake, fake, fake, fake, fake, fake,
+                                     16, 16, None) == -1
+
+
 def test_pass_row_bounds():
     g = _binding()
     # Llama4-Maverick shard: cap = 2 * 32768 / 16 = 4096; a chunk of 4096

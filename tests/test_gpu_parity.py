@@ -224,6 +224,25 @@ def test_pass_steps_parity(g, name):
         check_close(y_np[toks], o_y, f"y {name} pass {n}/{c}/{capped}")
         rest = np.setdiff1d(np.arange(w.tokens), toks)
         assert np.all(y_np[rest] == 7.0)
+        if w.dedup:
+            # return-path dedup: one partial row per (token, shard), then the
+            # sum at the source; the oracle regroups its own expert outputs
+            part = torch.full((drows, w.hidden), 7.0, dtype=torch.float32, device="cuda")
+            g.moe_combine_partial(p, out, roa, gate, do, dt, ex, part)
+            y2 = torch.full((w.tokens, w.hidden), 7.0, dtype=p.dtype, device="cuda")
+            g.moe_combine_from_partials(p, n, c, part, roa, ex, y2, rows)
+            o_part = oracle.combine_partial(op, o_out, lay["row_of_assign"], o_gate, slot_np,
+                                            lay["dedup_offsets"], lay["dedup_token"])
+            o_y2 = oracle.combine_from_partials(op, o_part, slot_np, lay["dedup_offsets"],
+                                                lay["dedup_token"], toks)
+            torch.cuda.synchronize()
+            part_np = host(part)
+            check_close(part_np[:U], o_part, f"partial {name} pass {n}/{c}/{capped}")
+            assert np.all(part_np[U:] == 7.0)
+            y2_np = host(y2)
+            check_close(y2_np[toks], o_y2, f"y from partials {name} pass {n}/{c}/{capped}")
+            check_close(y2_np[toks], o_y, f"y from partials vs combine {name} pass {n}/{c}/{capped}")
+            assert np.all(y2_np[rest] == 7.0)
 
 
 MODES = {0: "LAYER", 1: "FORCE_DROPLESS", 2: "CAPPED_ONLY", 3: "FORCE_CHUNKED"}

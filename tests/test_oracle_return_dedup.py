@@ -105,11 +105,16 @@ def test_partial_of_a_single_assignment_is_gate_times_row():
             np.testing.assert_array_equal(part[u], gates[t, j] * out[lay["row_of_assign"][t * k + j]])
 
 
-def test_bf16_partials_are_rounded_rows():
+def test_partials_are_not_rounded_and_y_is_rounded_once():
+    # bf16 storage rounds y once at the source; the partial rows stay exact
     p, slot, gates, lay, out = random_case(5, zipf=1.0)
     p16 = replace(p, bf16=True)
-    part64 = oracle.combine_partial(p, out, lay["row_of_assign"], gates, slot,
-                                    lay["dedup_offsets"], lay["dedup_token"])
-    part16 = oracle.combine_partial(p16, out, lay["row_of_assign"], gates, slot,
-                                    lay["dedup_offsets"], lay["dedup_token"])
-    np.testing.assert_array_equal(part16, oracle.round_bf16(part64))
+    args = (out, lay["row_of_assign"], gates, slot, lay["dedup_offsets"], lay["dedup_token"])
+    part64 = oracle.combine_partial(p, *args)
+    part16 = oracle.combine_partial(p16, *args)
+    np.testing.assert_array_equal(part16, part64)
+    y64 = oracle.combine_from_partials(p, part64, slot, lay["dedup_offsets"],
+                                       lay["dedup_token"], np.arange(p.tokens))
+    y16 = oracle.combine_from_partials(p16, part16, slot, lay["dedup_offsets"],
+                                       lay["dedup_token"], np.arange(p.tokens))
+    np.testing.assert_array_equal(y16, oracle.round_bf16(y64))
