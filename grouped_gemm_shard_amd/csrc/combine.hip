@@ -97,12 +97,12 @@ __global__ __launch_bounds__(256) void combine_kernel(Dims d, PassArgs pa, Layou
   if (BF16) {
     const uint16_t* o = (const uint16_t*)out;
     uint16_t* yr = (uint16_t*)y + (size_t)t * d.H;
-    // rows of at most 1024 columns: all of a token's (up to 4) assignments
-    // in flight at once; wider rows: 4 column groups, 2 assignments
+    // four assignments' row loads in flight; rows of at most 1024 columns
+    // take them in 2 column groups of 512, wider rows in 4
     if (d.H <= 1024)
       combine_bf16_token<4, 2>(o, rows, gts, d.k, d.H, max_rows, yr, lane);
     else
-      combine_bf16_token<2, 4>(o, rows, gts, d.k, d.H, max_rows, yr, lane);
+      combine_bf16_token<4, 4>(o, rows, gts, d.k, d.H, max_rows, yr, lane);
   } else {
     const float* o = (const float*)out;
     float* yr = (float*)y + (size_t)t * d.H;
