@@ -170,7 +170,11 @@ def kernel_figures(p, w, inp, info, reps):
         roa = b["roa"].cpu().numpy().reshape(w.tokens, w.top_k)
         toks = workloads_pass_tokens(w, b["n"], b["c"])
         tokens_res += int(np.sum((roa[toks] >= 0).any(axis=1)))
-    perm_bytes = (tokens_res + n_rows) * w.hidden * es
+    # each resident token's row read once and each pass row written once;
+    # with dedup the rows go through x_dedup (one row per token and shard,
+    # written and read once)
+    u_all = sum(int(b["do"][-1].item()) for b in bufs) if w.dedup else 0
+    perm_bytes = (tokens_res + 2 * u_all + n_rows) * w.hidden * es
     comb_bytes = n_rows * w.hidden * es + w.tokens * w.hidden * es
     del ec
     fig = dict(rows=n_rows, t_gmm=t_gmm, t_perm=t_perm, t_comb=t_comb, gemm_flops=gemm_flops,

@@ -13,7 +13,7 @@
 //
 // The layouts of every pass a call may take (the single pass and each
 // sequence chunk) are computed together, before any pass runs: local ranks
-// (one wave per sort block and pass), the scan (bases, group offsets, kept
+// (up to 16 waves per sort block and pass), the scan (bases, group offsets, kept
 // rows, GEMM tile schedule) and the placement of every element
 // (sorted_assign, row_of_assign, dedup lists, expand indices).  Without
 // dedup, scan and placement share one launch: each placement workgroup
@@ -91,20 +91,33 @@ __device__ __forceinline__ int dedup_rank(const Dims& d, const LayoutBuffers& lb
   return lb.bh_dedup[((size_t)j * kSortBlocks + e / g.blk) * d.S_res + kd] + packed_rank(v);
 }
 
+// Local ranks of one sort block of pass j: blockDim / 64 waves split the
+// block's elements into contiguous parts; each wave ranks its part against
+// running counts of its own (LDS), then the waves' counts per key become
+// exclusive bases (wave order = element order), which a second sweep adds
+// to the ranks.  Leaves per element the packed (key, rank within the sort
+// block) and per block the count of every key.
+constexpr int kLocalLds = 16384;  // ints of LDS for the waves' running counts
+
 template <int WHICH>  // bit 0: slot keys, bit 1: dedup keys
-__global__ __launch_bounds__(64) void layout_local_kernel(Dims d, LayoutSet ls,
-                                                          const int* __restrict__ soa,
-                                                          int home, LayoutBuffers lb,
-                                                          int drop_check) {
-  __shared__ int run_s[kMaxSlots];
-  __shared__ int run_d[kMaxSlots];
+__global__ __launch_bounds__(1024) void layout_local_kernel(Dims d, LayoutSet ls,
+                                                            const int* __restrict__ soa,
+                                                            int home, LayoutBuffers lb,
+                                                            int drop_check) {
+  __shared__ int runs[kLocalLds];
   const int j = blockIdx.y;
   if (!layout_live(ls, j)) return;
   const PassGeom g = pass_geom(d, ls, j);
-  const int e0 = blockIdx.x * g.blk, e1 = min(g.nelem, e0 + g.blk);
+  const int nw = blockDim.x >> 6, w = threadIdx.x >> 6;
+  const int GS = (WHICH & 1) ? d.G_res : 0, GD = (WHICH & 2) ? d.S_res : 0;
+  int* run_s = runs + w * (GS + GD);
+  int* run_d = run_s + GS;
+  const int b0 = blockIdx.x * g.blk, b1 = min(g.nelem, b0 + g.blk);
+  // this wave's part of the block, in whole rounds of 64 elements
+  const int part = (((b1 > b0 ? b1 - b0 : 0) + nw * 64 - 1) / (nw * 64)) * 64;
+  const int e0 = min(b1, b0 + w * part), e1 = min(b1, e0 + part);
   const int nb_s = key_bits(d.G_res), nb_d = key_bits(d.S_res);
-  for (int q = threadIdx.x; q < d.G_res; q += 64) run_s[q] = 0;
-  for (int q = threadIdx.x; q < d.S_res; q += 64) run_d[q] = 0;
+  for (int q = threadIdx.x; q < nw * (GS + GD); q += blockDim.x) runs[q] = 0;
   __syncthreads();
   for (int base = e0; base < e1; base += 64) {
     const int e = base + lane_id();
@@ -135,12 +148,32 @@ __global__ __launch_bounds__(64) void layout_local_kernel(Dims d, LayoutSet ls,
     }
   }
   __syncthreads();
-  if (WHICH & 1)
-    for (int q = threadIdx.x; q < d.G_res; q += 64)
-      lb.bh_slot[((size_t)j * kSortBlocks + blockIdx.x) * d.G_res + q] = run_s[q];
-  if (WHICH & 2)
-    for (int q = threadIdx.x; q < d.S_res; q += 64)
-      lb.bh_dedup[((size_t)j * kSortBlocks + blockIdx.x) * d.S_res + q] = run_d[q];
+  // per key: the waves' exclusive bases (in place) and the block's count
+  const int K = GS + GD;
+  for (int q = threadIdx.x; q < K; q += blockDim.x) {
+    int acc = 0;
+    for (int v = 0; v < nw; ++v) {
+      const int c = runs[v * K + q];
+      runs[v * K + q] = acc;
+      acc += c;
+    }
+    if (q < GS) lb.bh_slot[((size_t)j * kSortBlocks + blockIdx.x) * d.G_res + q] = acc;
+    else lb.bh_dedup[((size_t)j * kSortBlocks + blockIdx.x) * d.S_res + (q - GS)] = acc;
+  }
+  __syncthreads();
+  if (w == 0) return;  // the first wave's bases are all zero
+  for (int e = e0 + lane_id(); e < e1; e += 64) {
+    if (WHICH & 1) {
+      const unsigned v = lb.skey[g.e0 + e];
+      const int ks = packed_key(v);
+      if (ks >= 0) lb.skey[g.e0 + e] = pack_key(ks, packed_rank(v) + run_s[ks]);
+    }
+    if (WHICH & 2) {
+      const unsigned v = lb.dkey[g.e0 + e];
+      const int kd = packed_key(v);
+      if (kd >= 0) lb.dkey[g.e0 + e] = pack_key(kd, packed_rank(v) + run_d[kd]);
+    }
+  }
 }
 
 // Slot part of pass j's scan, from the rows per slot in totals (LDS): rows
@@ -444,7 +477,15 @@ bool layout_fused(const Dims& d) {
 hipError_t launch_layout(const Dims& d, const LayoutSet& ls, const int* soa, int home,
                          const LayoutBuffers& lb, const CountArgs* cnt, hipStream_t s) {
   const int np = layout_num_passes(ls);
-  const dim3 lb64(64), lgrid(kSortBlocks, np), sb(1024), sgrid(np);
+  const dim3 lgrid(kSortBlocks, np), sb(1024), sgrid(np);
+  // waves per sort block: enough for its elements (64 per wave per round),
+  // at most 16, and their running counts within the LDS budget
+  const int maxe_all = (d.T / d.L) * layout_max_lw(d, ls) * d.k;
+  const int blk = (maxe_all + kSortBlocks - 1) / kSortBlocks;
+  int nw = (blk + 63) / 64;
+  nw = nw < 1 ? 1 : (nw > 16 ? 16 : nw);
+  while (nw > 1 && nw * (d.G_res + d.S_res) > kLocalLds) --nw;
+  const dim3 lb64(64 * nw);
   const int maxe = (d.T / d.L) * layout_max_lw(d, ls) * d.k;
   if (layout_fused(d)) {
     // with the count step inside, every candidate pass is laid out
