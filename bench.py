@@ -46,8 +46,8 @@ PEAK_HBM_GBS = 8000.0
 # holds only for the kernel source it was measured on (sha256 of gmm.hip);
 # for any other source or workload the traffic is reported as null.
 GEMM_TRAFFIC = {"workload": "mid_bf16",
-                "gmm_src_sha256": "aab40b7b9c13480c019feae46cc84b2883a6ee1ca76196aa049b0efeb82b2ac3",
-                "bytes_per_layer": 238202196}
+                "gmm_src_sha256": "57ea78dca44865921743f96ff31122ddc4f6254b330aab47339bcd1e32517df2",
+                "bytes_per_layer": 237845547}
 
 
 def recorded_gemm_traffic(workload):
