@@ -189,9 +189,10 @@ def kernel_figures(p, w, inp, info, reps):
             part = torch.empty((b["dt"].shape[0], w.hidden), dtype=torch.float32, device="cuda")
             y2 = torch.empty_like(b["y"])
             t_part += time_calls(lambda: g.moe_combine_partial(
-                p, b["out"], b["roa"], gate, b["do"], b["dt"], b["ex"], part), reps)
+                p, b["n"], b["c"], b["capped"], b["out"], b["roa"], gate, b["do"], b["dt"],
+                b["ex"], part), reps)
             t_src += time_calls(lambda: g.moe_combine_from_partials(
-                p, b["n"], b["c"], part, b["roa"], b["ex"], y2, b["rows"]), reps)
+                p, b["n"], b["c"], b["capped"], part, b["roa"], b["ex"], y2, b["rows"]), reps)
             u_rows += int(b["do"][-1].item())
         fig.update(u_rows=u_rows, t_part=t_part, t_src=t_src,
                    part_bytes=n_rows * w.hidden * es + u_rows * w.hidden * 4,

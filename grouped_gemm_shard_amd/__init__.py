@@ -122,8 +122,8 @@ def _load():
                         sz, vp],
         "moe_gmm_swiglu": [P, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, sz, vp],
         "moe_combine": [P, i32, i32, vp, vp, vp, vp, vp],
-        "moe_combine_partial": [P, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp],
-        "moe_combine_from_partials": [P, i32, i32, vp, vp, vp, vp, i64, i64, vp],
+        "moe_combine_partial": [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp],
+        "moe_combine_from_partials": [P, i32, i32, i32, vp, vp, vp, vp, i64, i64, vp],
         "moe_layer_dropless_chunked": [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
@@ -268,13 +268,13 @@ def moe_combine(p: Problem, num_chunks, chunk, expert_out, row_of_assign, topk_g
         _ptr(topk_gate, torch.float32, "topk_gate"), _ptr(y, p.dtype, "y"), _stream(stream)))
 
 
-def moe_combine_partial(p: Problem, expert_out, row_of_assign, topk_gate, dedup_offsets,
-                        dedup_token, expand_idx, partial, stream=None):
+def moe_combine_partial(p: Problem, num_chunks, chunk, capped, expert_out, row_of_assign,
+                        topk_gate, dedup_offsets, dedup_token, expand_idx, partial, stream=None):
     """Return-path dedup, receiving side: one float32 partial row per (token,
-    shard).  max_rows / max_dedup_rows are the row counts of expert_out /
-    partial."""
+    shard) of the pass (chunk of num_chunks, capped or not).  max_rows /
+    max_dedup_rows are the row counts of expert_out / partial."""
     _check("moe_combine_partial", _lib().moe_combine_partial(
-        ctypes.byref(p.c()), _ptr(expert_out, p.dtype, "expert_out"),
+        ctypes.byref(p.c()), num_chunks, chunk, capped, _ptr(expert_out, p.dtype, "expert_out"),
         _ptr(row_of_assign, torch.int32, "row_of_assign"),
         _ptr(topk_gate, torch.float32, "topk_gate"),
         _ptr(dedup_offsets, torch.int32, "dedup_offsets"),
@@ -283,13 +283,13 @@ def moe_combine_partial(p: Problem, expert_out, row_of_assign, topk_gate, dedup_
         _stream(stream)))
 
 
-def moe_combine_from_partials(p: Problem, num_chunks, chunk, partial, row_of_assign, expand_idx, y,
-                              max_rows, stream=None):
-    """Return-path dedup, source side: y of the chunk's tokens from the
-    partial rows.  max_rows is the row count behind row_of_assign (the length
-    of expand_idx)."""
+def moe_combine_from_partials(p: Problem, num_chunks, chunk, capped, partial, row_of_assign,
+                              expand_idx, y, max_rows, stream=None):
+    """Return-path dedup, source side: y of the pass's tokens from the partial
+    rows.  max_rows is the row count behind row_of_assign (the length of
+    expand_idx)."""
     _check("moe_combine_from_partials", _lib().moe_combine_from_partials(
-        ctypes.byref(p.c()), num_chunks, chunk, _ptr(partial, torch.float32, "partial"),
+        ctypes.byref(p.c()), num_chunks, chunk, capped, _ptr(partial, torch.float32, "partial"),
         _ptr(row_of_assign, torch.int32, "row_of_assign"),
         _ptr(expand_idx, torch.int32, "expand_idx"), _ptr(y, p.dtype, "y"), max_rows,
         partial.shape[0], _stream(stream)))

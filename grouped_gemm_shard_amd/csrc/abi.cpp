@@ -480,11 +480,27 @@ int moe_combine(const moe_problem* p, int32_t num_chunks, int32_t chunk, const v
                                    y, (hipStream_t)stream));
 }
 
-int moe_combine_partial(const moe_problem* p, const void* expert_out,
-                        const int32_t* row_of_assign, const float* topk_gate,
-                        const int32_t* dedup_offsets, const int32_t* dedup_token,
-                        const int32_t* expand_idx, void* partial, int64_t max_rows,
-                        int64_t max_dedup_rows, void* stream) {
+// Row bounds of the pass the return-path entry points serve: the buffers
+// must hold its worst case (no silent truncation).
+int return_path_bounds(const Dims& d, int num_chunks, int chunk, int capped, int64_t max_rows,
+                       int64_t max_dedup_rows) {
+  if (!d.dedup) return MOE_EINVAL;
+  if (num_chunks < 1 || d.L % num_chunks != 0 || chunk < 0 || chunk >= num_chunks ||
+      (capped != 0 && capped != 1))
+    return MOE_EINVAL;
+  if (max_rows < 0 || max_dedup_rows < 0) return MOE_EINVAL;
+  int64_t rb, ub;
+  pass_bounds(d, num_chunks, capped, &rb, &ub);
+  if (max_rows < rb || max_dedup_rows < ub) return MOE_ECAPACITY;
+  if (max_rows >= (1ll << 31) || max_dedup_rows >= (1ll << 31)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+int moe_combine_partial(const moe_problem* p, int32_t num_chunks, int32_t chunk,
+                        int32_t capped, const void* expert_out, const int32_t* row_of_assign,
+                        const float* topk_gate, const int32_t* dedup_offsets,
+                        const int32_t* dedup_token, const int32_t* expand_idx, void* partial,
+                        int64_t max_rows, int64_t max_dedup_rows, void* stream) {
   Dims d;
   int st = make_dims(p, &d);
   if (st != MOE_OK) return st;
@@ -492,28 +508,26 @@ int moe_combine_partial(const moe_problem* p, const void* expert_out,
   if (!expert_out || !row_of_assign || !topk_gate || !dedup_offsets || !dedup_token ||
       !expand_idx || !partial)
     return MOE_EINVAL;
-  if (max_rows < 0 || max_dedup_rows < 0) return MOE_EINVAL;
   if (misaligned(expert_out, 16) || misaligned(partial, 16)) return MOE_EINVAL;
-  if (max_rows >= (1ll << 31) || max_dedup_rows >= (1ll << 31)) return MOE_EUNSUPPORTED;
+  st = return_path_bounds(d, num_chunks, chunk, capped, max_rows, max_dedup_rows);
+  if (st != MOE_OK) return st;
   return hip_status(launch_combine_partial(d, dedup_offsets + d.S_res, dedup_token, row_of_assign,
                                            expand_idx, topk_gate, expert_out, max_rows,
                                            max_dedup_rows, partial, (hipStream_t)stream));
 }
 
 int moe_combine_from_partials(const moe_problem* p, int32_t num_chunks, int32_t chunk,
-                              const void* partial, const int32_t* row_of_assign,
-                              const int32_t* expand_idx, void* y, int64_t max_rows,
-                              int64_t max_dedup_rows, void* stream) {
+                              int32_t capped, const void* partial,
+                              const int32_t* row_of_assign, const int32_t* expand_idx, void* y,
+                              int64_t max_rows, int64_t max_dedup_rows, void* stream) {
   Dims d;
   int st = make_dims(p, &d);
   if (st != MOE_OK) return st;
   if (!d.dedup) return MOE_EINVAL;
-  if (num_chunks < 1 || d.L % num_chunks != 0 || chunk < 0 || chunk >= num_chunks)
-    return MOE_EINVAL;
   if (!partial || !row_of_assign || !expand_idx || !y) return MOE_EINVAL;
-  if (max_rows < 0 || max_dedup_rows < 0) return MOE_EINVAL;
   if (misaligned(partial, 16) || misaligned(y, 16)) return MOE_EINVAL;
-  if (max_rows >= (1ll << 31) || max_dedup_rows >= (1ll << 31)) return MOE_EUNSUPPORTED;
+  st = return_path_bounds(d, num_chunks, chunk, capped, max_rows, max_dedup_rows);
+  if (st != MOE_OK) return st;
   const int lc = d.L / num_chunks;
   const PassArgs pa = static_pass_args(chunk * lc, lc, 0, 0, d.L);
   return hip_status(launch_combine_from_partials(d, pa, row_of_assign, expand_idx, partial,

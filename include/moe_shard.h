@@ -221,8 +221,8 @@ int moe_combine(const moe_problem* p, int32_t num_chunks, int32_t chunk,
  * with dedup a token goes once to each destination shard and is re-expanded
  * there ([DRED], code review: dedup and expand_indices).  This applies the
  * same to the return: for every dedup row u < dedup_offsets[S_res] of a
- * pass (token t = dedup_token[u] on one resident shard, the arrays that
- * moe_permute wrote),
+ * pass (chunk `chunk` of num_chunks, capped or not: token t = dedup_token[u]
+ * on one resident shard, the arrays that moe_permute wrote for that pass),
  *   partial[u] = sum over j ascending, over the assignments (t, j) whose row
  *                r = row_of_assign[t*k+j] lies in [0, max_rows) and has
  *                expand_idx[r] == u (its slot is on u's shard),
@@ -232,27 +232,29 @@ int moe_combine(const moe_problem* p, int32_t num_chunks, int32_t chunk,
  * dtype) so that y is rounded once, at the source: a second bf16 rounding
  * exceeds the layer's error bound at DeepSeek-V3-sized rows.  partial is
  * float32 [max_dedup_rows, H]; rows past dedup_offsets[S_res] are
- * untouched.  MOE_EINVAL when the problem has no dedup. */
-int moe_combine_partial(const moe_problem* p, const void* expert_out,
-                        const int32_t* row_of_assign, const float* topk_gate,
-                        const int32_t* dedup_offsets, const int32_t* dedup_token,
-                        const int32_t* expand_idx, void* partial, int64_t max_rows,
-                        int64_t max_dedup_rows, void* stream);
+ * untouched.  max_rows (rows of expert_out and expand_idx) and
+ * max_dedup_rows must hold the pass's worst case (moe_pass_max_rows), else
+ * MOE_ECAPACITY.  MOE_EINVAL when the problem has no dedup. */
+int moe_combine_partial(const moe_problem* p, int32_t num_chunks, int32_t chunk,
+                        int32_t capped, const void* expert_out, const int32_t* row_of_assign,
+                        const float* topk_gate, const int32_t* dedup_offsets,
+                        const int32_t* dedup_token, const int32_t* expand_idx, void* partial,
+                        int64_t max_rows, int64_t max_dedup_rows, void* stream);
 
 /* Return-path dedup (source side): for every token t of chunk `chunk` of
- * num_chunks,
+ * num_chunks (the pass moe_combine_partial served),
  *   y[t] = sum of partial[u] over the distinct dedup rows u = expand_idx[r]
  *          of the token's assignments with a row r in [0, max_rows), each
  *          taken once, at the token's first assignment on its shard (j
  *          ascending)
  * with fp32 accumulation (partial is float32), stored in the activation
  * dtype; 0 for a token with none: moe_combine regrouped by shard.  Rows of
- * other tokens of y are untouched.  MOE_EINVAL when the problem has no
- * dedup. */
+ * other tokens of y are untouched.  Bounds as for moe_combine_partial.
+ * MOE_EINVAL when the problem has no dedup. */
 int moe_combine_from_partials(const moe_problem* p, int32_t num_chunks, int32_t chunk,
-                              const void* partial, const int32_t* row_of_assign,
-                              const int32_t* expand_idx, void* y, int64_t max_rows,
-                              int64_t max_dedup_rows, void* stream);
+                              int32_t capped, const void* partial,
+                              const int32_t* row_of_assign, const int32_t* expand_idx, void* y,
+                              int64_t max_rows, int64_t max_dedup_rows, void* stream);
 
 /* a8. The whole layer ([FALLBACK] How): route, counts, plan, capacity and
  * overflow once, then the passes `mode` selects, writing y [T,H].  In LAYER

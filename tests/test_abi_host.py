@@ -88,26 +88,26 @@ def test_return_path_dedup_entry_points_validate_on_the_host():
     g = _binding()
     fake = ctypes.c_void_p(256)  # never dereferenced: validation fails first
     plain = problem().c()
-    dd = problem(dedup=True).c()
+    dd_p = problem(dedup=True)
+    dd = dd_p.c()
+    rows, drows = g.pass_max_rows(dd_p, 1, 0)
+    part = lambda c, n, ch, cap, eo, mr, md: g.lib.moe_combine_partial(  # noqa: E731
+        ctypes.byref(c), n, ch, cap, eo, fake, fake, fake, fake, fake, fake, mr, md, None)
+    src = lambda c, n, ch, cap, pa, mr, md: g.lib.moe_combine_from_partials(  # noqa: E731
+        ctypes.byref(c), n, ch, cap, pa, fake, fake, fake, mr, md, None)
     # without dedup there are no partial rows
-    assert g.lib.moe_combine_partial(ctypes.byref(plain), fake, fake, fake, fake, fake, fake, fake,
-                                     16, 16, None) == -1
-    assert g.lib.moe_combine_from_partials(ctypes.byref(plain), 1, 0, fake, fake, fake, fake, 16,
-                                           16, None) == -1
-    # null arrays, negative bounds, a chunk outside the chunk count
-    assert g.lib.moe_combine_partial(ctypes.byref(dd), None, fake, fake, fake, fake, fake, fake,
-                                     16, 16, None) == -1
-    assert g.lib.moe_combine_partial(ctypes.byref(dd), fake, fake, fake, fake, fake, fake, fake,
-                                     -1, 16, None) == -1
-    assert g.lib.moe_combine_from_partials(ctypes.byref(dd), 4, 4, fake, fake, fake, fake, 16, 16,
-                                           None) == -1
-    assert g.lib.moe_combine_from_partials(ctypes.byref(dd), 1, 0, fake, None, fake, fake, 16, 16,
-                                           None) == -1
+    assert part(plain, 1, 0, 0, fake, rows, drows) == -1
+    assert src(plain, 1, 0, 0, fake, rows, drows) == -1
+    # null arrays, negative bounds, a chunk outside the chunk count, bad capped
+    assert part(dd, 1, 0, 0, None, rows, drows) == -1
+    assert part(dd, 1, 0, 0, fake, -1, drows) == -1
+    assert src(dd, 4, 4, 0, fake, rows, drows) == -1
+    assert src(dd, 1, 0, 2, fake, rows, drows) == -1
     # misaligned rows
-    odd = ctypes.c_void_p(258)
-    assert g.lib.moe_combine_partial(ctypes.byref(dd), odd, fake, fake, fake, fake, fake, fake,
-                                     16, 16, None) == -1
-
+    assert part(dd, 1, 0, 0, ctypes.c_void_p(258), rows, drows) == -1
+    # buffers below the pass's worst case: never a silent truncation
+    assert part(dd, 1, 0, 0, fake, rows, drows - 1) == -3
+    assert src(dd, 1, 0, 0, fake, rows - 1, drows) == -3
 
 def test_pass_row_bounds():
     g = _binding()

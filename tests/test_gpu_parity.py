@@ -228,9 +228,9 @@ def test_pass_steps_parity(g, name):
             # return-path dedup: one partial row per (token, shard), then the
             # sum at the source; the oracle regroups its own expert outputs
             part = torch.full((drows, w.hidden), 7.0, dtype=torch.float32, device="cuda")
-            g.moe_combine_partial(p, out, roa, gate, do, dt, ex, part)
+            g.moe_combine_partial(p, n, c, capped, out, roa, gate, do, dt, ex, part)
             y2 = torch.full((w.tokens, w.hidden), 7.0, dtype=p.dtype, device="cuda")
-            g.moe_combine_from_partials(p, n, c, part, roa, ex, y2, rows)
+            g.moe_combine_from_partials(p, n, c, capped, part, roa, ex, y2, rows)
             o_part = oracle.combine_partial(op, o_out, lay["row_of_assign"], o_gate, slot_np,
                                             lay["dedup_offsets"], lay["dedup_token"])
             o_y2 = oracle.combine_from_partials(op, o_part, slot_np, lay["dedup_offsets"],

@@ -57,9 +57,9 @@ def step_api(g, p, w, inp, n, c, capped):
     y = torch.full((w.tokens, w.hidden), 7.0, dtype=p.dtype, device="cuda")
     g.moe_combine(p, n, c, out, roa, gate, y)
     part = torch.full((drows, w.hidden), 7.0, dtype=torch.float32, device="cuda")
-    g.moe_combine_partial(p, out, roa, gate, do, dt, ex, part)
+    g.moe_combine_partial(p, n, c, capped, out, roa, gate, do, dt, ex, part)
     y2 = torch.full((w.tokens, w.hidden), 7.0, dtype=p.dtype, device="cuda")
-    g.moe_combine_from_partials(p, n, c, part, roa, ex, y2, rows)
+    g.moe_combine_from_partials(p, n, c, capped, part, roa, ex, y2, rows)
     torch.cuda.synchronize()
     return dict(gate=gate, soa=soa, roa=roa, do=do, dt=dt, ex=ex, out=out, y=y, part=part, y2=y2,
                 rows=rows)
