@@ -5,7 +5,8 @@ tolerance, and the dropless, chunked and LAYER results bitwise equal).
 The cases sit at the edges the method allows: every token choosing every
 expert (k = E), one expert per shard with only some shards resident, a
 fallback whose chunks hold one position of each sequence, a single token,
-heavy capped drops, and the fp32 path with dedup and redundant slots.
+heavy capped drops, more resident slots than the fused layout holds, and the
+fp32 path with dedup and redundant slots.
 """
 
 import pytest
@@ -37,6 +38,11 @@ EDGES = {
     "capped_drops": W("capped_drops", tokens=256, seq_len=256, hidden=256, ffn=128,
                       num_experts=16, top_k=2, num_shards=4, res_lo=0, res_hi=4, factor=0.25,
                       num_chunks=4, zipf=1.0),
+    # 256 resident slots without dedup: the layout's three-launch path (the
+    # fused scan/placement holds at most 128 slots' block counts in LDS)
+    "many_slots": W("many_slots", tokens=512, seq_len=256, hidden=256, ffn=128,
+                    num_experts=256, top_k=4, num_shards=2, res_lo=0, res_hi=2, factor=1.0,
+                    num_chunks=2, zipf=0.8),
     # fp32 with dedup and two redundant slots
     "fp32_dedup_redundant": W("fp32_dedup_redundant", tokens=128, seq_len=128, hidden=64,
                               ffn=64, num_experts=8, top_k=3, num_shards=4, res_lo=0, res_hi=4,
