@@ -21,9 +21,14 @@ Where the pages are silent (gate function, SwiGLU, dtypes, shapes) the
 oracle follows the workload statement that accompanies them; each such
 reading is stated in the docstring of the function that makes it.
 
+The backward of the layer (``moe_backward``) is the chain rule of these
+functions; the pages outline it in [FALLBACK] How (the chunked scan's
+backward) and [RING] (the combine backward and the saved x_sorted).
+
 Arithmetic is float64.  Where the GPU path stores bfloat16 (the SwiGLU
 activation, the expert output and the layer output) the oracle rounds its
 float64 value to the nearest bfloat16 (ties to even) at the same point.
 """
 
 from .moe_oracle import *  # noqa: F401,F403
+from .moe_backward import *  # noqa: F401,F403
