@@ -13,7 +13,9 @@ shards holds all 4 chunks, so they run as one pass).
 
 After the timed steps, the grouped GEMM, the permute and the combine of the
 same passes are timed one call at a time with HIP events on the stream they
-run on, to give achieved TFLOP/s and GB/s against MI355X peaks.  The CPU
+run on, to give achieved TFLOP/s and GB/s against MI355X peaks.  The
+backward of the same passes (given the forward's saved x_sorted and expert
+outputs) is timed as a whole and step by step ("backward" in the JSON).  The CPU
 oracle is then timed on the host cores on the same inputs.  One JSON line is
 printed at the end.
 """
@@ -200,6 +202,76 @@ def kernel_figures(p, w, inp, info, reps):
     return fig
 
 
+def backward_figures(p, w, inp, info, reps):
+    """The backward of the same passes (the forward's saved x_sorted and
+    expert_out kept): weight transposes once, then per pass the combine's
+    backward, the grouped GEMM's backward (weight gradients carried across
+    the passes) and the permute's backward, then the gates' backward into
+    the logits.  Timed as a whole and call by call with HIP events."""
+    passes = pass_list(p, info)
+    idx, gate, cnt, bufs = build_passes(p, w, inp, passes)
+    dy = workloads.make_dy(w, device="cuda")
+    T, k, H, F, E = w.tokens, w.top_k, w.hidden, w.ffn, w.num_experts
+    wg, wu, wd = inp["weights"]
+    dev = "cuda"
+    for b in bufs:
+        run_permute(p, inp, cnt, b)
+        run_gmm(p, inp, cnt, b)
+        b["d_out"] = torch.empty((b["rows"], H), dtype=p.dtype, device=dev)
+        b["dxs"] = torch.empty((b["rows"], H), dtype=p.dtype, device=dev)
+        b["bws"] = torch.empty(g.bwd_workspace_bytes(p, b["rows"]), dtype=torch.uint8, device=dev)
+    if w.bf16:
+        wgu_t = torch.empty((w.e_res, H, 2 * F), dtype=p.dtype, device=dev)
+        wd_t = torch.empty((w.e_res, F, H), dtype=p.dtype, device=dev)
+    else:
+        wgu_t = wd_t = None
+    dwg = torch.empty((w.e_res, F, H), dtype=torch.float32, device=dev)
+    dwu = torch.empty_like(dwg)
+    dwd = torch.empty((w.e_res, H, F), dtype=torch.float32, device=dev)
+    d_gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    dx = torch.empty((T, H), dtype=p.dtype, device=dev)
+    d_logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+
+    def transpose():
+        if w.bf16:
+            g.moe_transpose_weights(p, wg, wu, wd, wgu_t, wd_t)
+
+    def comb(b):
+        g.moe_combine_bwd(p, b["n"], b["c"], dy, b["out"], b["roa"], gate, b["d_out"], d_gate)
+
+    def gmm(b, acc):
+        g.moe_gmm_swiglu_bwd(p, b["xs"], b["go"], cnt["se"], wg, wu, wd, wgu_t, wd_t,
+                             b["d_out"], b["dxs"], dwg, dwu, dwd, acc, b["bws"])
+
+    def perm(b):
+        g.moe_permute_bwd(p, b["n"], b["c"], b["dxs"], b["roa"], dx)
+
+    def route():
+        g.moe_route_bwd(p, idx, gate, d_gate, d_logits)
+
+    def step():
+        transpose()
+        for i, b in enumerate(bufs):
+            comb(b)
+            gmm(b, i > 0)
+            perm(b)
+        route()
+
+    torch.cuda.synchronize()
+    t_step = time_calls(step, reps)
+    t_tr = time_calls(transpose, reps) if w.bf16 else 0.0
+    t_cb = sum(time_calls(lambda: comb(b), reps) for b in bufs)
+    t_gb = sum(time_calls(lambda: gmm(b, 1), reps) for b in bufs)
+    t_pb = sum(time_calls(lambda: perm(b), reps) for b in bufs)
+    t_rb = time_calls(route, reps)
+    n_rows = sum(int(b["go"][-1].item()) for b in bufs)
+    # d_a (2NHF), gate/up recompute (4NHF), dx_sorted (4NHF), dWg+dWu (4NHF),
+    # dWd (2NHF)
+    flops = 16.0 * n_rows * H * F
+    return dict(t_step=t_step, t_tr=t_tr, t_cb=t_cb, t_gb=t_gb, t_pb=t_pb, t_rb=t_rb,
+                flops=flops, rows=n_rows)
+
+
 def workloads_pass_tokens(w, n, c):
     lc = w.seq_len // n
     b = np.arange(w.tokens // w.seq_len)[:, None] * w.seq_len
@@ -241,6 +313,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the backward of the layer's passes")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -288,6 +362,20 @@ def main():
     roof["traffic"] = recorded_gemm_traffic(w.name)
     roof["kernel"] = "grouped SwiGLU GEMM (gate/up + down launches), per layer"
 
+    bwd = None
+    if not args.no_backward:
+        log("[bench] backward timing")
+        bf = backward_figures(p, w, inp, info, args.kernel_reps)
+        bt = bf["flops"] / bf["t_gb"] / 1e12
+        bwd = {"us_per_layer": round(bf["t_step"] * 1e6, 2),
+               "tokens_s": round(w.tokens / bf["t_step"], 1),
+               "gemm_us": round(bf["t_gb"] * 1e6, 2), "gemm_tflops": round(bt, 2),
+               "gemm_frac_mfma_peak": round(bt / peak_mm, 4),
+               "transpose_us": round(bf["t_tr"] * 1e6, 2),
+               "combine_bwd_us": round(bf["t_cb"] * 1e6, 2),
+               "permute_bwd_us": round(bf["t_pb"] * 1e6, 2),
+               "route_bwd_us": round(bf["t_rb"] * 1e6, 2), "rows": bf["rows"]}
+
     if args.calib_copy:
         log("[bench] calibration copy: 1 GiB device-to-device, 3 times")
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -329,6 +417,7 @@ def main():
                     "us_per_layer": round(kf["t_comb"] * 1e6, 2)},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "backward": bwd,
     }
     if "u_rows" in kf:
         res["return_dedup"] = {

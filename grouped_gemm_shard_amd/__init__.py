@@ -23,6 +23,8 @@ __all__ = [
     "layer_workspace_bytes", "pass_max_rows", "moe_route", "moe_count_overflow",
     "moe_permute", "moe_gmm_swiglu", "moe_combine", "moe_combine_partial",
     "moe_combine_from_partials", "moe_layer_dropless_chunked", "status_string", "LayerRunner",
+    "bwd_workspace_bytes", "moe_transpose_weights", "moe_combine_bwd", "moe_gmm_swiglu_bwd",
+    "moe_permute_bwd", "moe_route_bwd",
 ]
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EHIP = 0, -1, -2, -3, -4
@@ -33,7 +35,9 @@ EXPORTED = ["moe_workspace_bytes", "moe_pass_max_rows", "moe_layer_workspace_byt
             "moe_layer_chunks_per_pass",
             "moe_route", "moe_count_overflow", "moe_permute", "moe_gmm_swiglu",
             "moe_combine", "moe_combine_partial", "moe_combine_from_partials",
-            "moe_layer_dropless_chunked", "moe_status_string"]
+            "moe_layer_dropless_chunked", "moe_bwd_workspace_bytes", "moe_transpose_weights",
+            "moe_combine_bwd", "moe_gmm_swiglu_bwd", "moe_permute_bwd", "moe_route_bwd",
+            "moe_status_string"]
 
 lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_shard.so")
 
@@ -125,6 +129,13 @@ def _load():
         "moe_combine_partial": [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp],
         "moe_combine_from_partials": [P, i32, i32, i32, vp, vp, vp, vp, i64, i64, vp],
         "moe_layer_dropless_chunked": [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_bwd_workspace_bytes": [P, i64, ctypes.POINTER(sz)],
+        "moe_transpose_weights": [P, vp, vp, vp, vp, vp, vp],
+        "moe_combine_bwd": [P, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp],
+        "moe_gmm_swiglu_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64,
+                               vp, sz, vp],
+        "moe_permute_bwd": [P, i32, i32, vp, vp, vp, i64, vp],
+        "moe_route_bwd": [P, vp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -303,6 +314,66 @@ def moe_layer_dropless_chunked(p: Problem, mode, x, logits, w_gate, w_up, w_down
         _ptr(w_gate, p.dtype, "w_gate"), _ptr(w_up, p.dtype, "w_up"),
         _ptr(w_down, p.dtype, "w_down"), _ptr(y, p.dtype, "y"),
         _ptr(info, torch.int32, "info"), w, nb, _stream(stream)))
+
+
+# ---- backward ---------------------------------------------------------------
+
+def bwd_workspace_bytes(p: Problem, max_rows: int) -> int:
+    out = ctypes.c_size_t()
+    _check("moe_bwd_workspace_bytes",
+           _lib().moe_bwd_workspace_bytes(ctypes.byref(p.c()), max_rows, ctypes.byref(out)))
+    return out.value
+
+
+def moe_transpose_weights(p: Problem, w_gate, w_up, w_down, w_gu_t, w_down_t, stream=None):
+    _check("moe_transpose_weights", _lib().moe_transpose_weights(
+        ctypes.byref(p.c()), _ptr(w_gate, p.dtype, "w_gate"), _ptr(w_up, p.dtype, "w_up"),
+        _ptr(w_down, p.dtype, "w_down"), _ptr(w_gu_t, p.dtype, "w_gu_t"),
+        _ptr(w_down_t, p.dtype, "w_down_t"), _stream(stream)))
+
+
+def moe_combine_bwd(p: Problem, num_chunks, chunk, dy, expert_out, row_of_assign, topk_gate,
+                    d_out, d_gate, stream=None):
+    """max_rows is the row count of expert_out and d_out (the smaller)."""
+    _check("moe_combine_bwd", _lib().moe_combine_bwd(
+        ctypes.byref(p.c()), num_chunks, chunk, _ptr(dy, p.dtype, "dy"),
+        _ptr(expert_out, p.dtype, "expert_out"), _ptr(row_of_assign, torch.int32, "row_of_assign"),
+        _ptr(topk_gate, torch.float32, "topk_gate"), _ptr(d_out, p.dtype, "d_out"),
+        _ptr(d_gate, torch.float32, "d_gate"), min(expert_out.shape[0], d_out.shape[0]),
+        _stream(stream)))
+
+
+def moe_gmm_swiglu_bwd(p: Problem, x_sorted, group_offsets, slot_expert, w_gate, w_up, w_down,
+                       w_gu_t, w_down_t, d_out, dx_sorted, dw_gate, dw_up, dw_down, accumulate,
+                       ws, stream=None):
+    """max_rows is the row count of x_sorted, d_out and dx_sorted (the
+    smallest).  w_gu_t / w_down_t may be None for float32 problems."""
+    w, nb = _ws(ws)
+    i32, f32 = torch.int32, torch.float32
+    max_rows = min(x_sorted.shape[0], d_out.shape[0], dx_sorted.shape[0])
+    _check("moe_gmm_swiglu_bwd", _lib().moe_gmm_swiglu_bwd(
+        ctypes.byref(p.c()), _ptr(x_sorted, p.dtype, "x_sorted"),
+        _ptr(group_offsets, i32, "group_offsets"), _ptr(slot_expert, i32, "slot_expert"),
+        _ptr(w_gate, p.dtype, "w_gate"), _ptr(w_up, p.dtype, "w_up"),
+        _ptr(w_down, p.dtype, "w_down"), _ptr(w_gu_t, p.dtype, "w_gu_t"),
+        _ptr(w_down_t, p.dtype, "w_down_t"), _ptr(d_out, p.dtype, "d_out"),
+        _ptr(dx_sorted, p.dtype, "dx_sorted"), _ptr(dw_gate, f32, "dw_gate"),
+        _ptr(dw_up, f32, "dw_up"), _ptr(dw_down, f32, "dw_down"), int(accumulate), max_rows, w,
+        nb, _stream(stream)))
+
+
+def moe_permute_bwd(p: Problem, num_chunks, chunk, dx_sorted, row_of_assign, dx, stream=None):
+    _check("moe_permute_bwd", _lib().moe_permute_bwd(
+        ctypes.byref(p.c()), num_chunks, chunk, _ptr(dx_sorted, p.dtype, "dx_sorted"),
+        _ptr(row_of_assign, torch.int32, "row_of_assign"), _ptr(dx, p.dtype, "dx"),
+        dx_sorted.shape[0], _stream(stream)))
+
+
+def moe_route_bwd(p: Problem, topk_idx, topk_gate, d_gate, d_logits, stream=None):
+    _check("moe_route_bwd", _lib().moe_route_bwd(
+        ctypes.byref(p.c()), _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(topk_gate, torch.float32, "topk_gate"), _ptr(d_gate, torch.float32, "d_gate"),
+        _ptr(d_logits, torch.float32, "d_logits"), _stream(stream)))
 
 
 class LayerRunner:

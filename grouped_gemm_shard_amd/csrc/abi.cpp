@@ -621,6 +621,119 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
   return st;
 }
 
+// ---- backward -----------------------------------------------------------
+
+int moe_bwd_workspace_bytes(const moe_problem* p, int64_t max_rows, size_t* bytes) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (bytes == nullptr || max_rows < 0) return MOE_EINVAL;
+  *bytes = gmm_bwd_scratch_bytes(d, max_rows);
+  return MOE_OK;
+}
+
+int moe_transpose_weights(const moe_problem* p, const void* w_gate, const void* w_up,
+                          const void* w_down, void* w_gu_t, void* w_down_t, void* stream) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (!d.bf16) return MOE_EUNSUPPORTED;
+  if (!w_gate || !w_up || !w_down || !w_gu_t || !w_down_t) return MOE_EINVAL;
+  if (misaligned(w_gate, 4) || misaligned(w_up, 4) || misaligned(w_down, 4) ||
+      misaligned(w_gu_t, 4) || misaligned(w_down_t, 4))
+    return MOE_EINVAL;
+  return hip_status(launch_transpose_weights(d, w_gate, w_up, w_down, w_gu_t, w_down_t,
+                                             (hipStream_t)stream));
+}
+
+int moe_combine_bwd(const moe_problem* p, int32_t num_chunks, int32_t chunk, const void* dy,
+                    const void* expert_out, const int32_t* row_of_assign,
+                    const float* topk_gate, void* d_out, float* d_gate, int64_t max_rows,
+                    void* stream) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (num_chunks < 1 || d.L % num_chunks != 0 || chunk < 0 || chunk >= num_chunks)
+    return MOE_EINVAL;
+  if (!dy || !expert_out || !row_of_assign || !topk_gate || !d_out || !d_gate || max_rows < 0)
+    return MOE_EINVAL;
+  if (misaligned(dy, 16) || misaligned(expert_out, 16) || misaligned(d_out, 16))
+    return MOE_EINVAL;
+  const int lc = d.L / num_chunks;
+  const PassArgs pa = static_pass_args(chunk * lc, lc, 0, 0, d.L);
+  return hip_status(launch_combine_bwd(d, pa, dy, expert_out, row_of_assign, topk_gate, d_out,
+                                       d_gate, max_rows, (hipStream_t)stream));
+}
+
+int moe_gmm_swiglu_bwd(const moe_problem* p, const void* x_sorted, const int32_t* group_offsets,
+                       const int32_t* slot_expert, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* w_gu_t, const void* w_down_t,
+                       const void* d_out, void* dx_sorted, float* dw_gate, float* dw_up,
+                       float* dw_down, int32_t accumulate, int64_t max_rows, void* ws,
+                       size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x_sorted || !group_offsets || !slot_expert || !w_gate || !w_up || !w_down || !d_out ||
+      !dx_sorted || !dw_gate || !dw_up || !dw_down || !ws || max_rows < 0 ||
+      (accumulate != 0 && accumulate != 1))
+    return MOE_EINVAL;
+  if (d.bf16 && (!w_gu_t || !w_down_t)) return MOE_EINVAL;
+  if (misaligned(ws, 256) || misaligned(x_sorted, 16) || misaligned(d_out, 16) ||
+      misaligned(w_gate, 16) || misaligned(w_up, 16) || misaligned(w_down, 4) ||
+      misaligned(dx_sorted, 4) || misaligned(dw_gate, 4) || misaligned(dw_up, 4) ||
+      misaligned(dw_down, 4) || (d.bf16 && (misaligned(w_gu_t, 16) || misaligned(w_down_t, 16))))
+    return MOE_EINVAL;
+  // buffer resources address A operands with 32-bit byte offsets
+  const int64_t wide = d.H > 2 * d.F ? d.H : 2 * d.F;
+  if (max_rows * wide * 2 >= ((int64_t)1 << 31)) return MOE_EUNSUPPORTED;
+  if (ws_bytes < gmm_bwd_scratch_bytes(d, max_rows)) return MOE_ECAPACITY;
+  GemmBwdArgs a;
+  a.x_sorted = x_sorted;
+  a.group_offsets = group_offsets;
+  a.slot_expert = slot_expert;
+  a.wg = w_gate;
+  a.wu = w_up;
+  a.wd = w_down;
+  a.wgu_t = w_gu_t;
+  a.wd_t = w_down_t;
+  a.d_out = d_out;
+  a.dx_sorted = dx_sorted;
+  a.dwg = dw_gate;
+  a.dwu = dw_up;
+  a.dwd = dw_down;
+  a.accumulate = accumulate;
+  a.max_rows = max_rows;
+  a.scratch = ws;
+  return hip_status(launch_gmm_bwd(d, a, (hipStream_t)stream));
+}
+
+int moe_permute_bwd(const moe_problem* p, int32_t num_chunks, int32_t chunk,
+                    const void* dx_sorted, const int32_t* row_of_assign, void* dx,
+                    int64_t max_rows, void* stream) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (num_chunks < 1 || d.L % num_chunks != 0 || chunk < 0 || chunk >= num_chunks)
+    return MOE_EINVAL;
+  if (!dx_sorted || !row_of_assign || !dx || max_rows < 0) return MOE_EINVAL;
+  if (misaligned(dx_sorted, 16) || misaligned(dx, 16)) return MOE_EINVAL;
+  const int lc = d.L / num_chunks;
+  const PassArgs pa = static_pass_args(chunk * lc, lc, 0, 0, d.L);
+  return hip_status(launch_permute_bwd(d, pa, dx_sorted, row_of_assign, dx, max_rows,
+                                       (hipStream_t)stream));
+}
+
+int moe_route_bwd(const moe_problem* p, const int32_t* topk_idx, const float* topk_gate,
+                  const float* d_gate, float* d_logits, void* stream) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !topk_gate || !d_gate || !d_logits) return MOE_EINVAL;
+  return hip_status(launch_route_bwd(d, topk_idx, topk_gate, d_gate, d_logits,
+                                     (hipStream_t)stream));
+}
+
 const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -268,6 +268,82 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
                                const void* w_down, void* y, int32_t* info,
                                void* ws, size_t ws_bytes, void* stream);
 
+/* ---- backward of the hot path ------------------------------------------- */
+/*
+ * The backward of one pass, step by step, as the chain rule of the steps
+ * above.  [FALLBACK] How runs the chunked passes in a scan whose backward
+ * recomputes one chunk at a time and carries the weight gradients across
+ * the chunks; [RING] (title, What) keeps the expert-sorted input x_sorted
+ * for the backward.  A caller runs, per pass of the forward (the same
+ * num_chunks / chunk / capped, and the arrays moe_permute wrote for it):
+ * moe_combine_bwd, moe_gmm_swiglu_bwd (accumulate = 0 on the first pass,
+ * 1 after), moe_permute_bwd; then once moe_route_bwd.  Gradients of
+ * weights, gates and logits are float32; row gradients (d_out, dx_sorted,
+ * dx) use the activation dtype.
+ */
+
+/* Scratch bytes of moe_gmm_swiglu_bwd for `max_rows` pass rows. */
+int moe_bwd_workspace_bytes(const moe_problem* p, int64_t max_rows, size_t* bytes);
+
+/* Transposed weight copies the bf16 data-gradient GEMMs read (reduction
+ * dimension contiguous), made once per weight update:
+ *   w_gu_t   [E_res, H, 2F]  w_gu_t[e][h][f] = w_gate[e][f][h],
+ *                            w_gu_t[e][h][F+f] = w_up[e][f][h];
+ *   w_down_t [E_res, F, H]   w_down_t[e][f][h] = w_down[e][h][f].
+ * MOE_EUNSUPPORTED for MOE_F32 (that path reads the weights directly). */
+int moe_transpose_weights(const moe_problem* p, const void* w_gate, const void* w_up,
+                          const void* w_down, void* w_gu_t, void* w_down_t, void* stream);
+
+/* Backward of moe_combine for the tokens of chunk `chunk` of num_chunks:
+ * for each assignment (t, j) with a row r = row_of_assign[t*k+j] in
+ * [0, max_rows),
+ *   d_out[r]       = topk_gate[t,j] * dy[t]         (activation dtype)
+ *   d_gate[t*k+j]  = <dy[t], expert_out[r]>         (float32, fp32 sum)
+ * and d_gate = 0 for an assignment without a row.  Rows of d_out no
+ * assignment of the pass points at, and d_gate of other tokens, are
+ * untouched.  dy [T,H]; expert_out and d_out [max_rows, H]. */
+int moe_combine_bwd(const moe_problem* p, int32_t num_chunks, int32_t chunk, const void* dy,
+                    const void* expert_out, const int32_t* row_of_assign,
+                    const float* topk_gate, void* d_out, float* d_gate, int64_t max_rows,
+                    void* stream);
+
+/* Backward of moe_gmm_swiglu over the same groups (group g runs resident
+ * slot g's expert, a replica slot its home expert).  With h_g = x Wg^T,
+ * h_u = x Wu^T, s = sigmoid(h_g):
+ *   d_a = d_out Wd;  d_hg = d_a h_u s (1 + h_g (1 - s));  d_hu = d_a h_g s;
+ *   dx_sorted = d_hg Wg + d_hu Wu                      [max_rows, H]
+ *   dw_gate[e] (+)= d_hg^T x_sorted,  dw_up[e] (+)= d_hu^T x_sorted  [E_res,F,H]
+ *   dw_down[e] (+)= d_out^T a,  a = SiLU(h_g) h_u (recomputed)        [E_res,H,F]
+ * summed over every row of every group of expert e (float32).  accumulate
+ * 0 overwrites the weight gradients (experts without rows get 0), 1 adds
+ * to them (the carry across passes).  d_a, d_hg, d_hu and a are rounded to
+ * the activation dtype where they are stored (in ws).  bf16 needs w_gu_t
+ * and w_down_t from moe_transpose_weights; fp32 ignores them.  Rows of
+ * dx_sorted past group_offsets[G_res] are untouched.  ws holds
+ * moe_bwd_workspace_bytes(p, max_rows). */
+int moe_gmm_swiglu_bwd(const moe_problem* p, const void* x_sorted, const int32_t* group_offsets,
+                       const int32_t* slot_expert, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* w_gu_t, const void* w_down_t,
+                       const void* d_out, void* dx_sorted, float* dw_gate, float* dw_up,
+                       float* dw_down, int32_t accumulate, int64_t max_rows, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Backward of moe_permute for the tokens of chunk `chunk` of num_chunks:
+ *   dx[t] = sum over j ascending of dx_sorted[row_of_assign[t*k+j]]
+ * over the rows in [0, max_rows) (fp32 sum, one rounding); 0 for a token
+ * with none.  Rows of other tokens of dx are untouched. */
+int moe_permute_bwd(const moe_problem* p, int32_t num_chunks, int32_t chunk,
+                    const void* dx_sorted, const int32_t* row_of_assign, void* dx,
+                    int64_t max_rows, void* stream);
+
+/* Backward of the gates into the logits, every token: only the k chosen
+ * logits get a gradient (the choice is piecewise constant);
+ *   SOFTMAX: d_l[idx_j] = g_j (d_g_j - sum_i g_i d_g_i)
+ *   SIGMOID: d_l[idx_j] = d_g_j g_j (1 - g_j)
+ * d_logits [T,E] float32 is written in full. */
+int moe_route_bwd(const moe_problem* p, const int32_t* topk_idx, const float* topk_gate,
+                  const float* d_gate, float* d_logits, void* stream);
+
 /* Text of a status code (static storage). */
 const char* moe_status_string(int status);
 

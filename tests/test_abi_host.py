@@ -172,3 +172,37 @@ def test_fallback_chunks_per_pass_stay_within_the_capped_buffer():
         r1, u1 = g.pass_max_rows(p, 1, 1)
         rc, uc = g.pass_max_rows(p, n, 0)
         assert rows_q <= max(r1, rc) and drows_q <= max(u1, uc)
+
+
+def test_backward_entry_points_validate_on_the_host():
+    g = _binding()
+    fake = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    c = problem().c()
+    rows = 16384
+    need = g.bwd_workspace_bytes(problem(), rows)
+    # scratch: tile offsets, d_a, d_hg|d_hu and the recomputed activation,
+    # 4F bf16 values per row
+    assert need >= rows * 4 * 512 * 2
+    gmm = lambda cc, acc, mr, ws, nb, wt=fake: g.lib.moe_gmm_swiglu_bwd(  # noqa: E731
+        ctypes.byref(cc), fake, fake, fake, fake, fake, fake, wt, wt, fake, fake, fake, fake, fake,
+        acc, mr, ws, nb, None)
+    assert gmm(c, 0, rows, None, need) == -1          # no workspace
+    assert gmm(c, 2, rows, fake, need) == -1          # accumulate is 0 or 1
+    assert gmm(c, 0, -1, fake, need) == -1            # negative rows
+    assert gmm(c, 0, rows, fake, need, None) == -1    # bf16 needs the transposed weights
+    assert gmm(c, 0, rows, ctypes.c_void_p(128), need) == -1  # ws alignment
+    assert gmm(c, 0, rows, fake, need - 1) == -3      # workspace too small
+    # 32-bit buffer offsets: rows * max(H, 2F) * 2 bytes must stay below 2^31
+    assert gmm(c, 0, 1 << 20, fake, 1 << 40) == -2
+    assert g.lib.moe_combine_bwd(ctypes.byref(c), 4, 4, fake, fake, fake, fake, fake, fake, rows,
+                                 None) == -1
+    assert g.lib.moe_combine_bwd(ctypes.byref(c), 1, 0, ctypes.c_void_p(258), fake, fake, fake,
+                                 fake, fake, rows, None) == -1
+    assert g.lib.moe_permute_bwd(ctypes.byref(c), 1, 0, None, fake, fake, rows, None) == -1
+    assert g.lib.moe_route_bwd(ctypes.byref(c), fake, None, fake, fake, None) == -1
+    assert g.lib.moe_transpose_weights(ctypes.byref(c), fake, fake, fake, None, fake, None) == -1
+    fp = problem(hidden=64, ffn=64)
+    fc = fp.c()
+    fc.dtype = 0  # float32 reads the weights directly: no transposed copies
+    assert g.lib.moe_transpose_weights(ctypes.byref(fc), fake, fake, fake, fake, fake,
+                                       None) == -2

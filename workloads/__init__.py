@@ -158,6 +158,13 @@ def make_weights(w: Workload, device="cpu"):
     return wg, wu, wd
 
 
+def make_dy(w: Workload, device="cpu") -> torch.Tensor:
+    """Upstream gradient of the layer output, [T,H] standard normal, in the
+    activation dtype (for the backward)."""
+    dy = _normal((w.tokens, w.hidden), w.seed, 5, 0, device)
+    return dy.to(torch.bfloat16) if w.bf16 else dy
+
+
 def make_inputs(w: Workload, device="cpu"):
     return dict(logits=make_logits(w, device), x=make_x(w, device), weights=make_weights(w, device))
 
