@@ -681,8 +681,8 @@ int moe_gmm_swiglu_bwd(const moe_problem* p, const void* x_sorted, const int32_t
   if (d.bf16 && (!w_gu_t || !w_down_t)) return MOE_EINVAL;
   if (misaligned(ws, 256) || misaligned(x_sorted, 16) || misaligned(d_out, 16) ||
       misaligned(w_gate, 16) || misaligned(w_up, 16) || misaligned(w_down, 4) ||
-      misaligned(dx_sorted, 4) || misaligned(dw_gate, 4) || misaligned(dw_up, 4) ||
-      misaligned(dw_down, 4) || (d.bf16 && (misaligned(w_gu_t, 16) || misaligned(w_down_t, 16))))
+      misaligned(dx_sorted, 4) || misaligned(dw_gate, 16) || misaligned(dw_up, 16) ||
+      misaligned(dw_down, 16) || (d.bf16 && (misaligned(w_gu_t, 16) || misaligned(w_down_t, 16))))
     return MOE_EINVAL;
   // buffer resources address A operands with 32-bit byte offsets
   const int64_t wide = d.H > 2 * d.F ? d.H : 2 * d.F;

@@ -249,6 +249,22 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Unit of the launch this block runs, or -1.  Blocks go round-robin over
+// the 8 XCDs (block b to XCD b % 8).  Each round of nb blocks (the blocks
+// resident on the chip at once, a multiple of 8; the grid is whole rounds)
+// covers that many consecutive units of the `total` units, and XCD x takes
+// the x-th eighth of the round, so the units one XCD runs together are
+// neighbours in the unit order and share their operand panels in its L2.
+__device__ __forceinline__ int xcd_unit(int nb, int total) {
+  const int bid = blockIdx.x;
+  const int rbase = (bid / nb) * nb;
+  const int rs = min(nb, total - rbase);
+  if (rs <= 0) return -1;
+  const int x = bid & 7, slot = (bid - rbase) >> 3;
+  const int L = rbase + (x * rs >> 3) + slot;
+  return L < rbase + ((x + 1) * rs >> 3) ? L : -1;
+}
+
 struct DgradParams {
   const uint16_t* A;        // [a_rows, K] rows of the pass
   int a_rows;
@@ -263,6 +279,7 @@ struct DgradParams {
   const int* tile_off;
   const int* slot_expert;
   int G, K, Nout, lo_slot, e_base, e_res, n_ntiles;
+  int round_blocks;         // blocks per round (xcd_unit)
   long long max_rows;
 };
 
@@ -282,9 +299,13 @@ __device__ __forceinline__ void dgrad_tile(const DgradParams& P) {
   constexpr int NS = 2;                        // acc sets (gate, up) or 1
   __shared__ __attribute__((aligned(1024))) char smem[kNST * SS];
 
-  const int nt = blockIdx.x % P.n_ntiles;
-  const int m = blockIdx.x / P.n_ntiles;
+  // units: m-tiles by n-tiles, n fastest (an XCD's run of units covers a
+  // few m-tiles by all n-tiles: the A rows are read once per XCD)
   const int total = P.tile_off[P.G];
+  const int unit = xcd_unit(P.round_blocks, total * P.n_ntiles);
+  if (unit < 0) return;
+  const int nt = unit % P.n_ntiles;
+  const int m = unit / P.n_ntiles;
   if (m >= total) return;
   int lo = 0, hi = P.G;
   while (hi - lo > 1) {
@@ -417,90 +438,258 @@ __global__ __launch_bounds__(256, 2) void dgrad_kernel(DgradParams P) {
 }
 
 // ---- weight-gradient GEMM --------------------------------------------------
+//
+// dW[e] = P^T Q summed over the rows of every group of expert e (P, Q
+// row-major with the row as the reduction index).  The rows of an expert
+// are cut into chunks of at most Kc rows (Kc sized so that the longest
+// chunk is no more than the chip's average share of the launch), so a hot
+// expert's reduction runs on several workgroups; an expert with one chunk
+// writes its gradient directly, the chunks of a split expert write float32
+// partials that a second kernel adds in chunk order (deterministic).
 
-struct WgradParams {
-  const uint16_t* Pm;   // [rows, I] (row-major, I contiguous)
-  const uint16_t* Qm;   // [rows, J]
-  float* C0;            // rows i < i_split: C0[e][i][j]
-  float* C1;            // rows i >= i_split: C1[e][i - i_split][j]
-  size_t c_stride;      // elements per expert of C0 / C1
-  int I, J, i_split;
-  const int* group_offsets;
-  const int* slot_expert;
-  int G, lo_slot, e_base, e_res, ni_tiles, nj_tiles;
-  long long max_rows;
-  int accumulate;
+constexpr int kWBK = 32;   // rows per stage
+constexpr int kWNST = 4;   // ring stages
+constexpr int kWMaxRes = 1024;
+
+// Per-expert plan of the weight-gradient launches, from the group offsets:
+// the expert's groups in group order (their first row and row count, as a
+// list per expert), its rows R_e, its chunk count nch_e = max(1,
+// ceil(R_e / Kc)), the first chunk index, and for split experts the first
+// partial slot.  chunk_e / chunk_i map a chunk to (expert, index); unused
+// chunk slots hold -1.  Offsets that are not non-decreasing within
+// [0, max_rows] count as empty groups.
+struct WgradPlan {
+  int* grp_off;    // [e_res + 1]
+  int* grp_row0;   // [G]
+  int* grp_len;    // [G]
+  int* rows;       // [e_res]
+  int* nch;        // [e_res]
+  int* pbase;      // [e_res]
+  int* chunk_e;    // [nc_ub]
+  int* chunk_i;    // [nc_ub]
+  int* meta;       // [0] chunks in use
 };
 
-// Next (group, row) step of expert e's rows after (g, r): the rows of its
-// groups in group order, 32 at a time.  g = G when there are none left.
-__device__ __forceinline__ void wgrad_next(const WgradParams& P, int e, int& g, int& r) {
-  r += kBK;
-  if (g >= 0 && g < P.G && r < P.group_offsets[g + 1]) return;
-  for (++g; g < P.G; ++g) {
-    if (P.slot_expert[P.lo_slot + g] - P.e_base != e) continue;
-    const int a = P.group_offsets[g], b = P.group_offsets[g + 1];
-    if (b > a && b <= P.max_rows && a >= 0) {
-      r = a;
-      return;
+__global__ __launch_bounds__(1024) void wgrad_plan_kernel(WgradPlan W, const int* group_offsets,
+                                                          const int* slot_expert, int G,
+                                                          int lo_slot, int e_base, int e_res,
+                                                          long long max_rows, int kc, int nc_ub) {
+  __shared__ int ge[kMaxSlots], gr[kMaxSlots], g0[kMaxSlots];
+  __shared__ int gcnt[kWMaxRes], rsum[kWMaxRes], cb[kWMaxRes + 1];
+  __shared__ int bad;
+  const int tid = threadIdx.x;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  for (int g = tid; g < G; g += blockDim.x) {
+    const int a = group_offsets[g], b = group_offsets[g + 1];
+    if (a < 0 || b < a || b > max_rows) bad = 1;
+    const int e = slot_expert[lo_slot + g] - e_base;
+    ge[g] = (e >= 0 && e < e_res) ? e : -1;
+    gr[g] = b - a;
+    g0[g] = a;
+  }
+  __syncthreads();
+  // a malformed offset sequence leaves every group empty, so the rows of
+  // all experts together never exceed max_rows (which bounds the chunks
+  // and partial slots)
+  if (bad)
+    for (int g = tid; g < G; g += blockDim.x) ge[g] = -1;
+  __syncthreads();
+  for (int e = tid; e < e_res; e += blockDim.x) {
+    int c = 0, r = 0;
+    for (int g = 0; g < G; ++g)
+      if (ge[g] == e) {
+        ++c;
+        r += gr[g];
+      }
+    gcnt[e] = c;
+    rsum[e] = r;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int go = 0, co = 0, po = 0;
+    for (int e = 0; e < e_res; ++e) {
+      W.grp_off[e] = go;
+      go += gcnt[e];
+      const int n = rsum[e] > kc ? (rsum[e] + kc - 1) / kc : 1;
+      W.rows[e] = rsum[e];
+      W.nch[e] = n;
+      W.pbase[e] = n > 1 ? po : -1;
+      if (n > 1) po += n;
+      cb[e] = co;
+      co += n;
     }
+    W.grp_off[e_res] = go;
+    cb[e_res] = co;
+    W.meta[0] = co < nc_ub ? co : nc_ub;
+  }
+  __syncthreads();
+  for (int e = tid; e < e_res; e += blockDim.x) {
+    int o = W.grp_off[e];
+    for (int g = 0; g < G; ++g)
+      if (ge[g] == e) {
+        W.grp_row0[o] = g0[g];
+        W.grp_len[o] = gr[g];
+        ++o;
+      }
+    for (int c = cb[e]; c < cb[e + 1] && c < nc_ub; ++c) {
+      W.chunk_e[c] = e;
+      W.chunk_i[c] = c - cb[e];
+    }
+  }
+  for (int c = cb[e_res] + tid; c < nc_ub; c += blockDim.x) {
+    W.chunk_e[c] = -1;
+    W.chunk_i[c] = 0;
   }
 }
 
-// One 128 x 128 tile of C[e] = P^T Q over expert e's rows.  4 waves in a
-// 2 x 2 grid, 64 x 64 per wave.  Each step stages 32 rows of both operands:
-// a thread loads one 4-byte pair of columns from 8 consecutive rows and
-// writes them to LDS as two 16-byte runs of 8 rows (row index contiguous),
-// so the MFMA fragments read 8 consecutive reduction elements at once.
-// Double-buffered: the next step's loads are in flight during the MFMAs.
-__global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradParams P) {
-  constexpr int RB = kBK * 2;  // 64 bytes: one operand column's 32 rows
-  constexpr int TS = 128 * RB;  // one operand tile
-  __shared__ __attribute__((aligned(1024))) char smem[2][2 * TS];
-  const int per_e = P.ni_tiles * P.nj_tiles;
-  const int e = blockIdx.x / per_e;
-  const int it = (blockIdx.x % per_e) / P.nj_tiles, jt = blockIdx.x % P.nj_tiles;
-  if (e >= P.e_res) return;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
+struct WgradParams {
+  const uint16_t* Pm;   // [a_rows, I] (row-major, I contiguous)
+  const uint16_t* Qm;   // [a_rows, J]
+  float* C0;            // rows i < i_split: C0[e][i][j]
+  float* C1;            // rows i >= i_split: C1[e][i - i_split][j]
+  float* part;          // [slots][I][J] partials of split experts
+  size_t c_stride;      // elements per expert of C0 / C1
+  int I, J, i_split;
+  int a_rows;
+  WgradPlan plan;
+  int kc, ni_tiles, nj_tiles;
+  long long slots;      // partial slots in part
+  int accumulate;
+};
+
+constexpr int kWMaxGroups = 1024;  // groups of one expert kept in LDS
+
+// Actual row of position p of the expert's row sequence, from the LDS copy
+// of its group list (first rows, then lengths); cur is the lane's group
+// cursor (positions only grow), base the sequence start of group cur.  No
+// global loads: the ring's loads stay the only vector-memory operations in
+// flight, so waiting for one stage never waits for a later one.
+__device__ __forceinline__ int wgrad_row(const int* gl, int ng, int p, int& cur, int& base) {
+  while (cur < ng && p >= base + gl[kWMaxGroups + cur]) {
+    base += gl[kWMaxGroups + cur];
+    ++cur;
+  }
+  return cur < ng ? gl[cur] + (p - base) : -1;
+}
+
+// 16-byte chunk permutation of a 256-byte LDS row (16 chunks): the
+// transpose reads of 4 consecutive rows at one column land on disjoint
+// 64-byte bank windows.
+__device__ __forceinline__ int wswz(int row) { return (row & 3) << 2; }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// ds_read_b64_tr_b16 as inline asm: the compiler cannot tell that the
+// builtin's LDS read does not alias the ring's in-flight buffer loads into
+// LDS, and waits for all of them before it; here the ring's own barrier
+// already guarantees the stage being read has landed.  The result is
+// pending until lgkm_wait_tie.
+__device__ __forceinline__ void lds_read_tr16(v4i16& r, unsigned addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+}
+
+// Waits until at most N LDS reads of this wave are outstanding; the
+// registers of one slice are tied to the wait so their uses stay after it.
+template <int N>
+__device__ __forceinline__ void lgkm_wait_tie(v4i16 (&a)[2][2], v4i16 (&b)[2][2]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[1][0]), "+v"(a[1][1]), "+v"(b[0][0]),
+                 "+v"(b[0][1]), "+v"(b[1][0]), "+v"(b[1][1])
+               : "n"(N));
+}
+
+__device__ __forceinline__ bf16x8 join8(const v4i16& lo, const v4i16& hi) {
+  bf16x8 v;
+  __builtin_memcpy(&v, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&v) + 8, &hi, 8);
+  return v;
+}
+
+// The 4 MFMAs of one 16-row slice (2 x 2 tiles of 32 x 32).
+__device__ __forceinline__ void mma_slice(const v4i16 (&a)[2][2], const v4i16 (&b)[2][2],
+                                          floatx16 (&acc)[2][2]) {
+  bf16x8 fa[2], fb[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    fa[m] = join8(a[m][0], a[m][1]);
+    fb[m] = join8(b[m][0], b[m][1]);
+  }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+}
+
+// One 128 x 128 tile of one chunk.  4 waves in a 2 x 2 grid, 64 x 64 per
+// wave.  Raw rows of both operands (256 bytes of the tile's columns each)
+// go from HBM into a 4-stage LDS ring with buffer_load ... lds; the MFMA
+// fragments are read with ds_read_tr16_b64, which hands each lane 4
+// consecutive rows of one column: lane 4a+b of each 16-lane group receives
+// element b of the 8-byte runs that lanes a, a+4, a+8 and a+12 address.
+__device__ __forceinline__ void wgrad_tile(const WgradParams& P, char* smem, int* gl) {
+  constexpr int RB = 256;                 // bytes per staged row (128 columns)
+  constexpr int OPB = kWBK * RB;          // one operand's stage (8 KB)
+  constexpr int SS = 2 * OPB;             // stage
+  constexpr int LPO = OPB / 1024 / 4;     // loads per wave per operand per stage (2)
+  constexpr int LPS = 2 * LPO;
+  const int tiles = P.ni_tiles * P.nj_tiles;
+  // units: chunks by tiles, tiles fastest, in block order (measured faster
+  // than the XCD-contiguous order here: a chunk's tiles spread over all
+  // XCDs start together, and the hot experts' chunks come first)
+  const int u = blockIdx.x / tiles;
+  const int t = blockIdx.x % tiles;
+  if (u >= P.plan.meta[0]) return;
+  const int e = P.plan.chunk_e[u];
+  if (e < 0) return;
+  const int ci = P.plan.chunk_i[u];
+  const int it = t / P.nj_tiles, jt = t % P.nj_tiles;
   const int i0 = it * 128, j0 = jt * 128;
+  const int R = P.plan.rows[e], nch = P.plan.nch[e];
+  const int k0 = ci * P.kc, k1 = min(R, k0 + P.kc);
+  const int KT = k1 > k0 ? (k1 - k0 + kWBK - 1) / kWBK : 0;
+  const int g_lo = P.plan.grp_off[e];
+  const int ng = min(P.plan.grp_off[e + 1] - g_lo, kWMaxGroups);
+  const bool direct = nch == 1;
+  const long long slot = direct ? 0 : (long long)P.plan.pbase[e] + ci;
+  if (!direct && (P.plan.pbase[e] < 0 || slot >= P.slots)) return;
 
-  int g = -1, r = -kBK;
-  wgrad_next(P, e, g, r);
-  int gend = g < P.G ? P.group_offsets[g + 1] : 0;
-
-  uint32_t pv[8], qv[8];
-  auto load = [&](int gr, int rr, int ge) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int x = tid; x < ng; x += blockDim.x) {
+    gl[x] = P.plan.grp_row0[g_lo + x];
+    gl[kWMaxGroups + x] = P.plan.grp_len[g_lo + x];
+  }
+  __syncthreads();
+  const int wm = w >> 1, wn = w & 1;
+  const __amdgpu_buffer_rsrc_t rp = raw_rsrc(P.Pm, (unsigned)P.a_rows * P.I * 2);
+  const __amdgpu_buffer_rsrc_t rq = raw_rsrc(P.Qm, (unsigned)P.a_rows * P.J * 2);
+  // this lane's staged rows (one per load) and their group cursors
+  int cur[LPO], base[LPO];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int row = rr + w * 8 + q;
-      if (gr < P.G && row < ge) {
-        pv[q] = *(const uint32_t*)(P.Pm + (size_t)row * P.I + i0 + lane * 2);
-        qv[q] = *(const uint32_t*)(P.Qm + (size_t)row * P.J + j0 + lane * 2);
-      } else {
-        pv[q] = 0u;
-        qv[q] = 0u;
-      }
-    }
-  };
-  // columns 2*lane and 2*lane+1, rows w*8 .. w*8+7 of the step
-  auto stage = [&](char* buf) {
+  for (int i = 0; i < LPO; ++i) {
+    cur[i] = 0;
+    base[i] = 0;
+  }
+  const int pch = lane & 15;  // physical 16-byte chunk of the lane's load
+  auto issue = [&](int step) {
+    char* st = smem + (step % kWNST) * SS;
 #pragma unroll
-    for (int op = 0; op < 2; ++op) {
-      const uint32_t* v = op == 0 ? pv : qv;
-      uint4 lo4, hi4;
-      lo4.x = (v[0] & 0xFFFFu) | (v[1] << 16);
-      lo4.y = (v[2] & 0xFFFFu) | (v[3] << 16);
-      lo4.z = (v[4] & 0xFFFFu) | (v[5] << 16);
-      lo4.w = (v[6] & 0xFFFFu) | (v[7] << 16);
-      hi4.x = (v[0] >> 16) | (v[1] & 0xFFFF0000u);
-      hi4.y = (v[2] >> 16) | (v[3] & 0xFFFF0000u);
-      hi4.z = (v[4] >> 16) | (v[5] & 0xFFFF0000u);
-      hi4.w = (v[6] >> 16) | (v[7] & 0xFFFF0000u);
-      char* t = buf + op * TS;
-      const int c0 = lane * 2, c1 = lane * 2 + 1;
-      *(uint4*)(t + c0 * RB + ((w ^ swz4(c0)) << 4)) = lo4;
-      *(uint4*)(t + c1 * RB + ((w ^ swz4(c1)) << 4)) = hi4;
+    for (int i = 0; i < LPO; ++i) {
+      const int rr = (i * 4 + w) * 4 + (lane >> 4);  // row within the stage
+      const int p = k0 + step * kWBK + rr;
+      const int row = p < k1 ? wgrad_row(gl, ng, p, cur[i], base[i]) : -1;
+      const int lch = pch ^ wswz(rr);
+      const int po = row >= 0 ? row * P.I * 2 + i0 * 2 + lch * 16 : (int)0x80000000;
+      const int qo = row >= 0 ? row * P.J * 2 + j0 * 2 + lch * 16 : (int)0x80000000;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (lds_void*)(st + (i * 4 + w) * 1024), 16, po,
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(st + OPB + (i * 4 + w) * 1024), 16,
+                                               qo, 0, 0, 0);
     }
   };
 
@@ -512,61 +701,133 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradParams P) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.0f;
 
-  int cur = 0;
-  if (g < P.G) {
-    load(g, r, gend);
-    stage(smem[0]);
+  // transpose-read addressing: source lane (group G = lane/16, s = lane%16)
+  // points at row 8*(G/2) + s/4 (+4 for the second half of the 8 values)
+  // and column 16*(G%2) + 4*(s%4) of the wave's 32-column MFMA tile.  The
+  // row's chunk permutation depends only on row % 4 = s/4, so each lane's
+  // reads differ by whole rows (constant byte offsets).
+  const int G = lane >> 4, s = lane & 15;
+  const int trow = 8 * (G >> 1) + (s >> 2);
+  const int tcol = 16 * (G & 1) + 4 * (s & 3);
+  unsigned a_off[2], b_off[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int ca = wm * 64 + m * 32 + tcol, cb = wn * 64 + m * 32 + tcol;
+    a_off[m] = trow * RB + (((ca >> 3) ^ wswz(trow)) << 4) + (ca & 7) * 2;
+    b_off[m] = OPB + trow * RB + (((cb >> 3) ^ wswz(trow)) << 4) + (cb & 7) * 2;
   }
-  __syncthreads();
-  while (g < P.G) {
-    int g2 = g, r2 = r;
-    wgrad_next(P, e, g2, r2);
-    const int gend2 = g2 < P.G ? P.group_offsets[g2 + 1] : 0;
-    if (g2 < P.G) load(g2, r2, gend2);
-    const char* sp = smem[cur];
-    const char* sq = sp + TS;
+  const unsigned lds0 = lds_addr(smem);
+
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int kc = ks * 2 + (lane >> 5);
-      bf16x8 a[2], b[2];
+  for (int s0 = 0; s0 < kWNST - 1; ++s0)
+    if (s0 < KT) issue(s0);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int ahead = min(KT - 1 - kt, kWNST - 2);
+    if (ahead >= 2) wait_vm_barrier<2 * LPS>();
+    else if (ahead == 1) wait_vm_barrier<LPS>();
+    else wait_vm_barrier<0>();
+    if (kt + kWNST - 1 < KT) issue(kt + kWNST - 1);
+    const unsigned st = lds0 + (kt % kWNST) * SS;
+    // both 16-row slices' fragments: [slice][mi or ni][half]
+    v4i16 ra[2][2][2], rb[2][2][2];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int row = wm * 64 + mi * 32 + (lane & 31);
-        a[mi] = *(const bf16x8*)(sp + row * RB + ((kc ^ swz4(row)) << 4));
-      }
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int row = wn * 64 + ni * 32 + (lane & 31);
-        b[ni] = *(const bf16x8*)(sq + row * RB + ((kc ^ swz4(row)) << 4));
-      }
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
-    }
-    if (g2 < P.G) stage(smem[cur ^ 1]);
-    __syncthreads();
-    cur ^= 1;
-    g = g2;
-    r = r2;
-    gend = gend2;
+        for (int h = 0; h < 2; ++h) {
+          const unsigned dr = (ks * 16 + 4 * h) * RB;
+          lds_read_tr16(ra[ks][m][h], st + a_off[m] + dr);
+          lds_read_tr16(rb[ks][m][h], st + b_off[m] + dr);
+        }
+    lgkm_wait_tie<8>(ra[0], rb[0]);
+    mma_slice(ra[0], rb[0], acc);
+    lgkm_wait_tie<0>(ra[1], rb[1]);
+    mma_slice(ra[1], rb[1], acc);
   }
 
+  // a single-chunk expert writes its gradient (skipped when there is
+  // nothing to add), a split expert's chunk its partial
+  if (direct && P.accumulate && KT == 0) return;
+  float* part = direct ? nullptr : P.part + (size_t)slot * P.I * P.J;
+  // output element (mi, q, ni) of this lane: row i of the tile's rows, column j
+  auto out_ptr = [&](int mi, int q, int ni) {
+    const int i = i0 + wm * 64 + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+    const int j = j0 + wn * 64 + ni * 32 + (lane & 31);
+    if (!direct) return part + (size_t)i * P.J + j;
+    if (i < P.i_split) return P.C0 + (size_t)e * P.c_stride + (size_t)i * P.J + j;
+    return P.C1 + (size_t)e * P.c_stride + (size_t)(i - P.i_split) * P.J + j;
+  };
+  if (direct && P.accumulate) {
+    // all old values are loaded before any is needed, so the loads overlap
+    // instead of each waiting a full memory round trip
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        floatx16 old;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) old[q] = *out_ptr(mi, q, ni);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[mi][ni][q] += old[q];
+      }
+  }
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int i = i0 + wm * 64 + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-      float* crow = i < P.i_split ? P.C0 + (size_t)e * P.c_stride + (size_t)i * P.J
-                                  : P.C1 + (size_t)e * P.c_stride + (size_t)(i - P.i_split) * P.J;
+    for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int j = j0 + wn * 64 + ni * 32 + (lane & 31);
-        const float v = acc[mi][ni][q];
-        crow[j] = P.accumulate ? crow[j] + v : v;
-      }
-    }
+      for (int q = 0; q < 16; ++q) *out_ptr(mi, q, ni) = acc[mi][ni][q];
+}
+
+__global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradParams P) {
+  __shared__ __attribute__((aligned(1024))) char smem[kWNST * 2 * kWBK * 256];
+  __shared__ int gl[2 * kWMaxGroups];
+  wgrad_tile(P, smem, gl);
+}
+
+// dW[e] (+)= the sum of a split expert's partials, in chunk order.
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(WgradParams P) {
+  const int e = blockIdx.y;
+  const int n = P.plan.nch[e];
+  if (n <= 1 || P.plan.pbase[e] < 0 || (long long)P.plan.pbase[e] + n > P.slots) return;
+  const long long IJ = (long long)P.I * P.J;
+  const long long idx = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (idx >= IJ) return;
+  const float* part = P.part + (size_t)P.plan.pbase[e] * IJ + idx;
+  float4 s = *(const float4*)part;
+  for (int c = 1; c < n; ++c) {
+    const float4 v = *(const float4*)(part + (size_t)c * IJ);
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  const int i = (int)(idx / P.J), j = (int)(idx % P.J);
+  float* dst = i < P.i_split ? P.C0 + (size_t)e * P.c_stride + (size_t)i * P.J + j
+                             : P.C1 + (size_t)e * P.c_stride + (size_t)(i - P.i_split) * P.J + j;
+  if (P.accumulate) {
+    const float4 o = *(const float4*)dst;
+    s.x += o.x;
+    s.y += o.y;
+    s.z += o.z;
+    s.w += o.w;
+  }
+  *(float4*)dst = s;
+}
+
+// Rows per chunk: no chunk longer than the chip's average share (512
+// workgroup slots) of the launch with the fewest tiles per expert, and at
+// least 256.  Split experts need at most floor(2 max_rows / Kc) partials.
+inline int wgrad_kc(const Dims& d, int64_t max_rows) {
+  const long long tmin = (long long)(d.H / 128) * (d.F / 128);
+  long long kc = (max_rows * tmin + 511) / 512;
+  kc = (kc + kWBK - 1) / kWBK * kWBK;
+  return (int)(kc < 256 ? 256 : kc > (1 << 30) ? (1 << 30) : kc);
+}
+inline long long wgrad_slots(int64_t max_rows, int kc) { return 2 * max_rows / kc; }
+inline long long wgrad_nc_ub(const Dims& d, int64_t max_rows, int kc) {
+  return (long long)d.S_res * d.El + max_rows / kc;
 }
 
 // ---- fp32 path (small fp32 problems): one thread per output element -------
@@ -671,12 +932,78 @@ __global__ __launch_bounds__(256) void f32_dw_kernel(F32Bwd P, int which) {
 
 inline size_t a256(size_t b) { return (b + 255) / 256 * 256; }
 
+// Blocks of one round of a kernel's unit order (xcd_unit): the compute
+// units rounded down to a multiple of 8 (the XCDs) times the workgroups of
+// the kernel that fit on one, cached per device and kernel.
+int bwd_round_blocks(const void* kernel, int threads, int which) {
+  static int cache[64][4] = {};
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev][which] == 0) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 8)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) != hipSuccess ||
+        occ < 1)
+      occ = 1;
+    cache[dev][which] = cus / 8 * 8 * occ;
+  }
+  return cache[dev][which];
+}
+
+inline unsigned whole_rounds(long long units, int nb) {
+  return (unsigned)((units + nb - 1) / nb * nb);
+}
+
+}  // namespace
+
+namespace {
+
+// Scratch of the bf16 backward after the tile offsets and the d_h, act and
+// d_a rows: the weight-gradient plan and the partials of split experts.
+struct WgradScratch {
+  WgradPlan plan;
+  float* part;
+  size_t bytes;
+};
+
+WgradScratch carve_wgrad(const Dims& d, int64_t max_rows, char* base) {
+  const int e_res = d.S_res * d.El;
+  const int kc = wgrad_kc(d, max_rows);
+  const long long nc = wgrad_nc_ub(d, max_rows, kc);
+  const long long slots = wgrad_slots(max_rows, kc);
+  WgradScratch w;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + o : nullptr;
+    o += a256(bytes);
+    return p;
+  };
+  w.plan.grp_off = (int*)take((size_t)(e_res + 1) * 4);
+  w.plan.grp_row0 = (int*)take((size_t)d.G_res * 4);
+  w.plan.grp_len = (int*)take((size_t)d.G_res * 4);
+  w.plan.rows = (int*)take((size_t)e_res * 4);
+  w.plan.nch = (int*)take((size_t)e_res * 4);
+  w.plan.pbase = (int*)take((size_t)e_res * 4);
+  w.plan.chunk_e = (int*)take((size_t)nc * 4);
+  w.plan.chunk_i = (int*)take((size_t)nc * 4);
+  w.plan.meta = (int*)take(64);
+  w.part = (float*)take((size_t)slots * 2 * d.F * d.H * 4);
+  w.bytes = o;
+  return w;
+}
+
 }  // namespace
 
 size_t gmm_bwd_scratch_bytes(const Dims& d, int64_t max_rows) {
   const size_t el = d.bf16 ? 2 : 4;
-  return a256((size_t)(d.G_res + 1) * 4) + 3 * a256((size_t)max_rows * d.F * el) +
-         a256((size_t)max_rows * d.F * el);
+  size_t b = a256((size_t)(d.G_res + 1) * 4) + 3 * a256((size_t)max_rows * d.F * el) +
+             a256((size_t)max_rows * d.F * el);
+  if (d.bf16) b += carve_wgrad(d, max_rows, nullptr).bytes;
+  return b;
 }
 
 hipError_t launch_transpose_weights(const Dims& d, const void* wg, const void* wu,
@@ -742,6 +1069,7 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   void* act = ws;
   ws += a256((size_t)rows * d.F * el);
   void* d_a = ws;
+  ws += a256((size_t)rows * d.F * el);
   if (!d.bf16) {
     F32Bwd P;
     P.x = (const float*)a.x_sorted;
@@ -799,8 +1127,11 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   P.K = d.H;
   P.Nout = d.F;
   P.n_ntiles = d.F / kBN;
-  hipLaunchKernelGGL(dgrad_kernel<false>, dim3((unsigned)(mt_ub * P.n_ntiles)), dim3(256), 0, s,
-                     P);
+  const int nb_plain = bwd_round_blocks(reinterpret_cast<const void*>(dgrad_kernel<false>), 256, 0);
+  const int nb_sw = bwd_round_blocks(reinterpret_cast<const void*>(dgrad_kernel<true>), 256, 1);
+  P.round_blocks = nb_plain;
+  hipLaunchKernelGGL(dgrad_kernel<false>, dim3(whole_rounds(mt_ub * P.n_ntiles, nb_plain)),
+                     dim3(256), 0, s, P);
   // gate and up products recomputed; SwiGLU backward and the activation
   DgradParams Q = P;
   Q.A = (const uint16_t*)a.x_sorted;
@@ -810,8 +1141,9 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   Q.d_a = (const uint16_t*)d_a;
   Q.d_h = (uint16_t*)d_h;
   Q.act = (uint16_t*)act;
-  hipLaunchKernelGGL(dgrad_kernel<true>, dim3((unsigned)(mt_ub * Q.n_ntiles)), dim3(256), 0, s,
-                     Q);
+  Q.round_blocks = nb_sw;
+  hipLaunchKernelGGL(dgrad_kernel<true>, dim3(whole_rounds(mt_ub * Q.n_ntiles, nb_sw)),
+                     dim3(256), 0, s, Q);
   // dx_sorted = [d_hg | d_hu] [Wg ; Wu]  (K = 2F, against [Wg ; Wu]^T [H, 2F])
   DgradParams X = P;
   X.A = (const uint16_t*)d_h;
@@ -821,31 +1153,34 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   X.K = 2 * d.F;
   X.Nout = d.H;
   X.n_ntiles = d.H / kBN;
-  hipLaunchKernelGGL(dgrad_kernel<false>, dim3((unsigned)(mt_ub * X.n_ntiles)), dim3(256), 0, s,
-                     X);
-  // [dWg ; dWu] = [d_hg | d_hu]^T x_sorted
+  hipLaunchKernelGGL(dgrad_kernel<false>, dim3(whole_rounds(mt_ub * X.n_ntiles, nb_plain)),
+                     dim3(256), 0, s, X);
+  // weight gradients: plan (rows and chunks per expert), then
+  // [dWg ; dWu] = [d_hg | d_hu]^T x_sorted and dWd = d_out^T act, each with
+  // the fixed-order sum of split experts' partials
+  const WgradScratch wsc = carve_wgrad(d, rows, ws);
+  const int kc = wgrad_kc(d, rows);
+  const long long nc = wgrad_nc_ub(d, rows, kc);
+  hipLaunchKernelGGL(wgrad_plan_kernel, dim3(1), dim3(1024), 0, s, wsc.plan, a.group_offsets,
+                     a.slot_expert, d.G_res, d.lo_slot, d.e_base, e_res, (long long)rows, kc,
+                     (int)nc);
   WgradParams W;
   W.Pm = (const uint16_t*)d_h;
   W.Qm = (const uint16_t*)a.x_sorted;
   W.C0 = a.dwg;
   W.C1 = a.dwu;
+  W.part = wsc.part;
   W.c_stride = (size_t)d.F * d.H;
   W.I = 2 * d.F;
   W.J = d.H;
   W.i_split = d.F;
-  W.group_offsets = a.group_offsets;
-  W.slot_expert = a.slot_expert;
-  W.G = d.G_res;
-  W.lo_slot = d.lo_slot;
-  W.e_base = d.e_base;
-  W.e_res = e_res;
-  W.max_rows = rows;
+  W.a_rows = (int)rows;
+  W.plan = wsc.plan;
+  W.kc = kc;
+  W.slots = wgrad_slots(rows, kc);
   W.accumulate = a.accumulate;
   W.ni_tiles = W.I / 128;
   W.nj_tiles = W.J / 128;
-  hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)(e_res * W.ni_tiles * W.nj_tiles)), dim3(256),
-                     0, s, W);
-  // dWd = d_out^T act
   WgradParams V = W;
   V.Pm = (const uint16_t*)a.d_out;
   V.Qm = (const uint16_t*)act;
@@ -855,8 +1190,13 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   V.i_split = d.H;
   V.ni_tiles = V.I / 128;
   V.nj_tiles = V.J / 128;
-  hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)(e_res * V.ni_tiles * V.nj_tiles)), dim3(256),
-                     0, s, V);
+  for (const WgradParams* q : {&W, &V}) {
+    hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)(nc * q->ni_tiles * q->nj_tiles)),
+                       dim3(256), 0, s, *q);
+    const long long ij4 = ((long long)q->I * q->J / 4 + 255) / 256;
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)ij4, (unsigned)e_res), dim3(256), 0, s,
+                       *q);
+  }
   return hipGetLastError();
 }
 
