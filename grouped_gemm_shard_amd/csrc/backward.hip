@@ -450,6 +450,7 @@ __global__ __launch_bounds__(256, 2) void dgrad_kernel(DgradParams P) {
 constexpr int kWBK = 32;   // rows per stage
 constexpr int kWNST = 4;   // ring stages
 constexpr int kWMaxRes = 1024;
+constexpr int kWMaxChunks = 2048;
 
 // Per-expert plan of the weight-gradient launches, from the group offsets:
 // the expert's groups in group order (their first row and row count, as a
@@ -467,6 +468,8 @@ struct WgradPlan {
   int* pbase;      // [e_res]
   int* chunk_e;    // [nc_ub]
   int* chunk_i;    // [nc_ub]
+  int* order_e;    // [nc_ub] chunks by row count, longest first (ties: chunk order)
+  int* order_i;    // [nc_ub]
   int* meta;       // [0] chunks in use
 };
 
@@ -521,7 +524,7 @@ __global__ __launch_bounds__(1024) void wgrad_plan_kernel(WgradPlan W, const int
     }
     W.grp_off[e_res] = go;
     cb[e_res] = co;
-    W.meta[0] = co < nc_ub ? co : nc_ub;
+    W.meta[0] = min(min(co, nc_ub), kWMaxChunks);
   }
   __syncthreads();
   for (int e = tid; e < e_res; e += blockDim.x) {
@@ -540,6 +543,25 @@ __global__ __launch_bounds__(1024) void wgrad_plan_kernel(WgradPlan W, const int
   for (int c = cb[e_res] + tid; c < nc_ub; c += blockDim.x) {
     W.chunk_e[c] = -1;
     W.chunk_i[c] = 0;
+  }
+  __syncthreads();
+  // chunks by row count, longest first: a round of the launch then holds
+  // chunks of about the same length on every XCD
+  // (at most e_res + max_rows / kc <= 1024 + 512 chunks: kc >= max_rows/512)
+  __shared__ int len_s[kWMaxChunks];
+  const int nc = min(min(cb[e_res], nc_ub), kWMaxChunks);
+  for (int c = tid; c < nc; c += blockDim.x)
+    len_s[c] = min(kc, rsum[W.chunk_e[c]] - W.chunk_i[c] * kc);
+  __syncthreads();
+  for (int c = tid; c < nc; c += blockDim.x) {
+    const int lc = len_s[c];
+    int rank = 0;
+    for (int o = 0; o < nc; ++o) {
+      const int lo = len_s[o];
+      rank += (lo > lc || (lo == lc && o < c)) ? 1 : 0;
+    }
+    W.order_e[rank] = W.chunk_e[c];
+    W.order_i[rank] = W.chunk_i[c];
   }
 }
 
@@ -639,15 +661,17 @@ __device__ __forceinline__ void wgrad_tile(const WgradParams& P, char* smem, int
   constexpr int LPO = OPB / 1024 / 4;     // loads per wave per operand per stage (2)
   constexpr int LPS = 2 * LPO;
   const int tiles = P.ni_tiles * P.nj_tiles;
-  // units: chunks by tiles, tiles fastest, in block order (measured faster
-  // than the XCD-contiguous order here: a chunk's tiles spread over all
-  // XCDs start together, and the hot experts' chunks come first)
+  // units: chunks (longest first) by tiles, tiles fastest, in block order.
+  // Consecutive blocks go to different XCDs, so each XCD runs a share of
+  // every chunk's tiles.  (Running whole chunks per XCD fetches every row
+  // from HBM once instead of ~4.5 times, but measured 15% slower: an XCD's
+  // workgroups then all read the same rows at once.)
   const int u = blockIdx.x / tiles;
   const int t = blockIdx.x % tiles;
   if (u >= P.plan.meta[0]) return;
-  const int e = P.plan.chunk_e[u];
+  const int e = P.plan.order_e[u];
   if (e < 0) return;
-  const int ci = P.plan.chunk_i[u];
+  const int ci = P.plan.order_i[u];
   const int it = t / P.nj_tiles, jt = t % P.nj_tiles;
   const int i0 = it * 128, j0 = jt * 128;
   const int R = P.plan.rows[e], nch = P.plan.nch[e];
@@ -990,6 +1014,8 @@ WgradScratch carve_wgrad(const Dims& d, int64_t max_rows, char* base) {
   w.plan.pbase = (int*)take((size_t)e_res * 4);
   w.plan.chunk_e = (int*)take((size_t)nc * 4);
   w.plan.chunk_i = (int*)take((size_t)nc * 4);
+  w.plan.order_e = (int*)take((size_t)nc * 4);
+  w.plan.order_i = (int*)take((size_t)nc * 4);
   w.plan.meta = (int*)take(64);
   w.part = (float*)take((size_t)slots * 2 * d.F * d.H * 4);
   w.bytes = o;
