@@ -204,8 +204,7 @@ def kernel_figures(p, w, inp, info, reps):
 
 def backward_figures(p, w, inp, info, reps):
     """The backward of the same passes (the forward's saved x_sorted and
-    expert_out kept): weight transposes once, then per pass the combine's
-    backward, the grouped GEMM's backward (weight gradients carried across
+    expert_out kept): per pass the combine's backward, the grouped GEMM's backward (weight gradients carried across
     the passes) and the permute's backward, then the gates' backward into
     the logits.  Timed as a whole and call by call with HIP events."""
     passes = pass_list(p, info)
@@ -220,11 +219,6 @@ def backward_figures(p, w, inp, info, reps):
         b["d_out"] = torch.empty((b["rows"], H), dtype=p.dtype, device=dev)
         b["dxs"] = torch.empty((b["rows"], H), dtype=p.dtype, device=dev)
         b["bws"] = torch.empty(g.bwd_workspace_bytes(p, b["rows"]), dtype=torch.uint8, device=dev)
-    if w.bf16:
-        wgu_t = torch.empty((w.e_res, H, 2 * F), dtype=p.dtype, device=dev)
-        wd_t = torch.empty((w.e_res, F, H), dtype=p.dtype, device=dev)
-    else:
-        wgu_t = wd_t = None
     dwg = torch.empty((w.e_res, F, H), dtype=torch.float32, device=dev)
     dwu = torch.empty_like(dwg)
     dwd = torch.empty((w.e_res, H, F), dtype=torch.float32, device=dev)
@@ -232,16 +226,12 @@ def backward_figures(p, w, inp, info, reps):
     dx = torch.empty((T, H), dtype=p.dtype, device=dev)
     d_logits = torch.empty((T, E), dtype=torch.float32, device=dev)
 
-    def transpose():
-        if w.bf16:
-            g.moe_transpose_weights(p, wg, wu, wd, wgu_t, wd_t)
-
     def comb(b):
         g.moe_combine_bwd(p, b["n"], b["c"], dy, b["out"], b["roa"], gate, b["d_out"], d_gate)
 
     def gmm(b, acc):
-        g.moe_gmm_swiglu_bwd(p, b["xs"], b["go"], cnt["se"], wg, wu, wd, wgu_t, wd_t,
-                             b["d_out"], b["dxs"], dwg, dwu, dwd, acc, b["bws"])
+        g.moe_gmm_swiglu_bwd(p, b["xs"], b["go"], cnt["se"], wg, wu, wd, b["d_out"], b["dxs"],
+                             dwg, dwu, dwd, acc, b["bws"])
 
     def perm(b):
         g.moe_permute_bwd(p, b["n"], b["c"], b["dxs"], b["roa"], dx)
@@ -250,7 +240,6 @@ def backward_figures(p, w, inp, info, reps):
         g.moe_route_bwd(p, idx, gate, d_gate, d_logits)
 
     def step():
-        transpose()
         for i, b in enumerate(bufs):
             comb(b)
             gmm(b, i > 0)
@@ -259,7 +248,6 @@ def backward_figures(p, w, inp, info, reps):
 
     torch.cuda.synchronize()
     t_step = time_calls(step, reps)
-    t_tr = time_calls(transpose, reps) if w.bf16 else 0.0
     t_cb = sum(time_calls(lambda: comb(b), reps) for b in bufs)
     t_gb = sum(time_calls(lambda: gmm(b, 1), reps) for b in bufs)
     t_pb = sum(time_calls(lambda: perm(b), reps) for b in bufs)
@@ -268,7 +256,7 @@ def backward_figures(p, w, inp, info, reps):
     # d_a (2NHF), gate/up recompute (4NHF), dx_sorted (4NHF), dWg+dWu (4NHF),
     # dWd (2NHF)
     flops = 16.0 * n_rows * H * F
-    return dict(t_step=t_step, t_tr=t_tr, t_cb=t_cb, t_gb=t_gb, t_pb=t_pb, t_rb=t_rb,
+    return dict(t_step=t_step, t_cb=t_cb, t_gb=t_gb, t_pb=t_pb, t_rb=t_rb,
                 flops=flops, rows=n_rows)
 
 
@@ -371,7 +359,6 @@ def main():
                "tokens_s": round(w.tokens / bf["t_step"], 1),
                "gemm_us": round(bf["t_gb"] * 1e6, 2), "gemm_tflops": round(bt, 2),
                "gemm_frac_mfma_peak": round(bt / peak_mm, 4),
-               "transpose_us": round(bf["t_tr"] * 1e6, 2),
                "combine_bwd_us": round(bf["t_cb"] * 1e6, 2),
                "permute_bwd_us": round(bf["t_pb"] * 1e6, 2),
                "route_bwd_us": round(bf["t_rb"] * 1e6, 2), "rows": bf["rows"]}

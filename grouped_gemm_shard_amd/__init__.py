@@ -23,7 +23,7 @@ __all__ = [
     "layer_workspace_bytes", "pass_max_rows", "moe_route", "moe_count_overflow",
     "moe_permute", "moe_gmm_swiglu", "moe_combine", "moe_combine_partial",
     "moe_combine_from_partials", "moe_layer_dropless_chunked", "status_string", "LayerRunner",
-    "bwd_workspace_bytes", "moe_transpose_weights", "moe_combine_bwd", "moe_gmm_swiglu_bwd",
+    "bwd_workspace_bytes", "moe_combine_bwd", "moe_gmm_swiglu_bwd",
     "moe_permute_bwd", "moe_route_bwd",
 ]
 
@@ -35,8 +35,7 @@ EXPORTED = ["moe_workspace_bytes", "moe_pass_max_rows", "moe_layer_workspace_byt
             "moe_layer_chunks_per_pass",
             "moe_route", "moe_count_overflow", "moe_permute", "moe_gmm_swiglu",
             "moe_combine", "moe_combine_partial", "moe_combine_from_partials",
-            "moe_layer_dropless_chunked", "moe_bwd_workspace_bytes", "moe_transpose_weights",
-            "moe_combine_bwd", "moe_gmm_swiglu_bwd", "moe_permute_bwd", "moe_route_bwd",
+            "moe_layer_dropless_chunked", "moe_bwd_workspace_bytes", "moe_combine_bwd", "moe_gmm_swiglu_bwd", "moe_permute_bwd", "moe_route_bwd",
             "moe_status_string"]
 
 lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_shard.so")
@@ -130,10 +129,9 @@ def _load():
         "moe_combine_from_partials": [P, i32, i32, i32, vp, vp, vp, vp, i64, i64, vp],
         "moe_layer_dropless_chunked": [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_bwd_workspace_bytes": [P, i64, ctypes.POINTER(sz)],
-        "moe_transpose_weights": [P, vp, vp, vp, vp, vp, vp],
         "moe_combine_bwd": [P, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp],
-        "moe_gmm_swiglu_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64,
-                               vp, sz, vp],
+        "moe_gmm_swiglu_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, vp, sz,
+                               vp],
         "moe_permute_bwd": [P, i32, i32, vp, vp, vp, i64, vp],
         "moe_route_bwd": [P, vp, vp, vp, vp, vp],
     }
@@ -325,13 +323,6 @@ def bwd_workspace_bytes(p: Problem, max_rows: int) -> int:
     return out.value
 
 
-def moe_transpose_weights(p: Problem, w_gate, w_up, w_down, w_gu_t, w_down_t, stream=None):
-    _check("moe_transpose_weights", _lib().moe_transpose_weights(
-        ctypes.byref(p.c()), _ptr(w_gate, p.dtype, "w_gate"), _ptr(w_up, p.dtype, "w_up"),
-        _ptr(w_down, p.dtype, "w_down"), _ptr(w_gu_t, p.dtype, "w_gu_t"),
-        _ptr(w_down_t, p.dtype, "w_down_t"), _stream(stream)))
-
-
 def moe_combine_bwd(p: Problem, num_chunks, chunk, dy, expert_out, row_of_assign, topk_gate,
                     d_out, d_gate, stream=None):
     """max_rows is the row count of expert_out and d_out (the smaller)."""
@@ -344,10 +335,9 @@ def moe_combine_bwd(p: Problem, num_chunks, chunk, dy, expert_out, row_of_assign
 
 
 def moe_gmm_swiglu_bwd(p: Problem, x_sorted, group_offsets, slot_expert, w_gate, w_up, w_down,
-                       w_gu_t, w_down_t, d_out, dx_sorted, dw_gate, dw_up, dw_down, accumulate,
-                       ws, stream=None):
+                       d_out, dx_sorted, dw_gate, dw_up, dw_down, accumulate, ws, stream=None):
     """max_rows is the row count of x_sorted, d_out and dx_sorted (the
-    smallest).  w_gu_t / w_down_t may be None for float32 problems."""
+    smallest)."""
     w, nb = _ws(ws)
     i32, f32 = torch.int32, torch.float32
     max_rows = min(x_sorted.shape[0], d_out.shape[0], dx_sorted.shape[0])
@@ -355,8 +345,7 @@ def moe_gmm_swiglu_bwd(p: Problem, x_sorted, group_offsets, slot_expert, w_gate,
         ctypes.byref(p.c()), _ptr(x_sorted, p.dtype, "x_sorted"),
         _ptr(group_offsets, i32, "group_offsets"), _ptr(slot_expert, i32, "slot_expert"),
         _ptr(w_gate, p.dtype, "w_gate"), _ptr(w_up, p.dtype, "w_up"),
-        _ptr(w_down, p.dtype, "w_down"), _ptr(w_gu_t, p.dtype, "w_gu_t"),
-        _ptr(w_down_t, p.dtype, "w_down_t"), _ptr(d_out, p.dtype, "d_out"),
+        _ptr(w_down, p.dtype, "w_down"), _ptr(d_out, p.dtype, "d_out"),
         _ptr(dx_sorted, p.dtype, "dx_sorted"), _ptr(dw_gate, f32, "dw_gate"),
         _ptr(dw_up, f32, "dw_up"), _ptr(dw_down, f32, "dw_down"), int(accumulate), max_rows, w,
         nb, _stream(stream)))

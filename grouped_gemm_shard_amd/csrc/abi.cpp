@@ -632,20 +632,6 @@ int moe_bwd_workspace_bytes(const moe_problem* p, int64_t max_rows, size_t* byte
   return MOE_OK;
 }
 
-int moe_transpose_weights(const moe_problem* p, const void* w_gate, const void* w_up,
-                          const void* w_down, void* w_gu_t, void* w_down_t, void* stream) {
-  Dims d;
-  int st = make_dims(p, &d);
-  if (st != MOE_OK) return st;
-  if (!d.bf16) return MOE_EUNSUPPORTED;
-  if (!w_gate || !w_up || !w_down || !w_gu_t || !w_down_t) return MOE_EINVAL;
-  if (misaligned(w_gate, 4) || misaligned(w_up, 4) || misaligned(w_down, 4) ||
-      misaligned(w_gu_t, 4) || misaligned(w_down_t, 4))
-    return MOE_EINVAL;
-  return hip_status(launch_transpose_weights(d, w_gate, w_up, w_down, w_gu_t, w_down_t,
-                                             (hipStream_t)stream));
-}
-
 int moe_combine_bwd(const moe_problem* p, int32_t num_chunks, int32_t chunk, const void* dy,
                     const void* expert_out, const int32_t* row_of_assign,
                     const float* topk_gate, void* d_out, float* d_gate, int64_t max_rows,
@@ -667,10 +653,9 @@ int moe_combine_bwd(const moe_problem* p, int32_t num_chunks, int32_t chunk, con
 
 int moe_gmm_swiglu_bwd(const moe_problem* p, const void* x_sorted, const int32_t* group_offsets,
                        const int32_t* slot_expert, const void* w_gate, const void* w_up,
-                       const void* w_down, const void* w_gu_t, const void* w_down_t,
-                       const void* d_out, void* dx_sorted, float* dw_gate, float* dw_up,
-                       float* dw_down, int32_t accumulate, int64_t max_rows, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       const void* w_down, const void* d_out, void* dx_sorted, float* dw_gate,
+                       float* dw_up, float* dw_down, int32_t accumulate, int64_t max_rows,
+                       void* ws, size_t ws_bytes, void* stream) {
   Dims d;
   int st = make_dims(p, &d);
   if (st != MOE_OK) return st;
@@ -678,11 +663,10 @@ int moe_gmm_swiglu_bwd(const moe_problem* p, const void* x_sorted, const int32_t
       !dx_sorted || !dw_gate || !dw_up || !dw_down || !ws || max_rows < 0 ||
       (accumulate != 0 && accumulate != 1))
     return MOE_EINVAL;
-  if (d.bf16 && (!w_gu_t || !w_down_t)) return MOE_EINVAL;
   if (misaligned(ws, 256) || misaligned(x_sorted, 16) || misaligned(d_out, 16) ||
-      misaligned(w_gate, 16) || misaligned(w_up, 16) || misaligned(w_down, 4) ||
+      misaligned(w_gate, 16) || misaligned(w_up, 16) || misaligned(w_down, 16) ||
       misaligned(dx_sorted, 4) || misaligned(dw_gate, 16) || misaligned(dw_up, 16) ||
-      misaligned(dw_down, 16) || (d.bf16 && (misaligned(w_gu_t, 16) || misaligned(w_down_t, 16))))
+      misaligned(dw_down, 16))
     return MOE_EINVAL;
   // buffer resources address A operands with 32-bit byte offsets
   const int64_t wide = d.H > 2 * d.F ? d.H : 2 * d.F;
@@ -695,8 +679,6 @@ int moe_gmm_swiglu_bwd(const moe_problem* p, const void* x_sorted, const int32_t
   a.wg = w_gate;
   a.wu = w_up;
   a.wd = w_down;
-  a.wgu_t = w_gu_t;
-  a.wd_t = w_down_t;
   a.d_out = d_out;
   a.dx_sorted = dx_sorted;
   a.dwg = dw_gate;

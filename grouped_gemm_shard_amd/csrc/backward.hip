@@ -10,18 +10,18 @@
 //  * combine backward: d_out[row(t,j)] = g_tj dy_t and d_gate[t,j] =
 //    <dy_t, out[row(t,j)]>, one wave per token;
 //  * grouped GEMM backward (bf16, MFMA): with h_g = x Wg^T, h_u = x Wu^T,
-//      d_a  = d_out Wd                          (GEMM, K = H, against Wd^T)
+//      d_a  = d_out Wd                          (GEMM, K = H)
 //      d_hg = d_a h_u SiLU'(h_g), d_hu = d_a SiLU(h_g), a = SiLU(h_g) h_u
 //           (the forward's GEMM1 recomputed, SwiGLU backward in its epilogue)
-//      dx_sorted = [d_hg | d_hu] [Wg ; Wu]      (GEMM, K = 2F, against
-//                                                [Wg ; Wu]^T)
+//      dx_sorted = [d_hg | d_hu] [Wg ; Wu]      (GEMM, K = 2F)
 //      [dWg ; dWu] = [d_hg | d_hu]^T x_sorted,  dWd = d_out^T a
 //                                               (reductions over each
 //                                                expert's ragged rows)
-//    The data-gradient GEMMs read the weights transposed (K contiguous),
-//    made once per weight update by moe_transpose_weights; the
-//    weight-gradient GEMMs reduce over rows, so their operands are
-//    transposed on the way into LDS;
+//    Where an operand is stored with the reduction index as its row (Wd
+//    and Wg/Wu in the d_a and dx GEMMs, both operands of the weight
+//    gradients), its rows are staged in LDS as they are and the MFMA
+//    fragments are read with gfx950's LDS transpose read, so no transposed
+//    copy is ever made;
 //  * permute backward: dx_t = the sum of dx_sorted over the token's rows,
 //    one wave per token;
 //  * gate backward into the logits, one wave per token.
@@ -167,29 +167,6 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Dims d, const int* idx, 
   }
 }
 
-// ---- weight transposes -----------------------------------------------------
-
-// out[e][c][col0 + r] = in[e][r][c] for 64 x 64 tiles (R, C multiples of 64).
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* in, uint16_t* out, int R,
-                                                        int C, long long in_e, long long out_e,
-                                                        int ldo, int col0) {
-  __shared__ uint16_t tile[64][66];
-  const int ct = blockIdx.x, rt = blockIdx.y, e = blockIdx.z;
-  const uint16_t* src = in + (size_t)e * in_e + (size_t)rt * 64 * C + (size_t)ct * 64;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-  for (int r = ty; r < 64; r += 8) {
-    const uint32_t w = *(const uint32_t*)(src + (size_t)r * C + tx * 2);
-    tile[r][tx * 2] = (uint16_t)(w & 0xFFFF);
-    tile[r][tx * 2 + 1] = (uint16_t)(w >> 16);
-  }
-  __syncthreads();
-  uint16_t* dst = out + (size_t)e * out_e + (size_t)ct * 64 * ldo + col0 + (size_t)rt * 64;
-  for (int c = ty; c < 64; c += 8) {
-    const uint32_t w = (uint32_t)tile[tx * 2][c] | ((uint32_t)tile[tx * 2 + 1][c] << 16);
-    *(uint32_t*)(dst + (size_t)c * ldo + tx * 2) = w;
-  }
-}
-
 // ---- m-tiles of the data-gradient GEMMs ------------------------------------
 
 constexpr int kBM = 128;  // rows per tile
@@ -265,6 +242,47 @@ __device__ __forceinline__ int xcd_unit(int nb, int total) {
   return L < rbase + ((x + 1) * rs >> 3) ? L : -1;
 }
 
+// 16-byte chunk permutation of a 256-byte LDS row (16 chunks): the
+// transpose reads of 4 consecutive rows at one column land on disjoint
+// 64-byte bank windows.
+__device__ __forceinline__ int wswz(int row) { return (row & 3) << 2; }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// ds_read_b64_tr_b16 as inline asm: the compiler cannot tell that the
+// builtin's LDS read does not alias the ring's in-flight buffer loads into
+// LDS, and waits for all of them before it; here the ring's own barrier
+// already guarantees the stage being read has landed.  The result is
+// pending until lgkm_wait_tie.
+__device__ __forceinline__ void lds_read_tr16(v4i16& r, unsigned addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+}
+
+// Waits until at most N LDS reads of this wave are outstanding; the
+// registers of one slice are tied to the wait so their uses stay after it.
+template <int N>
+__device__ __forceinline__ void lgkm_wait_tie(v4i16 (&a)[2][2], v4i16 (&b)[2][2]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[1][0]), "+v"(a[1][1]), "+v"(b[0][0]),
+                 "+v"(b[0][1]), "+v"(b[1][0]), "+v"(b[1][1])
+               : "n"(N));
+}
+
+__device__ __forceinline__ void lgkm_wait_tie(v4i16 (&b)[2][2]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0][0]), "+v"(b[0][1]), "+v"(b[1][0]), "+v"(b[1][1]));
+}
+
+__device__ __forceinline__ bf16x8 join8(const v4i16& lo, const v4i16& hi) {
+  bf16x8 v;
+  __builtin_memcpy(&v, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&v) + 8, &hi, 8);
+  return v;
+}
+
 struct DgradParams {
   const uint16_t* A;        // [a_rows, K] rows of the pass
   int a_rows;
@@ -280,6 +298,7 @@ struct DgradParams {
   const int* slot_expert;
   int G, K, Nout, lo_slot, e_base, e_res, n_ntiles;
   int round_blocks;         // blocks per round (xcd_unit)
+  int k_split;              // reduction-major B: rows [0, k_split) from B0, the rest from B1
   long long max_rows;
 };
 
@@ -435,6 +454,156 @@ __device__ __forceinline__ void dgrad_tile(const DgradParams& P) {
 template <bool SW>
 __global__ __launch_bounds__(256, 2) void dgrad_kernel(DgradParams P) {
   dgrad_tile<SW>(P);
+}
+
+// Plain tile C = A B with B stored reduction-major, [K][Nout] per expert
+// (the weights as they are: Wd [H, F] for d_a = d_out Wd, and Wg, Wu
+// [F, H] stacked along K for dx = d_hg Wg + d_hu Wu), so no transposed
+// copy is needed.  A stages as in dgrad_tile; B stages 32 reduction rows of
+// the tile's 128 columns (256 bytes each), and its fragments come from
+// ds_read_b64_tr_b16, which hands each lane 4 consecutive reduction rows of
+// one column (the same reads as the weight-gradient kernel).
+__device__ __forceinline__ void dgrad_kmajor_tile(const DgradParams& P) {
+  constexpr int RB = kBK * 2;                  // A: 64 bytes per row per stage
+  constexpr int CPR = kBK / 8;
+  constexpr int RPI = 1024 / RB;
+  constexpr int AI = kBM / RPI / 4;            // 2
+  constexpr int BRB = kBN * 2;                 // B: 256 bytes per reduction row
+  constexpr int BI = kBK * BRB / 1024 / 4;     // 2
+  constexpr int LPS = AI + BI;
+  constexpr int SA = kBM * RB, SS = SA + kBK * BRB;
+  __shared__ __attribute__((aligned(1024))) char smem[kNST * SS];
+
+  const int total = P.tile_off[P.G];
+  const int unit = xcd_unit(P.round_blocks, total * P.n_ntiles);
+  if (unit < 0) return;
+  const int nt = unit % P.n_ntiles;
+  const int m = unit / P.n_ntiles;
+  if (m >= total) return;
+  int lo = 0, hi = P.G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (P.tile_off[mid] <= m) lo = mid;
+    else hi = mid;
+  }
+  const int g = lo;
+  const int gend = P.group_offsets[g + 1];
+  const int row0 = P.group_offsets[g] + (m - P.tile_off[g]) * kBM;
+  if (row0 < 0 || row0 >= gend || gend > P.max_rows) return;
+  const int rows = min(kBM, gend - row0);
+  const int e = P.slot_expert[P.lo_slot + g] - P.e_base;
+  if (e < 0 || e >= P.e_res) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int K = P.K, KT = K / kBK;
+  const __amdgpu_buffer_rsrc_t ra = raw_rsrc(P.A, (unsigned)P.a_rows * K * 2);
+  const __amdgpu_buffer_rsrc_t rb0 =
+      raw_rsrc(P.B0 + (size_t)e * P.b_stride, (unsigned)P.k_split * P.Nout * 2);
+  const __amdgpu_buffer_rsrc_t rb1 =
+      raw_rsrc(P.B1 + (size_t)e * P.b_stride, (unsigned)(K - P.k_split) * P.Nout * 2);
+  int a_off[AI], b_off[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int row = (i * 4 + w) * RPI + lane / CPR;
+    a_off[i] = row < rows ? (row0 + row) * K * 2 + (((lane % CPR) ^ swz4(row)) << 4)
+                          : (int)0x80000000;
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int kr = (i * 4 + w) * 4 + (lane >> 4);  // reduction row within the stage
+    b_off[i] = kr * P.Nout * 2 + nt * kBN * 2 + (((lane & 15) ^ wswz(kr)) << 4);
+  }
+  auto issue = [&](int step) {
+    char* st = smem + (step % kNST) * SS;
+    const int k0 = step * kBK;
+#pragma unroll
+    for (int i = 0; i < AI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (i * 4 + w) * RPI * RB), 16,
+                                               a_off[i], k0 * 2, 0, 0);
+    // a stage's 32 reduction rows lie in one of the two stacked matrices
+    const bool second = k0 >= P.k_split;
+    const int kb = (second ? k0 - P.k_split : k0) * P.Nout * 2;
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? rb1 : rb0,
+                                               (lds_void*)(st + SA + (i * 4 + w) * 1024), 16,
+                                               b_off[i], kb, 0, 0);
+  };
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.0f;
+  int a_row[2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) a_row[mi] = wm * 64 + mi * 32 + (lane & 31);
+  // transpose-read offsets of B (see wgrad_tile)
+  const int G4 = lane >> 4, s4 = lane & 15;
+  const int trow = 8 * (G4 >> 1) + (s4 >> 2);
+  const int tcol = 16 * (G4 & 1) + 4 * (s4 & 3);
+  unsigned b_tr[2];
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) {
+    const int c = wn * 64 + ni * 32 + tcol;
+    b_tr[ni] = SA + trow * BRB + (((c >> 3) ^ wswz(trow)) << 4) + (c & 7) * 2;
+  }
+  const unsigned lds0 = lds_addr(smem);
+
+#pragma unroll
+  for (int s0 = 0; s0 < kNST - 1; ++s0)
+    if (s0 < KT) issue(s0);
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 1 < KT) wait_vm_barrier<LPS>();
+    else wait_vm_barrier<0>();
+    if (kt + kNST - 1 < KT) issue(kt + kNST - 1);
+    const char* sa = smem + (kt % kNST) * SS;
+    const unsigned st = lds0 + (kt % kNST) * SS;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      v4i16 rb[2][2];
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          lds_read_tr16(rb[ni][h], st + b_tr[ni] + (ks * 16 + 4 * h) * BRB);
+      const int kc = ks * 2 + (lane >> 5);
+      bf16x8 a[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+        a[mi] = *(const bf16x8*)(sa + a_row[mi] * RB + ((kc ^ swz4(a_row[mi])) << 4));
+      lgkm_wait_tie(rb);
+      bf16x8 b[2];
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) b[ni] = join8(rb[ni][0], rb[ni][1]);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int lr = wm * 64 + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+      if (lr >= rows) continue;
+      const size_t r = (size_t)(row0 + lr);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int c = nt * kBN + wn * 64 + ni * 32 + (lane & 31);
+        P.C[r * P.Nout + c] = f2bf(acc[mi][ni][q]);
+      }
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void dgrad_kmajor_kernel(DgradParams P) {
+  dgrad_kmajor_tile(P);
 }
 
 // ---- weight-gradient GEMM --------------------------------------------------
@@ -595,42 +764,6 @@ __device__ __forceinline__ int wgrad_row(const int* gl, int ng, int p, int& cur,
   return cur < ng ? gl[cur] + (p - base) : -1;
 }
 
-// 16-byte chunk permutation of a 256-byte LDS row (16 chunks): the
-// transpose reads of 4 consecutive rows at one column land on disjoint
-// 64-byte bank windows.
-__device__ __forceinline__ int wswz(int row) { return (row & 3) << 2; }
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return (unsigned)(size_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// ds_read_b64_tr_b16 as inline asm: the compiler cannot tell that the
-// builtin's LDS read does not alias the ring's in-flight buffer loads into
-// LDS, and waits for all of them before it; here the ring's own barrier
-// already guarantees the stage being read has landed.  The result is
-// pending until lgkm_wait_tie.
-__device__ __forceinline__ void lds_read_tr16(v4i16& r, unsigned addr) {
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
-}
-
-// Waits until at most N LDS reads of this wave are outstanding; the
-// registers of one slice are tied to the wait so their uses stay after it.
-template <int N>
-__device__ __forceinline__ void lgkm_wait_tie(v4i16 (&a)[2][2], v4i16 (&b)[2][2]) {
-  asm volatile("s_waitcnt lgkmcnt(%8)"
-               : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[1][0]), "+v"(a[1][1]), "+v"(b[0][0]),
-                 "+v"(b[0][1]), "+v"(b[1][0]), "+v"(b[1][1])
-               : "n"(N));
-}
-
-__device__ __forceinline__ bf16x8 join8(const v4i16& lo, const v4i16& hi) {
-  bf16x8 v;
-  __builtin_memcpy(&v, &lo, 8);
-  __builtin_memcpy(reinterpret_cast<char*>(&v) + 8, &hi, 8);
-  return v;
-}
 
 // The 4 MFMAs of one 16-row slice (2 x 2 tiles of 32 x 32).
 __device__ __forceinline__ void mma_slice(const v4i16 (&a)[2][2], const v4i16 (&b)[2][2],
@@ -1032,23 +1165,6 @@ size_t gmm_bwd_scratch_bytes(const Dims& d, int64_t max_rows) {
   return b;
 }
 
-hipError_t launch_transpose_weights(const Dims& d, const void* wg, const void* wu,
-                                    const void* wd, void* wgu_t, void* wd_t, hipStream_t s) {
-  const int e_res = d.S_res * d.El;
-  // [E,F,H] gate / up -> [E,H,2F] (gate in columns [0,F), up in [F,2F))
-  hipLaunchKernelGGL(transpose_kernel, dim3(d.H / 64, d.F / 64, e_res), dim3(256), 0, s,
-                     (const uint16_t*)wg, (uint16_t*)wgu_t, d.F, d.H, (long long)d.F * d.H,
-                     (long long)d.H * 2 * d.F, 2 * d.F, 0);
-  hipLaunchKernelGGL(transpose_kernel, dim3(d.H / 64, d.F / 64, e_res), dim3(256), 0, s,
-                     (const uint16_t*)wu, (uint16_t*)wgu_t, d.F, d.H, (long long)d.F * d.H,
-                     (long long)d.H * 2 * d.F, 2 * d.F, d.F);
-  // [E,H,F] down -> [E,F,H]
-  hipLaunchKernelGGL(transpose_kernel, dim3(d.F / 64, d.H / 64, e_res), dim3(256), 0, s,
-                     (const uint16_t*)wd, (uint16_t*)wd_t, d.H, d.F, (long long)d.H * d.F,
-                     (long long)d.F * d.H, d.H, 0);
-  return hipGetLastError();
-}
-
 hipError_t launch_combine_bwd(const Dims& d, const PassArgs& pa, const void* dy,
                               const void* out, const int* roa, const float* gate, void* d_out,
                               float* d_gate, int64_t max_rows, hipStream_t s) {
@@ -1145,24 +1261,29 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   P.d_a = nullptr;
   P.d_h = nullptr;
   P.act = nullptr;
-  // d_a = d_out Wd  (K = H, against Wd^T [F, H])
+  // d_a = d_out Wd  (K = H; Wd [H, F] read reduction-major)
+  const int nb_km = bwd_round_blocks(reinterpret_cast<const void*>(dgrad_kmajor_kernel), 256, 0);
+  const int nb_sw = bwd_round_blocks(reinterpret_cast<const void*>(dgrad_kernel<true>), 256, 1);
   P.A = (const uint16_t*)a.d_out;
-  P.B0 = P.B1 = (const uint16_t*)a.wd_t;
-  P.b_stride = (size_t)d.F * d.H;
+  P.B0 = P.B1 = (const uint16_t*)a.wd;
+  P.b_stride = (size_t)d.H * d.F;
   P.C = (uint16_t*)d_a;
   P.K = d.H;
+  P.k_split = d.H;
   P.Nout = d.F;
   P.n_ntiles = d.F / kBN;
-  const int nb_plain = bwd_round_blocks(reinterpret_cast<const void*>(dgrad_kernel<false>), 256, 0);
-  const int nb_sw = bwd_round_blocks(reinterpret_cast<const void*>(dgrad_kernel<true>), 256, 1);
-  P.round_blocks = nb_plain;
-  hipLaunchKernelGGL(dgrad_kernel<false>, dim3(whole_rounds(mt_ub * P.n_ntiles, nb_plain)),
+  P.round_blocks = nb_km;
+  hipLaunchKernelGGL(dgrad_kmajor_kernel, dim3(whole_rounds(mt_ub * P.n_ntiles, nb_km)),
                      dim3(256), 0, s, P);
   // gate and up products recomputed; SwiGLU backward and the activation
   DgradParams Q = P;
   Q.A = (const uint16_t*)a.x_sorted;
   Q.B0 = (const uint16_t*)a.wg;
   Q.B1 = (const uint16_t*)a.wu;
+  Q.b_stride = (size_t)d.F * d.H;
+  Q.K = d.H;
+  Q.Nout = d.F;
+  Q.n_ntiles = d.F / kBN;
   Q.C = nullptr;
   Q.d_a = (const uint16_t*)d_a;
   Q.d_h = (uint16_t*)d_h;
@@ -1170,16 +1291,19 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   Q.round_blocks = nb_sw;
   hipLaunchKernelGGL(dgrad_kernel<true>, dim3(whole_rounds(mt_ub * Q.n_ntiles, nb_sw)),
                      dim3(256), 0, s, Q);
-  // dx_sorted = [d_hg | d_hu] [Wg ; Wu]  (K = 2F, against [Wg ; Wu]^T [H, 2F])
+  // dx_sorted = [d_hg | d_hu] [Wg ; Wu]  (K = 2F; Wg and Wu [F, H] stacked
+  // along the reduction and read reduction-major)
   DgradParams X = P;
   X.A = (const uint16_t*)d_h;
-  X.B0 = X.B1 = (const uint16_t*)a.wgu_t;
-  X.b_stride = (size_t)d.H * 2 * d.F;
+  X.B0 = (const uint16_t*)a.wg;
+  X.B1 = (const uint16_t*)a.wu;
+  X.b_stride = (size_t)d.F * d.H;
   X.C = (uint16_t*)a.dx_sorted;
   X.K = 2 * d.F;
+  X.k_split = d.F;
   X.Nout = d.H;
   X.n_ntiles = d.H / kBN;
-  hipLaunchKernelGGL(dgrad_kernel<false>, dim3(whole_rounds(mt_ub * X.n_ntiles, nb_plain)),
+  hipLaunchKernelGGL(dgrad_kmajor_kernel, dim3(whole_rounds(mt_ub * X.n_ntiles, nb_km)),
                      dim3(256), 0, s, X);
   // weight gradients: plan (rows and chunks per expert), then
   // [dWg ; dWu] = [d_hg | d_hu]^T x_sorted and dWd = d_out^T act, each with

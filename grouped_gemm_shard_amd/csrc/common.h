@@ -332,10 +332,9 @@ hipError_t launch_combine(const Dims& d, const PassArgs& pa, const LayoutSet& ls
 
 // ---- backward ---------------------------------------------------------------
 
-// Grouped-GEMM backward of one pass (bf16: transposed weights wgu_t
-// [E_res, H, 2F] and wd_t [E_res, F, H] from launch_transpose_weights; fp32:
-// the weights themselves).  Weight gradients are float32, overwritten or
-// (accumulate) added to.  scratch holds gmm_bwd_scratch_bytes(d, max_rows).
+// Grouped-GEMM backward of one pass.  Weight gradients are float32,
+// overwritten or (accumulate) added to.  scratch holds
+// gmm_bwd_scratch_bytes(d, max_rows).
 struct GemmBwdArgs {
   const void* x_sorted;
   const int* group_offsets;
@@ -343,8 +342,6 @@ struct GemmBwdArgs {
   const void* wg;
   const void* wu;
   const void* wd;
-  const void* wgu_t;
-  const void* wd_t;
   const void* d_out;
   void* dx_sorted;
   float* dwg;
@@ -356,8 +353,6 @@ struct GemmBwdArgs {
 };
 size_t gmm_bwd_scratch_bytes(const Dims& d, int64_t max_rows);
 hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s);
-hipError_t launch_transpose_weights(const Dims& d, const void* wg, const void* wu,
-                                    const void* wd, void* wgu_t, void* wd_t, hipStream_t s);
 hipError_t launch_combine_bwd(const Dims& d, const PassArgs& pa, const void* dy,
                               const void* out, const int* roa, const float* gate, void* d_out,
                               float* d_gate, int64_t max_rows, hipStream_t s);

@@ -285,15 +285,6 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
 /* Scratch bytes of moe_gmm_swiglu_bwd for `max_rows` pass rows. */
 int moe_bwd_workspace_bytes(const moe_problem* p, int64_t max_rows, size_t* bytes);
 
-/* Transposed weight copies the bf16 data-gradient GEMMs read (reduction
- * dimension contiguous), made once per weight update:
- *   w_gu_t   [E_res, H, 2F]  w_gu_t[e][h][f] = w_gate[e][f][h],
- *                            w_gu_t[e][h][F+f] = w_up[e][f][h];
- *   w_down_t [E_res, F, H]   w_down_t[e][f][h] = w_down[e][h][f].
- * MOE_EUNSUPPORTED for MOE_F32 (that path reads the weights directly). */
-int moe_transpose_weights(const moe_problem* p, const void* w_gate, const void* w_up,
-                          const void* w_down, void* w_gu_t, void* w_down_t, void* stream);
-
 /* Backward of moe_combine for the tokens of chunk `chunk` of num_chunks:
  * for each assignment (t, j) with a row r = row_of_assign[t*k+j] in
  * [0, max_rows),
@@ -317,16 +308,15 @@ int moe_combine_bwd(const moe_problem* p, int32_t num_chunks, int32_t chunk, con
  * summed over every row of every group of expert e (float32).  accumulate
  * 0 overwrites the weight gradients (experts without rows get 0), 1 adds
  * to them (the carry across passes).  d_a, d_hg, d_hu and a are rounded to
- * the activation dtype where they are stored (in ws).  bf16 needs w_gu_t
- * and w_down_t from moe_transpose_weights; fp32 ignores them.  Rows of
- * dx_sorted past group_offsets[G_res] are untouched.  ws holds
- * moe_bwd_workspace_bytes(p, max_rows). */
+ * the activation dtype where they are stored (in ws).  The weights are
+ * read as they are (no transposed copies).  Rows of dx_sorted past
+ * group_offsets[G_res] are untouched.  ws holds moe_bwd_workspace_bytes(p,
+ * max_rows); the weight gradients are 16-byte aligned. */
 int moe_gmm_swiglu_bwd(const moe_problem* p, const void* x_sorted, const int32_t* group_offsets,
                        const int32_t* slot_expert, const void* w_gate, const void* w_up,
-                       const void* w_down, const void* w_gu_t, const void* w_down_t,
-                       const void* d_out, void* dx_sorted, float* dw_gate, float* dw_up,
-                       float* dw_down, int32_t accumulate, int64_t max_rows, void* ws,
-                       size_t ws_bytes, void* stream);
+                       const void* w_down, const void* d_out, void* dx_sorted, float* dw_gate,
+                       float* dw_up, float* dw_down, int32_t accumulate, int64_t max_rows,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of moe_permute for the tokens of chunk `chunk` of num_chunks:
  *   dx[t] = sum over j ascending of dx_sorted[row_of_assign[t*k+j]]

@@ -183,13 +183,13 @@ def test_backward_entry_points_validate_on_the_host():
     # scratch: tile offsets, d_a, d_hg|d_hu and the recomputed activation,
     # 4F bf16 values per row
     assert need >= rows * 4 * 512 * 2
-    gmm = lambda cc, acc, mr, ws, nb, wt=fake: g.lib.moe_gmm_swiglu_bwd(  # noqa: E731
-        ctypes.byref(cc), fake, fake, fake, fake, fake, fake, wt, wt, fake, fake, fake, fake, fake,
-        acc, mr, ws, nb, None)
+    gmm = lambda cc, acc, mr, ws, nb, wd=fake: g.lib.moe_gmm_swiglu_bwd(  # noqa: E731
+        ctypes.byref(cc), fake, fake, fake, fake, fake, wd, fake, fake, fake, fake, fake, acc, mr,
+        ws, nb, None)
     assert gmm(c, 0, rows, None, need) == -1          # no workspace
     assert gmm(c, 2, rows, fake, need) == -1          # accumulate is 0 or 1
     assert gmm(c, 0, -1, fake, need) == -1            # negative rows
-    assert gmm(c, 0, rows, fake, need, None) == -1    # bf16 needs the transposed weights
+    assert gmm(c, 0, rows, fake, need, None) == -1    # no down weights
     assert gmm(c, 0, rows, ctypes.c_void_p(128), need) == -1  # ws alignment
     assert gmm(c, 0, rows, fake, need - 1) == -3      # workspace too small
     # 32-bit buffer offsets: rows * max(H, 2F) * 2 bytes must stay below 2^31
@@ -200,9 +200,3 @@ def test_backward_entry_points_validate_on_the_host():
                                  fake, fake, rows, None) == -1
     assert g.lib.moe_permute_bwd(ctypes.byref(c), 1, 0, None, fake, fake, rows, None) == -1
     assert g.lib.moe_route_bwd(ctypes.byref(c), fake, None, fake, fake, None) == -1
-    assert g.lib.moe_transpose_weights(ctypes.byref(c), fake, fake, fake, None, fake, None) == -1
-    fp = problem(hidden=64, ffn=64)
-    fc = fp.c()
-    fc.dtype = 0  # float32 reads the weights directly: no transposed copies
-    assert g.lib.moe_transpose_weights(ctypes.byref(fc), fake, fake, fake, fake, fake,
-                                       None) == -2

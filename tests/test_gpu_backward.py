@@ -1,5 +1,5 @@
-"""GPU parity of the backward (moe_combine_bwd, moe_transpose_weights,
-moe_gmm_swiglu_bwd, moe_permute_bwd, moe_route_bwd) through the C ABI.
+"""GPU parity of the backward (moe_combine_bwd, moe_gmm_swiglu_bwd,
+moe_permute_bwd, moe_route_bwd) through the C ABI.
 
 Each case runs the forward's steps and the backward's steps pass by pass,
 as a caller of the step API would (the passes the GPU's own overflow flag
@@ -55,12 +55,6 @@ def gpu_backward(g, w, mode, inp, dy):
     rows, drows = g.pass_max_rows(p, n, capped)
     e_res = w.e_res
     wg, wu, wd = inp["weights"]
-    if w.bf16:
-        wgu_t = torch.empty((e_res, H, 2 * F), dtype=p.dtype, device="cuda")
-        wd_t = torch.empty((e_res, F, H), dtype=p.dtype, device="cuda")
-        g.moe_transpose_weights(p, wg, wu, wd, wgu_t, wd_t)
-    else:
-        wgu_t = wd_t = None
     nan = float("nan")
     dwg = torch.full((e_res, F, H), nan, dtype=torch.float32, device="cuda")
     dwu = torch.full((e_res, F, H), nan, dtype=torch.float32, device="cuda")
@@ -83,8 +77,7 @@ def gpu_backward(g, w, mode, inp, dy):
         d_out = torch.zeros((rows, H), dtype=p.dtype, device="cuda")
         g.moe_combine_bwd(p, n, c, dy, out, roa, gate, d_out, d_gate)
         dxs = torch.zeros((rows, H), dtype=p.dtype, device="cuda")
-        g.moe_gmm_swiglu_bwd(p, xs, go, se, wg, wu, wd, wgu_t, wd_t, d_out, dxs, dwg, dwu, dwd,
-                             c > 0, bws)
+        g.moe_gmm_swiglu_bwd(p, xs, go, se, wg, wu, wd, d_out, dxs, dwg, dwu, dwd, c > 0, bws)
         g.moe_permute_bwd(p, n, c, dxs, roa, dx)
     d_logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
     g.moe_route_bwd(p, idx, gate, d_gate, d_logits)
