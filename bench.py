@@ -256,8 +256,24 @@ def backward_figures(p, w, inp, info, reps):
     # d_a (2NHF), gate/up recompute (4NHF), dx_sorted (4NHF), dWg+dWu (4NHF),
     # dWd (2NHF)
     flops = 16.0 * n_rows * H * F
+    # algorithmic bytes of the grouped-GEMM backward calls (the timed ones
+    # accumulate): per launch, its operands once and its outputs once.
+    # x_sorted and d_out are read twice (recompute / d_a, then the weight
+    # gradients), Wg and Wu twice (recompute, dx) and Wd once for every
+    # expert with rows in the pass; d_a written and read, d_h written and
+    # read twice, act written and read, dx_sorted written; the float32
+    # weight gradients of the resident experts read and written.
+    es = 2 if w.bf16 else 4
+    se = cnt["se"].cpu().numpy()
+    w_bytes = 0
+    for b in bufs:
+        go = b["go"].cpu().numpy()
+        used = {int(se[w.res_lo * p.spd + q]) for q in range(p.g_res) if go[q + 1] > go[q]}
+        w_bytes += len(used) * 5 * H * F * es
+    row_bytes = n_rows * (4 * H + 2 * F + 6 * F + 2 * F + H) * es
+    dw_bytes = len(bufs) * 2 * w.e_res * 3 * H * F * 4
     return dict(t_step=t_step, t_cb=t_cb, t_gb=t_gb, t_pb=t_pb, t_rb=t_rb,
-                flops=flops, rows=n_rows)
+                flops=flops, rows=n_rows, gemm_bytes=w_bytes + row_bytes + dw_bytes)
 
 
 def workloads_pass_tokens(w, n, c):
@@ -355,13 +371,25 @@ def main():
         log("[bench] backward timing")
         bf = backward_figures(p, w, inp, info, args.kernel_reps)
         bt = bf["flops"] / bf["t_gb"] / 1e12
+        bgbs = bf["gemm_bytes"] / bf["t_gb"] / 1e9
+        bai = bf["flops"] / bf["gemm_bytes"]
+        if bai * PEAK_HBM_GBS / 1e3 >= peak_mm:
+            broof = dict(bound="mfma", achieved=round(bt, 2), peak=peak_mm, unit="TFLOP/s",
+                         frac=round(bt / peak_mm, 4))
+        else:
+            broof = dict(bound="hbm", achieved=round(bgbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                         frac=round(bgbs / PEAK_HBM_GBS, 4))
+        broof.update(traffic=None, arith_intensity=round(bai, 1),
+                     kernel="grouped-GEMM backward call (d_a, gate/up recompute, dx_sorted, "
+                            "weight gradients; accumulating)")
         bwd = {"us_per_layer": round(bf["t_step"] * 1e6, 2),
                "tokens_s": round(w.tokens / bf["t_step"], 1),
                "gemm_us": round(bf["t_gb"] * 1e6, 2), "gemm_tflops": round(bt, 2),
                "gemm_frac_mfma_peak": round(bt / peak_mm, 4),
                "combine_bwd_us": round(bf["t_cb"] * 1e6, 2),
                "permute_bwd_us": round(bf["t_pb"] * 1e6, 2),
-               "route_bwd_us": round(bf["t_rb"] * 1e6, 2), "rows": bf["rows"]}
+               "route_bwd_us": round(bf["t_rb"] * 1e6, 2), "rows": bf["rows"],
+               "roofline": broof}
 
     if args.calib_copy:
         log("[bench] calibration copy: 1 GiB device-to-device, 3 times")

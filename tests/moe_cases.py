@@ -78,6 +78,27 @@ def check_close(got, ref, what=""):
     return rel, mean
 
 
+def check_close_grad(got, ref, what=""):
+    """The layer's tolerance for a gradient.  Gradients are linear in the
+    upstream gradient dy, whose scale is arbitrary, so both bounds are taken
+    relative to the reference's largest magnitude: max |diff| / max |ref| <=
+    2e-2 (as for the outputs) and mean |diff| / max |ref| <= 1e-3 (the
+    outputs' mean-abs bound, made scale-free)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    if ref.size == 0:
+        return 0.0, 0.0
+    diff = np.abs(got - ref)
+    scale = float(np.max(np.abs(ref)))
+    scale = scale if scale > 0 else 1.0
+    rel = float(np.max(diff)) / scale
+    mean = float(np.mean(diff)) / scale
+    assert rel <= MAX_REL, f"{what}: max rel {rel:.3e} > {MAX_REL}"
+    assert mean <= MEAN_ABS, f"{what}: mean abs / max |ref| {mean:.3e} > {MEAN_ABS}"
+    return rel, mean
+
+
 class LazyExperts:
     """w[e] -> float64 host copy of one resident expert's matrix, fetched on
     demand so that full-size weights never sit on the host all at once."""
