@@ -15,7 +15,9 @@ After the timed steps, the grouped GEMM, the permute and the combine of the
 same passes are timed one call at a time with HIP events on the stream they
 run on, to give achieved TFLOP/s and GB/s against MI355X peaks.  The
 backward of the same passes (given the forward's saved x_sorted and expert
-outputs) is timed as a whole and step by step ("backward" in the JSON).  The CPU
+outputs) is timed as a whole and step by step ("backward" in the JSON), and so is
+the whole-layer backward call (which also recomputes the routing, layouts,
+x_sorted and expert outputs) and a training step's layer forward plus it.  The CPU
 oracle is then timed on the host cores on the same inputs.  One JSON line is
 printed at the end.
 """
@@ -370,6 +372,13 @@ def main():
     if not args.no_backward:
         log("[bench] backward timing")
         bf = backward_figures(p, w, inp, info, args.kernel_reps)
+        # the whole layer's backward in one call: routing, layouts, x_sorted
+        # and the expert outputs recomputed, then every pass's backward
+        brun = g.LayerBackwardRunner(p, g.MODE_LAYER)
+        dy = workloads.make_dy(w, device="cuda")
+        t_layer_bwd = time_calls(lambda: brun(inp["x"], inp["logits"], *inp["weights"], dy),
+                                 args.kernel_reps)
+        del brun
         bt = bf["flops"] / bf["t_gb"] / 1e12
         bgbs = bf["gemm_bytes"] / bf["t_gb"] / 1e9
         bai = bf["flops"] / bf["gemm_bytes"]
@@ -382,7 +391,9 @@ def main():
         broof.update(traffic=None, arith_intensity=round(bai, 1),
                      kernel="grouped-GEMM backward call (d_a, gate/up recompute, dx_sorted, "
                             "weight gradients; accumulating)")
-        bwd = {"us_per_layer": round(bf["t_step"] * 1e6, 2),
+        bwd = {"layer_call_us": round(t_layer_bwd * 1e6, 2),
+               "train_step_us": round((ms / 1e3 + t_layer_bwd) * 1e6, 2),
+               "us_per_layer": round(bf["t_step"] * 1e6, 2),
                "tokens_s": round(w.tokens / bf["t_step"], 1),
                "gemm_us": round(bf["t_gb"] * 1e6, 2), "gemm_tflops": round(bt, 2),
                "gemm_frac_mfma_peak": round(bt / peak_mm, 4),

@@ -24,7 +24,8 @@ __all__ = [
     "moe_permute", "moe_gmm_swiglu", "moe_combine", "moe_combine_partial",
     "moe_combine_from_partials", "moe_layer_dropless_chunked", "status_string", "LayerRunner",
     "bwd_workspace_bytes", "moe_combine_bwd", "moe_gmm_swiglu_bwd",
-    "moe_permute_bwd", "moe_route_bwd",
+    "moe_permute_bwd", "moe_route_bwd", "layer_bwd_workspace_bytes", "moe_layer_bwd",
+    "LayerBackwardRunner",
 ]
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EHIP = 0, -1, -2, -3, -4
@@ -35,8 +36,9 @@ EXPORTED = ["moe_workspace_bytes", "moe_pass_max_rows", "moe_layer_workspace_byt
             "moe_layer_chunks_per_pass",
             "moe_route", "moe_count_overflow", "moe_permute", "moe_gmm_swiglu",
             "moe_combine", "moe_combine_partial", "moe_combine_from_partials",
-            "moe_layer_dropless_chunked", "moe_bwd_workspace_bytes", "moe_combine_bwd", "moe_gmm_swiglu_bwd", "moe_permute_bwd", "moe_route_bwd",
-            "moe_status_string"]
+            "moe_layer_dropless_chunked", "moe_bwd_workspace_bytes", "moe_combine_bwd",
+            "moe_gmm_swiglu_bwd", "moe_permute_bwd", "moe_route_bwd",
+            "moe_layer_bwd_workspace_bytes", "moe_layer_bwd", "moe_status_string"]
 
 lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_shard.so")
 
@@ -134,6 +136,8 @@ def _load():
                                vp],
         "moe_permute_bwd": [P, i32, i32, vp, vp, vp, i64, vp],
         "moe_route_bwd": [P, vp, vp, vp, vp, vp],
+        "moe_layer_bwd_workspace_bytes": [P, i32, ctypes.POINTER(sz)],
+        "moe_layer_bwd": [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -363,6 +367,48 @@ def moe_route_bwd(p: Problem, topk_idx, topk_gate, d_gate, d_logits, stream=None
         ctypes.byref(p.c()), _ptr(topk_idx, torch.int32, "topk_idx"),
         _ptr(topk_gate, torch.float32, "topk_gate"), _ptr(d_gate, torch.float32, "d_gate"),
         _ptr(d_logits, torch.float32, "d_logits"), _stream(stream)))
+
+
+def layer_bwd_workspace_bytes(p: Problem, mode: int) -> int:
+    out = ctypes.c_size_t()
+    _check("moe_layer_bwd_workspace_bytes",
+           _lib().moe_layer_bwd_workspace_bytes(ctypes.byref(p.c()), mode, ctypes.byref(out)))
+    return out.value
+
+
+def moe_layer_bwd(p: Problem, mode, x, logits, w_gate, w_up, w_down, dy, dx, d_logits, dw_gate,
+                  dw_up, dw_down, ws, stream=None):
+    w, nb = _ws(ws)
+    f32 = torch.float32
+    _check("moe_layer_bwd", _lib().moe_layer_bwd(
+        ctypes.byref(p.c()), mode, _ptr(x, p.dtype, "x"), _ptr(logits, f32, "logits"),
+        _ptr(w_gate, p.dtype, "w_gate"), _ptr(w_up, p.dtype, "w_up"),
+        _ptr(w_down, p.dtype, "w_down"), _ptr(dy, p.dtype, "dy"), _ptr(dx, p.dtype, "dx"),
+        _ptr(d_logits, f32, "d_logits"), _ptr(dw_gate, f32, "dw_gate"),
+        _ptr(dw_up, f32, "dw_up"), _ptr(dw_down, f32, "dw_down"), w, nb, _stream(stream)))
+
+
+class LayerBackwardRunner:
+    """Owns the gradient and workspace tensors of repeated layer backward
+    calls."""
+
+    def __init__(self, p: Problem, mode: int, device="cuda"):
+        self.p, self.mode = p, mode
+        e_res = p.s_res * p.e_loc
+        f32 = torch.float32
+        self.ws = torch.empty(layer_bwd_workspace_bytes(p, mode), dtype=torch.uint8,
+                              device=device)
+        self.dx = torch.empty((p.tokens, p.hidden), dtype=p.dtype, device=device)
+        self.d_logits = torch.empty((p.tokens, p.num_experts), dtype=f32, device=device)
+        self.dw_gate = torch.empty((e_res, p.ffn, p.hidden), dtype=f32, device=device)
+        self.dw_up = torch.empty_like(self.dw_gate)
+        self.dw_down = torch.empty((e_res, p.hidden, p.ffn), dtype=f32, device=device)
+
+    def __call__(self, x, logits, w_gate, w_up, w_down, dy, stream=None):
+        moe_layer_bwd(self.p, self.mode, x, logits, w_gate, w_up, w_down, dy, self.dx,
+                      self.d_logits, self.dw_gate, self.dw_up, self.dw_down, self.ws, stream)
+        return dict(dx=self.dx, d_logits=self.d_logits, dw_gate=self.dw_gate,
+                    dw_up=self.dw_up, dw_down=self.dw_down)
 
 
 class LayerRunner:

@@ -647,8 +647,9 @@ int moe_combine_bwd(const moe_problem* p, int32_t num_chunks, int32_t chunk, con
     return MOE_EINVAL;
   const int lc = d.L / num_chunks;
   const PassArgs pa = static_pass_args(chunk * lc, lc, 0, 0, d.L);
-  return hip_status(launch_combine_bwd(d, pa, dy, expert_out, row_of_assign, topk_gate, d_out,
-                                       d_gate, max_rows, (hipStream_t)stream));
+  return hip_status(launch_combine_bwd(d, pa, single_layout(d, num_chunks, chunk, 0), dy,
+                                       expert_out, row_of_assign, 0, topk_gate, d_out, d_gate,
+                                       max_rows, (hipStream_t)stream));
 }
 
 int moe_gmm_swiglu_bwd(const moe_problem* p, const void* x_sorted, const int32_t* group_offsets,
@@ -675,6 +676,8 @@ int moe_gmm_swiglu_bwd(const moe_problem* p, const void* x_sorted, const int32_t
   GemmBwdArgs a;
   a.x_sorted = x_sorted;
   a.group_offsets = group_offsets;
+  a.go_stride = 0;
+  a.pa = static_pass_args(0, d.L, 0, 0, d.L);
   a.slot_expert = slot_expert;
   a.wg = w_gate;
   a.wu = w_up;
@@ -702,7 +705,8 @@ int moe_permute_bwd(const moe_problem* p, int32_t num_chunks, int32_t chunk,
   if (misaligned(dx_sorted, 16) || misaligned(dx, 16)) return MOE_EINVAL;
   const int lc = d.L / num_chunks;
   const PassArgs pa = static_pass_args(chunk * lc, lc, 0, 0, d.L);
-  return hip_status(launch_permute_bwd(d, pa, dx_sorted, row_of_assign, dx, max_rows,
+  return hip_status(launch_permute_bwd(d, pa, single_layout(d, num_chunks, chunk, 0),
+                                       dx_sorted, row_of_assign, 0, dx, max_rows,
                                        (hipStream_t)stream));
 }
 
@@ -714,6 +718,177 @@ int moe_route_bwd(const moe_problem* p, const int32_t* topk_idx, const float* to
   if (!topk_idx || !topk_gate || !d_gate || !d_logits) return MOE_EINVAL;
   return hip_status(launch_route_bwd(d, topk_idx, topk_gate, d_gate, d_logits,
                                      (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of moe_layer_bwd: the forward layer's (routing, counts, layouts,
+// one set of pass buffers), then per pass x_sorted, d_out and dx_sorted
+// rows, the gate gradients, and the grouped-GEMM backward's scratch.
+struct LayerBwdWs {
+  LayerWs fwd;
+  void* x_sorted;
+  void* d_out;
+  void* dxs;
+  float* d_gate;
+  void* gmm;
+  size_t bytes;
+};
+
+LayerBwdWs carve_layer_bwd(const Dims& d, const LayoutSet& ls, int64_t rows, int64_t drows,
+                           char* base) {
+  LayerBwdWs w;
+  // the backward's passes run on the caller's stream and use the first
+  // buffer set of the forward's layout
+  w.fwd = carve_layer(d, ls, rows, drows, base);
+  size_t off = w.fwd.bytes;
+  auto take = [&](size_t b) {
+    char* p = base ? base + off : nullptr;
+    off += al256(b > 0 ? b : 1);
+    return (void*)p;
+  };
+  const size_t es = d.bf16 ? 2 : 4;
+  w.x_sorted = take((size_t)rows * d.H * es);
+  w.d_out = take((size_t)rows * d.H * es);
+  w.dxs = take((size_t)rows * d.H * es);
+  w.d_gate = (float*)take((size_t)d.T * d.k * 4);
+  w.gmm = take(gmm_bwd_scratch_bytes(d, rows));
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_bwd_workspace_bytes(const moe_problem* p, int32_t mode, size_t* bytes) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (bytes == nullptr || mode < MOE_MODE_LAYER || mode > MOE_MODE_FORCE_CHUNKED)
+    return MOE_EINVAL;
+  int64_t rows, drows;
+  layer_bounds(d, mode, &rows, &drows);
+  const int q = chunk_batch(d, rows, drows);
+  *bytes = carve_layer_bwd(d, layer_layout(d, mode, q, nullptr), rows, drows, nullptr).bytes;
+  return MOE_OK;
+}
+
+int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float* logits,
+                  const void* w_gate, const void* w_up, const void* w_down, const void* dy,
+                  void* dx, float* d_logits, float* dw_gate, float* dw_up, float* dw_down,
+                  void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (mode < MOE_MODE_LAYER || mode > MOE_MODE_FORCE_CHUNKED) return MOE_EINVAL;
+  if (!x || !logits || !w_gate || !w_up || !w_down || !dy || !dx || !d_logits || !dw_gate ||
+      !dw_up || !dw_down || !ws)
+    return MOE_EINVAL;
+  if (misaligned(ws, 256) || misaligned(x, 16) || misaligned(dy, 16) || misaligned(dx, 16) ||
+      misaligned(w_gate, 16) || misaligned(w_up, 16) || misaligned(w_down, 16) ||
+      misaligned(dw_gate, 16) || misaligned(dw_up, 16) || misaligned(dw_down, 16))
+    return MOE_EINVAL;
+  int64_t rows, drows;
+  layer_bounds(d, mode, &rows, &drows);
+  if (!fits_rsrc(d, rows, drows)) return MOE_EUNSUPPORTED;
+  const int64_t wide = d.H > 2 * d.F ? d.H : 2 * d.F;
+  if (d.bf16 && rows * wide * 2 >= ((int64_t)1 << 31)) return MOE_EUNSUPPORTED;
+  const int q = chunk_batch(d, rows, drows);
+  const LayerBwdWs w0 = carve_layer_bwd(d, layer_layout(d, mode, q, nullptr), rows, drows,
+                                        nullptr);
+  if (ws_bytes < w0.bytes) return MOE_ECAPACITY;
+  const LayerBwdWs w = carve_layer_bwd(d, layer_layout(d, mode, q, nullptr), rows, drows,
+                                       (char*)ws);
+  const LayerWs& f = w.fwd;
+  const LayoutSet ls = layer_layout(d, mode, q, f.status + 1);
+  hipStream_t s = (hipStream_t)stream;
+
+  // the forward's routing, counts, plan, overflow flag and pass layouts,
+  // recomputed from x (the pass choice stays on the device)
+  hipError_t e = launch_route(d, logits, f.topk_idx, f.topk_gate,
+                              count_hist_area(d, f.count_scratch), s);
+  if (e != hipSuccess) return MOE_EHIP;
+  const bool reroute = d.R > 0 && d.B > 0;
+  const LayoutBuffers lb = carve_layout(d, ls, f.layout_scratch);
+  if (!reroute && layout_fused(d)) {
+    const CountArgs c = layer_count_args(d, f.topk_idx, f.expert_counts, f.slot_expert, f.ndiv,
+                                         f.shard_counts, f.status, f.count_scratch, nullptr,
+                                         mode);
+    e = launch_layout(d, ls, f.topk_idx, 1, lb, &c, s);
+    if (e != hipSuccess) return MOE_EHIP;
+  } else {
+    e = launch_count(d, f.topk_idx, f.expert_counts, f.slot_expert, f.ndiv,
+                     reroute ? f.slot_of_assign : nullptr, f.shard_counts, f.status,
+                     f.count_scratch, 1, nullptr, mode, s);
+    if (e != hipSuccess) return MOE_EHIP;
+    e = launch_layout(d, ls, reroute ? f.slot_of_assign : f.topk_idx, reroute ? 0 : 1, lb,
+                      nullptr, s);
+    if (e != hipSuccess) return MOE_EHIP;
+  }
+
+  // per pass: x_sorted and the expert outputs recomputed ([FALLBACK] How:
+  // the scan's backward recomputes each chunk), then the combine, grouped
+  // GEMM and permute backward; the weight gradients are overwritten by the
+  // first pass slot and accumulated by the others (a slot the device does
+  // not take leaves them alone)
+  const long long tk = (long long)d.T * d.k;
+  const int es = d.bf16 ? 2 : 4;
+  const int slots = layer_pass_slots(ls);
+  for (int b = 0; b < slots; ++b) {
+    PassArgs pa;
+    if (ls.ovf != nullptr) {
+      const int s0 = b * ls.win;
+      pa = static_pass_args(s0, ls.win < d.L - s0 ? ls.win : d.L - s0, 0, b, d.L);
+      pa.ovf = ls.ovf;
+    } else {
+      pa = static_pass(d, ls, b);
+    }
+    e = launch_gather_rows(lb.meta, kLayoutMeta, lb.sorted_assign, tk, d.k, x, w.x_sorted,
+                           d.H * es, d.T, rows, pa, s);
+    if (e != hipSuccess) return MOE_EHIP;
+    GemmPass gp;
+    memset(&gp, 0, sizeof(gp));
+    gp.a_src = w.x_sorted;
+    gp.a_src_rows = (int)rows;
+    gp.a_div = 1;
+    gp.group_offsets = lb.group_offsets;
+    gp.tile_off = lb.tile_off;
+    gp.tile_group = lb.tile_group;
+    gp.go_stride = d.G_res + 1;
+    gp.tg_stride = tile_map_len(d);
+    gp.split_ok = false;
+    e = launch_gmm(d, pa, gp, f.slot_expert, w_gate, w_up, w_down, f.act[0], f.out[0], rows,
+                   nullptr, s);
+    if (e != hipSuccess) return MOE_EHIP;
+    e = launch_combine_bwd(d, pa, ls, dy, f.out[0], lb.row_of_assign, tk, f.topk_gate, w.d_out,
+                           w.d_gate, rows, s);
+    if (e != hipSuccess) return MOE_EHIP;
+    GemmBwdArgs a;
+    a.x_sorted = w.x_sorted;
+    a.group_offsets = lb.group_offsets;
+    a.go_stride = d.G_res + 1;
+    a.pa = pa;
+    a.slot_expert = f.slot_expert;
+    a.wg = w_gate;
+    a.wu = w_up;
+    a.wd = w_down;
+    a.d_out = w.d_out;
+    a.dx_sorted = w.dxs;
+    a.dwg = dw_gate;
+    a.dwu = dw_up;
+    a.dwd = dw_down;
+    a.accumulate = b > 0;
+    a.max_rows = rows;
+    a.scratch = w.gmm;
+    e = launch_gmm_bwd(d, a, s);
+    if (e != hipSuccess) return MOE_EHIP;
+    e = launch_permute_bwd(d, pa, ls, w.dxs, lb.row_of_assign, tk, dx, rows, s);
+    if (e != hipSuccess) return MOE_EHIP;
+  }
+  return hip_status(launch_route_bwd(d, f.topk_idx, f.topk_gate, w.d_gate, d_logits, s));
 }
 
 const char* moe_status_string(int status) {

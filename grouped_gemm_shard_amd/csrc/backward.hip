@@ -73,12 +73,14 @@ struct Vec {
 // ---- combine backward ------------------------------------------------------
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void combine_bwd_kernel(Dims d, PassArgs pa, const void* dy,
-                                                          const void* out, const int* roa,
+__global__ __launch_bounds__(256) void combine_bwd_kernel(Dims d, PassArgs pa, LayoutSet ls,
+                                                          const void* dy, const void* out,
+                                                          const int* roa, long long roa_stride,
                                                           const float* gate, void* d_out,
                                                           float* d_gate, long long max_rows) {
   const PassInfo pi = resolve_pass(pa);
   if (!pi.active) return;
+  roa += (size_t)layout_set_of(ls, pi.j) * roa_stride;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= pass_tokens(d, pi)) return;
   const int t = pass_token(d, pi, i);
@@ -109,11 +111,13 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(Dims d, PassArgs pa, c
 // ---- permute backward ------------------------------------------------------
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void permute_bwd_kernel(Dims d, PassArgs pa, const void* dxs,
-                                                          const int* roa, void* dx,
+__global__ __launch_bounds__(256) void permute_bwd_kernel(Dims d, PassArgs pa, LayoutSet ls,
+                                                          const void* dxs, const int* roa,
+                                                          long long roa_stride, void* dx,
                                                           long long max_rows) {
   const PassInfo pi = resolve_pass(pa);
   if (!pi.active) return;
+  roa += (size_t)layout_set_of(ls, pi.j) * roa_stride;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= pass_tokens(d, pi)) return;
   const int t = pass_token(d, pi, i);
@@ -174,18 +178,24 @@ constexpr int kBN = 128;  // output columns per tile
 constexpr int kBK = 32;   // reduction columns per stage
 constexpr int kNST = 3;   // ring stages
 
-// tile_off[g] = m-tiles of groups before g (kBM rows each); offsets that are
-// not non-decreasing within [0, limit] give no tiles.
-__global__ __launch_bounds__(1024) void bwd_tiles_kernel(int G, int limit,
-                                                         const int* group_offsets,
-                                                         int* tile_off) {
+// The pass's group offsets, copied to go_copy (layout pi.j of a layer
+// call's passes, go_stride apart; all zero, i.e. no rows, for a pass slot
+// that is not taken), and tile_off[g] = m-tiles of groups before g (kBM rows
+// each).  Every later kernel of the backward reads go_copy.  Offsets that
+// are not non-decreasing within [0, limit] give no tiles.
+__global__ __launch_bounds__(1024) void bwd_tiles_kernel(int G, int limit, PassArgs pa,
+                                                         const int* group_offsets, int go_stride,
+                                                         int* go_copy, int* tile_off) {
   __shared__ int wsum[16];
   __shared__ int bad;
   if (threadIdx.x == 0) bad = 0;
   __syncthreads();
+  const PassInfo pi = resolve_pass(pa);
+  group_offsets += (size_t)pi.j * go_stride;
   const int g = threadIdx.x, lane = g & 63, w = g >> 6;
+  for (int x = g; x <= G; x += blockDim.x) go_copy[x] = pi.active ? group_offsets[x] : 0;
   int v = 0;
-  if (g < G) {
+  if (g < G && pi.active) {
     const int a = group_offsets[g], b = group_offsets[g + 1];
     if (a < 0 || b < a || b > limit) bad = 1;
     v = (b - a + kBM - 1) / kBM;
@@ -1159,36 +1169,39 @@ WgradScratch carve_wgrad(const Dims& d, int64_t max_rows, char* base) {
 
 size_t gmm_bwd_scratch_bytes(const Dims& d, int64_t max_rows) {
   const size_t el = d.bf16 ? 2 : 4;
-  size_t b = a256((size_t)(d.G_res + 1) * 4) + 3 * a256((size_t)max_rows * d.F * el) +
+  size_t b = 2 * a256((size_t)(d.G_res + 1) * 4) + 3 * a256((size_t)max_rows * d.F * el) +
              a256((size_t)max_rows * d.F * el);
   if (d.bf16) b += carve_wgrad(d, max_rows, nullptr).bytes;
   return b;
 }
 
-hipError_t launch_combine_bwd(const Dims& d, const PassArgs& pa, const void* dy,
-                              const void* out, const int* roa, const float* gate, void* d_out,
+hipError_t launch_combine_bwd(const Dims& d, const PassArgs& pa, const LayoutSet& ls,
+                              const void* dy, const void* out, const int* roa,
+                              long long roa_stride, const float* gate, void* d_out,
                               float* d_gate, int64_t max_rows, hipStream_t s) {
-  const int ntok = (d.T / d.L) * pa.lw;
+  // a pass of a layer call covers at most its window; the single pass L
+  const int ntok = (d.T / d.L) * (pa.ovf != nullptr ? d.L : pa.lw);
   const dim3 grid((ntok + 3) / 4);
   if (d.bf16)
-    hipLaunchKernelGGL(combine_bwd_kernel<true>, grid, dim3(256), 0, s, d, pa, dy, out, roa, gate,
-                       d_out, d_gate, (long long)max_rows);
+    hipLaunchKernelGGL(combine_bwd_kernel<true>, grid, dim3(256), 0, s, d, pa, ls, dy, out, roa,
+                       roa_stride, gate, d_out, d_gate, (long long)max_rows);
   else
-    hipLaunchKernelGGL(combine_bwd_kernel<false>, grid, dim3(256), 0, s, d, pa, dy, out, roa,
-                       gate, d_out, d_gate, (long long)max_rows);
+    hipLaunchKernelGGL(combine_bwd_kernel<false>, grid, dim3(256), 0, s, d, pa, ls, dy, out, roa,
+                       roa_stride, gate, d_out, d_gate, (long long)max_rows);
   return hipGetLastError();
 }
 
-hipError_t launch_permute_bwd(const Dims& d, const PassArgs& pa, const void* dxs,
-                              const int* roa, void* dx, int64_t max_rows, hipStream_t s) {
-  const int ntok = (d.T / d.L) * pa.lw;
+hipError_t launch_permute_bwd(const Dims& d, const PassArgs& pa, const LayoutSet& ls,
+                              const void* dxs, const int* roa, long long roa_stride, void* dx,
+                              int64_t max_rows, hipStream_t s) {
+  const int ntok = (d.T / d.L) * (pa.ovf != nullptr ? d.L : pa.lw);
   const dim3 grid((ntok + 3) / 4);
   if (d.bf16)
-    hipLaunchKernelGGL(permute_bwd_kernel<true>, grid, dim3(256), 0, s, d, pa, dxs, roa, dx,
-                       (long long)max_rows);
+    hipLaunchKernelGGL(permute_bwd_kernel<true>, grid, dim3(256), 0, s, d, pa, ls, dxs, roa,
+                       roa_stride, dx, (long long)max_rows);
   else
-    hipLaunchKernelGGL(permute_bwd_kernel<false>, grid, dim3(256), 0, s, d, pa, dxs, roa, dx,
-                       (long long)max_rows);
+    hipLaunchKernelGGL(permute_bwd_kernel<false>, grid, dim3(256), 0, s, d, pa, ls, dxs, roa,
+                       roa_stride, dx, (long long)max_rows);
   return hipGetLastError();
 }
 
@@ -1206,12 +1219,18 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   const size_t el = d.bf16 ? 2 : 4;
   int* tile_off = (int*)ws;
   ws += a256((size_t)(d.G_res + 1) * 4);
+  int* go = (int*)ws;  // the pass's group offsets (bwd_tiles_kernel)
+  ws += a256((size_t)(d.G_res + 1) * 4);
   void* d_h = ws;
   ws += 2 * a256((size_t)rows * d.F * el);
   void* act = ws;
   ws += a256((size_t)rows * d.F * el);
   void* d_a = ws;
   ws += a256((size_t)rows * d.F * el);
+  long long lim = (long long)d.T * d.k;
+  if (rows < lim) lim = rows;
+  hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(1024), 0, s, d.G_res, (int)lim, a.pa,
+                     a.group_offsets, a.go_stride, go, tile_off);
   if (!d.bf16) {
     F32Bwd P;
     P.x = (const float*)a.x_sorted;
@@ -1225,7 +1244,7 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
     P.dwg = a.dwg;
     P.dwu = a.dwu;
     P.dwd = a.dwd;
-    P.group_offsets = a.group_offsets;
+    P.group_offsets = go;
     P.slot_expert = a.slot_expert;
     P.G = d.G_res;
     P.H = d.H;
@@ -1243,13 +1262,9 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
                          which);
     return hipGetLastError();
   }
-  long long lim = (long long)d.T * d.k;
-  if (rows < lim) lim = rows;
-  hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(1024), 0, s, d.G_res, (int)lim,
-                     a.group_offsets, tile_off);
   const long long mt_ub = (rows + kBM - 1) / kBM + d.G_res;
   DgradParams P;
-  P.group_offsets = a.group_offsets;
+  P.group_offsets = go;
   P.tile_off = tile_off;
   P.slot_expert = a.slot_expert;
   P.G = d.G_res;
@@ -1311,7 +1326,7 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   const WgradScratch wsc = carve_wgrad(d, rows, ws);
   const int kc = wgrad_kc(d, rows);
   const long long nc = wgrad_nc_ub(d, rows, kc);
-  hipLaunchKernelGGL(wgrad_plan_kernel, dim3(1), dim3(1024), 0, s, wsc.plan, a.group_offsets,
+  hipLaunchKernelGGL(wgrad_plan_kernel, dim3(1), dim3(1024), 0, s, wsc.plan, go,
                      a.slot_expert, d.G_res, d.lo_slot, d.e_base, e_res, (long long)rows, kc,
                      (int)nc);
   WgradParams W;

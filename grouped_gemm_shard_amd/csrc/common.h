@@ -337,7 +337,9 @@ hipError_t launch_combine(const Dims& d, const PassArgs& pa, const LayoutSet& ls
 // gmm_bwd_scratch_bytes(d, max_rows).
 struct GemmBwdArgs {
   const void* x_sorted;
-  const int* group_offsets;
+  const int* group_offsets;  // of layout pa's j, go_stride ints per layout
+  int go_stride;
+  PassArgs pa;
   const int* slot_expert;
   const void* wg;
   const void* wu;
@@ -353,11 +355,15 @@ struct GemmBwdArgs {
 };
 size_t gmm_bwd_scratch_bytes(const Dims& d, int64_t max_rows);
 hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s);
-hipError_t launch_combine_bwd(const Dims& d, const PassArgs& pa, const void* dy,
-                              const void* out, const int* roa, const float* gate, void* d_out,
+// Combine / permute backward of a pass; row_of_assign advances by
+// roa_stride per row_of_assign set of the pass's layout (as launch_combine).
+hipError_t launch_combine_bwd(const Dims& d, const PassArgs& pa, const LayoutSet& ls,
+                              const void* dy, const void* out, const int* roa,
+                              long long roa_stride, const float* gate, void* d_out,
                               float* d_gate, int64_t max_rows, hipStream_t s);
-hipError_t launch_permute_bwd(const Dims& d, const PassArgs& pa, const void* dxs,
-                              const int* roa, void* dx, int64_t max_rows, hipStream_t s);
+hipError_t launch_permute_bwd(const Dims& d, const PassArgs& pa, const LayoutSet& ls,
+                              const void* dxs, const int* roa, long long roa_stride, void* dx,
+                              int64_t max_rows, hipStream_t s);
 hipError_t launch_route_bwd(const Dims& d, const int* idx, const float* gate,
                             const float* d_gate, float* d_logits, hipStream_t s);
 

@@ -334,6 +334,28 @@ int moe_permute_bwd(const moe_problem* p, int32_t num_chunks, int32_t chunk,
 int moe_route_bwd(const moe_problem* p, const int32_t* topk_idx, const float* topk_gate,
                   const float* d_gate, float* d_logits, void* stream);
 
+/* Workspace bytes of moe_layer_bwd in `mode`. */
+int moe_layer_bwd_workspace_bytes(const moe_problem* p, int32_t mode, size_t* bytes);
+
+/* Backward of moe_layer_dropless_chunked(p, mode, x, logits, weights) for
+ * the upstream gradient dy [T,H] ([FALLBACK] How: the chunked scan's
+ * backward recomputes each chunk and carries the weight gradients across
+ * the chunks).  Routing, counts, plan, the overflow flag and the pass
+ * layouts are recomputed from x and logits, and the device takes the same
+ * passes as the forward (LAYER: the capped pass or the dropless chunk
+ * batches, from the flag, with no host synchronisation).  Per pass:
+ * x_sorted and the expert outputs recomputed, then the combine, grouped
+ * GEMM and permute backward of that pass.  Outputs:
+ *   dx [T,H] (activation dtype; 0 for a token with no resident row),
+ *   d_logits [T,E] float32 (only chosen logits are nonzero),
+ *   dw_gate, dw_up [E_res,F,H], dw_down [E_res,H,F] float32, overwritten
+ *   (the sum over every pass).
+ * Pointers 16-byte aligned; ws holds moe_layer_bwd_workspace_bytes(p, mode). */
+int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float* logits,
+                  const void* w_gate, const void* w_up, const void* w_down, const void* dy,
+                  void* dx, float* d_logits, float* dw_gate, float* dw_up, float* dw_down,
+                  void* ws, size_t ws_bytes, void* stream);
+
 /* Text of a status code (static storage). */
 const char* moe_status_string(int status);
 

@@ -200,3 +200,18 @@ def test_backward_entry_points_validate_on_the_host():
                                  fake, fake, rows, None) == -1
     assert g.lib.moe_permute_bwd(ctypes.byref(c), 1, 0, None, fake, fake, rows, None) == -1
     assert g.lib.moe_route_bwd(ctypes.byref(c), fake, None, fake, fake, None) == -1
+
+
+def test_layer_backward_validates_on_the_host():
+    g = _binding()
+    fake = ctypes.c_void_p(256)
+    c = problem().c()
+    need = g.layer_bwd_workspace_bytes(problem(), g.MODE_LAYER)
+    assert need > g.layer_workspace_bytes(problem(), g.MODE_LAYER)
+    call = lambda mode, ws, nb, dy=fake: g.lib.moe_layer_bwd(  # noqa: E731
+        ctypes.byref(c), mode, fake, fake, fake, fake, fake, dy, fake, fake, fake, fake, fake, ws,
+        nb, None)
+    assert call(9, fake, need) == -1        # mode
+    assert call(0, fake, need, None) == -1  # no upstream gradient
+    assert call(0, None, need) == -1        # no workspace
+    assert call(0, fake, need - 1) == -3    # workspace too small

@@ -129,3 +129,54 @@ def test_backward_modes(mode):
 def test_backward_mid_full_size():
     # the benchmark's layer at full size, through its chunked fallback
     compare(workloads.CONFIGS["mid_bf16"], 0)
+
+
+# ---- the whole layer's backward in one call (moe_layer_bwd) ----------------
+
+def compare_layer(w, mode):
+    """moe_layer_bwd against the oracle's backward of the same layer call;
+    every output starts as NaN so that anything left unwritten fails."""
+    import grouped_gemm_shard_amd as g
+    say(f"[layer-backward] {w.name} mode={mode}")
+    p = binding_problem(w)
+    inp = workloads.make_inputs(w, device="cuda")
+    dy = workloads.make_dy(w, device="cuda")
+    run = g.LayerBackwardRunner(p, mode)
+    for t in (run.dx, run.d_logits, run.dw_gate, run.dw_up, run.dw_down):
+        t.fill_(float("nan"))
+    got = run(inp["x"], inp["logits"], *inp["weights"], dy)
+    torch.cuda.synchronize()
+    got = {k: host(v) for k, v in got.items()}
+    ref = oracle_backward(w, mode, inp, dy)
+    for name in ("dx", "d_logits", "dw_gate", "dw_up", "dw_down"):
+        assert np.all(np.isfinite(got[name])), name
+        rel, mean = check_close_grad(got[name], ref[name], f"{w.name} {name}")
+        say(f"  {name:9s} max-rel {rel:.2e} mean/max {mean:.2e}")
+    # no atomics anywhere: a second call gives the same bits
+    again = run(inp["x"], inp["logits"], *inp["weights"], dy)
+    torch.cuda.synchronize()
+    for name in ("dx", "d_logits", "dw_gate", "dw_up", "dw_down"):
+        assert np.array_equal(host(again[name]), got[name]), name
+
+
+NO_DEDUP_SMALL = W("bwd_small", tokens=512, seq_len=256, hidden=256, ffn=256, num_experts=16,
+                   top_k=2, num_shards=4, res_lo=0, res_hi=4, factor=1.0, num_chunks=4,
+                   zipf=1.2)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "dsv3_small", "maverick_mid", "dedup_small",
+                                  "dsv3_ep8_small", "maverick_wide"])
+def test_layer_backward_against_oracle(name):
+    w = workloads.CONFIGS.get(name) or MEDIUM[name]
+    compare_layer(w, 0)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("which", ["dedup", "plain"])
+def test_layer_backward_modes(which, mode):
+    compare_layer(SMALL_DEDUP if which == "dedup" else NO_DEDUP_SMALL, mode)
+
+
+@pytest.mark.slow
+def test_layer_backward_mid_full_size():
+    compare_layer(workloads.CONFIGS["mid_bf16"], 0)
