@@ -649,7 +649,7 @@ int moe_combine_bwd(const moe_problem* p, int32_t num_chunks, int32_t chunk, con
   const PassArgs pa = static_pass_args(chunk * lc, lc, 0, 0, d.L);
   return hip_status(launch_combine_bwd(d, pa, single_layout(d, num_chunks, chunk, 0), dy,
                                        expert_out, row_of_assign, 0, topk_gate, d_out, d_gate,
-                                       max_rows, (hipStream_t)stream));
+                                       max_rows, 3, (hipStream_t)stream));
 }
 
 int moe_gmm_swiglu_bwd(const moe_problem* p, const void* x_sorted, const int32_t* group_offsets,
@@ -690,6 +690,7 @@ int moe_gmm_swiglu_bwd(const moe_problem* p, const void* x_sorted, const int32_t
   a.accumulate = accumulate;
   a.max_rows = max_rows;
   a.scratch = ws;
+  a.out_recompute = nullptr;
   return hip_status(launch_gmm_bwd(d, a, (hipStream_t)stream));
 }
 
@@ -849,22 +850,28 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
     e = launch_gather_rows(lb.meta, kLayoutMeta, lb.sorted_assign, tk, d.k, x, w.x_sorted,
                            d.H * es, d.T, rows, pa, s);
     if (e != hipSuccess) return MOE_EHIP;
-    GemmPass gp;
-    memset(&gp, 0, sizeof(gp));
-    gp.a_src = w.x_sorted;
-    gp.a_src_rows = (int)rows;
-    gp.a_div = 1;
-    gp.group_offsets = lb.group_offsets;
-    gp.tile_off = lb.tile_off;
-    gp.tile_group = lb.tile_group;
-    gp.go_stride = d.G_res + 1;
-    gp.tg_stride = tile_map_len(d);
-    gp.split_ok = false;
-    e = launch_gmm(d, pa, gp, f.slot_expert, w_gate, w_up, w_down, f.act[0], f.out[0], rows,
-                   nullptr, s);
-    if (e != hipSuccess) return MOE_EHIP;
+    // bf16: the rows g*dy need no expert output, and the grouped-GEMM
+    // backward recomputes the activation anyway, so it also returns the
+    // expert outputs (act Wd^T) and the gate gradients come after it; fp32
+    // recomputes the forward first
+    if (!d.bf16) {
+      GemmPass gp;
+      memset(&gp, 0, sizeof(gp));
+      gp.a_src = w.x_sorted;
+      gp.a_src_rows = (int)rows;
+      gp.a_div = 1;
+      gp.group_offsets = lb.group_offsets;
+      gp.tile_off = lb.tile_off;
+      gp.tile_group = lb.tile_group;
+      gp.go_stride = d.G_res + 1;
+      gp.tg_stride = tile_map_len(d);
+      gp.split_ok = false;
+      e = launch_gmm(d, pa, gp, f.slot_expert, w_gate, w_up, w_down, f.act[0], f.out[0], rows,
+                     nullptr, s);
+      if (e != hipSuccess) return MOE_EHIP;
+    }
     e = launch_combine_bwd(d, pa, ls, dy, f.out[0], lb.row_of_assign, tk, f.topk_gate, w.d_out,
-                           w.d_gate, rows, s);
+                           w.d_gate, rows, d.bf16 ? 1 : 3, s);
     if (e != hipSuccess) return MOE_EHIP;
     GemmBwdArgs a;
     a.x_sorted = w.x_sorted;
@@ -883,8 +890,14 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
     a.accumulate = b > 0;
     a.max_rows = rows;
     a.scratch = w.gmm;
+    a.out_recompute = d.bf16 ? f.out[0] : nullptr;
     e = launch_gmm_bwd(d, a, s);
     if (e != hipSuccess) return MOE_EHIP;
+    if (d.bf16) {
+      e = launch_combine_bwd(d, pa, ls, dy, f.out[0], lb.row_of_assign, tk, f.topk_gate, nullptr,
+                             w.d_gate, rows, 2, s);
+      if (e != hipSuccess) return MOE_EHIP;
+    }
     e = launch_permute_bwd(d, pa, ls, w.dxs, lb.row_of_assign, tk, dx, rows, s);
     if (e != hipSuccess) return MOE_EHIP;
   }

@@ -72,12 +72,14 @@ struct Vec {
 
 // ---- combine backward ------------------------------------------------------
 
+// what: bit 0 writes the rows g * dy, bit 1 the gate gradients <dy, out>.
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(Dims d, PassArgs pa, LayoutSet ls,
                                                           const void* dy, const void* out,
                                                           const int* roa, long long roa_stride,
                                                           const float* gate, void* d_out,
-                                                          float* d_gate, long long max_rows) {
+                                                          float* d_gate, long long max_rows,
+                                                          int what) {
   const PassInfo pi = resolve_pass(pa);
   if (!pi.active) return;
   roa += (size_t)layout_set_of(ls, pi.j) * roa_stride;
@@ -86,25 +88,32 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(Dims d, PassArgs pa, L
   const int t = pass_token(d, pi, i);
   const int lane = threadIdx.x & 63;
   constexpr int N = Vec<BF16>::N;
+  const bool rows = what & 1, dots = what & 2;
   for (int j = 0; j < d.k; ++j) {
     const int r = roa[(size_t)t * d.k + j];
     float dot = 0.0f;
     if (r >= 0 && r < max_rows) {
       const float g = gate[(size_t)t * d.k + j];
       for (int c = lane * N; c < d.H; c += 64 * N) {
-        Vec<BF16> a, o;
+        Vec<BF16> a;
         a.load(dy, (size_t)t * d.H + c);
-        o.load(out, (size_t)r * d.H + c);
+        if (dots) {
+          Vec<BF16> o;
+          o.load(out, (size_t)r * d.H + c);
 #pragma unroll
-        for (int q = 0; q < N; ++q) {
-          dot = fmaf(a.v[q], o.v[q], dot);
-          a.v[q] *= g;
+          for (int q = 0; q < N; ++q) dot = fmaf(a.v[q], o.v[q], dot);
         }
-        a.store(d_out, (size_t)r * d.H + c);
+        if (rows) {
+#pragma unroll
+          for (int q = 0; q < N; ++q) a.v[q] *= g;
+          a.store(d_out, (size_t)r * d.H + c);
+        }
       }
     }
-    dot = wave_sum(dot);
-    if (lane == 0) d_gate[(size_t)t * d.k + j] = dot;
+    if (dots) {
+      dot = wave_sum(dot);
+      if (lane == 0) d_gate[(size_t)t * d.k + j] = dot;
+    }
   }
 }
 
@@ -1178,16 +1187,16 @@ size_t gmm_bwd_scratch_bytes(const Dims& d, int64_t max_rows) {
 hipError_t launch_combine_bwd(const Dims& d, const PassArgs& pa, const LayoutSet& ls,
                               const void* dy, const void* out, const int* roa,
                               long long roa_stride, const float* gate, void* d_out,
-                              float* d_gate, int64_t max_rows, hipStream_t s) {
+                              float* d_gate, int64_t max_rows, int what, hipStream_t s) {
   // a pass of a layer call covers at most its window; the single pass L
   const int ntok = (d.T / d.L) * (pa.ovf != nullptr ? d.L : pa.lw);
   const dim3 grid((ntok + 3) / 4);
   if (d.bf16)
     hipLaunchKernelGGL(combine_bwd_kernel<true>, grid, dim3(256), 0, s, d, pa, ls, dy, out, roa,
-                       roa_stride, gate, d_out, d_gate, (long long)max_rows);
+                       roa_stride, gate, d_out, d_gate, (long long)max_rows, what);
   else
     hipLaunchKernelGGL(combine_bwd_kernel<false>, grid, dim3(256), 0, s, d, pa, ls, dy, out, roa,
-                       roa_stride, gate, d_out, d_gate, (long long)max_rows);
+                       roa_stride, gate, d_out, d_gate, (long long)max_rows, what);
   return hipGetLastError();
 }
 
@@ -1306,6 +1315,22 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   Q.round_blocks = nb_sw;
   hipLaunchKernelGGL(dgrad_kernel<true>, dim3(whole_rounds(mt_ub * Q.n_ntiles, nb_sw)),
                      dim3(256), 0, s, Q);
+  if (a.out_recompute != nullptr) {
+    // the expert outputs from the recomputed activation: act Wd^T (K = F,
+    // Wd [H, F] K-contiguous)
+    DgradParams O = P;
+    O.A = (const uint16_t*)act;
+    O.B0 = O.B1 = (const uint16_t*)a.wd;
+    O.b_stride = (size_t)d.H * d.F;
+    O.C = (uint16_t*)a.out_recompute;
+    O.K = d.F;
+    O.Nout = d.H;
+    O.n_ntiles = d.H / kBN;
+    const int nb_o = bwd_round_blocks(reinterpret_cast<const void*>(dgrad_kernel<false>), 256, 3);
+    O.round_blocks = nb_o;
+    hipLaunchKernelGGL(dgrad_kernel<false>, dim3(whole_rounds(mt_ub * O.n_ntiles, nb_o)),
+                       dim3(256), 0, s, O);
+  }
   // dx_sorted = [d_hg | d_hu] [Wg ; Wu]  (K = 2F; Wg and Wu [F, H] stacked
   // along the reduction and read reduction-major)
   DgradParams X = P;

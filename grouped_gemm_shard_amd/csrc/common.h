@@ -352,15 +352,17 @@ struct GemmBwdArgs {
   int accumulate;
   int64_t max_rows;
   void* scratch;
+  void* out_recompute;  // bf16: if set, expert outputs from the recomputed activation
 };
 size_t gmm_bwd_scratch_bytes(const Dims& d, int64_t max_rows);
 hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s);
 // Combine / permute backward of a pass; row_of_assign advances by
 // roa_stride per row_of_assign set of the pass's layout (as launch_combine).
+// what: bit 0 the rows g * dy into d_out, bit 1 the gate gradients (reads out).
 hipError_t launch_combine_bwd(const Dims& d, const PassArgs& pa, const LayoutSet& ls,
                               const void* dy, const void* out, const int* roa,
                               long long roa_stride, const float* gate, void* d_out,
-                              float* d_gate, int64_t max_rows, hipStream_t s);
+                              float* d_gate, int64_t max_rows, int what, hipStream_t s);
 hipError_t launch_permute_bwd(const Dims& d, const PassArgs& pa, const LayoutSet& ls,
                               const void* dxs, const int* roa, long long roa_stride, void* dx,
                               int64_t max_rows, hipStream_t s);
