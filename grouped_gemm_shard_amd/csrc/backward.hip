@@ -1315,6 +1315,33 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   Q.round_blocks = nb_sw;
   hipLaunchKernelGGL(dgrad_kernel<true>, dim3(whole_rounds(mt_ub * Q.n_ntiles, nb_sw)),
                      dim3(256), 0, s, Q);
+  // dx_sorted = [d_hg | d_hu] [Wg ; Wu]  (K = 2F; Wg and Wu [F, H] stacked
+  // along the reduction and read reduction-major)
+  DgradParams X = P;
+  X.A = (const uint16_t*)d_h;
+  X.B0 = (const uint16_t*)a.wg;
+  X.B1 = (const uint16_t*)a.wu;
+  X.b_stride = (size_t)d.F * d.H;
+  X.C = (uint16_t*)a.dx_sorted;
+  X.K = 2 * d.F;
+  X.k_split = d.F;
+  X.Nout = d.H;
+  X.n_ntiles = d.H / kBN;
+  // dx_sorted (and the expert outputs) on the side stream, the weight
+  // gradients on the caller's: both only read what the launches above wrote,
+  // so the data-gradient GEMM fills the weight gradients' uneven last rounds
+  SideStream* ss = side_stream();
+  std::unique_lock<std::mutex> lock(side_mutex(), std::defer_lock);
+  hipStream_t sx = s;
+  if (ss != nullptr) {
+    lock.lock();
+    hipError_t e = hipEventRecord(ss->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+    if (e != hipSuccess) return e;
+    sx = ss->s;
+  }
+  hipLaunchKernelGGL(dgrad_kmajor_kernel, dim3(whole_rounds(mt_ub * X.n_ntiles, nb_km)),
+                     dim3(256), 0, sx, X);
   if (a.out_recompute != nullptr) {
     // the expert outputs from the recomputed activation: act Wd^T (K = F,
     // Wd [H, F] K-contiguous)
@@ -1329,22 +1356,8 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
     const int nb_o = bwd_round_blocks(reinterpret_cast<const void*>(dgrad_kernel<false>), 256, 3);
     O.round_blocks = nb_o;
     hipLaunchKernelGGL(dgrad_kernel<false>, dim3(whole_rounds(mt_ub * O.n_ntiles, nb_o)),
-                       dim3(256), 0, s, O);
+                       dim3(256), 0, sx, O);
   }
-  // dx_sorted = [d_hg | d_hu] [Wg ; Wu]  (K = 2F; Wg and Wu [F, H] stacked
-  // along the reduction and read reduction-major)
-  DgradParams X = P;
-  X.A = (const uint16_t*)d_h;
-  X.B0 = (const uint16_t*)a.wg;
-  X.B1 = (const uint16_t*)a.wu;
-  X.b_stride = (size_t)d.F * d.H;
-  X.C = (uint16_t*)a.dx_sorted;
-  X.K = 2 * d.F;
-  X.k_split = d.F;
-  X.Nout = d.H;
-  X.n_ntiles = d.H / kBN;
-  hipLaunchKernelGGL(dgrad_kmajor_kernel, dim3(whole_rounds(mt_ub * X.n_ntiles, nb_km)),
-                     dim3(256), 0, s, X);
   // weight gradients: plan (rows and chunks per expert), then
   // [dWg ; dWu] = [d_hg | d_hu]^T x_sorted and dWd = d_out^T act, each with
   // the fixed-order sum of split experts' partials
@@ -1386,6 +1399,13 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
     const long long ij4 = ((long long)q->I * q->J / 4 + 255) / 256;
     hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)ij4, (unsigned)e_res), dim3(256), 0, s,
                        *q);
+  }
+  if (ss != nullptr) {
+    // join even after a failed launch: the caller's stream must not run
+    // ahead of the side stream's work
+    hipError_t e = hipEventRecord(ss->join, ss->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, ss->join, 0);
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }
