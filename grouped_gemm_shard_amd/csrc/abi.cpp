@@ -83,7 +83,7 @@ int make_dims(const moe_problem* p, Dims* d) {
   d->n_default = n;
   // tall tiles halve the operand traffic per flop where the reduction is
   // long; short ones waste less on small groups
-  d->gemm_bm = d->H >= 2048 ? 256 : 128;
+  d->gemm_bm = d->H >= MOE_GEMM_BIG_MIN_H ? 256 : 128;
   return MOE_OK;
 }
 
@@ -216,6 +216,7 @@ struct LayerWs {
   void* x_dedup[2];
   void* act[2];
   void* out[2];
+  int* gsync[2];
   size_t bytes;
 };
 
@@ -252,6 +253,7 @@ LayerWs carve_layer(const Dims& d, const LayoutSet& ls, int64_t rows, int64_t dr
     w.x_dedup[i] = own ? take(d.dedup ? (size_t)drows * d.H * es : 0) : nullptr;
     w.act[i] = own ? take((size_t)rows * d.F * es) : nullptr;
     w.out[i] = own ? take((size_t)rows * d.H * es) : nullptr;
+    w.gsync[i] = own && d.bf16 ? (int*)take(gmm_sync_bytes(d)) : nullptr;
   }
   w.bytes = off;
   return w;
@@ -301,6 +303,7 @@ int run_pass(const Dims& d, const PassArgs& pa, const LayoutSet& ls, const Layou
   gp.go_stride = d.G_res + 1;
   gp.tg_stride = tile_map_len(d);
   gp.split_ok = split_ok;
+  gp.sync = w.gsync[set];
   hipError_t e = launch_gmm(d, pa, gp, w.slot_expert, wg, wu, wd, w.act[set], w.out[set], rows,
                             nullptr, s);
   if (e != hipSuccess) return MOE_EHIP;

@@ -19,6 +19,11 @@ constexpr int kMaxExperts = 1024;   // E limit (route keeps E/64 logits per lane
 constexpr int kMaxTopK = 32;        // one lane per chosen expert in route/combine
 constexpr int kSortBlocks = 64;     // blocks of the stable counting sort
 constexpr int kGemmBMMin = 128;     // smallest grouped-GEMM tile height
+// Hidden sizes from which the grouped GEMM runs 256-row tiles (long
+// reductions, where the taller tile halves the operand traffic per flop).
+#ifndef MOE_GEMM_BIG_MIN_H
+#define MOE_GEMM_BIG_MIN_H 2048
+#endif
 constexpr int kMaxChunks = 64;      // sequence chunks of the fallback
 
 // Problem dimensions, derived once on the host and passed by value.
@@ -295,8 +300,11 @@ struct GemmPass {
   const int* tile_group;
   int go_stride, tg_stride;
   bool split_ok;          // long-F passes may split their m-tiles over the side stream
+  int* sync;              // bf16: counters of the one-launch GEMM1+GEMM2 kernel
+                          // (gmm_sync_bytes); null: from scratch if given, else two launches
 };
 size_t gmm_scratch_bytes(const Dims& d);
+size_t gmm_sync_bytes(const Dims& d);
 
 // A second stream per device (default priority), with the events that fork
 // work onto it from a caller's stream and join it back.  Whoever enqueues

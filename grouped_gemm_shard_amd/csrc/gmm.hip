@@ -50,6 +50,7 @@ namespace moe {
 namespace {
 
 constexpr int BNB = 256;  // weight rows per tile
+typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int GM = 8;     // m-tiles per band of the tile order
 
 // Tile shapes <BM, BK, stages, waves, waves along N>: BIG for long
@@ -65,6 +66,14 @@ constexpr int GM = 8;     // m-tiles per band of the tile order
 #endif
 #ifndef MOE_GEMM_REM
 #define MOE_GEMM_REM 128, 64, 3, 8, 4
+#endif
+// Tile shapes whose passes run GEMM1 and GEMM2 as one launch (bit 0: 128-row
+// tiles, bit 1: 256-row tiles); the others run two launches.  Measured on
+// MI355X: one launch is 5% faster on the mid-sized layer (128-row tiles) and
+// 10-20% slower on the 256-row shapes, whose two-launch tile order keeps
+// every XCD on the same few experts at a time.
+#ifndef MOE_GEMM_FUSE
+#define MOE_GEMM_FUSE 1
 #endif
 constexpr int shape_rows(int bm, int, int, int, int) { return bm; }
 constexpr int shape_waves(int, int, int, int nw, int) { return nw; }
@@ -90,6 +99,7 @@ struct GemmParams {
   int round_blocks;        // blocks per round of the tile order (a multiple of 8):
                            // the blocks resident on the chip at once
   int part, parts;         // this launch covers m-tiles [M*part/parts, M*(part+1)/parts)
+  int mt_cap;              // fused kernel: m-tiles its completion flags can hold
   long long max_rows;
   PassArgs pa;
 };
@@ -123,12 +133,11 @@ __device__ __forceinline__ void vm_wait_barrier() {
 
 // Starts the loads of K step `step` into its ring stage: each wave-wide
 // load fills RPI consecutive rows (1 KB) of the stage.
-template <int BM, int BK, int NST, bool SWIGLU, int NW>
+template <int BM, int BK, int NST, bool SWIGLU, int NW, bool ACOH>
 __device__ __forceinline__ void gmm_issue(char* smem, int step, int w,
                                           __amdgpu_buffer_rsrc_t ra_r, __amdgpu_buffer_rsrc_t rb0,
                                           __amdgpu_buffer_rsrc_t rb1,
-                                          const int (&a_off)[BM / (1024 / (BK * 2)) / NW],
-                                          const int (&b_off)[BNB / (1024 / (BK * 2)) / NW]) {
+                                          const int* a_off, const int* b_off) {
   constexpr int RB = BK * 2, RPI = 1024 / RB;
   constexpr int AI = BM / RPI / NW, BI = BNB / RPI / NW;
   constexpr int SA = BM * RB, SS = (BM + BNB) * RB;
@@ -136,8 +145,12 @@ __device__ __forceinline__ void gmm_issue(char* smem, int step, int w,
   const int kb = step * BK * 2;
 #pragma unroll
   for (int i = 0; i < AI; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_r, (lds_void*)(st + (i * NW + w) * RPI * RB), 16,
-                                             a_off[i], kb, 0, 0);
+    if constexpr (ACOH)  // cache policy sc1
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_r, (lds_void*)(st + (i * NW + w) * RPI * RB),
+                                               16, a_off[i], kb, 0, 16);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_r, (lds_void*)(st + (i * NW + w) * RPI * RB),
+                                               16, a_off[i], kb, 0, 0);
 #pragma unroll
   for (int i = 0; i < BI; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(SWIGLU && i >= BI / 2 ? rb1 : rb0,
@@ -186,8 +199,12 @@ __device__ __forceinline__ void live_dispatch(int live, F& f) {
 
 // One BM x 256 tile (GEMM1: BM x 128 act columns) of group rows
 // [row0, row0 + rows), rows <= BM, of weight n-tile nt of local expert e;
-// smem holds at least NST * (BM + 256) * BK * 2 bytes.
-template <int BM, int BK, int NST, int NW, int NWN, bool SWIGLU>
+// smem holds at least NST * (BM + 256) * BK * 2 bytes.  COH: the act
+// exchanged inside the fused kernel is written (GEMM1) and read (GEMM2)
+// device-coherently, so a tile on another XCD sees it without cache
+// maintenance (cache policy sc1: device-scope coherent, written through to
+// and read from the level all XCDs share).
+template <int BM, int BK, int NST, int NW, int NWN, bool SWIGLU, bool COH = false>
 __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const int* aidx,
                                          int row0, int rows, int nt, int e) {
   constexpr int RB = BK * 2;          // LDS bytes per row of a stage
@@ -202,7 +219,7 @@ __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const 
   constexpr int NI = BNB / NWN / 32;   // 32-column MFMA tiles per wave
   static_assert(NI >= 2 && NI % 2 == 0, "a SwiGLU wave pairs gate and up tiles");
   static_assert(AI >= 1 && BI >= 2 && MI >= 1, "tile shape");
-  static_assert(NST >= 2 && NST <= 4, "stages");
+  static_assert(NST >= 2 && NST <= 5, "stages");
 
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -262,7 +279,7 @@ __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const 
 
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
-    if (s < KT) gmm_issue<BM, BK, NST, SWIGLU, NW>(smem, s, w, ra_r, rb0, rb1, a_off, b_off);
+    if (s < KT) gmm_issue<BM, BK, NST, SWIGLU, NW, COH && !SWIGLU>(smem, s, w, ra_r, rb0, rb1, a_off, b_off);
 
   // Software pipeline across K steps: the last slice's fragments are read
   // before the barrier, and its MFMAs are issued after it, overlapping the
@@ -278,11 +295,12 @@ __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const 
     constexpr int LV = decltype(live_c)::value;
     for (int kt = 0; kt < KT; ++kt) {
       const int ahead = min(KT - 1 - kt, NST - 2);  // stages allowed to stay in flight
-      if (ahead >= 2) vm_wait_barrier<2 * LPS>();
+      if (ahead >= 3) vm_wait_barrier<3 * LPS>();
+      else if (ahead == 2) vm_wait_barrier<2 * LPS>();
       else if (ahead == 1) vm_wait_barrier<LPS>();
       else vm_wait_barrier<0>();
       if (kt + NST - 1 < KT)
-        gmm_issue<BM, BK, NST, SWIGLU, NW>(smem, kt + NST - 1, w, ra_r, rb0, rb1, a_off, b_off);
+        gmm_issue<BM, BK, NST, SWIGLU, NW, COH && !SWIGLU>(smem, kt + NST - 1, w, ra_r, rb0, rb1, a_off, b_off);
       const char* sa = smem + (kt % NST) * SS;
       const char* sb = sa + SA;
       // slice 0 of this step goes to set 0; slice NS-1 of the previous step
@@ -339,6 +357,19 @@ __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const 
   constexpr int RPIO = (64 * NW) / CPRO;          // rows per pass of the block
   static_assert((64 * NW) % CPRO == 0 && BM % RPIO == 0, "store passes");
   uint16_t* cbase = P.C + (size_t)row0 * P.Nout + (size_t)nt * OUTC;
+  if (COH && SWIGLU) {
+    // stores past the tile's last row fall outside the buffer range and are dropped
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(cbase, (unsigned)(((rows - 1) * P.Nout + OUTC) * 2));
+#pragma unroll
+    for (int it = 0; it < BM / RPIO; ++it) {
+      const int r = it * RPIO + tid / CPRO, ch = tid % CPRO;
+      if (r < rows)
+        __builtin_amdgcn_raw_buffer_store_b128(*(const v4i*)(smem + r * STRIDE + ch * 16), rc,
+                                               (r * P.Nout + ch * 8) * 2, 0, 16 /* sc1 */);
+    }
+    return;
+  }
 #pragma unroll
   for (int it = 0; it < BM / RPIO; ++it) {
     const int r = it * RPIO + tid / CPRO, ch = tid % CPRO;
@@ -405,6 +436,115 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
     gmm_tile<MOE_GEMM_REM, SWIGLU>(P, smem, aidx, row0, rows, nt, e);
   else
     gmm_tile<BM, BK, NST, NW, NWN, SWIGLU>(P, smem, aidx, row0, rows, nt, e);
+}
+
+// Both GEMMs of a pass in one launch.  GEMM2 of an m-tile needs every act
+// column of that m-tile, that is all GEMM1 n-tiles of it, and nothing else;
+// in two launches the chip idles while GEMM1's last short round of tiles
+// runs, and again at GEMM2's.  Here the m-tiles are split into 8 contiguous
+// runs, one per group of workgroups (block b is in group b % 8, the XCD the
+// dispatcher round-robins it to, so a run's weight panels stay in one L2).
+// Each workgroup takes one ticket from its group's counter: the group's
+// GEMM1 tiles come first (bands of GM m-tiles, n-tile by n-tile), then its
+// GEMM2 tiles in the same band order; tickets past the end exit.  A GEMM1
+// tile bumps its m-tile's flag after its act stores; a GEMM2 tile waits for
+// the flag to reach the GEMM1 n-tile count.  A workgroup only ever waits on
+// GEMM1 tiles whose tickets came before its own, held by workgroups already
+// running that wait on nothing, so every wait ends (and is bounded
+// besides).  sync: [8 groups][16] counters, then one flag per m-tile, all
+// zero at launch.
+//
+// Visibility of act: GEMM1 writes it through to the device-wide level
+// (cache policy sc1), and waits for the stores before bumping the flag.  No
+// cache of the reader can hold an older copy of those rows: they are read
+// in this launch only after their flag, and caches start the launch clean;
+// the reader still drops its CU's L1 before its loads.
+constexpr int kSyncFlags = 128;     // ints before the flags
+constexpr int kSpinLimit = 1 << 22; // ~0.2 s of sleeps: far beyond any GEMM1 tile
+
+template <int BM, int BK, int NST, int NW, int NWN>
+__global__ __launch_bounds__(64 * NW, 1) void gmm_fused_kernel(GemmParams P1, GemmParams P2,
+                                                               int* sync) {
+  constexpr bool HAS_REM = BM > kRemBM;
+  constexpr int RING = NST * (BM + BNB) * BK * 2;
+  static_assert(!HAS_REM || shape_waves(MOE_GEMM_REM) == NW, "REM runs in the same block");
+  __shared__ __attribute__((aligned(1024))) char smem[HAS_REM && kRemRing > RING ? kRemRing : RING];
+  __shared__ int s_ticket;
+  PassInfo pi = resolve_pass(P1.pa);
+  if (!pi.active) return;
+  const int* group_offsets = P1.group_offsets + (size_t)pi.j * P1.go_stride;
+  const int* tile_off = P1.tile_off + (size_t)pi.j * P1.go_stride;
+  const int* tile_group = P1.tile_group + (size_t)pi.j * P1.tg_stride;
+  const int M = tile_off[P1.G];
+  if (group_offsets[P1.G] > P1.max_rows || M < 0 || M > P1.mt_cap) return;  // malformed
+  const int v = blockIdx.x & 7;
+  const int m0 = (int)(((long long)M * v) >> 3);
+  const int mv = (int)(((long long)M * (v + 1)) >> 3) - m0;
+  const int n1 = P1.n_ntiles, n2 = P2.n_ntiles;
+  const int t1 = mv * n1, tot = t1 + mv * n2;
+  if (blockIdx.x / 8 >= tot) return;  // more workgroups than the group's tickets
+  const int tid = threadIdx.x;
+  if (tid == 0) s_ticket = atomicAdd(sync + v * 16, 1);
+  __syncthreads();
+  const int t = s_ticket;
+  if (t >= tot) return;
+  const bool first = t < t1;
+  const int nn = first ? n1 : n2;
+  const int L = first ? t : t - t1;
+  const int band = L / (GM * nn);
+  const int gm = min(GM, mv - band * GM);
+  const int r = L - band * GM * nn;
+  const int nt = r / gm;
+  const int m = m0 + band * GM + (r - nt * gm);
+  int* flag = sync + kSyncFlags + m;
+  // the tile's rows and expert (none when the map is malformed or the slot
+  // hosts no resident expert: the flag still counts the tile)
+  int row0 = 0, rows = 0, e = -1;
+  const int g = tile_group[m];
+  if (g >= 0 && g < P1.G) {
+    const int gend = group_offsets[g + 1];
+    row0 = group_offsets[g] + (m - tile_off[g]) * BM;
+    if (row0 >= 0 && row0 < gend && gend <= P1.max_rows) {
+      rows = min(BM, gend - row0);
+      e = P1.slot_expert[P1.lo_slot + g] - P1.e_base;
+      if (e >= P1.e_res) e = -1;
+    }
+  }
+  if (first) {
+    if (e >= 0) {
+      const int* aidx = P1.a_index ? P1.a_index + (size_t)pi.j * P1.a_index_stride : nullptr;
+      if (HAS_REM && rows <= kRemBM)
+        gmm_tile<MOE_GEMM_REM, true, true>(P1, smem, aidx, row0, rows, nt, e);
+      else
+        gmm_tile<BM, BK, NST, NW, NWN, true, true>(P1, smem, aidx, row0, rows, nt, e);
+    }
+    // every thread's write-through act stores are complete before the flag
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) atomicAdd(flag, 1);
+    return;
+  }
+  if (tid == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n1 &&
+           ++spins < kSpinLimit)
+      __builtin_amdgcn_s_sleep(2);
+  }
+  __syncthreads();
+  if (e < 0) return;
+  asm volatile("buffer_inv sc0" ::: "memory");  // this CU's L1
+  if (HAS_REM && rows <= kRemBM)
+    gmm_tile<MOE_GEMM_REM, false>(P2, smem, nullptr, row0, rows, nt, e);
+  else
+    gmm_tile<BM, BK, NST, NW, NWN, false>(P2, smem, nullptr, row0, rows, nt, e);
+}
+
+// Zeroes the fused kernel's counters and flags (a fill kernel, so that the
+// layer stays capturable in a graph).
+__global__ __launch_bounds__(256) void gmm_sync_clear_kernel(int* sync, int n, PassArgs pa) {
+  PassInfo pi = resolve_pass(pa);
+  if (!pi.active) return;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) sync[i] = 0;
 }
 
 // fp32 path (the tiny fp32 workload): one thread per output element.
@@ -534,9 +674,8 @@ int resident_blocks() {
   std::lock_guard<std::mutex> lock(mu);
   if (occ[dev] == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(gmm_bf16_kernel<BM, BK, NST, true, NW, NWN>),
-            64 * NW, 0) != hipSuccess || n < 1)
+    const void* k = reinterpret_cast<const void*>(gmm_bf16_kernel<BM, BK, NST, true, NW, NWN>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 64 * NW, 0) != hipSuccess || n < 1)
       n = 1;
     occ[dev] = n;
   }
@@ -547,7 +686,7 @@ template <int BM, int BK, int NST, int NW, int NWN>
 hipError_t launch_bf16(const Dims& d, const PassArgs& pa, const GemmPass& gp, const int* toff,
                        const int* tgroup, int go_stride, int tg_stride, const int* slot_expert,
                        const void* wg, const void* wu, const void* wd, void* act, void* out,
-                       int64_t max_rows, hipStream_t s) {
+                       int64_t max_rows, int* gsync, hipStream_t s) {
   const long long mt_ub = (max_rows + BM - 1) / BM + d.G_res;
   GemmParams p1;
   p1.A = (const uint16_t*)gp.a_src;
@@ -587,6 +726,22 @@ hipError_t launch_bf16(const Dims& d, const PassArgs& pa, const GemmPass& gp, co
   p2.K = d.F;
   p2.Nout = d.H;
   p2.n_ntiles = d.H / 256;
+  p1.mt_cap = p2.mt_cap = tile_map_len(d);
+  p1.part = p2.part = 0;
+  p1.parts = p2.parts = 1;
+
+  if (gsync != nullptr && (MOE_GEMM_FUSE & (BM == 256 ? 2 : 1))) {
+    // both GEMMs in one launch, after zeroing its counters and flags
+    const int nsync = kSyncFlags + p1.mt_cap;
+    hipLaunchKernelGGL(gmm_sync_clear_kernel, dim3(1), dim3(256), 0, s, gsync, nsync, pa);
+    // one workgroup per ticket: 8 groups of up to ceil(mt_ub / 8) m-tiles,
+    // GEMM1 and GEMM2 tiles
+    const long long nbf = 8 * ((mt_ub + 7) / 8) * (long long)(p1.n_ntiles + p2.n_ntiles);
+    p1.round_blocks = p2.round_blocks = 0;
+    hipLaunchKernelGGL((gmm_fused_kernel<BM, BK, NST, NW, NWN>), dim3((unsigned)nbf),
+                       dim3(64 * NW), 0, s, p1, p2, gsync);
+    return hipGetLastError();
+  }
 
   // GEMM2 of a set of m-tiles needs only GEMM1 of the same m-tiles, so with
   // long GEMM2 reductions (F >= 4096) the m-tiles run as two independent
@@ -652,9 +807,13 @@ std::mutex& side_mutex() {
   return mu;
 }
 
+size_t gmm_sync_bytes(const Dims& d) {
+  return ((size_t)(kSyncFlags + tile_map_len(d)) * 4 + 255) / 256 * 256;
+}
+
 size_t gmm_scratch_bytes(const Dims& d) {
   return ((size_t)(d.G_res + 1) * 4 + 255) / 256 * 256 +
-         ((size_t)tile_map_len(d) * 4 + 255) / 256 * 256;
+         ((size_t)tile_map_len(d) * 4 + 255) / 256 * 256 + gmm_sync_bytes(d);
 }
 
 hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const GemmPass& gp,
@@ -664,6 +823,7 @@ hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const GemmPass& gp,
     const int* toff = gp.tile_off;
     const int* tgroup = gp.tile_group;
     int go_stride = gp.go_stride, tg_stride = gp.tg_stride;
+    int* gsync = gp.sync;
     if (toff == nullptr || tgroup == nullptr) {
       int* t0 = (int*)scratch;
       int* t1 = (int*)((char*)scratch + ((size_t)(d.G_res + 1) * 4 + 255) / 256 * 256);
@@ -671,6 +831,9 @@ hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const GemmPass& gp,
       if (max_rows < lim) lim = max_rows;
       hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, d.G_res, d.gemm_bm,
                          (int)lim, gp.group_offsets, t0, t1, pa);
+      // the fused kernel's counters follow the tile map in scratch
+      if (gsync == nullptr)
+        gsync = (int*)((char*)t1 + ((size_t)tile_map_len(d) * 4 + 255) / 256 * 256);
       toff = t0;
       tgroup = t1;
       go_stride = 0;
@@ -679,10 +842,10 @@ hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const GemmPass& gp,
     hipError_t e;
     if (d.gemm_bm == 256)
       e = launch_bf16<MOE_GEMM_BIG>(d, pa, gp, toff, tgroup, go_stride, tg_stride, slot_expert,
-                                    wg, wu, wd, act, out, max_rows, s);
+                                    wg, wu, wd, act, out, max_rows, gsync, s);
     else
       e = launch_bf16<MOE_GEMM_SMALL>(d, pa, gp, toff, tgroup, go_stride, tg_stride, slot_expert,
-                                      wg, wu, wd, act, out, max_rows, s);
+                                      wg, wu, wd, act, out, max_rows, gsync, s);
     if (e != hipSuccess) return e;
   } else {
     F32Params p1;
