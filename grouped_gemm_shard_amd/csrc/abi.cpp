@@ -216,7 +216,10 @@ struct LayerWs {
   void* x_dedup[2];
   void* act[2];
   void* out[2];
-  int* gsync[2];
+  // one-launch grouped GEMM counters, one block of sync_stride ints per pass
+  // slot (bf16), zeroed by the route launch of the call
+  int* gsync;
+  int sync_stride, sync_slots;
   size_t bytes;
 };
 
@@ -253,8 +256,10 @@ LayerWs carve_layer(const Dims& d, const LayoutSet& ls, int64_t rows, int64_t dr
     w.x_dedup[i] = own ? take(d.dedup ? (size_t)drows * d.H * es : 0) : nullptr;
     w.act[i] = own ? take((size_t)rows * d.F * es) : nullptr;
     w.out[i] = own ? take((size_t)rows * d.H * es) : nullptr;
-    w.gsync[i] = own && d.bf16 ? (int*)take(gmm_sync_bytes(d)) : nullptr;
   }
+  w.sync_stride = (int)(gmm_sync_bytes(d) / 4);
+  w.sync_slots = d.bf16 ? layer_pass_slots(ls) : 0;
+  w.gsync = w.sync_slots > 0 ? (int*)take((size_t)w.sync_slots * gmm_sync_bytes(d)) : nullptr;
   w.bytes = off;
   return w;
 }
@@ -277,7 +282,7 @@ bool fits_rsrc(const Dims& d, int64_t rows, int64_t drows) {
 // Then the combine of the pass's tokens.
 int run_pass(const Dims& d, const PassArgs& pa, const LayoutSet& ls, const LayoutBuffers& lb,
              const void* x, const void* wg, const void* wu, const void* wd, void* y,
-             const LayerWs& w, int set, bool split_ok, int64_t rows, int64_t drows,
+             const LayerWs& w, int set, int slot, bool split_ok, int64_t rows, int64_t drows,
              hipStream_t s) {
   const long long tk = (long long)d.T * d.k;
   const int es = d.bf16 ? 2 : 4;
@@ -303,7 +308,7 @@ int run_pass(const Dims& d, const PassArgs& pa, const LayoutSet& ls, const Layou
   gp.go_stride = d.G_res + 1;
   gp.tg_stride = tile_map_len(d);
   gp.split_ok = split_ok;
-  gp.sync = w.gsync[set];
+  gp.sync = w.gsync != nullptr ? w.gsync + (size_t)slot * w.sync_stride : nullptr;
   hipError_t e = launch_gmm(d, pa, gp, w.slot_expert, wg, wu, wd, w.act[set], w.out[set], rows,
                             nullptr, s);
   if (e != hipSuccess) return MOE_EHIP;
@@ -562,7 +567,8 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
   hipStream_t s = (hipStream_t)stream;
 
   hipError_t e = launch_route(d, logits, w.topk_idx, w.topk_gate,
-                              count_hist_area(d, w.count_scratch), s);
+                              count_hist_area(d, w.count_scratch), s, w.gsync,
+                              w.sync_slots * w.sync_stride);
   if (e != hipSuccess) return MOE_EHIP;
   // without rerouting every assignment goes to its expert's home slot, so
   // the layout reads the top-k directly; when the layout fuses its scan and
@@ -611,8 +617,8 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
     } else {
       pa = static_pass(d, ls, b);
     }
-    st = run_pass(d, pa, ls, lb, x, w_gate, w_up, w_down, y, w, set, ss == nullptr, rows, drows,
-                  sb);
+    st = run_pass(d, pa, ls, lb, x, w_gate, w_up, w_down, y, w, set, b, ss == nullptr, rows,
+                  drows, sb);
   }
   if (ss != nullptr) {
     // join even after a failed launch, so the caller's stream never runs

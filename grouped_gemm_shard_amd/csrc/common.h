@@ -202,8 +202,10 @@ __host__ __device__ __forceinline__ int route_hist_blocks(const Dims& d) {
 
 // Router top-k.  With ph non-null (route_hist_blocks(d) x E ints) it also
 // leaves per-block expert histograms for launch_count.
+// zero / zero_n: ints the route launch also clears (counters that later
+// launches of the same call expect at zero), or none.
 hipError_t launch_route(const Dims& d, const float* logits, int* idx, float* gate, int* ph,
-                        hipStream_t s);
+                        hipStream_t s, int* zero = nullptr, int zero_n = 0);
 
 // Scratch of the count step: per-block expert histograms and error flags,
 // and for rerouting kSortBlocks*R ints of block histograms and T*k packed
@@ -301,10 +303,13 @@ struct GemmPass {
   int go_stride, tg_stride;
   bool split_ok;          // long-F passes may split their m-tiles over the side stream
   int* sync;              // bf16: counters of the one-launch GEMM1+GEMM2 kernel
-                          // (gmm_sync_bytes); null: from scratch if given, else two launches
+                          // (gmm_sync_bytes), zeroed by an earlier launch of the
+                          // call; null: in scratch (zeroed with the tile map) when
+                          // tile_off is null, else two launches
 };
 size_t gmm_scratch_bytes(const Dims& d);
 size_t gmm_sync_bytes(const Dims& d);
+int gmm_sync_ints(const Dims& d);  // ints of gmm_sync_bytes the kernel expects at zero
 
 // A second stream per device (default priority), with the events that fork
 // work onto it from a caller's stream and join it back.  Whoever enqueues

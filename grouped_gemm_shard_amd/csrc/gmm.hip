@@ -539,14 +539,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_fused_kernel(GemmParams P1, Ge
     gmm_tile<BM, BK, NST, NW, NWN, false>(P2, smem, nullptr, row0, rows, nt, e);
 }
 
-// Zeroes the fused kernel's counters and flags (a fill kernel, so that the
-// layer stays capturable in a graph).
-__global__ __launch_bounds__(256) void gmm_sync_clear_kernel(int* sync, int n, PassArgs pa) {
-  PassInfo pi = resolve_pass(pa);
-  if (!pi.active) return;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) sync[i] = 0;
-}
-
 // fp32 path (the tiny fp32 workload): one thread per output element.
 struct F32Params {
   const float* A;
@@ -605,9 +597,10 @@ __global__ __launch_bounds__(256) void gmm_f32_kernel(F32Params P) {
 __global__ __launch_bounds__(1024) void tile_schedule_kernel(int G, int bm, int limit,
                                                              const int* group_offsets,
                                                              int* tile_off, int* tile_group,
-                                                             PassArgs pa) {
+                                                             int* sync, int sync_n, PassArgs pa) {
   PassInfo pi = resolve_pass(pa);
   if (!pi.active) return;
+  for (int i = threadIdx.x; i < sync_n; i += blockDim.x) sync[i] = 0;
   __shared__ int tmp[16];
   __shared__ int bad;
   if (threadIdx.x == 0) bad = 0;
@@ -731,9 +724,7 @@ hipError_t launch_bf16(const Dims& d, const PassArgs& pa, const GemmPass& gp, co
   p1.parts = p2.parts = 1;
 
   if (gsync != nullptr && (MOE_GEMM_FUSE & (BM == 256 ? 2 : 1))) {
-    // both GEMMs in one launch, after zeroing its counters and flags
-    const int nsync = kSyncFlags + p1.mt_cap;
-    hipLaunchKernelGGL(gmm_sync_clear_kernel, dim3(1), dim3(256), 0, s, gsync, nsync, pa);
+    // both GEMMs in one launch (its counters and flags were zeroed before)
     // one workgroup per ticket: 8 groups of up to ceil(mt_ub / 8) m-tiles,
     // GEMM1 and GEMM2 tiles
     const long long nbf = 8 * ((mt_ub + 7) / 8) * (long long)(p1.n_ntiles + p2.n_ntiles);
@@ -807,9 +798,9 @@ std::mutex& side_mutex() {
   return mu;
 }
 
-size_t gmm_sync_bytes(const Dims& d) {
-  return ((size_t)(kSyncFlags + tile_map_len(d)) * 4 + 255) / 256 * 256;
-}
+int gmm_sync_ints(const Dims& d) { return kSyncFlags + tile_map_len(d); }
+
+size_t gmm_sync_bytes(const Dims& d) { return ((size_t)gmm_sync_ints(d) * 4 + 255) / 256 * 256; }
 
 size_t gmm_scratch_bytes(const Dims& d) {
   return ((size_t)(d.G_res + 1) * 4 + 255) / 256 * 256 +
@@ -829,11 +820,12 @@ hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const GemmPass& gp,
       int* t1 = (int*)((char*)scratch + ((size_t)(d.G_res + 1) * 4 + 255) / 256 * 256);
       long long lim = (long long)d.T * d.k;
       if (max_rows < lim) lim = max_rows;
-      hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, d.G_res, d.gemm_bm,
-                         (int)lim, gp.group_offsets, t0, t1, pa);
       // the fused kernel's counters follow the tile map in scratch
-      if (gsync == nullptr)
-        gsync = (int*)((char*)t1 + ((size_t)tile_map_len(d) * 4 + 255) / 256 * 256);
+      int* t2 = (int*)((char*)t1 + ((size_t)tile_map_len(d) * 4 + 255) / 256 * 256);
+      if (gsync == nullptr) gsync = t2;
+      hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, d.G_res, d.gemm_bm,
+                         (int)lim, gp.group_offsets, t0, t1, gsync == t2 ? t2 : nullptr,
+                         gsync == t2 ? gmm_sync_ints(d) : 0, pa);
       toff = t0;
       tgroup = t1;
       go_stride = 0;

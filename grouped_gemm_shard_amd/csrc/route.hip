@@ -91,8 +91,12 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
                                                      int E, int k, int gate,
                                                      int* __restrict__ idx,
                                                      float* __restrict__ gate_out,
-                                                     int* __restrict__ ph) {
+                                                     int* __restrict__ ph, int* zero,
+                                                     int zero_n) {
   __shared__ int hist[kMaxExperts];
+  // counters a later launch of the call expects at zero
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < zero_n; i += blockDim.x) zero[i] = 0;
   if (ph != nullptr) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
     __syncthreads();
@@ -118,21 +122,21 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
 
 
 hipError_t launch_route(const Dims& d, const float* logits, int* idx, float* gate, int* ph,
-                        hipStream_t s) {
+                        hipStream_t s, int* zero, int zero_n) {
   // with partial histograms: a fixed grid (rows of ph), tokens strided over it
   const int nb = ph != nullptr ? route_hist_blocks(d) : (d.T + 15) / 16;
   dim3 grid(nb), block(1024);
   int vpl = (d.E + 63) / 64;
   if (vpl <= 1)
-    hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, s, logits, d.T, d.E, d.k, d.gate, idx, gate, ph);
+    hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, s, logits, d.T, d.E, d.k, d.gate, idx, gate, ph, zero, zero_n);
   else if (vpl <= 2)
-    hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, s, logits, d.T, d.E, d.k, d.gate, idx, gate, ph);
+    hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, s, logits, d.T, d.E, d.k, d.gate, idx, gate, ph, zero, zero_n);
   else if (vpl <= 4)
-    hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, s, logits, d.T, d.E, d.k, d.gate, idx, gate, ph);
+    hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, s, logits, d.T, d.E, d.k, d.gate, idx, gate, ph, zero, zero_n);
   else if (vpl <= 8)
-    hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, s, logits, d.T, d.E, d.k, d.gate, idx, gate, ph);
+    hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, s, logits, d.T, d.E, d.k, d.gate, idx, gate, ph, zero, zero_n);
   else
-    hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, s, logits, d.T, d.E, d.k, d.gate, idx, gate, ph);
+    hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, s, logits, d.T, d.E, d.k, d.gate, idx, gate, ph, zero, zero_n);
   return hipGetLastError();
 }
 
