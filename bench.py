@@ -44,14 +44,15 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
-# HBM traffic of the grouped GEMM (both launches) per mid_bf16 layer, from two
-# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by what the counters
-# read for a plain 1 GiB device copy (FETCH_SIZE x1.9999, WRITE_SIZE x1.0).  It
-# holds only for the kernel source it was measured on (sha256 of gmm.hip);
-# for any other source or workload the traffic is reported as null.
+# HBM traffic of the grouped GEMM (its one launch: GEMM1 and GEMM2 fused) per
+# mid_bf16 layer, from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE)
+# scaled by what the counters read for a plain 1 GiB device copy (FETCH_SIZE
+# x1.99985, WRITE_SIZE x1.0).  It holds only for the kernel source it was
+# measured on (sha256 of gmm.hip); for any other source or workload the
+# traffic is reported as null.
 GEMM_TRAFFIC = {"workload": "mid_bf16",
-                "gmm_src_sha256": "57ea78dca44865921743f96ff31122ddc4f6254b330aab47339bcd1e32517df2",
-                "bytes_per_layer": 237845547}
+                "gmm_src_sha256": "89deae133cb21130df1c26a8d819246b6a3753b4a1e9dfe6b8256f7751eb9d28",
+                "bytes_per_layer": 257104578}
 
 
 def recorded_gemm_traffic(workload):
@@ -366,7 +367,11 @@ def main():
         roof = dict(bound="hbm", achieved=round(gemm_gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(gemm_gbs / PEAK_HBM_GBS, 4), traffic=None)
     roof["traffic"] = recorded_gemm_traffic(w.name)
-    roof["kernel"] = "grouped SwiGLU GEMM (gate/up + down launches), per layer"
+    # 128-row tiles (hidden < 2048) run GEMM1 and GEMM2 as one launch
+    roof["kernel"] = ("grouped SwiGLU GEMM per layer: " +
+                      ("GEMM1 and GEMM2 in one launch" if w.hidden < 2048
+                       else "GEMM1 and GEMM2 launches") +
+                      ", with the step call's tile schedule")
 
     bwd = None
     if not args.no_backward:
