@@ -446,20 +446,24 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
 // dispatcher round-robins it to, so a run's weight panels stay in one L2).
 // Each workgroup takes one ticket from its group's counter: the group's
 // GEMM1 tiles come first (bands of GM m-tiles, n-tile by n-tile), then its
-// GEMM2 tiles in the same band order; tickets past the end exit.  A GEMM1
-// tile bumps its m-tile's flag after its act stores; a GEMM2 tile waits for
-// the flag to reach the GEMM1 n-tile count.  A workgroup only ever waits on
-// GEMM1 tiles whose tickets came before its own, held by workgroups already
-// running that wait on nothing, so every wait ends (and is bounded
-// besides).  sync: [8 groups][16] counters, then one flag per m-tile, all
-// zero at launch.
+// GEMM2 tiles; tickets past the end exit.  A GEMM1 tile bumps its m-tile's
+// count after its act stores, and the tile that completes the count appends
+// the m-tile to the group's ready list.  GEMM2 tickets take the m-tiles in
+// ready-list order (the i-th n2 tickets: the i-th m-tile to complete), so a
+// GEMM2 tile waits only while no further m-tile has completed.  A workgroup
+// only ever waits on GEMM1 tiles whose tickets came before its own, held by
+// workgroups already running that wait on nothing, so every wait ends (and
+// is bounded besides).  sync: [8 groups][16] ints (ticket counter, ready
+// count), one count per m-tile, then the ready lists (group v's at its first
+// m-tile), all zero at launch.
 //
 // Visibility of act: GEMM1 writes it through to the device-wide level
-// (cache policy sc1), and waits for the stores before bumping the flag.  No
+// (cache policy sc1) and waits for the stores before its count; the ready
+// entry is written after the last count, with a device-scope store.  No
 // cache of the reader can hold an older copy of those rows: they are read
-// in this launch only after their flag, and caches start the launch clean;
-// the reader still drops its CU's L1 before its loads.
-constexpr int kSyncFlags = 128;     // ints before the flags
+// in this launch only after their ready entry, and caches start the launch
+// clean; the reader still drops its CU's L1 before its loads.
+constexpr int kSyncFlags = 128;     // ints before the per-m-tile counts
 constexpr int kSpinLimit = 1 << 22; // ~0.2 s of sleeps: far beyond any GEMM1 tile
 
 template <int BM, int BK, int NST, int NW, int NWN>
@@ -469,7 +473,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_fused_kernel(GemmParams P1, Ge
   constexpr int RING = NST * (BM + BNB) * BK * 2;
   static_assert(!HAS_REM || shape_waves(MOE_GEMM_REM) == NW, "REM runs in the same block");
   __shared__ __attribute__((aligned(1024))) char smem[HAS_REM && kRemRing > RING ? kRemRing : RING];
-  __shared__ int s_ticket;
+  __shared__ int s_ticket, s_m;
   PassInfo pi = resolve_pass(P1.pa);
   if (!pi.active) return;
   const int* group_offsets = P1.group_offsets + (size_t)pi.j * P1.go_stride;
@@ -489,14 +493,32 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_fused_kernel(GemmParams P1, Ge
   const int t = s_ticket;
   if (t >= tot) return;
   const bool first = t < t1;
-  const int nn = first ? n1 : n2;
-  const int L = first ? t : t - t1;
-  const int band = L / (GM * nn);
-  const int gm = min(GM, mv - band * GM);
-  const int r = L - band * GM * nn;
-  const int nt = r / gm;
-  const int m = m0 + band * GM + (r - nt * gm);
-  int* flag = sync + kSyncFlags + m;
+  int* ready = sync + kSyncFlags + P1.mt_cap + m0;  // the group's completed m-tiles, + 1
+  int m, nt;
+  if (first) {
+    // GEMM1 tiles in bands of GM m-tiles, n-tile by n-tile
+    const int band = t / (GM * n1);
+    const int gm = min(GM, mv - band * GM);
+    const int r = t - band * GM * n1;
+    nt = r / gm;
+    m = m0 + band * GM + (r - nt * gm);
+  } else {
+    // the GEMM2 tiles of the i-th m-tile of the group to complete its GEMM1
+    // tiles, n-tile by n-tile
+    const int u = t - t1, i = u / n2;
+    nt = u - i * n2;
+    if (tid == 0) {
+      int spins = 0, val;
+      while ((val = __hip_atomic_load(ready + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
+                 0 &&
+             ++spins < kSpinLimit)
+        __builtin_amdgcn_s_sleep(2);
+      s_m = val - 1;  // -1 only if the bounded wait ran out
+    }
+    __syncthreads();
+    m = s_m;
+    if (m < m0 || m >= m0 + mv) return;
+  }
   // the tile's rows and expert (none when the map is malformed or the slot
   // hosts no resident expert: the flag still counts the tile)
   int row0 = 0, rows = 0, e = -1;
@@ -518,19 +540,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_fused_kernel(GemmParams P1, Ge
       else
         gmm_tile<BM, BK, NST, NW, NWN, true, true>(P1, smem, aidx, row0, rows, nt, e);
     }
-    // every thread's write-through act stores are complete before the flag
+    // every thread's write-through act stores are complete before the flag;
+    // the m-tile's last GEMM1 tile appends it to the group's ready list
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) atomicAdd(flag, 1);
+    if (tid == 0 && atomicAdd(sync + kSyncFlags + m, 1) == n1 - 1) {
+      const int slot = atomicAdd(sync + v * 16 + 1, 1);
+      if (slot < mv)
+        __hip_atomic_store(ready + slot, m + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     return;
   }
-  if (tid == 0) {
-    int spins = 0;
-    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n1 &&
-           ++spins < kSpinLimit)
-      __builtin_amdgcn_s_sleep(2);
-  }
-  __syncthreads();
   if (e < 0) return;
   asm volatile("buffer_inv sc0" ::: "memory");  // this CU's L1
   if (HAS_REM && rows <= kRemBM)
@@ -538,6 +558,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_fused_kernel(GemmParams P1, Ge
   else
     gmm_tile<BM, BK, NST, NW, NWN, false>(P2, smem, nullptr, row0, rows, nt, e);
 }
+
 
 // fp32 path (the tiny fp32 workload): one thread per output element.
 struct F32Params {
@@ -798,7 +819,7 @@ std::mutex& side_mutex() {
   return mu;
 }
 
-int gmm_sync_ints(const Dims& d) { return kSyncFlags + tile_map_len(d); }
+int gmm_sync_ints(const Dims& d) { return kSyncFlags + 2 * tile_map_len(d); }
 
 size_t gmm_sync_bytes(const Dims& d) { return ((size_t)gmm_sync_ints(d) * 4 + 255) / 256 * 256; }
 
