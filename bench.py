@@ -51,8 +51,8 @@ PEAK_HBM_GBS = 8000.0
 # measured on (sha256 of gmm.hip); for any other source or workload the
 # traffic is reported as null.
 GEMM_TRAFFIC = {"workload": "mid_bf16",
-                "gmm_src_sha256": "89deae133cb21130df1c26a8d819246b6a3753b4a1e9dfe6b8256f7751eb9d28",
-                "bytes_per_layer": 257104578}
+                "gmm_src_sha256": "9f12ead96736eb9d27e2c44f3002b62c4e20739d687e4735d65104c779c070f0",
+                "bytes_per_layer": 257437256}
 
 
 def recorded_gemm_traffic(workload):
