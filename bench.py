@@ -17,9 +17,11 @@ run on, to give achieved TFLOP/s and GB/s against MI355X peaks.  The
 backward of the same passes (given the forward's saved x_sorted and expert
 outputs) is timed as a whole and step by step ("backward" in the JSON), and so is
 the whole-layer backward call (which also recomputes the routing, layouts,
-x_sorted and expert outputs) and a training step's layer forward plus it.  The CPU
-oracle is then timed on the host cores on the same inputs.  One JSON line is
-printed at the end.
+x_sorted and expert outputs) and a training step's layer forward plus it.  A
+plain device copy and the vendor library's dense bf16 GEMM are timed as what
+this box reaches outside the library ("measured_peaks").  The CPU oracle is
+then timed on the host cores on the same inputs.  One JSON line is printed at
+the end.
 """
 
 from __future__ import annotations
@@ -279,6 +281,30 @@ def backward_figures(p, w, inp, info, reps):
                 flops=flops, rows=n_rows, gemm_bytes=w_bytes + row_bytes + dw_bytes)
 
 
+def measured_peaks(reps=10):
+    """What this machine reaches outside the library, as context for the
+    fractions of the spec peaks: a plain 1 GiB device-to-device copy (bytes
+    read + written per second) and torch's dense bf16 GEMM (the vendor
+    library) at 8192^3.  Timed with HIP events on the current stream."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = time_calls(lambda: dst.copy_(src), reps)
+    del src, dst
+    n = 8192
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    a = torch.randn((n, n), generator=gen, device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), generator=gen, device="cuda").to(torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    t_mm = time_calls(lambda: torch.mm(a, b, out=c), reps)
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"hbm_copy_gbs": round(2 * (1 << 30) / t_copy / 1e9, 1),
+            "dense_bf16_gemm_tflops": round(2.0 * n ** 3 / t_mm / 1e12, 1),
+            "method": "1 GiB device copy (read + written bytes); torch.mm bf16 8192^3; "
+                      f"HIP events, mean of {reps}"}
+
+
 def workloads_pass_tokens(w, n, c):
     lc = w.seq_len // n
     b = np.arange(w.tokens // w.seq_len)[:, None] * w.seq_len
@@ -416,6 +442,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    log("[bench] measured peaks (plain copy, vendor dense GEMM)")
+    peaks = measured_peaks()
+    roof["frac_of_measured"] = round(
+        roof["achieved"] / (peaks["hbm_copy_gbs"] if roof["bound"] == "hbm"
+                            else peaks["dense_bf16_gemm_tflops"] if w.bf16 else peak_mm), 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
@@ -440,12 +472,17 @@ def main():
                    "fallback_ran": int(info[1]),
                    "chunks_per_pass": g.layer_chunks_per_pass(p, g.MODE_LAYER)},
         "gemm": {"tflops": round(gemm_tflops, 2), "frac_mfma_peak": round(gemm_tflops / peak_mm, 4),
+                 "frac_of_dense_gemm": (round(gemm_tflops / peaks["dense_bf16_gemm_tflops"], 4)
+                                        if w.bf16 else None),
                  "gbs": round(gemm_gbs, 1), "arith_intensity": round(ai, 1),
                  "us_per_layer": round(kf["t_gmm"] * 1e6, 2), "rows": kf["rows"]},
         "permute": {"gbs": round(perm_gbs, 1), "frac_hbm_peak": round(perm_gbs / PEAK_HBM_GBS, 4),
+                    "frac_measured_copy": round(perm_gbs / peaks["hbm_copy_gbs"], 4),
                     "us_per_layer": round(kf["t_perm"] * 1e6, 2)},
         "combine": {"gbs": round(comb_gbs, 1), "frac_hbm_peak": round(comb_gbs / PEAK_HBM_GBS, 4),
+                    "frac_measured_copy": round(comb_gbs / peaks["hbm_copy_gbs"], 4),
                     "us_per_layer": round(kf["t_comb"] * 1e6, 2)},
+        "measured_peaks": peaks,
         "roofline": roof,
         "cpu_baseline": cpu,
         "backward": bwd,
