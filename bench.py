@@ -377,6 +377,18 @@ def main():
     ms = (t1 - t0) / args.steps * 1e3
     tokens_s = w.tokens / (ms / 1e3)
 
+    # the same layer in the other modes: the capped pass alone (rows beyond
+    # the buffer dropped), the chunked dropless fallback always, and the
+    # single uncapped pass (worst-case buffer)
+    mode_ms = {}
+    for name, mode in (("capped_only", g.MODE_CAPPED_ONLY), ("force_chunked", g.MODE_FORCE_CHUNKED),
+                       ("force_dropless", g.MODE_FORCE_DROPLESS)):
+        mrun = g.LayerRunner(p, mode)
+        mode_ms[name] = time_calls(lambda: mrun(inp["x"], inp["logits"], *inp["weights"]),
+                                   args.kernel_reps) * 1e3
+        del mrun
+    torch.cuda.empty_cache()
+
     log("[bench] per-kernel timing")
     kf = kernel_figures(p, w, inp, info, args.kernel_reps)
     peak_mm = PEAK_BF16_TFLOPS if w.bf16 else PEAK_FP32_TFLOPS
@@ -484,6 +496,13 @@ def main():
                     "us_per_layer": round(kf["t_comb"] * 1e6, 2)},
         "measured_peaks": peaks,
         "roofline": roof,
+        "layer_modes": {
+            "assignments_per_s": round(kf["rows"] / (ms / 1e3), 1),
+            "ms_layer": round(ms, 4),
+            **{f"ms_{k}": round(v, 4) for k, v in mode_ms.items()},
+            "layer_over_capped_only": round(ms / mode_ms["capped_only"], 3),
+            "note": "assignments/s: rows of the passes LAYER mode took per second of the "
+                    "layer step; the other modes are timed one call at a time with HIP events"},
         "cpu_baseline": cpu,
         "backward": bwd,
     }
