@@ -202,7 +202,10 @@ int moe_permute(const moe_problem* p, int32_t num_chunks, int32_t chunk, int32_t
  * uses its home expert's weights):
  *   act[n]        = SiLU(x_sorted[n] Wg^T) * (x_sorted[n] Wu^T)   [max_rows,F]
  *   expert_out[n] = act[n] Wd^T                                   [max_rows,H]
- * SiLU(z) = z/(1+exp(-z)).  Rows past group_offsets[G_res] are untouched. */
+ * SiLU(z) = z/(1+exp(-z)).  Rows past group_offsets[G_res] are untouched.
+ * bf16: offsets that are not a non-decreasing sequence within [0, min(max_rows,
+ * T*k)] compute nothing (act and expert_out untouched); the status is still
+ * MOE_OK, since the offsets are read on the device only. */
 int moe_gmm_swiglu(const moe_problem* p, const void* x_sorted, const int32_t* group_offsets,
                    const int32_t* slot_expert, const void* w_gate, const void* w_up,
                    const void* w_down, void* act, void* expert_out, int64_t max_rows,

@@ -7,9 +7,12 @@ expert (k = E), one expert per shard with only some shards resident, a
 fallback whose chunks hold one position of each sequence, a single token,
 heavy capped drops, more resident slots than the fused layout holds, 256-row
 GEMM tiles with the long-F split, and the fp32 path with dedup and redundant
-slots.
+slots.  The grouped GEMM is also given malformed group offsets (both tile
+heights): it must compute nothing, and the same workspace must then serve a
+well-formed call.
 """
 
+import numpy as np
 import pytest
 import torch
 
@@ -80,3 +83,53 @@ def test_edge_layer_all_modes(name):
         ys[mode] = y
     assert torch.equal(ys[g.MODE_FORCE_DROPLESS], ys[g.MODE_FORCE_CHUNKED])
     assert torch.equal(ys[g.MODE_LAYER], ys[g.MODE_FORCE_DROPLESS])
+
+
+MALFORMED = {
+    # group offsets that are not non-decreasing within [0, rows]: the first
+    # group ends before it starts
+    "decreasing": lambda G, rows: [0, 64, 32] + [64] * (G - 2),
+    # the last offset past the rows the buffers hold
+    "past_rows": lambda G, rows: [0] + [rows + 1] * G,
+    # a negative first offset
+    "negative": lambda G, rows: [-8] + [16] * G,
+}
+
+
+@pytest.mark.parametrize("hidden", [256, 2048])   # 128-row tiles (one launch), 256-row tiles
+@pytest.mark.parametrize("case", sorted(MALFORMED))
+def test_gmm_malformed_offsets_touch_nothing(case, hidden):
+    """The bf16 grouped GEMM given group offsets that are not a non-decreasing
+    sequence within [0, rows] computes nothing: act and expert_out keep their
+    contents (the tile schedule gives no tiles, so no workgroup waits or
+    writes)."""
+    import grouped_gemm_shard_amd as g
+    w = W(f"malformed_{hidden}", tokens=64, seq_len=64, hidden=hidden, ffn=256, num_experts=8,
+          top_k=2, num_shards=4, res_lo=0, res_hi=4, factor=2.0, num_chunks=2)
+    p = binding_problem(w)
+    say(f"[gmm malformed] {case} H={hidden}")
+    rows = 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    xs = torch.randn((rows, hidden), generator=gen, device="cuda").to(torch.bfloat16)
+    wts = workloads.make_weights(w, device="cuda")
+    se = torch.arange(p.num_slots, dtype=torch.int32, device="cuda")  # home slots, no replicas
+    go = torch.tensor(MALFORMED[case](p.g_res, rows), dtype=torch.int32, device="cuda")
+    assert go.numel() == p.g_res + 1
+    act = torch.full((rows, w.ffn), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = torch.full((rows, hidden), 7.0, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(g.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    g.moe_gmm_swiglu(p, xs, go, se, *wts, act, out, ws)
+    torch.cuda.synchronize()
+    assert torch.all(act == 7.0) and torch.all(out == 7.0)
+    # the same workspace then serves a well-formed call (counters re-zeroed)
+    go_ok = torch.tensor([min(16 * i, rows) for i in range(p.g_res + 1)], dtype=torch.int32,
+                         device="cuda")
+    g.moe_gmm_swiglu(p, xs, go_ok, se, *wts, act, out, ws)
+    torch.cuda.synchronize()
+    n = int(go_ok[-1].item())
+    o_act, o_out = oracle.gmm_swiglu(oracle_problem(w), host(xs[:n]), ints(go_ok),
+                                     np.arange(p.g_res), *[host(t) for t in wts])
+    check_close(host(act[:n]), o_act, f"act after malformed {case} H={hidden}")
+    check_close(host(out[:n]), o_out, f"expert_out after malformed {case} H={hidden}")
+    assert torch.all(out[n:] == 7.0)
