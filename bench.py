@@ -53,8 +53,8 @@ PEAK_HBM_GBS = 8000.0
 # measured on (sha256 of gmm.hip); for any other source or workload the
 # traffic is reported as null.
 GEMM_TRAFFIC = {"workload": "mid_bf16",
-                "gmm_src_sha256": "9f12ead96736eb9d27e2c44f3002b62c4e20739d687e4735d65104c779c070f0",
-                "bytes_per_layer": 257437256}
+                "gmm_src_sha256": "6bd49b9048391c64aef857c6ad9679726fff97383f26937cdf13b718e0908179",
+                "bytes_per_layer": 260268700}
 
 
 def recorded_gemm_traffic(workload):

@@ -520,7 +520,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_fused_kernel(GemmParams P1, Ge
     if (m < m0 || m >= m0 + mv) return;
   }
   // the tile's rows and expert (none when the map is malformed or the slot
-  // hosts no resident expert: the flag still counts the tile)
+  // hosts no resident expert: the m-tile's count still counts the tile)
   int row0 = 0, rows = 0, e = -1;
   const int g = tile_group[m];
   if (g >= 0 && g < P1.G) {
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_fused_kernel(GemmParams P1, Ge
       else
         gmm_tile<BM, BK, NST, NW, NWN, true, true>(P1, smem, aidx, row0, rows, nt, e);
     }
-    // every thread's write-through act stores are complete before the flag;
+    // every thread's write-through act stores are complete before the count;
     // the m-tile's last GEMM1 tile appends it to the group's ready list
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -558,7 +558,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_fused_kernel(GemmParams P1, Ge
   else
     gmm_tile<BM, BK, NST, NW, NWN, false>(P2, smem, nullptr, row0, rows, nt, e);
 }
-
 
 // fp32 path (the tiny fp32 workload): one thread per output element.
 struct F32Params {
