@@ -25,7 +25,8 @@ __all__ = [
     "moe_combine_from_partials", "moe_layer_dropless_chunked", "status_string", "LayerRunner",
     "bwd_workspace_bytes", "moe_combine_bwd", "moe_gmm_swiglu_bwd",
     "moe_permute_bwd", "moe_route_bwd", "layer_bwd_workspace_bytes", "moe_layer_bwd",
-    "LayerBackwardRunner",
+    "LayerBackwardRunner", "testing_set_gemm_wait_limit", "ERR_BAD_INDEX", "ERR_BAD_OFFSETS",
+    "ERR_GEMM_WAIT",
 ]
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EHIP = 0, -1, -2, -3, -4
@@ -38,7 +39,11 @@ EXPORTED = ["moe_workspace_bytes", "moe_pass_max_rows", "moe_layer_workspace_byt
             "moe_combine", "moe_combine_partial", "moe_combine_from_partials",
             "moe_layer_dropless_chunked", "moe_bwd_workspace_bytes", "moe_combine_bwd",
             "moe_gmm_swiglu_bwd", "moe_permute_bwd", "moe_route_bwd",
-            "moe_layer_bwd_workspace_bytes", "moe_layer_bwd", "moe_status_string"]
+            "moe_layer_bwd_workspace_bytes", "moe_layer_bwd", "moe_status_string",
+            "moe_testing_set_gemm_wait_limit"]
+
+# Device-side error bits (include/moe_shard.h)
+ERR_BAD_INDEX, ERR_BAD_OFFSETS, ERR_GEMM_WAIT = 1, 2, 4
 
 lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_shard.so")
 
@@ -122,10 +127,10 @@ def _load():
         "moe_layer_workspace_bytes": [P, i32, ctypes.POINTER(sz)],
         "moe_layer_chunks_per_pass": [P, i32, ctypes.POINTER(i32)],
         "moe_route": [P, vp, vp, vp, vp],
-        "moe_count_overflow": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_count_overflow": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_permute": [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp,
                         sz, vp],
-        "moe_gmm_swiglu": [P, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, sz, vp],
+        "moe_gmm_swiglu": [P, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp],
         "moe_combine": [P, i32, i32, vp, vp, vp, vp, vp],
         "moe_combine_partial": [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp],
         "moe_combine_from_partials": [P, i32, i32, i32, vp, vp, vp, vp, i64, i64, vp],
@@ -138,6 +143,7 @@ def _load():
         "moe_route_bwd": [P, vp, vp, vp, vp, vp],
         "moe_layer_bwd_workspace_bytes": [P, i32, ctypes.POINTER(sz)],
         "moe_layer_bwd": [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_testing_set_gemm_wait_limit": [i32],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -164,6 +170,13 @@ def __getattr__(name):
     if name == "lib":
         return _lib()
     raise AttributeError(name)
+
+
+def testing_set_gemm_wait_limit(spins: int):
+    """Test hook (include/moe_testing.h): bound of the grouped GEMM's wait in
+    sleeps for every later call; 0 restores the default, < 0 gives up at
+    once."""
+    _check("moe_testing_set_gemm_wait_limit", _lib().moe_testing_set_gemm_wait_limit(spins))
 
 
 def status_string(status: int) -> str:
@@ -233,15 +246,16 @@ def moe_route(p: Problem, logits, topk_idx, topk_gate, stream=None):
 
 
 def moe_count_overflow(p: Problem, topk_idx, expert_counts, slot_expert, ndiv, slot_of_assign,
-                       shard_counts, status, ws, stream=None):
+                       shard_counts, status, ws, stream=None, required_factor=None):
+    """required_factor: a float32 tensor of one element, or None."""
     w, nb = _ws(ws)
     i32 = torch.int32
     _check("moe_count_overflow", _lib().moe_count_overflow(
         ctypes.byref(p.c()), _ptr(topk_idx, i32, "topk_idx"),
         _ptr(expert_counts, i32, "expert_counts"), _ptr(slot_expert, i32, "slot_expert"),
         _ptr(ndiv, i32, "ndiv"), _ptr(slot_of_assign, i32, "slot_of_assign"),
-        _ptr(shard_counts, i32, "shard_counts"), _ptr(status, i32, "status"), w, nb,
-        _stream(stream)))
+        _ptr(shard_counts, i32, "shard_counts"), _ptr(status, i32, "status"),
+        _ptr(required_factor, torch.float32, "required_factor"), w, nb, _stream(stream)))
 
 
 def moe_permute(p: Problem, num_chunks, chunk, capped, x, slot_of_assign, group_offsets,
@@ -261,7 +275,9 @@ def moe_permute(p: Problem, num_chunks, chunk, capped, x, slot_of_assign, group_
 
 
 def moe_gmm_swiglu(p: Problem, x_sorted, group_offsets, slot_expert, w_gate, w_up, w_down, act,
-                   expert_out, ws, stream=None):
+                   expert_out, ws, stream=None, status=None):
+    """status: an int32 tensor of one element (receives the MOE_ERR_* bits),
+    or None."""
     w, nb = _ws(ws)
     i32 = torch.int32
     max_rows = min(x_sorted.shape[0], act.shape[0], expert_out.shape[0])
@@ -270,7 +286,8 @@ def moe_gmm_swiglu(p: Problem, x_sorted, group_offsets, slot_expert, w_gate, w_u
         _ptr(group_offsets, i32, "group_offsets"), _ptr(slot_expert, i32, "slot_expert"),
         _ptr(w_gate, p.dtype, "w_gate"), _ptr(w_up, p.dtype, "w_up"),
         _ptr(w_down, p.dtype, "w_down"), _ptr(act, p.dtype, "act"),
-        _ptr(expert_out, p.dtype, "expert_out"), max_rows, w, nb, _stream(stream)))
+        _ptr(expert_out, p.dtype, "expert_out"), max_rows, _ptr(status, i32, "status"), w, nb,
+        _stream(stream)))
 
 
 def moe_combine(p: Problem, num_chunks, chunk, expert_out, row_of_assign, topk_gate, y,
@@ -418,7 +435,8 @@ class LayerRunner:
         self.p, self.mode = p, mode
         self.ws = torch.empty(layer_workspace_bytes(p, mode), dtype=torch.uint8, device=device)
         self.y = torch.empty((p.tokens, p.hidden), dtype=p.dtype, device=device)
-        self.info = torch.zeros(4, dtype=torch.int32, device=device)
+        # [overflow, fallback_ran, cap, max shard count, MOE_ERR_* bits]
+        self.info = torch.zeros(5, dtype=torch.int32, device=device)
 
     def __call__(self, x, logits, w_gate, w_up, w_down, stream=None):
         moe_layer_dropless_chunked(self.p, self.mode, x, logits, w_gate, w_up, w_down, self.y,

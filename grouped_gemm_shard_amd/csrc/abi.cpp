@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "common.h"
+#include "moe_testing.h"
 #include "sort.h"
 
 using namespace moe;
@@ -76,7 +77,7 @@ int make_dims(const moe_problem* p, Dims* d) {
     d->cap = -1;
   }
   // chunks: given, or ceil(S / factor) (the same page's Shortcomings:
-  // "8x for EP16 / factor 2")
+  // example: 16 shards at factor 2 make eight chunks)
   int n = p->num_chunks;
   if (n == 0) n = f > 0.0 ? (int)ceil((double)d->S / f) : 1;
   if (n < 1 || n > d->L || d->L % n != 0) return MOE_EINVAL;
@@ -220,6 +221,9 @@ struct LayerWs {
   // slot (bf16), zeroed by the route launch of the call
   int* gsync;
   int sync_stride, sync_slots;
+  // where the grouped GEMM reports MOE_ERR_* bits (not carved: the caller's
+  // info word, else status[3])
+  int* err;
   size_t bytes;
 };
 
@@ -260,6 +264,7 @@ LayerWs carve_layer(const Dims& d, const LayoutSet& ls, int64_t rows, int64_t dr
   w.sync_stride = (int)(gmm_sync_bytes(d) / 4);
   w.sync_slots = d.bf16 ? layer_pass_slots(ls) : 0;
   w.gsync = w.sync_slots > 0 ? (int*)take((size_t)w.sync_slots * gmm_sync_bytes(d)) : nullptr;
+  w.err = w.status != nullptr ? w.status + 3 : nullptr;
   w.bytes = off;
   return w;
 }
@@ -309,6 +314,7 @@ int run_pass(const Dims& d, const PassArgs& pa, const LayoutSet& ls, const Layou
   gp.tg_stride = tile_map_len(d);
   gp.split_ok = split_ok;
   gp.sync = w.gsync != nullptr ? w.gsync + (size_t)slot * w.sync_stride : nullptr;
+  gp.err = w.err;
   hipError_t e = launch_gmm(d, pa, gp, w.slot_expert, wg, wu, wd, w.act[set], w.out[set], rows,
                             nullptr, s);
   if (e != hipSuccess) return MOE_EHIP;
@@ -376,8 +382,8 @@ int moe_route(const moe_problem* p, const float* logits, int32_t* topk_idx, floa
 
 int moe_count_overflow(const moe_problem* p, const int32_t* topk_idx, int32_t* expert_counts,
                        int32_t* slot_expert, int32_t* ndiv, int32_t* slot_of_assign,
-                       int32_t* shard_counts, int32_t* status, void* ws, size_t ws_bytes,
-                       void* stream) {
+                       int32_t* shard_counts, int32_t* status, float* required_factor, void* ws,
+                       size_t ws_bytes, void* stream) {
   Dims d;
   int st = make_dims(p, &d);
   if (st != MOE_OK) return st;
@@ -387,7 +393,8 @@ int moe_count_overflow(const moe_problem* p, const int32_t* topk_idx, int32_t* e
   if (misaligned(ws, 256)) return MOE_EINVAL;
   if (ws_bytes < count_scratch_bytes(d)) return MOE_ECAPACITY;
   return hip_status(launch_count(d, topk_idx, expert_counts, slot_expert, ndiv, slot_of_assign,
-                                 shard_counts, status, ws, 0, nullptr, 0, (hipStream_t)stream));
+                                 shard_counts, status, ws, 0, nullptr, 0, required_factor,
+                                 (hipStream_t)stream));
 }
 
 int moe_permute(const moe_problem* p, int32_t num_chunks, int32_t chunk, int32_t capped,
@@ -446,8 +453,8 @@ int moe_permute(const moe_problem* p, int32_t num_chunks, int32_t chunk, int32_t
 
 int moe_gmm_swiglu(const moe_problem* p, const void* x_sorted, const int32_t* group_offsets,
                    const int32_t* slot_expert, const void* w_gate, const void* w_up,
-                   const void* w_down, void* act, void* expert_out, int64_t max_rows, void* ws,
-                   size_t ws_bytes, void* stream) {
+                   const void* w_down, void* act, void* expert_out, int64_t max_rows,
+                   int32_t* status, void* ws, size_t ws_bytes, void* stream) {
   Dims d;
   int st = make_dims(p, &d);
   if (st != MOE_OK) return st;
@@ -467,7 +474,10 @@ int moe_gmm_swiglu(const moe_problem* p, const void* x_sorted, const int32_t* gr
   gp.a_src_rows = (int)max_rows;
   gp.a_div = 1;
   gp.group_offsets = group_offsets;
-  gp.split_ok = true;
+  // the step call runs on the caller's stream only (a layer call may split
+  // a long-F single pass over its side stream)
+  gp.split_ok = false;
+  gp.err = status;
   return hip_status(launch_gmm(d, pa, gp, slot_expert, w_gate, w_up, w_down, act, expert_out,
                                max_rows, ws, (hipStream_t)stream));
 }
@@ -563,6 +573,9 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
   if (ws_bytes < w0.bytes) return MOE_ECAPACITY;
   // status[1] (the overflow flag) lives in the workspace
   LayerWs w = carve_layer(d, layer_layout(d, mode, q, nullptr), rows, drows, (char*)ws);
+  // the count step writes the error bits found so far to info[4] (and
+  // status[3]); the grouped GEMM adds its own to the same word
+  if (info != nullptr) w.err = info + 4;
   const LayoutSet ls = layer_layout(d, mode, q, w.status + 1);
   hipStream_t s = (hipStream_t)stream;
 
@@ -583,7 +596,7 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
   } else {
     e = launch_count(d, w.topk_idx, w.expert_counts, w.slot_expert, w.ndiv,
                      reroute ? w.slot_of_assign : nullptr, w.shard_counts, w.status,
-                     w.count_scratch, 1, info, mode, s);
+                     w.count_scratch, 1, info, mode, nullptr, s);
     if (e != hipSuccess) return MOE_EHIP;
     e = launch_layout(d, ls, reroute ? w.slot_of_assign : w.topk_idx, reroute ? 0 : 1, lb,
                       nullptr, s);
@@ -832,7 +845,7 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
   } else {
     e = launch_count(d, f.topk_idx, f.expert_counts, f.slot_expert, f.ndiv,
                      reroute ? f.slot_of_assign : nullptr, f.shard_counts, f.status,
-                     f.count_scratch, 1, nullptr, mode, s);
+                     f.count_scratch, 1, nullptr, mode, nullptr, s);
     if (e != hipSuccess) return MOE_EHIP;
     e = launch_layout(d, ls, reroute ? f.slot_of_assign : f.topk_idx, reroute ? 0 : 1, lb,
                       nullptr, s);
@@ -911,6 +924,11 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
     if (e != hipSuccess) return MOE_EHIP;
   }
   return hip_status(launch_route_bwd(d, f.topk_idx, f.topk_gate, w.d_gate, d_logits, s));
+}
+
+int moe_testing_set_gemm_wait_limit(int32_t spins) {
+  set_gemm_wait_limit(spins);
+  return MOE_OK;
 }
 
 const char* moe_status_string(int status) {

@@ -220,7 +220,7 @@ int* count_hist_area(const Dims& d, void* scratch);
 hipError_t launch_count(const Dims& d, const int* idx, int* expert_counts, int* slot_expert,
                         int* ndiv, int* slot_of_assign, int* shard_counts, int* status,
                         void* scratch, int hist_ready, int* info_out, int info_mode,
-                        hipStream_t s);
+                        float* rfactor, hipStream_t s);
 
 // Arguments of the count step without rerouting (one workgroup): the top-k,
 // per-block expert histograms ph [nb][E] (pbad: per-block bad-id flags, or
@@ -238,6 +238,7 @@ struct CountArgs {
   int* status;
   int* info;            // may be null
   int info_mode;
+  float* rfactor;       // may be null
 };
 // The CountArgs of a layer call whose route step left its histograms in the
 // count scratch.
@@ -302,6 +303,7 @@ struct GemmPass {
   const int* tile_group;
   int go_stride, tg_stride;
   bool split_ok;          // long-F passes may split their m-tiles over the side stream
+  int* err;               // MOE_ERR_* bits of the GEMM are OR-ed into *err (may be null)
   int* sync;              // bf16: counters of the one-launch GEMM1+GEMM2 kernel
                           // (gmm_sync_bytes), zeroed by an earlier launch of the
                           // call; null: in scratch (zeroed with the tile map) when
@@ -322,6 +324,11 @@ struct SideStream {
 };
 SideStream* side_stream();
 std::mutex& side_mutex();
+// Bound of the grouped GEMM's wait for rows another tile of the same launch
+// produces, in sleeps; < 0 makes every such wait give up at once (tests of
+// the MOE_ERR_GEMM_WAIT path).
+int gemm_wait_limit();
+void set_gemm_wait_limit(int spins);  // 0 restores the default
 hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const GemmPass& gp,
                       const int* slot_expert, const void* wg, const void* wu, const void* wd,
                       void* act, void* out, int64_t max_rows, void* scratch, hipStream_t s);

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(1024) void count_sum_kernel(Dims d, const int* __re
   __syncthreads();
   if (threadIdx.x == 0) {
     status[0] = status[1] = status[2] = 0;
-    status[3] = bad ? 1 : 0;
+    status[3] = bad ? MOE_ERR_BAD_INDEX : 0;
   }
 }
 
@@ -207,7 +207,8 @@ __global__ __launch_bounds__(256) void dedup_count_kernel(Dims d,
 
 // status = [cap, overflow, max shard count, error bits]; a strict ">" check.
 __global__ __launch_bounds__(1024) void finalize_kernel(Dims d, const int* __restrict__ shard_counts,
-                                                        int* status, int* info, int info_mode) {
+                                                        int* status, int* info, int info_mode,
+                                                        float* rfactor) {
   __shared__ int red[16];
   int m = 0;
   for (int s = threadIdx.x; s < d.S; s += blockDim.x) m = max(m, shard_counts[s]);
@@ -228,7 +229,9 @@ __global__ __launch_bounds__(1024) void finalize_kernel(Dims d, const int* __res
       info[1] = ran;
       info[2] = d.cap;
       info[3] = mx;
+      info[4] = status[3];
     }
+    if (rfactor != nullptr) *rfactor = required_factor(d, mx);
   }
 }
 
@@ -260,13 +263,14 @@ CountArgs layer_count_args(const Dims& d, const int* idx, int* expert_counts, in
                            int* ndiv, int* shard_counts, int* status, void* scratch, int* info,
                            int info_mode) {
   CountArgs c = {idx, (const int*)scratch, nullptr, route_hist_blocks(d), expert_counts,
-                 slot_expert, ndiv, nullptr, shard_counts, status, info, info_mode};
+                 slot_expert, ndiv, nullptr, shard_counts, status, info, info_mode, nullptr};
   return c;
 }
 
 hipError_t launch_count(const Dims& d, const int* idx, int* expert_counts, int* slot_expert,
                         int* ndiv, int* slot_of_assign, int* shard_counts, int* status,
-                        void* scratch, int hist_ready, int* info, int info_mode, hipStream_t st) {
+                        void* scratch, int hist_ready, int* info, int info_mode, float* rfactor,
+                        hipStream_t st) {
   size_t n = (size_t)d.T * d.k;
   const int nb = route_hist_blocks(d);
   char* p = (char*)scratch;
@@ -290,7 +294,7 @@ hipError_t launch_count(const Dims& d, const int* idx, int* expert_counts, int* 
   const bool reroute = d.R > 0 && d.B > 0;
   if (!reroute) {
     CountArgs c = {idx, ph, pbad, nb, expert_counts, slot_expert, ndiv, slot_of_assign,
-                   shard_counts, status, info, info_mode};
+                   shard_counts, status, info, info_mode, rfactor};
     hipLaunchKernelGGL(count_fused_kernel, dim3(1), dim3(1024), 0, st, d, c);
     return hipGetLastError();
   }
@@ -312,7 +316,7 @@ hipError_t launch_count(const Dims& d, const int* idx, int* expert_counts, int* 
                        shard_counts);
   }
   hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1024), 0, st, d, shard_counts, status, info,
-                     info_mode);
+                     info_mode, rfactor);
   return hipGetLastError();
 }
 

@@ -44,20 +44,29 @@ __device__ __forceinline__ void sum_hist(const Dims& d, const int* __restrict__ 
   __syncthreads();
 }
 
+// The smallest buffer factor that would have fit: max shard count over the
+// balanced share T*k/S ("Support moe_dropless_fallback=layer on the ragged
+// all-to-all MoE path", Shortcomings: the figure the overflow log reports).
+__device__ __forceinline__ float required_factor(const Dims& d, int mx) {
+  return (float)((double)mx * (double)d.S / ((double)d.T * (double)d.k));
+}
+
 __device__ __forceinline__ void write_status(const Dims& d, int mx, int bad, int* status,
-                                             int* info, int info_mode) {
+                                             int* info, int info_mode, float* rfactor) {
   int ovf = (d.cap >= 0 && mx > d.cap) ? 1 : 0;
   status[0] = d.cap;
   status[1] = ovf;
   status[2] = mx;
-  status[3] = bad ? 1 : 0;
+  status[3] = bad ? MOE_ERR_BAD_INDEX : 0;
   if (info != nullptr) {
     int ran = info_mode == MOE_MODE_FORCE_CHUNKED ? 1 : (info_mode == MOE_MODE_LAYER ? ovf : 0);
     info[0] = ovf;
     info[1] = ran;
     info[2] = d.cap;
     info[3] = mx;
+    info[4] = status[3];
   }
+  if (rfactor != nullptr) *rfactor = required_factor(d, mx);
 }
 
 // The whole count step without rerouting, in one workgroup: expert counts
@@ -137,7 +146,7 @@ __device__ __forceinline__ void count_fused_body(const Dims& d, const CountArgs&
   if (threadIdx.x == 0) {
     int mx = 0;
     for (int w = 0; w < (int)(blockDim.x >> 6); ++w) mx = max(mx, red[w]);
-    write_status(d, mx, bad, status, info, info_mode);
+    write_status(d, mx, bad, status, info, info_mode, c.rfactor);
   }
 }
 

@@ -40,6 +40,7 @@
 // of the run, so the blocks an XCD runs together cover a few m-tiles by a
 // few n-tiles of one expert and share both operand panels in its L2, and
 // every XCD gets the same share of tall and short tiles.
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -102,7 +103,14 @@ struct GemmParams {
   int mt_cap;              // fused kernel: m-tiles its completion flags can hold
   long long max_rows;
   PassArgs pa;
+  int* err;                // MOE_ERR_* bits are OR-ed in here (may be null)
+  int spin_limit;          // fused kernel: sleeps before a wait gives up (< 0: at once)
 };
+
+// Reports an error bit found by the device (one report per block).
+__device__ __forceinline__ void report(int* err, int bit) {
+  if (err != nullptr && threadIdx.x == 0) atomicOr(err, bit);
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -133,7 +141,7 @@ __device__ __forceinline__ void vm_wait_barrier() {
 
 // Starts the loads of K step `step` into its ring stage: each wave-wide
 // load fills RPI consecutive rows (1 KB) of the stage.
-template <int BM, int BK, int NST, bool SWIGLU, int NW, bool ACOH>
+template <int BM, int BK, int NST, bool SWIGLU, int NW>
 __device__ __forceinline__ void gmm_issue(char* smem, int step, int w,
                                           __amdgpu_buffer_rsrc_t ra_r, __amdgpu_buffer_rsrc_t rb0,
                                           __amdgpu_buffer_rsrc_t rb1,
@@ -145,12 +153,8 @@ __device__ __forceinline__ void gmm_issue(char* smem, int step, int w,
   const int kb = step * BK * 2;
 #pragma unroll
   for (int i = 0; i < AI; ++i)
-    if constexpr (ACOH)  // cache policy sc1
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_r, (lds_void*)(st + (i * NW + w) * RPI * RB),
-                                               16, a_off[i], kb, 0, 16);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_r, (lds_void*)(st + (i * NW + w) * RPI * RB),
-                                               16, a_off[i], kb, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_r, (lds_void*)(st + (i * NW + w) * RPI * RB), 16,
+                                             a_off[i], kb, 0, 0);
 #pragma unroll
   for (int i = 0; i < BI; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(SWIGLU && i >= BI / 2 ? rb1 : rb0,
@@ -199,11 +203,12 @@ __device__ __forceinline__ void live_dispatch(int live, F& f) {
 
 // One BM x 256 tile (GEMM1: BM x 128 act columns) of group rows
 // [row0, row0 + rows), rows <= BM, of weight n-tile nt of local expert e;
-// smem holds at least NST * (BM + 256) * BK * 2 bytes.  COH: the act
-// exchanged inside the fused kernel is written (GEMM1) and read (GEMM2)
-// device-coherently, so a tile on another XCD sees it without cache
-// maintenance (cache policy sc1: device-scope coherent, written through to
-// and read from the level all XCDs share).
+// smem holds at least NST * (BM + 256) * BK * 2 bytes.  COH (GEMM1 of the
+// one-launch kernel only): the act rows are stored with cache policy sc1,
+// written through the XCD's L2 to the memory side that every XCD reads, so
+// a GEMM2 tile of the same launch on another XCD can read them.  The GEMM2
+// side loads with the default policy; what makes that safe is stated at
+// the one-launch kernel.
 template <int BM, int BK, int NST, int NW, int NWN, bool SWIGLU, bool COH = false>
 __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const int* aidx,
                                          int row0, int rows, int nt, int e) {
@@ -279,7 +284,7 @@ __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const 
 
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
-    if (s < KT) gmm_issue<BM, BK, NST, SWIGLU, NW, COH && !SWIGLU>(smem, s, w, ra_r, rb0, rb1, a_off, b_off);
+    if (s < KT) gmm_issue<BM, BK, NST, SWIGLU, NW>(smem, s, w, ra_r, rb0, rb1, a_off, b_off);
 
   // Software pipeline across K steps: the last slice's fragments are read
   // before the barrier, and its MFMAs are issued after it, overlapping the
@@ -300,7 +305,7 @@ __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const 
       else if (ahead == 1) vm_wait_barrier<LPS>();
       else vm_wait_barrier<0>();
       if (kt + NST - 1 < KT)
-        gmm_issue<BM, BK, NST, SWIGLU, NW, COH && !SWIGLU>(smem, kt + NST - 1, w, ra_r, rb0, rb1, a_off, b_off);
+        gmm_issue<BM, BK, NST, SWIGLU, NW>(smem, kt + NST - 1, w, ra_r, rb0, rb1, a_off, b_off);
       const char* sa = smem + (kt % NST) * SS;
       const char* sb = sa + SA;
       // slice 0 of this step goes to set 0; slice NS-1 of the previous step
@@ -391,7 +396,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   const int* tile_off = P.tile_off + (size_t)pi.j * P.go_stride;
   const int* tile_group = P.tile_group + (size_t)pi.j * P.tg_stride;
   const int total_mt = tile_off[P.G];
-  if (group_offsets[P.G] > P.max_rows || total_mt < 0) return;  // malformed: touch nothing
+  if (group_offsets[P.G] > P.max_rows || total_mt < 0) {  // malformed: touch nothing
+    if (blockIdx.x == 0) report(P.err, MOE_ERR_BAD_OFFSETS);
+    return;
+  }
   // this launch's part of the m-tiles
   const int m0 = (int)(((long long)total_mt * P.part) / P.parts);
   const int mx = (int)(((long long)total_mt * (P.part + 1)) / P.parts) - m0;
@@ -457,14 +465,18 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
 // count), one count per m-tile, then the ready lists (group v's at its first
 // m-tile), all zero at launch.
 //
-// Visibility of act: GEMM1 writes it through to the device-wide level
-// (cache policy sc1) and waits for the stores before its count; the ready
-// entry is written after the last count, with a device-scope store.  No
-// cache of the reader can hold an older copy of those rows: they are read
-// in this launch only after their ready entry, and caches start the launch
-// clean; the reader still drops its CU's L1 before its loads.
+// Visibility of act: GEMM1 stores it write-through (sc1) past its own L2
+// and waits for those stores (s_waitcnt 0) before it bumps the m-tile's
+// count with a device-scope atomic; the ready entry is stored (agent scope)
+// after the last count.  The GEMM2 tile loads with the default policy,
+// which is safe because no cache on its side can hold an older copy of
+// those rows: its XCD's L2 has not seen them in this launch (they are read
+// only after their ready entry is set, the kernel starts with clean caches,
+// and nothing else in the launch reads act), and the tile drops its CU's
+// L1 (buffer_inv sc0) before loading.  The bumps and the entry are relaxed
+// atomics at agent scope: the ordering the reader needs comes from the
+// writer's wait for its stores before the bump.
 constexpr int kSyncFlags = 128;     // ints before the per-m-tile counts
-constexpr int kSpinLimit = 1 << 22; // ~0.2 s of sleeps: far beyond any GEMM1 tile
 
 template <int BM, int BK, int NST, int NW, int NWN>
 __global__ __launch_bounds__(64 * NW, 1) void gmm_fused_kernel(GemmParams P1, GemmParams P2,
@@ -480,7 +492,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_fused_kernel(GemmParams P1, Ge
   const int* tile_off = P1.tile_off + (size_t)pi.j * P1.go_stride;
   const int* tile_group = P1.tile_group + (size_t)pi.j * P1.tg_stride;
   const int M = tile_off[P1.G];
-  if (group_offsets[P1.G] > P1.max_rows || M < 0 || M > P1.mt_cap) return;  // malformed
+  if (group_offsets[P1.G] > P1.max_rows || M < 0 || M > P1.mt_cap) {  // malformed
+    if (blockIdx.x == 0) report(P1.err, MOE_ERR_BAD_OFFSETS);
+    return;
+  }
   const int v = blockIdx.x & 7;
   const int m0 = (int)(((long long)M * v) >> 3);
   const int mv = (int)(((long long)M * (v + 1)) >> 3) - m0;
@@ -508,16 +523,22 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_fused_kernel(GemmParams P1, Ge
     const int u = t - t1, i = u / n2;
     nt = u - i * n2;
     if (tid == 0) {
-      int spins = 0, val;
-      while ((val = __hip_atomic_load(ready + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
-                 0 &&
-             ++spins < kSpinLimit)
-        __builtin_amdgcn_s_sleep(2);
+      int spins = 0, val = 0;
+      if (P1.spin_limit >= 0)
+        while ((val = __hip_atomic_load(ready + i, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT)) == 0 &&
+               ++spins < P1.spin_limit)
+          __builtin_amdgcn_s_sleep(2);
       s_m = val - 1;  // -1 only if the bounded wait ran out
     }
     __syncthreads();
     m = s_m;
-    if (m < m0 || m >= m0 + mv) return;
+    if (m < m0 || m >= m0 + mv) {
+      // gave up: these rows of expert_out are not written, and the call
+      // says so
+      report(P1.err, MOE_ERR_GEMM_WAIT);
+      return;
+    }
   }
   // the tile's rows and expert (none when the map is malformed or the slot
   // hosts no resident expert: the m-tile's count still counts the tile)
@@ -575,6 +596,7 @@ struct F32Params {
   int G, K, Nout, lo_slot, e_base, e_res;
   long long max_rows;
   PassArgs pa;
+  const int* valid;  // m-tile count of validated offsets (0: compute nothing), or null
 };
 
 template <bool SWIGLU>
@@ -582,6 +604,7 @@ __global__ __launch_bounds__(256) void gmm_f32_kernel(F32Params P) {
   PassInfo pi = resolve_pass(P.pa);
   if (!pi.active) return;
   const int* go = P.group_offsets + (size_t)pi.j * P.go_stride;
+  if (P.valid != nullptr && *P.valid == 0) return;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int row = (int)(idx / P.Nout), col = (int)(idx - (long long)row * P.Nout);
   if (row >= go[P.G] || go[P.G] > P.max_rows) return;
@@ -617,7 +640,8 @@ __global__ __launch_bounds__(256) void gmm_f32_kernel(F32Params P) {
 __global__ __launch_bounds__(1024) void tile_schedule_kernel(int G, int bm, int limit,
                                                              const int* group_offsets,
                                                              int* tile_off, int* tile_group,
-                                                             int* sync, int sync_n, PassArgs pa) {
+                                                             int* sync, int sync_n, PassArgs pa,
+                                                             int* err) {
   PassInfo pi = resolve_pass(pa);
   if (!pi.active) return;
   for (int i = threadIdx.x; i < sync_n; i += blockDim.x) sync[i] = 0;
@@ -635,6 +659,8 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(int G, int bm, int 
   }
   __syncthreads();
   if (bad) v = 0;
+  // the first launch of a step call: starts the call's error word
+  if (err != nullptr && threadIdx.x == 0) *err = bad ? MOE_ERR_BAD_OFFSETS : 0;
   int x = v;
   for (int off = 1; off < 64; off <<= 1) {
     int y = __shfl_up(x, off);
@@ -740,6 +766,8 @@ hipError_t launch_bf16(const Dims& d, const PassArgs& pa, const GemmPass& gp, co
   p2.Nout = d.H;
   p2.n_ntiles = d.H / 256;
   p1.mt_cap = p2.mt_cap = tile_map_len(d);
+  p1.err = p2.err = gp.err;
+  p1.spin_limit = p2.spin_limit = gemm_wait_limit();
   p1.part = p2.part = 0;
   p1.parts = p2.parts = 1;
 
@@ -818,6 +846,18 @@ std::mutex& side_mutex() {
   return mu;
 }
 
+namespace {
+// ~0.2 s of sleeps: far beyond any tile's own work
+constexpr int kDefaultWaitLimit = 1 << 22;
+std::atomic<int> g_wait_limit{kDefaultWaitLimit};
+}  // namespace
+
+int gemm_wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
+
+void set_gemm_wait_limit(int spins) {
+  g_wait_limit.store(spins == 0 ? kDefaultWaitLimit : spins, std::memory_order_relaxed);
+}
+
 int gmm_sync_ints(const Dims& d) { return kSyncFlags + 2 * tile_map_len(d); }
 
 size_t gmm_sync_bytes(const Dims& d) { return ((size_t)gmm_sync_ints(d) * 4 + 255) / 256 * 256; }
@@ -845,7 +885,7 @@ hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const GemmPass& gp,
       if (gsync == nullptr) gsync = t2;
       hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, d.G_res, d.gemm_bm,
                          (int)lim, gp.group_offsets, t0, t1, gsync == t2 ? t2 : nullptr,
-                         gsync == t2 ? gmm_sync_ints(d) : 0, pa);
+                         gsync == t2 ? gmm_sync_ints(d) : 0, pa, gp.err);
       toff = t0;
       tgroup = t1;
       go_stride = 0;
@@ -860,6 +900,19 @@ hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const GemmPass& gp,
                                       wg, wu, wd, act, out, max_rows, gsync, s);
     if (e != hipSuccess) return e;
   } else {
+    // a step call validates the offsets (and starts its error word) with
+    // the tile schedule; malformed offsets leave no m-tiles, and the
+    // kernels then compute nothing
+    const int* valid = nullptr;
+    if (gp.tile_off == nullptr) {
+      int* t0 = (int*)scratch;
+      int* t1 = (int*)((char*)scratch + ((size_t)(d.G_res + 1) * 4 + 255) / 256 * 256);
+      long long lim = (long long)d.T * d.k;
+      if (max_rows < lim) lim = max_rows;
+      hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, d.G_res, d.gemm_bm,
+                         (int)lim, gp.group_offsets, t0, t1, nullptr, 0, pa, gp.err);
+      valid = t0 + d.G_res;
+    }
     F32Params p1;
     p1.A = (const float*)gp.a_src;
     p1.a_index = gp.a_index;
@@ -881,6 +934,7 @@ hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const GemmPass& gp,
     p1.e_res = d.S_res * d.El;
     p1.max_rows = max_rows;
     p1.pa = pa;
+    p1.valid = valid;
     long long n1 = max_rows * (long long)d.F;
     hipLaunchKernelGGL(gmm_f32_kernel<true>, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s,
                        p1);

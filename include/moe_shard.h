@@ -25,11 +25,11 @@
  *    aligned), sized by moe_workspace_bytes / moe_layer_workspace_bytes.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work: nothing synchronises the host, so integer outputs are
- *    valid once the stream reaches them.  moe_gmm_swiglu with F >= 4096 and
- *    moe_layer_dropless_chunked with two or more passes put part of their
- *    work on the side stream, forked from `stream` and joined back to it by
- *    events inside the call, so everything is complete when `stream` reaches
- *    the point after the call.  Concurrent calls on one device serialise
+ *    valid once the stream reaches them.  moe_layer_dropless_chunked puts
+ *    part of its work on the side stream (with two or more passes, or a
+ *    single pass with F >= 4096), forked from `stream` and joined back to it
+ *    by events inside the call, so everything is complete when `stream`
+ *    reaches the point after the call.  Concurrent calls on one device serialise
  *    only that enqueue (a mutex), not their GPU work.
  *  - Errors: a negative moe_status, returned after validating every argument
  *    on the host and before any launch.  A failed launch returns MOE_EHIP.
@@ -37,7 +37,12 @@
  *    MOE_ECAPACITY ([DRED], dedup truncation comment).
  *  - Index arrays produced by moe_route are trusted by later calls; indices
  *    outside [0, E) are skipped by the kernels (no out-of-bounds access) and
- *    raise bit 0 of status[3].
+ *    raise MOE_ERR_BAD_INDEX.
+ *  - Errors only the device can see (the data decides them) are reported as
+ *    the MOE_ERR_* bits below in a device word the call writes: status[3] of
+ *    moe_count_overflow, info[4] of moe_layer_dropless_chunked, *status of
+ *    moe_gmm_swiglu.  Nothing is ever dropped without a bit saying so
+ *    ([DRED], dedup truncation comment: silent loss is the failure to avoid).
  *  - Layouts are row-major.  dtype MOE_BF16: x, weights, act, expert_out and
  *    y are bfloat16 (fp32 accumulation; act, expert_out and y rounded to
  *    nearest even); MOE_F32: all float32.  Logits and gates are float32.
@@ -67,6 +72,17 @@ typedef enum {
   MOE_ECAPACITY = -3,   /* a caller buffer or the workspace is too small      */
   MOE_EHIP = -4         /* a HIP launch or copy failed                         */
 } moe_status;
+
+/* Device-side error bits (OR-ed together). */
+enum {
+  MOE_ERR_BAD_INDEX = 1,   /* a top-k expert index outside [0, E) was skipped       */
+  MOE_ERR_BAD_OFFSETS = 2, /* group offsets not non-decreasing within [0, max_rows]:
+                              the grouped GEMM computed nothing                      */
+  MOE_ERR_GEMM_WAIT = 4    /* a grouped-GEMM tile gave up its bounded wait for its
+                              input rows (another tile of the same launch never
+                              finished them): its rows of expert_out were not
+                              written                                                */
+};
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
@@ -137,8 +153,9 @@ int moe_layer_workspace_bytes(const moe_problem* p, int32_t mode, size_t* bytes)
 /* Chunks of the dropless fallback that moe_layer_dropless_chunked runs as
  * one pass in `mode`: the most consecutive chunks whose worst-case rows fit
  * the buffers the call is sized for, so running them together never needs
- * more memory than the capped buffer ([FALLBACK] How: a chunk's worst-case
- * buffer is no larger than the capped one, so peak HBM does not grow).  The
+ * more memory than the capped buffer ([FALLBACK] How: the fallback keeps
+ * each chunk's worst case within the capped buffer, so the layer's peak
+ * HBM stays that of the capped layer).  The
  * tokens of the chunks are disjoint and every grouped-GEMM row is computed
  * on its own, so y is the same as chunk by chunk.  1 = one chunk per pass. */
 int moe_layer_chunks_per_pass(const moe_problem* p, int32_t mode, int32_t* chunks);
@@ -163,12 +180,15 @@ int moe_route(const moe_problem* p, const float* logits, int32_t* topk_idx,
  *   shard_counts  [S]    rows each shard would receive (assignments, or
  *                        distinct tokens with dedup);
  *   status        [4]    cap (-1 = uncapped), overflow (0/1: some shard
- *                        count > cap), max shard count, error bits.
- * The required factor of [FALLBACK] Shortcomings is status[2] / (T*k/S). */
+ *                        count > cap), max shard count, MOE_ERR_* bits;
+ *   required_factor [1]  float32, may be NULL: the smallest buffer factor
+ *                        that would have fit, max shard count / (T*k/S)
+ *                        ([FALLBACK] Shortcomings: the figure the overflow
+ *                        log reports). */
 int moe_count_overflow(const moe_problem* p, const int32_t* topk_idx,
                        int32_t* expert_counts, int32_t* slot_expert, int32_t* ndiv,
                        int32_t* slot_of_assign, int32_t* shard_counts, int32_t* status,
-                       void* ws, size_t ws_bytes, void* stream);
+                       float* required_factor, void* ws, size_t ws_bytes, void* stream);
 
 /* a4+a5. Layout and permute of one pass: chunk `chunk` of `num_chunks`
  * (token t = b*L + s is in chunk c when s*n/L == c; num_chunks 1 = all
@@ -203,13 +223,16 @@ int moe_permute(const moe_problem* p, int32_t num_chunks, int32_t chunk, int32_t
  *   act[n]        = SiLU(x_sorted[n] Wg^T) * (x_sorted[n] Wu^T)   [max_rows,F]
  *   expert_out[n] = act[n] Wd^T                                   [max_rows,H]
  * SiLU(z) = z/(1+exp(-z)).  Rows past group_offsets[G_res] are untouched.
- * bf16: offsets that are not a non-decreasing sequence within [0, min(max_rows,
- * T*k)] compute nothing (act and expert_out untouched); the status is still
- * MOE_OK, since the offsets are read on the device only. */
+ * status (device, one int32, may be NULL) receives the MOE_ERR_* bits of
+ * the call: offsets that are not a non-decreasing sequence within [0,
+ * min(max_rows, T*k)] compute nothing (act and expert_out untouched) and
+ * set MOE_ERR_BAD_OFFSETS; a tile that gave up its bounded wait sets
+ * MOE_ERR_GEMM_WAIT.  The return value is still MOE_OK in both cases, since
+ * the offsets are read on the device only. */
 int moe_gmm_swiglu(const moe_problem* p, const void* x_sorted, const int32_t* group_offsets,
                    const int32_t* slot_expert, const void* w_gate, const void* w_up,
                    const void* w_down, void* act, void* expert_out, int64_t max_rows,
-                   void* ws, size_t ws_bytes, void* stream);
+                   int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /* a7. Gate-weighted combine of one pass: for every token t of the pass,
  *   y[t] = sum over j ascending of topk_gate[t,j] * expert_out[row_of_assign[t*k+j]]
@@ -265,7 +288,8 @@ int moe_combine_from_partials(const moe_problem* p, int32_t num_chunks, int32_t 
  * chunks (moe_layer_chunks_per_pass of them per pass) from the overflow
  * flag, with no host synchronisation.
  * info (device, may be NULL) receives [overflow, fallback_ran, cap, max
- * shard count].  ws must hold moe_layer_workspace_bytes(p, mode). */
+ * shard count, MOE_ERR_* bits] (5 int32).  ws must hold
+ * moe_layer_workspace_bytes(p, mode). */
 int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x,
                                const float* logits, const void* w_gate, const void* w_up,
                                const void* w_down, void* y, int32_t* info,
@@ -274,9 +298,9 @@ int moe_layer_dropless_chunked(const moe_problem* p, int32_t mode, const void* x
 /* ---- backward of the hot path ------------------------------------------- */
 /*
  * The backward of one pass, step by step, as the chain rule of the steps
- * above.  [FALLBACK] How runs the chunked passes in a scan whose backward
- * recomputes one chunk at a time and carries the weight gradients across
- * the chunks; [RING] (title, What) keeps the expert-sorted input x_sorted
+ * above.  [FALLBACK] How runs the chunked passes in a scan; the scan's
+ * backward redoes each chunk's forward and keeps the weight gradients as a
+ * running sum across chunks; [RING] (title, What) keeps the expert-sorted input x_sorted
  * for the backward.  A caller runs, per pass of the forward (the same
  * num_chunks / chunk / capped, and the arrays moe_permute wrote for it):
  * moe_combine_bwd, moe_gmm_swiglu_bwd (accumulate = 0 on the first pass,

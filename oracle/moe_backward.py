@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE ONLY: nothing on the product path may import this
 module (the package docstring states the rule).
 
 The pages describe the backward only in outline: [FALLBACK] How runs the
-chunked passes in a scan whose backward recomputes one chunk at a time and
-carries the weight gradients across the chunks; [RING] (title and What)
+chunked passes in a scan, and the scan's backward redoes each chunk's
+forward and keeps the weight gradients as a running sum across chunks; [RING] (title and What)
 saves the expert-sorted input x_sorted for the backward and computes the
 combine's backward.  The derivatives themselves are those of the forward
 functions of moe_oracle, written out here by the chain rule:

@@ -285,7 +285,8 @@ def required_factor(counts_per_shard: np.ndarray, p: Problem) -> float:
 
 def default_num_chunks(num_shards: int, factor: float) -> int:
     """Chunk count when none is given: ceil(S / factor), the reading of
-    [FALLBACK] Shortcomings ("8x for EP16 / factor 2")."""
+    [FALLBACK] Shortcomings (its example: 16 shards at factor 2, an
+    eight-fold slowdown, i.e. eight chunks)."""
     return int(math.ceil(num_shards / float(np.float32(factor))))
 
 

@@ -1,6 +1,6 @@
 """Host-side checks of libmoe_shard.so (no GPU needed, no kernel launches).
 
-The library must load, export every function include/moe_shard.h declares,
+The library must load, export every function the headers under include/ declare,
 and reject invalid problems on the host with the documented status codes
 before touching the GPU.  Buffer bounds follow the pages' capacity rules.
 """
@@ -28,8 +28,13 @@ def _binding():
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "moe_shard.h")).read()
-    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(moe_\w+)\(", text, re.M)))
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            text = open(os.path.join(inc, h)).read()
+            names |= set(re.findall(r"^(?:int|const char\*)\s+(moe_\w+)\(", text, re.M))
+    return sorted(names)
 
 
 def test_exports_match_header():
@@ -113,7 +118,8 @@ def test_pass_row_bounds():
     g = _binding()
     # Llama4-Maverick shard: cap = 2 * 32768 / 16 = 4096; a chunk of 4096
     # tokens has a worst case of 4096 rows per shard, no more than the cap
-    # (the fallback page: the chunk buffer is no larger than the capped one).
+    # (the fallback page, How: a chunk's worst-case buffer fits within the
+    # capped one).
     mav = problem(tokens=32768, seq_len=8192, hidden=5120, ffn=8192, num_experts=128, top_k=1,
                   num_shards=16, res_lo=0, res_hi=1, factor=2.0, num_chunks=8, gate="sigmoid")
     assert g.pass_max_rows(mav, 8, 0) == (4096, 0)

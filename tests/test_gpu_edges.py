@@ -78,7 +78,7 @@ def test_edge_layer_all_modes(name):
         torch.cuda.synchronize()
         cap = -1 if want["cap"] is None else want["cap"]
         assert info.tolist() == [int(want["overflow"]), int(want["fallback_ran"]), cap,
-                                 int(want["shard_counts"].max())], name
+                                 int(want["shard_counts"].max()), 0], name
         check_close(host(y), want["y"], f"y {name} mode {mode}")
         ys[mode] = y
     assert torch.equal(ys[g.MODE_FORCE_DROPLESS], ys[g.MODE_FORCE_CHUNKED])
@@ -96,37 +96,42 @@ MALFORMED = {
 }
 
 
-@pytest.mark.parametrize("hidden", [256, 2048])   # 128-row tiles (one launch), 256-row tiles
+@pytest.mark.parametrize("hidden,bf16", [(256, True), (2048, True), (256, False)])
 @pytest.mark.parametrize("case", sorted(MALFORMED))
-def test_gmm_malformed_offsets_touch_nothing(case, hidden):
-    """The bf16 grouped GEMM given group offsets that are not a non-decreasing
-    sequence within [0, rows] computes nothing: act and expert_out keep their
-    contents (the tile schedule gives no tiles, so no workgroup waits or
-    writes)."""
+def test_gmm_malformed_offsets_touch_nothing(case, hidden, bf16):
+    """The grouped GEMM given group offsets that are not a non-decreasing
+    sequence within [0, rows] computes nothing (act and expert_out keep their
+    contents: the tile schedule gives no tiles, so no workgroup waits or
+    writes) and says so: MOE_ERR_BAD_OFFSETS in its status word.  Both bf16
+    tile heights (128 rows, one launch; 256 rows) and fp32."""
     import grouped_gemm_shard_amd as g
     w = W(f"malformed_{hidden}", tokens=64, seq_len=64, hidden=hidden, ffn=256, num_experts=8,
-          top_k=2, num_shards=4, res_lo=0, res_hi=4, factor=2.0, num_chunks=2)
+          top_k=2, num_shards=4, res_lo=0, res_hi=4, factor=2.0, num_chunks=2, bf16=bf16)
+    dt = torch.bfloat16 if bf16 else torch.float32
     p = binding_problem(w)
     say(f"[gmm malformed] {case} H={hidden}")
     rows = 128
     gen = torch.Generator(device="cuda")
     gen.manual_seed(3)
-    xs = torch.randn((rows, hidden), generator=gen, device="cuda").to(torch.bfloat16)
+    xs = torch.randn((rows, hidden), generator=gen, device="cuda").to(dt)
     wts = workloads.make_weights(w, device="cuda")
     se = torch.arange(p.num_slots, dtype=torch.int32, device="cuda")  # home slots, no replicas
     go = torch.tensor(MALFORMED[case](p.g_res, rows), dtype=torch.int32, device="cuda")
     assert go.numel() == p.g_res + 1
-    act = torch.full((rows, w.ffn), 7.0, dtype=torch.bfloat16, device="cuda")
-    out = torch.full((rows, hidden), 7.0, dtype=torch.bfloat16, device="cuda")
+    act = torch.full((rows, w.ffn), 7.0, dtype=dt, device="cuda")
+    out = torch.full((rows, hidden), 7.0, dtype=dt, device="cuda")
     ws = torch.empty(g.workspace_bytes(p), dtype=torch.uint8, device="cuda")
-    g.moe_gmm_swiglu(p, xs, go, se, *wts, act, out, ws)
+    status = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    g.moe_gmm_swiglu(p, xs, go, se, *wts, act, out, ws, status=status)
     torch.cuda.synchronize()
     assert torch.all(act == 7.0) and torch.all(out == 7.0)
+    assert int(status.item()) == g.ERR_BAD_OFFSETS
     # the same workspace then serves a well-formed call (counters re-zeroed)
     go_ok = torch.tensor([min(16 * i, rows) for i in range(p.g_res + 1)], dtype=torch.int32,
                          device="cuda")
-    g.moe_gmm_swiglu(p, xs, go_ok, se, *wts, act, out, ws)
+    g.moe_gmm_swiglu(p, xs, go_ok, se, *wts, act, out, ws, status=status)
     torch.cuda.synchronize()
+    assert int(status.item()) == 0
     n = int(go_ok[-1].item())
     o_act, o_out = oracle.gmm_swiglu(oracle_problem(w), host(xs[:n]), ints(go_ok),
                                      np.arange(p.g_res), *[host(t) for t in wts])

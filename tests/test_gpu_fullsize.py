@@ -65,7 +65,7 @@ def test_full_size_layer(name):
     sc = oracle.shard_counts(slot, op)
     cap = oracle.capacity(op)
     ovf = oracle.overflow(sc, cap)
-    assert info == [int(ovf), int(ovf), -1 if cap is None else cap, int(sc.max())]
+    assert info == [int(ovf), int(ovf), -1 if cap is None else cap, int(sc.max()), 0]
 
     say(f"[full] {name}: step API route/count")
     idx = torch.empty((w.tokens, w.top_k), dtype=torch.int32, device="cuda")

@@ -58,9 +58,11 @@ def gpu_count(g, p, idx):
     ws = torch.empty(g.workspace_bytes(p), dtype=torch.uint8, device="cuda")
     out = dict(expert_counts=i32(p.num_experts, -7), slot_expert=i32(p.num_slots, -7),
                ndiv=i32(p.num_experts, -7), slot_of_assign=i32(p.tokens * p.top_k, -7),
-               shard_counts=i32(p.num_shards, -7), status=i32(4, -7))
+               shard_counts=i32(p.num_shards, -7), status=i32(4, -7),
+               required_factor=torch.full((1,), -7.0, dtype=torch.float32, device="cuda"))
     g.moe_count_overflow(p, idx, out["expert_counts"], out["slot_expert"], out["ndiv"],
-                         out["slot_of_assign"], out["shard_counts"], out["status"], ws)
+                         out["slot_of_assign"], out["shard_counts"], out["status"], ws,
+                         required_factor=out["required_factor"])
     return out
 
 
@@ -120,6 +122,11 @@ def _count_case(g, w, logits_np):
         assert np.array_equal(ints(got[key]).ravel(), np.asarray(want[key]).ravel()), key
     st = ints(got["status"])
     assert st.tolist() == [want["cap"], want["overflow"], want["max"], 0]
+    # the figure [FALLBACK] Shortcomings logs, max shard count / (T*k/S), as
+    # float32 (the integer quotient rounded once)
+    rf = float(got["required_factor"].item())
+    want_rf = oracle.required_factor(np.asarray(want["shard_counts"]), op)
+    assert abs(rf - want_rf) <= 1e-6 * max(1.0, want_rf), (rf, want_rf)
     return want
 
 
@@ -262,7 +269,7 @@ def test_layer_modes(g, name):
         torch.cuda.synchronize()
         cap = -1 if want["cap"] is None else want["cap"]
         assert info.tolist() == [int(want["overflow"]), int(want["fallback_ran"]), cap,
-                                 int(want["shard_counts"].max())]
+                                 int(want["shard_counts"].max()), 0]
         check_close(host(y), want["y"], f"y {name} {MODES[mode]}")
         ys[mode] = y
         del run

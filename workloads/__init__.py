@@ -176,5 +176,6 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 
 def default_chunks(num_shards: int, factor: float) -> int:
     """ceil(S / factor): the fallback's chunk count read from the example
-    "8x for EP16 / factor 2" on the fallback page (Shortcomings)."""
+    the fallback page's Shortcomings example (16-way expert parallelism at
+    factor 2 gives an eight-fold slowdown, i.e. eight chunks)."""
     return int(math.ceil(num_shards / factor))
