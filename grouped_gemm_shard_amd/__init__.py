@@ -25,7 +25,7 @@ __all__ = [
     "moe_combine_from_partials", "moe_layer_dropless_chunked", "status_string", "LayerRunner",
     "bwd_workspace_bytes", "moe_combine_bwd", "moe_gmm_swiglu_bwd",
     "moe_permute_bwd", "moe_route_bwd", "layer_bwd_workspace_bytes", "moe_layer_bwd",
-    "LayerBackwardRunner", "testing_set_gemm_wait_limit", "ERR_BAD_INDEX", "ERR_BAD_OFFSETS",
+    "LayerBackwardRunner", "testing_set_gemm_wait_limit", "moe_gmm_swiglu_noalloc", "ERR_BAD_INDEX", "ERR_BAD_OFFSETS",
     "ERR_GEMM_WAIT",
 ]
 
@@ -40,7 +40,7 @@ EXPORTED = ["moe_workspace_bytes", "moe_pass_max_rows", "moe_layer_workspace_byt
             "moe_layer_dropless_chunked", "moe_bwd_workspace_bytes", "moe_combine_bwd",
             "moe_gmm_swiglu_bwd", "moe_permute_bwd", "moe_route_bwd",
             "moe_layer_bwd_workspace_bytes", "moe_layer_bwd", "moe_status_string",
-            "moe_testing_set_gemm_wait_limit"]
+            "moe_testing_set_gemm_wait_limit", "moe_gmm_swiglu_noalloc"]
 
 # Device-side error bits (include/moe_shard.h)
 ERR_BAD_INDEX, ERR_BAD_OFFSETS, ERR_GEMM_WAIT = 1, 2, 4
@@ -144,6 +144,7 @@ def _load():
         "moe_layer_bwd_workspace_bytes": [P, i32, ctypes.POINTER(sz)],
         "moe_layer_bwd": [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_testing_set_gemm_wait_limit": [i32],
+        "moe_gmm_swiglu_noalloc": [P, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -287,6 +288,21 @@ def moe_gmm_swiglu(p: Problem, x_sorted, group_offsets, slot_expert, w_gate, w_u
         _ptr(w_gate, p.dtype, "w_gate"), _ptr(w_up, p.dtype, "w_up"),
         _ptr(w_down, p.dtype, "w_down"), _ptr(act, p.dtype, "act"),
         _ptr(expert_out, p.dtype, "expert_out"), max_rows, _ptr(status, i32, "status"), w, nb,
+        _stream(stream)))
+
+
+def moe_gmm_swiglu_noalloc(p: Problem, x_sorted, group_offsets, slot_expert, w_gate, w_up,
+                           w_down, act, expert_out, stream=None, status=None):
+    """moe_gmm_swiglu without a workspace: its scratch is the library's own
+    fixed device array (for callers that cannot allocate)."""
+    i32 = torch.int32
+    max_rows = min(x_sorted.shape[0], act.shape[0], expert_out.shape[0])
+    _check("moe_gmm_swiglu_noalloc", _lib().moe_gmm_swiglu_noalloc(
+        ctypes.byref(p.c()), _ptr(x_sorted, p.dtype, "x_sorted"),
+        _ptr(group_offsets, i32, "group_offsets"), _ptr(slot_expert, i32, "slot_expert"),
+        _ptr(w_gate, p.dtype, "w_gate"), _ptr(w_up, p.dtype, "w_up"),
+        _ptr(w_down, p.dtype, "w_down"), _ptr(act, p.dtype, "act"),
+        _ptr(expert_out, p.dtype, "expert_out"), max_rows, _ptr(status, i32, "status"),
         _stream(stream)))
 
 

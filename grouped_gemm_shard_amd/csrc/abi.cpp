@@ -482,6 +482,75 @@ int moe_gmm_swiglu(const moe_problem* p, const void* x_sorted, const int32_t* gr
                                max_rows, ws, (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Scratch of moe_gmm_swiglu_noalloc: the tile schedule and the one-launch
+// kernel's counters, in a file-scope device array instead of a caller
+// workspace.  Every GPU the library runs on holds its own copy until the
+// process ends.  Host code never uses the array's name as an address (on
+// the host it is only a stand-in); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kNoAllocScratchBytes = (size_t)2 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of this device's scratch array, or null if the lookup
+// failed (first call on each device, with that device current).
+void* noalloc_scratch() {
+  static void* ptr[kMaxDevices] = {nullptr};
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptr[dev] = a;
+  }
+  return ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_gmm_swiglu_noalloc(const moe_problem* p, const void* x_sorted,
+                           const int32_t* group_offsets, const int32_t* slot_expert,
+                           const void* w_gate, const void* w_up, const void* w_down, void* act,
+                           void* expert_out, int64_t max_rows, int32_t* status, void* stream) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x_sorted || !group_offsets || !slot_expert || !w_gate || !w_up || !w_down || !act ||
+      !expert_out || max_rows < 0)
+    return MOE_EINVAL;
+  if (misaligned(x_sorted, 16) || misaligned(act, 16) || misaligned(w_gate, 16) ||
+      misaligned(w_up, 16) || misaligned(w_down, 16))
+    return MOE_EINVAL;
+  if (max_rows >= (1ll << 31) / 2) return MOE_EUNSUPPORTED;
+  if (!fits_rsrc(d, max_rows, 0)) return MOE_EUNSUPPORTED;
+  // the problem's scratch must fit the fixed array
+  if (gmm_scratch_bytes(d) > kNoAllocScratchBytes) return MOE_ECAPACITY;
+  void* ws = noalloc_scratch();
+  if (ws == nullptr) return MOE_EHIP;
+  const PassArgs pa = static_pass_args(0, d.L, 0, 0, d.L);
+  GemmPass gp;
+  memset(&gp, 0, sizeof(gp));
+  gp.a_src = x_sorted;
+  gp.a_src_rows = (int)max_rows;
+  gp.a_div = 1;
+  gp.group_offsets = group_offsets;
+  gp.split_ok = false;
+  gp.err = status;
+  // the same launches as moe_gmm_swiglu; its first launch (the tile
+  // schedule) clears the counters the later ones expect at zero
+  return hip_status(launch_gmm(d, pa, gp, slot_expert, w_gate, w_up, w_down, act, expert_out,
+                               max_rows, ws, (hipStream_t)stream));
+}
+
 int moe_combine(const moe_problem* p, int32_t num_chunks, int32_t chunk, const void* expert_out,
                 const int32_t* row_of_assign, const float* topk_gate, void* y, void* stream) {
   Dims d;

@@ -234,6 +234,23 @@ int moe_gmm_swiglu(const moe_problem* p, const void* x_sorted, const int32_t* gr
                    const void* w_down, void* act, void* expert_out, int64_t max_rows,
                    int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_gmm_swiglu for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, arguments and results, with no workspace argument.
+ * Its scratch (the tile schedule and the one-launch kernel's counters, a
+ * few KB for the workloads here) lives in a fixed 2 MiB device array inside
+ * the library, one per GPU, held until the process ends; a problem whose
+ * scratch (G_res+1 + 3*(T*k/128 + G_res + 1) + 128 ints, rounded) exceeds
+ * it returns MOE_ECAPACITY.  The call allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine.  Every call on one GPU shares
+ * that GPU's array and clears the parts it needs at its start, so calls
+ * that overlap on one GPU (concurrent streams) race and must be serialised
+ * by the caller. */
+int moe_gmm_swiglu_noalloc(const moe_problem* p, const void* x_sorted,
+                           const int32_t* group_offsets, const int32_t* slot_expert,
+                           const void* w_gate, const void* w_up, const void* w_down, void* act,
+                           void* expert_out, int64_t max_rows, int32_t* status, void* stream);
+
 /* a7. Gate-weighted combine of one pass: for every token t of the pass,
  *   y[t] = sum over j ascending of topk_gate[t,j] * expert_out[row_of_assign[t*k+j]]
  * over the assignments with a row (fp32 accumulation); 0 for a token with
