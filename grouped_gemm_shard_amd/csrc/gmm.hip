@@ -81,6 +81,7 @@ constexpr int shape_waves(int, int, int, int nw, int) { return nw; }
 constexpr int shape_ring(int bm, int bk, int nst, int, int) { return nst * (bm + BNB) * bk * 2; }
 constexpr int kRemBM = shape_rows(MOE_GEMM_REM);
 constexpr int kRemRing = shape_ring(MOE_GEMM_REM);
+constexpr int kPpRing = 10 * 128 * 128;  // the 256-row loop's ten 16 KB quarters
 
 struct GemmParams {
   const uint16_t* A;       // row source (whole array; rows past a group read as zero)
@@ -137,6 +138,23 @@ __device__ __forceinline__ int swz(int row) {
 template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Waits until at most N of this wave's global->LDS loads are outstanding
+// (no barrier).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier that no instruction is scheduled across (the phases of
+// the two wave groups must not bleed into each other).
+__device__ __forceinline__ void pp_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Starts the loads of K step `step` into its ring stage: each wave-wide
@@ -383,11 +401,231 @@ __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const 
   }
 }
 
+// One 256 x 256 tile (GEMM1: 256 x 128 act columns) with more than 128
+// rows of the group, for long reductions (H >= 2048).  8 waves in two groups
+// of four (one wave of each group per SIMD) take turns: while one group
+// multiplies, the other reads its fragments of the next K step from LDS and
+// issues global->LDS loads, so every SIMD's matrix pipe is fed by one wave
+// while the other moves data.
+//
+// K steps of 64 columns.  Each step's operands are four 16 KB quarters:
+// A rows 0-127 (read by group 0), A rows 128-255 (group 1), B rows 0-127
+// and B rows 128-255 (both groups); quarter q = 4*step + part lives in LDS
+// slot q % 10 (160 KB).  Phases: group 0 reads step k in phase 2k+1 (MEM)
+// and multiplies it in phase 2k+2 (COMP), group 1 one phase later, with a
+// barrier between phases.  Group 0 issues quarters 4j+7 and 4j+8 in MEM(j),
+// group 1 quarters 4j+9 and 4j+10 in MEM(j), each into a slot whose
+// previous quarter both groups have read by then; group 0 waits for its
+// loads at the end of its COMP phase, group 1 at the end of its MEM phase,
+// so every quarter of step k+1 has landed before the barrier after which it
+// is read.  The loads are spread over both groups' MEM phases: a wave
+// issuing an LDS-direct load stalls until the texture unit accepts it, so
+// loads kept off the multiplying wave keep its MFMAs back to back, and two
+// quarters per phase keep the unit busy in both phases.
+//
+// 16x16x32 MFMAs (each wave 64 x 128: 4 x 8 tiles).  Measured on MI355X
+// against 32x32x16: the same work takes more cycles but the chip holds a
+// higher clock under its power limit, 3-4% faster on dense shapes.
+//
+// GEMM1's B tile is 128 gate rows (quarter 2) and the 128 up rows of the
+// same act columns (quarter 3); a wave takes 64 act columns: 4 gate tiles
+// from quarter 2 and the matching 4 up tiles from quarter 3, so the SwiGLU
+// epilogue pairs them in registers.  GEMM2's wave takes 128 output columns
+// from one B quarter.  A rows past the group read as zero; a wave whose 64
+// rows are all past the group skips its reads and MFMAs.
+template <bool SWIGLU>
+__device__ __forceinline__ void gmm_tile_pp(const GemmParams& P, char* smem, const int* aidx,
+                                            int row0, int rows, int nt, int e) {
+  constexpr int BK = 64, RB = BK * 2, CPR = BK / 8, RPI = 1024 / RB;  // 8 rows per load
+  constexpr int QS = 128 * RB;       // bytes per quarter
+  constexpr int LQ = 128 / RPI / 4;  // loads per wave per quarter (4)
+  constexpr int NQ_PRO = 8;          // quarters of the first two steps
+  constexpr int MI = 4, NI = 8;      // 16x16 tiles per wave
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = w >> 2, wig = w & 3;
+  const int wml = wig >> 1, wn = wig & 1;
+  const int K = P.K, KT = K / BK, NQ = 4 * KT;
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(P.A, (unsigned)P.a_rows * K * 2);
+  __amdgpu_buffer_rsrc_t rb0, rb1;
+  if (SWIGLU) {
+    rb0 = make_rsrc(P.B0 + (size_t)e * P.b_stride + (size_t)nt * 128 * K, 128u * K * 2);
+    rb1 = make_rsrc(P.B1 + (size_t)e * P.b_stride + (size_t)nt * 128 * K, 128u * K * 2);
+  } else {
+    rb0 = make_rsrc(P.B0 + (size_t)e * P.b_stride + (size_t)nt * 256 * K, 128u * K * 2);
+    rb1 = make_rsrc(P.B0 + (size_t)e * P.b_stride + (size_t)nt * 256 * K + (size_t)128 * K,
+                    128u * K * 2);
+  }
+  // A: a group only ever loads its own quarter (rows grp*128..); load i of
+  // wave wig fills rows (i*4 + wig)*8 + lane/8 of it.  B rows are
+  // contiguous: rows 32 apart share the chunk swizzle.
+  int a_off[LQ];
+#pragma unroll
+  for (int i = 0; i < LQ; ++i) {
+    const int row = (i * 4 + wig) * RPI + lane / CPR;
+    const int trow = grp * 128 + row;
+    int src = -1;
+    if (trow < rows) src = aidx ? aidx[row0 + trow] / P.a_div : row0 + trow;
+    a_off[i] = (src >= 0 && src < P.a_rows) ? src * K * 2 + (((lane % CPR) ^ swz<BK>(row)) << 4)
+                                           : (int)0x80000000;
+  }
+  const int brow0 = wig * RPI + lane / CPR;
+  const int b_off0 = brow0 * K * 2 + (((lane % CPR) ^ swz<BK>(brow0)) << 4);
+  const int b_step = 4 * RPI * K * 2;
+  // quarter q's loads: this group's A quarter, or B rows 0-127 / 128-255
+  auto issue_a = [&](int q) {
+    if (q >= NQ) return;
+    char* st = smem + (q % 10) * QS;
+    const int kb = (q >> 2) * BK * 2;
+#pragma unroll
+    for (int i = 0; i < LQ; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (i * 4 + wig) * RPI * RB), 16,
+                                               a_off[i], kb, 0, 0);
+  };
+  auto issue_b = [&](int q, __amdgpu_buffer_rsrc_t rb) {
+    if (q >= NQ) return;
+    char* st = smem + (q % 10) * QS;
+    const int kb = (q >> 2) * BK * 2;
+#pragma unroll
+    for (int i = 0; i < LQ; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + (i * 4 + wig) * RPI * RB), 16,
+                                               b_off0 + i * b_step, kb, 0, 0);
+  };
+  // fragment rows within their quarters (16x16x32: lane reads row lane%16)
+  int ar[MI], br[NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) ar[mi] = wml * 64 + mi * 16 + (lane & 15);
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+    br[ni] = (SWIGLU ? wn * 64 + (ni & 3) * 16 : ni * 16) + (lane & 15);
+  floatx4 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[mi][ni][q] = 0.0f;
+  // a wave with no row of the group skips its fragment reads and MFMAs
+  const bool live = grp * 128 + wml * 64 < rows;
+
+  // prologue: steps 0 and 1; group 0 its A quarters and B rows 0-127,
+  // group 1 its A quarters and B rows 128-255
+  if (grp == 0) {
+    issue_a(0); issue_b(2, rb0); issue_a(4); issue_b(6, rb0);
+  } else {
+    issue_a(1); issue_b(3, rb1); issue_a(5); issue_b(7, rb1);
+  }
+  vm_wait<0>();
+  pp_barrier();
+  if (grp == 1) pp_barrier();
+  bf16x8 a[2][MI], b[2][NI];
+  for (int kt = 0; kt < KT; ++kt) {
+    const char* sa = smem + ((4 * kt + grp) % 10) * QS;
+    const char* sb0 = smem + ((4 * kt + 2) % 10) * QS;
+    const char* sb1 = smem + ((4 * kt + 3) % 10) * QS;
+    const char* sbw = SWIGLU ? sb0 : (wn ? sb1 : sb0);
+    // MEM phase: this group's two quarters (group 0: B rows 128-255 of
+    // step kt+1 and its A quarter of step kt+2; group 1: its A quarter and
+    // B rows 0-127 of step kt+2), then the step's fragments
+    const int q0 = 4 * kt + 7 + 2 * grp, q1 = q0 + 1;
+    if (grp == 0) {
+      if (q0 >= NQ_PRO) issue_b(q0, rb1);
+      issue_a(q1);
+    } else {
+      issue_a(q0);
+      issue_b(q1, rb0);
+    }
+    if (live) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int kc = ks * 4 + (lane >> 4);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+          a[ks][mi] = *(const bf16x8*)(sa + ar[mi] * RB + ((kc ^ swz<BK>(ar[mi])) << 4));
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const char* sb = SWIGLU ? (ni < 4 ? sb0 : sb1) : sbw;
+          b[ks][ni] = *(const bf16x8*)(sb + br[ni] * RB + ((kc ^ swz<BK>(br[ni])) << 4));
+        }
+      }
+    }
+    if (grp == 1) {
+      // quarters up to 4kt+6 landed; its two newest may stay in flight
+      if (q1 < NQ) vm_wait<2 * LQ>();
+      else if (q0 < NQ) vm_wait<LQ>();
+      else vm_wait<0>();
+    }
+    lgkm_wait0();
+    pp_barrier();
+    // COMP phase
+    if (live) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+            acc[mi][ni] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][mi], b[ks][ni], acc[mi][ni], 0, 0, 0);
+    }
+    if (grp == 0) {
+      // quarters up to 4kt+7 landed; its newest (4kt+8) may stay in flight
+      if (q1 >= NQ_PRO && q1 < NQ) vm_wait<LQ>();
+      else vm_wait<0>();
+    }
+    pp_barrier();
+  }
+  if (grp == 0) pp_barrier();
+
+  // Epilogue through LDS (the ring is free: every wave passed the last
+  // barrier after its last reads), then whole 16-byte row chunks.
+  // 16x16 accumulator layout: register q of a lane holds row
+  // (lane/16)*4 + q, column lane%16.
+  constexpr int OUTC = SWIGLU ? 128 : BNB;
+  constexpr int ROWB = OUTC * 2;
+  constexpr int STRIDE = ROWB + 16;
+  static_assert(256 * STRIDE <= 10 * QS, "output tile fits the ring");
+  const int wm0 = grp * 128 + wml * 64;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int lr = wm0 + mi * 16 + (lane >> 4) * 4 + q;
+      uint16_t* orow = (uint16_t*)(smem + lr * STRIDE);
+      if (SWIGLU) {
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const float gv = acc[mi][ni][q], uv = acc[mi][ni + 4][q];
+          // SiLU(g) * u with the hardware reciprocal (~1 ulp)
+          const float av = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+          orow[wn * 64 + ni * 16 + (lane & 15)] = f2bf(av);
+        }
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          orow[wn * 128 + ni * 16 + (lane & 15)] = f2bf(acc[mi][ni][q]);
+      }
+    }
+  __syncthreads();
+  constexpr int CPRO = ROWB / 16;
+  constexpr int RPIO = 512 / CPRO;
+  uint16_t* cbase = P.C + (size_t)row0 * P.Nout + (size_t)nt * OUTC;
+#pragma unroll
+  for (int it = 0; it < 256 / RPIO; ++it) {
+    const int r = it * RPIO + tid / CPRO, ch = tid % CPRO;
+    if (r < rows)
+      *(uint4*)(cbase + (size_t)r * P.Nout + ch * 8) = *(const uint4*)(smem + r * STRIDE + ch * 16);
+  }
+}
+
 template <int BM, int BK, int NST, bool SWIGLU, int NW, int NWN>
 __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
-  // one ring for either tile shape the kernel may run
+  // one ring for either tile shape the kernel may run; 256-row tiles run
+  // the two-group loop over its 160 KB ring of quarters
   constexpr bool HAS_REM = BM > kRemBM;
-  constexpr int RING = NST * (BM + BNB) * BK * 2;
+  constexpr int RING = BM == 256 ? kPpRing : NST * (BM + BNB) * BK * 2;
+  static_assert(BM != 256 || NW == 8, "the 256-row loop runs 8 waves");
   static_assert(!HAS_REM || shape_waves(MOE_GEMM_REM) == NW, "REM runs in the same block");
   __shared__ __attribute__((aligned(1024))) char smem[HAS_REM && kRemRing > RING ? kRemRing : RING];
   PassInfo pi = resolve_pass(P.pa);
@@ -442,6 +680,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   // in L2 with the group's other tiles), half the MFMA work.
   if (HAS_REM && rows <= kRemBM)
     gmm_tile<MOE_GEMM_REM, SWIGLU>(P, smem, aidx, row0, rows, nt, e);
+  else if constexpr (BM == 256)
+    gmm_tile_pp<SWIGLU>(P, smem, aidx, row0, rows, nt, e);
   else
     gmm_tile<BM, BK, NST, NW, NWN, SWIGLU>(P, smem, aidx, row0, rows, nt, e);
 }
