@@ -21,8 +21,9 @@ the same passes (given the forward's saved x_sorted and expert outputs) is
 timed as a whole and step by step ("backward" in the JSON), and so is the
 whole-layer backward call (which also recomputes the routing, layouts,
 x_sorted and expert outputs) and a training step's layer forward plus it.
-A plain device copy and the vendor library's dense bf16 GEMM are timed as
-what this box reaches outside the library ("measured_peaks").  The CPU
+The library's calibration kernels (a streaming copy and a matrix-core loop)
+and the vendor library's dense bf16 GEMM are timed as what this machine reaches
+outside the layer ("measured_peaks").  The CPU
 oracle is then timed on the host cores on the same inputs (the whole layer
 where it finishes within the budget, else the plain layer definition on a
 stated sample of tokens).  One JSON line is printed at the end.
@@ -50,15 +51,17 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
-# HBM traffic of the grouped GEMM (its one launch: GEMM1 and GEMM2 fused) per
-# mid_bf16 layer, from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE)
-# scaled by what the counters read for a plain 1 GiB device copy (FETCH_SIZE
-# x1.99985, WRITE_SIZE x1.0).  It holds only for the kernel source it was
-# measured on (sha256 of gmm.hip); for any other source or workload the
-# traffic is reported as null.
-GEMM_TRAFFIC = {"workload": "mid_bf16",
-                "gmm_src_sha256": "6bd49b9048391c64aef857c6ad9679726fff97383f26937cdf13b718e0908179",
-                "bytes_per_layer": 260268700}
+# HBM traffic of the grouped GEMM per layer (every GEMM launch of one LAYER
+# call), from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by
+# what the counters read for the calibration copy of 1 GiB (FETCH_SIZE
+# x1.99997, WRITE_SIZE x1.0).  It holds only for the kernel source it was
+# measured on (sha256 of gmm.hip) and that workload; otherwise the traffic
+# is reported as null.
+GEMM_TRAFFIC = {
+    "maverick_shard": {
+        "gmm_src_sha256": "873365a19b90e84973d0b6b46de908e03b490aee39737550ab00271988060bc3",
+        "bytes_per_layer": 31563072768},
+}
 
 
 def recorded_gemm_traffic(workload):
@@ -66,9 +69,10 @@ def recorded_gemm_traffic(workload):
     src = os.path.join(ROOT, "grouped_gemm_shard_amd", "csrc", "gmm.hip")
     with open(src, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
-    if workload != GEMM_TRAFFIC["workload"] or sha != GEMM_TRAFFIC["gmm_src_sha256"]:
+    rec = GEMM_TRAFFIC.get(workload)
+    if rec is None or sha != rec["gmm_src_sha256"]:
         return None
-    return GEMM_TRAFFIC["bytes_per_layer"]
+    return rec["bytes_per_layer"]
 
 
 def cache_note(w, p):
@@ -326,27 +330,36 @@ def backward_figures(p, w, inp, info, reps):
 
 
 def measured_peaks(reps=10):
-    """What this machine reaches outside the library, as context for the
-    fractions of the spec peaks: a plain 1 GiB device-to-device copy (bytes
-    read + written per second) and torch's dense bf16 GEMM (the vendor
-    library) at 8192^3.  Timed with HIP events on the current stream."""
-    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    """What this machine reaches outside the layer, as context for the fractions
+    of the spec peaks: the library's own calibration kernels
+    (include/moe_calib.h) -- a streaming copy of 1 GiB (bytes read +
+    written per second) and a matrix-core loop of bf16 MFMAs on registers --
+    and, for comparison, the vendor library's dense bf16 GEMM (torch.mm,
+    hipBLASLt) at 8192^3.  Timed with HIP events on the current stream."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
-    t_copy = time_calls(lambda: dst.copy_(src), reps)
+    t_copy = time_calls(lambda: g.calib_copy(src, dst), reps)
     del src, dst
-    n = 8192
+    sink = torch.empty(512, dtype=torch.float32, device="cuda")
+    blocks = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    flops = g.calib_mfma(blocks, 4000, sink)
+    t_mfma = time_calls(lambda: g.calib_mfma(blocks, 4000, sink), reps)
+    m = 8192
     gen = torch.Generator(device="cuda")
     gen.manual_seed(0)
-    a = torch.randn((n, n), generator=gen, device="cuda").to(torch.bfloat16)
-    b = torch.randn((n, n), generator=gen, device="cuda").to(torch.bfloat16)
-    c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    a = torch.randn((m, m), generator=gen, device="cuda").to(torch.bfloat16)
+    b = torch.randn((m, m), generator=gen, device="cuda").to(torch.bfloat16)
+    c = torch.empty((m, m), dtype=torch.bfloat16, device="cuda")
     t_mm = time_calls(lambda: torch.mm(a, b, out=c), reps)
     del a, b, c
     torch.cuda.empty_cache()
-    return {"hbm_copy_gbs": round(2 * (1 << 30) / t_copy / 1e9, 1),
-            "dense_bf16_gemm_tflops": round(2.0 * n ** 3 / t_mm / 1e12, 1),
-            "method": "1 GiB device copy (read + written bytes); torch.mm bf16 8192^3; "
-                      f"HIP events, mean of {reps}"}
+    return {"hbm_copy_gbs": round(2 * n / t_copy / 1e9, 1),
+            "mfma_loop_tflops": round(flops / t_mfma / 1e12, 1),
+            "vendor_dense_bf16_gemm_tflops": round(2.0 * m ** 3 / t_mm / 1e12, 1),
+            "method": "moe_calib_copy 1 GiB (read + written bytes); moe_calib_mfma "
+                      f"({blocks} workgroups x 8 waves x 4000 rounds of 8 16x16x32 bf16 MFMAs); "
+                      f"torch.mm bf16 8192^3; HIP events, mean of {reps}"}
 
 
 def workloads_pass_tokens(w, n, c):
@@ -454,7 +467,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward of the layer's passes")
     ap.add_argument("--calib-copy", action="store_true",
-                    help="also run a plain 1 GiB device copy (reference for HBM counters)")
+                    help="also run the calibration copy of 1 GiB (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs one expert-parallel shard per "
@@ -556,19 +569,19 @@ def main():
                "roofline": broof}
 
     if args.calib_copy:
-        log("[bench] calibration copy: 1 GiB device-to-device, 3 times")
+        log("[bench] calibration copy: moe_calib_copy of 1 GiB, 3 times")
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            g.calib_copy(src, dst)
         torch.cuda.synchronize()
         del src, dst
 
-    log("[bench] measured peaks (plain copy, vendor dense GEMM)")
+    log("[bench] measured peaks (calibration copy and MFMA loop, vendor dense GEMM)")
     peaks = measured_peaks()
     roof["frac_of_measured"] = round(
         roof["achieved"] / (peaks["hbm_copy_gbs"] if roof["bound"] == "hbm"
-                            else peaks["dense_bf16_gemm_tflops"] if w.bf16 else peak_mm), 4)
+                            else peaks["mfma_loop_tflops"] if w.bf16 else peak_mm), 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -595,8 +608,10 @@ def main():
                    "chunks_per_pass": g.layer_chunks_per_pass(p, g.MODE_LAYER),
                    "cache": cache_note(w, p)},
         "gemm": {"tflops": round(gemm_tflops, 2), "frac_mfma_peak": round(gemm_tflops / peak_mm, 4),
-                 "frac_of_dense_gemm": (round(gemm_tflops / peaks["dense_bf16_gemm_tflops"], 4)
-                                        if w.bf16 else None),
+                 "frac_of_mfma_loop": (round(gemm_tflops / peaks["mfma_loop_tflops"], 4)
+                                       if w.bf16 else None),
+                 "frac_of_vendor_gemm": (round(gemm_tflops / peaks["vendor_dense_bf16_gemm_tflops"], 4)
+                                         if w.bf16 else None),
                  "gbs": round(gemm_gbs, 1), "arith_intensity": round(ai, 1),
                  "us_per_layer": round(kf["t_gmm_sched"] * 1e6, 2),
                  "schedule": "every pass's GEMM calls replayed on the layer's two-stream "

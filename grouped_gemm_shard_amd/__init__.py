@@ -25,7 +25,8 @@ __all__ = [
     "moe_combine_from_partials", "moe_layer_dropless_chunked", "status_string", "LayerRunner",
     "bwd_workspace_bytes", "moe_combine_bwd", "moe_gmm_swiglu_bwd",
     "moe_permute_bwd", "moe_route_bwd", "layer_bwd_workspace_bytes", "moe_layer_bwd",
-    "LayerBackwardRunner", "testing_set_gemm_wait_limit", "moe_gmm_swiglu_noalloc", "ERR_BAD_INDEX", "ERR_BAD_OFFSETS",
+    "LayerBackwardRunner", "testing_set_gemm_wait_limit", "moe_gmm_swiglu_noalloc",
+    "calib_copy", "calib_mfma", "ERR_BAD_INDEX", "ERR_BAD_OFFSETS",
     "ERR_GEMM_WAIT",
 ]
 
@@ -40,7 +41,8 @@ EXPORTED = ["moe_workspace_bytes", "moe_pass_max_rows", "moe_layer_workspace_byt
             "moe_layer_dropless_chunked", "moe_bwd_workspace_bytes", "moe_combine_bwd",
             "moe_gmm_swiglu_bwd", "moe_permute_bwd", "moe_route_bwd",
             "moe_layer_bwd_workspace_bytes", "moe_layer_bwd", "moe_status_string",
-            "moe_testing_set_gemm_wait_limit", "moe_gmm_swiglu_noalloc"]
+            "moe_testing_set_gemm_wait_limit", "moe_gmm_swiglu_noalloc", "moe_calib_copy",
+            "moe_calib_mfma"]
 
 # Device-side error bits (include/moe_shard.h)
 ERR_BAD_INDEX, ERR_BAD_OFFSETS, ERR_GEMM_WAIT = 1, 2, 4
@@ -145,6 +147,8 @@ def _load():
         "moe_layer_bwd": [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_testing_set_gemm_wait_limit": [i32],
         "moe_gmm_swiglu_noalloc": [P, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp],
+        "moe_calib_copy": [vp, vp, i64, i32, vp],
+        "moe_calib_mfma": [i32, i32, vp, ctypes.POINTER(i64), vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -178,6 +182,23 @@ def testing_set_gemm_wait_limit(spins: int):
     sleeps for every later call; 0 restores the default, < 0 gives up at
     once."""
     _check("moe_testing_set_gemm_wait_limit", _lib().moe_testing_set_gemm_wait_limit(spins))
+
+
+def calib_copy(src, dst, blocks=4096, stream=None):
+    """Streaming copy kernel (include/moe_calib.h): src and dst are byte
+    tensors of the same size."""
+    _check("moe_calib_copy", _lib().moe_calib_copy(_ptr(src, torch.uint8, "src"),
+                                                   _ptr(dst, torch.uint8, "dst"), src.numel(),
+                                                   blocks, _stream(stream)))
+
+
+def calib_mfma(blocks, iters, sink, stream=None) -> int:
+    """Matrix-core peak loop (include/moe_calib.h); returns its bf16 flops."""
+    flops = ctypes.c_int64()
+    _check("moe_calib_mfma", _lib().moe_calib_mfma(blocks, iters,
+                                                   _ptr(sink, torch.float32, "sink"),
+                                                   ctypes.byref(flops), _stream(stream)))
+    return flops.value
 
 
 def status_string(status: int) -> str:

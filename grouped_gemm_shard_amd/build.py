@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_shard.so")
-SOURCES = ["route.hip", "count.hip", "layout.hip", "gmm.hip", "combine.hip", "backward.hip", "abi.cpp"]
+SOURCES = ["route.hip", "count.hip", "layout.hip", "gmm.hip", "combine.hip", "backward.hip", "calib.hip",
+           "abi.cpp"]
 ARCH = "gfx950"
 
 

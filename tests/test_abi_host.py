@@ -221,3 +221,17 @@ def test_layer_backward_validates_on_the_host():
     assert call(0, fake, need, None) == -1  # no upstream gradient
     assert call(0, None, need) == -1        # no workspace
     assert call(0, fake, need - 1) == -3    # workspace too small
+
+
+def test_calib_rejects_bad_arguments_on_the_host():
+    """The calibration entry points validate before any launch."""
+    g = _binding()
+    L = g._lib()
+    buf = ctypes.create_string_buffer(64)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    assert L.moe_calib_copy(p, None, 16, 1, None) == -1           # null destination
+    assert L.moe_calib_copy(p, p, 24, 1, None) == -1               # not a multiple of 16
+    assert L.moe_calib_copy(p, p, 16, 0, None) == -1               # no workgroups
+    f = ctypes.c_int64()
+    assert L.moe_calib_mfma(0, 1, p, ctypes.byref(f), None) == -1  # no workgroups
+    assert L.moe_calib_mfma(1, 1, None, ctypes.byref(f), None) == -1
