@@ -184,7 +184,7 @@ def testing_set_gemm_wait_limit(spins: int):
     _check("moe_testing_set_gemm_wait_limit", _lib().moe_testing_set_gemm_wait_limit(spins))
 
 
-def calib_copy(src, dst, blocks=4096, stream=None):
+def calib_copy(src, dst, blocks=8192, stream=None):
     """Streaming copy kernel (include/moe_calib.h): src and dst are byte
     tensors of the same size."""
     _check("moe_calib_copy", _lib().moe_calib_copy(_ptr(src, torch.uint8, "src"),
