@@ -7,7 +7,8 @@ benchmark times (LAYER mode).
   that defines them, on the GPU with torch indexing: x_sorted[n] ==
   x[sorted_assign[n] / k], x_dedup[u] == x[dedup_token[u]], x_sorted[n] ==
   x_dedup[expand_idx[n]].
-* y of the whole LAYER call is compared on a seeded sample of tokens with
+* y of the whole LAYER call is compared on at least 512 tokens -- one in
+  every group of every pass the layer took, then a seeded sample -- with
   the oracle's plain definition of the dropless layer (which the chunked
   fallback must equal), to the layer's tolerance; tokens with no resident
   assignment must be exactly 0.
@@ -25,6 +26,7 @@ from workloads import CONFIGS
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 FULL = ["dsv3_shard", "maverick_shard", "dedup_redundant", "dsv3_ep8_receive"]
+Y_SAMPLE = 512
 
 
 class LazyRows:
@@ -85,6 +87,8 @@ def test_full_size_layer(name):
     assert np.array_equal(ints(scv), sc)
 
     passes = [(w.num_chunks, c, 0) for c in range(w.num_chunks)] if ovf else [(1, 0, 1)]
+    rng = np.random.default_rng(7)
+    touch = set()  # one token per (pass, group) for the sampled y
     for (n, c, capped) in passes:
         say(f"[full] {name}: pass n={n} c={c} capped={capped}")
         rows, drows = g.pass_max_rows(p, n, capped)
@@ -100,6 +104,10 @@ def test_full_size_layer(name):
         lay = oracle.pass_layout(op, slot, toks, cap if capped else None)
         torch.cuda.synchronize()
         N = lay["num_rows"]
+        o_go = lay["group_offsets"]
+        for q in range(len(o_go) - 1):
+            if o_go[q + 1] > o_go[q]:
+                touch.add(int(lay["sorted_assign"][rng.integers(o_go[q], o_go[q + 1])]) // w.top_k)
         assert np.array_equal(ints(go), lay["group_offsets"])
         assert np.array_equal(ints(sa)[:N], lay["sorted_assign"])
         pass_a = (toks[:, None] * w.top_k + np.arange(w.top_k)[None, :]).ravel()
@@ -116,13 +124,17 @@ def test_full_size_layer(name):
         del xs, xd
 
     say(f"[full] {name}: sampled y against the oracle")
-    rng = np.random.default_rng(7)
-    sample = np.sort(rng.choice(w.tokens, size=16, replace=False))
+    # a token in every group of every pass, then seeded tokens up to
+    # Y_SAMPLE (non-resident ones included)
     resident = [t for t in range(w.tokens)
                 if any(w.res_lo <= slot[t, j] // p.spd < w.res_hi for j in range(w.top_k))]
-    if resident:
-        extra = rng.choice(np.asarray(resident), size=min(8, len(resident)), replace=False)
-        sample = np.unique(np.concatenate([sample, extra]))
+    sample = set(touch)
+    for t in rng.permutation(w.tokens):
+        if len(sample) >= Y_SAMPLE:
+            break
+        sample.add(int(t))
+    sample = np.asarray(sorted(sample), dtype=np.int64)
+    assert len(sample) >= min(Y_SAMPLE, w.tokens)
     wg, wu, wd = (LazyExperts(t) for t in inp["weights"])
     want = oracle.layer_plain_tokens(op, logits, LazyRows(inp["x"]), wg, wu, wd, sample)
     got = host(y[torch.from_numpy(sample).cuda()])

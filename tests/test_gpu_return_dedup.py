@@ -4,13 +4,8 @@ test_pass_steps_parity covers.
 
 * fp32: a small fp32 problem with dedup and redundant slots, every pass of
   the chunked mode, against the oracle's own pipeline.
-* Full size (dedup_redundant): the oracle's float64 GEMM is out of reach
-  at this size, so the check is by the properties that define the rows, on
-  the GPU's own expert_out: for a seeded sample of tokens, y from the
-  partial rows equals the float64 gate-weighted sum of the token's rows (the
-  combine regrouped); for a seeded sample of dedup rows, the partial row
-  equals the float64 sum of the rows it regroups; both within the layer's
-  tolerance, and rows past the pass's count are untouched.
+* Full size (dedup_redundant): in test_gpu_fullsize_float.py, against
+  the oracle's return path on the GPU's expert_out.
 """
 
 import numpy as np
@@ -97,46 +92,3 @@ def test_fp32_return_path_against_oracle(n, c):
     check_close(y2[toks], o_y2, f"fp32 y from partials n={n} c={c}")
     rest = np.setdiff1d(np.arange(w.tokens), toks)
     assert np.all(y2[rest] == 7.0)
-
-
-@pytest.mark.slow
-def test_full_size_return_path_properties():
-    import grouped_gemm_shard_amd as g
-    torch.cuda.empty_cache()
-    w = workloads.CONFIGS["dedup_redundant"]
-    p = binding_problem(w)
-    inp = workloads.make_inputs(w, device="cuda")
-    say("[return-dedup] full size dedup_redundant")
-    r = step_api(g, p, w, inp, 1, 0, 0)
-    U = int(ints(r["do"])[-1])
-    k = w.top_k
-    part = r["part"]
-    assert bool((part[U:] == 7.0).all())
-    rng = np.random.default_rng(0)
-    roa = ints(r["roa"]).reshape(w.tokens, k)
-    ex = ints(r["ex"])
-    dt = ints(r["dt"])
-    gate = r["gate"].cpu().numpy().astype(np.float64)
-    # sampled tokens: y from the partial rows is the combine of the token's
-    # rows, regrouped by shard
-    toks = rng.choice(w.tokens, size=256, replace=False)
-    got, want = [], []
-    for t in toks:
-        acc = np.zeros(w.hidden, dtype=np.float64)
-        for j in range(k):
-            row = int(roa[t, j])
-            if row >= 0:
-                acc += gate[t, j] * host(r["out"][row])
-        got.append(host(r["y2"][t]))
-        want.append(acc)
-    check_close(np.stack(got), np.stack(want), "y from partials (full size, sampled tokens)")
-    # sampled partial rows: the gate-weighted sum of the expert_out rows
-    # whose dedup row they are
-    for u in rng.choice(U, size=64, replace=False):
-        t = int(dt[u])
-        acc = np.zeros(w.hidden, dtype=np.float64)
-        for j in range(k):
-            row = int(roa[t, j])
-            if row >= 0 and int(ex[row]) == u:
-                acc += gate[t, j] * host(r["out"][row])
-        check_close(host(part[u])[None, :], acc[None, :], f"partial row {u} (full size)")
