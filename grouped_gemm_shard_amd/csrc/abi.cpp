@@ -433,9 +433,11 @@ int moe_permute(const moe_problem* p, int32_t num_chunks, int32_t chunk, int32_t
     lb.dedup_token = dedup_token;
     lb.expand_idx = expand_idx;
   }
-  hipError_t e = launch_layout(d, ls, slot_of_assign, 0, lb, nullptr, s);
-  if (e != hipSuccess) return MOE_EHIP;
   const int row_bytes = d.H * (d.bf16 ? 2 : 4);
+  hipError_t e = launch_permute_one(d, ls, slot_of_assign, lb, x, x_sorted, row_bytes, max_rows, s);
+  if (e != hipErrorNotSupported) return hip_status(e);
+  e = launch_layout(d, ls, slot_of_assign, 0, lb, nullptr, s);
+  if (e != hipSuccess) return MOE_EHIP;
   const int lc = d.L / num_chunks;
   const PassArgs pa = static_pass_args(chunk * lc, lc, capped, 0, d.L);
   if (d.dedup) {

@@ -282,6 +282,12 @@ hipError_t launch_layout(const Dims& d, const LayoutSet& ls, const int* slots, i
 
 // dst[r] = src[index[r] / div] for r < *count, per pass: count, index are
 // base pointers advanced by count_stride / index_stride per layout j.
+// The standalone permute of a single small pass without dedup in one
+// launch (layout and x_sorted); hipErrorNotSupported where it does not
+// apply.
+hipError_t launch_permute_one(const Dims& d, const LayoutSet& ls, const int* soa,
+                              const LayoutBuffers& lb, const void* x, void* x_sorted,
+                              int row_bytes, int64_t max_rows, hipStream_t s);
 hipError_t launch_gather_rows(const int* count, int count_stride, const int* index,
                               long long index_stride, int div, const void* src, void* dst,
                               int row_bytes, int src_rows, int64_t max_rows, const PassArgs& pa,
