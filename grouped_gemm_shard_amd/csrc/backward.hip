@@ -639,6 +639,7 @@ constexpr int kWBK = 32;   // rows per stage
 constexpr int kWNST = 4;   // ring stages
 constexpr int kWMaxRes = 1024;
 constexpr int kWMaxChunks = 2048;
+constexpr int kWOld = 16;  // 16-byte runs per thread of a 128 x 128 float tile
 
 // Per-expert plan of the weight-gradient launches, from the group offsets:
 // the expert's groups in group order (their first row and row count, as a
@@ -894,6 +895,25 @@ __device__ __forceinline__ void wgrad_tile(const WgradParams& P, char* smem, int
   }
   const unsigned lds0 = lds_addr(smem);
 
+  if (direct && P.accumulate && KT == 0) return;
+  float* part = direct ? nullptr : P.part + (size_t)slot * P.I * P.J;
+  // element (i, j) of expert e's gradient, or of the chunk's partial
+  auto out_ptr = [&](int i, int j) {
+    if (!direct) return part + (size_t)i * P.J + j;
+    if (i < P.i_split) return P.C0 + (size_t)e * P.c_stride + (size_t)i * P.J + j;
+    return P.C1 + (size_t)e * P.c_stride + (size_t)(i - P.i_split) * P.J + j;
+  };
+  // an accumulated gradient's old values, 16-byte runs of the tile's rows
+  // (thread tid: rows tid/32 + 8m, columns 4 (tid%32) ...), loaded now so
+  // that their latency passes during the reduction loop
+  const bool rmw = direct && P.accumulate;
+  float4 old[kWOld];
+  if (rmw) {
+#pragma unroll
+    for (int m = 0; m < kWOld; ++m)
+      old[m] = *(const float4*)out_ptr(i0 + (tid >> 5) + 8 * m, j0 + (tid & 31) * 4);
+  }
+
 #pragma unroll
   for (int s0 = 0; s0 < kWNST - 1; ++s0)
     if (s0 < KT) issue(s0);
@@ -923,40 +943,39 @@ __device__ __forceinline__ void wgrad_tile(const WgradParams& P, char* smem, int
   }
 
   // a single-chunk expert writes its gradient (skipped when there is
-  // nothing to add), a split expert's chunk its partial
-  if (direct && P.accumulate && KT == 0) return;
-  float* part = direct ? nullptr : P.part + (size_t)slot * P.I * P.J;
-  // output element (mi, q, ni) of this lane: row i of the tile's rows, column j
-  auto out_ptr = [&](int mi, int q, int ni) {
-    const int i = i0 + wm * 64 + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-    const int j = j0 + wn * 64 + ni * 32 + (lane & 31);
-    if (!direct) return part + (size_t)i * P.J + j;
-    if (i < P.i_split) return P.C0 + (size_t)e * P.c_stride + (size_t)i * P.J + j;
-    return P.C1 + (size_t)e * P.c_stride + (size_t)(i - P.i_split) * P.J + j;
-  };
-  if (direct && P.accumulate) {
-    // all old values are loaded before any is needed, so the loads overlap
-    // instead of each waiting a full memory round trip
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        floatx16 old;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) old[q] = *out_ptr(mi, q, ni);
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[mi][ni][q] += old[q];
-      }
-  }
+  // nothing to add), a split expert's chunk its partial.  The tile goes
+  // through LDS (the ring, 64 KB = 128 x 128 floats) so that every thread
+  // then reads, adds and stores whole 16-byte runs of rows; the old values
+  // of an accumulated gradient were loaded before the reduction loop.
+  __syncthreads();  // every wave is done with the ring
+  float* tile = (float*)smem;
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) *out_ptr(mi, q, ni) = acc[mi][ni][q];
+      for (int q = 0; q < 16; ++q) {
+        const int i = wm * 64 + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+        const int j = wn * 64 + ni * 32 + (lane & 31);
+        tile[i * 128 + j] = acc[mi][ni][q];
+      }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < kWOld; ++m) {
+    const int i = (tid >> 5) + 8 * m, j = (tid & 31) * 4;
+    float4 v = *(const float4*)(tile + i * 128 + j);
+    if (rmw) {
+      v.x += old[m].x;
+      v.y += old[m].y;
+      v.z += old[m].z;
+      v.w += old[m].w;
+    }
+    *(float4*)out_ptr(i0 + i, j0 + j) = v;
+  }
 }
 
 __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradParams P) {
+  static_assert(kWNST * 2 * kWBK * 256 >= 128 * 128 * 4, "the epilogue's tile fits the ring");
   __shared__ __attribute__((aligned(1024))) char smem[kWNST * 2 * kWBK * 256];
   __shared__ int gl[2 * kWMaxGroups];
   wgrad_tile(P, smem, gl);
@@ -1402,6 +1421,8 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   for (const WgradParams* q : {&W, &V}) {
     hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)(nc * q->ni_tiles * q->nj_tiles)),
                        dim3(256), 0, s, *q);
+    // an expert is split only when it has more than kc rows
+    if (kc >= rows) continue;
     const long long ij4 = ((long long)q->I * q->J / 4 + 255) / 256;
     hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)ij4, (unsigned)e_res), dim3(256), 0, s,
                        *q);
