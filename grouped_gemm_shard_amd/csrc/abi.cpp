@@ -818,16 +818,37 @@ int moe_route_bwd(const moe_problem* p, const int32_t* topk_idx, const float* to
 
 namespace {
 
+// Whether a layer backward takes the weight gradients of all its passes in
+// one launch at the end (bf16, two or more pass slots, every pass's groups
+// together within kMaxSlots, every operand offset within 31 bits).  The
+// passes then keep their x_sorted, d_out, d_h and act rows, and the float32
+// gradients are written once instead of read and written once per pass
+// (the pages' scan carries them from chunk to chunk; holding every chunk's
+// rows at once is what a GPU with this much memory can afford).
+bool defer_wgrad(const Dims& d, int slots, int64_t rows) {
+  if (!d.bf16 || slots < 2 || (int64_t)slots * d.G_res > kMaxSlots) return false;
+  const int64_t wide = d.H > 2 * d.F ? d.H : 2 * d.F;
+  return (int64_t)slots * rows * wide * 2 < ((int64_t)1 << 31);
+}
+
 // Workspace of moe_layer_bwd: the forward layer's (routing, counts, layouts,
-// one set of pass buffers), then per pass x_sorted, d_out and dx_sorted
-// rows, the gate gradients, and the grouped-GEMM backward's scratch.
+// one set of pass buffers), then x_sorted and d_out rows (per pass slot
+// when the weight gradients are deferred, else one set), dx_sorted rows, the
+// gate gradients, the grouped-GEMM backward's scratch and, deferred, every
+// pass's d_h and act rows and group offsets and the weight gradients'
+// scratch.
 struct LayerBwdWs {
   LayerWs fwd;
+  bool defer;
   void* x_sorted;
   void* d_out;
   void* dxs;
   float* d_gate;
   void* gmm;
+  void* d_h_all;
+  void* act_all;
+  int* go_all;
+  void* wgrad;
   size_t bytes;
 };
 
@@ -844,11 +865,22 @@ LayerBwdWs carve_layer_bwd(const Dims& d, const LayoutSet& ls, int64_t rows, int
     return (void*)p;
   };
   const size_t es = d.bf16 ? 2 : 4;
-  w.x_sorted = take((size_t)rows * d.H * es);
-  w.d_out = take((size_t)rows * d.H * es);
+  const int slots = layer_pass_slots(ls);
+  w.defer = defer_wgrad(d, slots, rows);
+  const size_t sets = w.defer ? (size_t)slots : 1;
+  w.x_sorted = take(sets * rows * d.H * es);
+  w.d_out = take(sets * rows * d.H * es);
   w.dxs = take((size_t)rows * d.H * es);
   w.d_gate = (float*)take((size_t)d.T * d.k * 4);
   w.gmm = take(gmm_bwd_scratch_bytes(d, rows));
+  w.d_h_all = w.act_all = w.wgrad = nullptr;
+  w.go_all = nullptr;
+  if (w.defer) {
+    w.d_h_all = take(sets * rows * 2 * d.F * es);
+    w.act_all = take(sets * rows * d.F * es);
+    w.go_all = (int*)take(sets * (d.G_res + 1) * 4);
+    w.wgrad = take(wgrad_sets_scratch_bytes(d, slots, rows));
+  }
   w.bytes = off;
   return w;
 }
@@ -927,7 +959,8 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
   // the scan's backward recomputes each chunk), then the combine, grouped
   // GEMM and permute backward; the weight gradients are overwritten by the
   // first pass slot and accumulated by the others (a slot the device does
-  // not take leaves them alone)
+  // not take leaves them alone), or, deferred (defer_wgrad), taken over all
+  // pass slots' rows after the loop
   const long long tk = (long long)d.T * d.k;
   const int es = d.bf16 ? 2 : 4;
   const int slots = layer_pass_slots(ls);
@@ -940,8 +973,13 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
     } else {
       pa = static_pass(d, ls, b);
     }
-    e = launch_gather_rows(lb.meta, kLayoutMeta, lb.sorted_assign, tk, d.k, x, w.x_sorted,
-                           d.H * es, d.T, rows, pa, s);
+    // this pass's x_sorted and d_out rows (their own per pass slot when
+    // the weight gradients come at the end)
+    const size_t set = w.defer ? (size_t)b : 0;
+    void* xs_b = (char*)w.x_sorted + set * rows * d.H * es;
+    void* dout_b = (char*)w.d_out + set * rows * d.H * es;
+    e = launch_gather_rows(lb.meta, kLayoutMeta, lb.sorted_assign, tk, d.k, x, xs_b, d.H * es,
+                           d.T, rows, pa, s);
     if (e != hipSuccess) return MOE_EHIP;
     // bf16: the rows g*dy need no expert output, and the grouped-GEMM
     // backward recomputes the activation anyway, so it also returns the
@@ -950,7 +988,7 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
     if (!d.bf16) {
       GemmPass gp;
       memset(&gp, 0, sizeof(gp));
-      gp.a_src = w.x_sorted;
+      gp.a_src = xs_b;
       gp.a_src_rows = (int)rows;
       gp.a_div = 1;
       gp.group_offsets = lb.group_offsets;
@@ -963,11 +1001,11 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
                      nullptr, s);
       if (e != hipSuccess) return MOE_EHIP;
     }
-    e = launch_combine_bwd(d, pa, ls, dy, f.out[0], lb.row_of_assign, tk, f.topk_gate, w.d_out,
+    e = launch_combine_bwd(d, pa, ls, dy, f.out[0], lb.row_of_assign, tk, f.topk_gate, dout_b,
                            w.d_gate, rows, d.bf16 ? 1 : 3, s);
     if (e != hipSuccess) return MOE_EHIP;
     GemmBwdArgs a;
-    a.x_sorted = w.x_sorted;
+    a.x_sorted = xs_b;
     a.group_offsets = lb.group_offsets;
     a.go_stride = d.G_res + 1;
     a.pa = pa;
@@ -975,7 +1013,7 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
     a.wg = w_gate;
     a.wu = w_up;
     a.wd = w_down;
-    a.d_out = w.d_out;
+    a.d_out = dout_b;
     a.dx_sorted = w.dxs;
     a.dwg = dw_gate;
     a.dwu = dw_up;
@@ -984,6 +1022,12 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
     a.max_rows = rows;
     a.scratch = w.gmm;
     a.out_recompute = d.bf16 ? f.out[0] : nullptr;
+    if (w.defer) {
+      a.go_out = w.go_all + set * (d.G_res + 1);
+      a.d_h_ext = (char*)w.d_h_all + set * rows * 2 * d.F * es;
+      a.act_ext = (char*)w.act_all + set * rows * d.F * es;
+      a.wgrad = 0;
+    }
     e = launch_gmm_bwd(d, a, s);
     if (e != hipSuccess) return MOE_EHIP;
     if (d.bf16) {
@@ -992,6 +1036,13 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
       if (e != hipSuccess) return MOE_EHIP;
     }
     e = launch_permute_bwd(d, pa, ls, w.dxs, lb.row_of_assign, tk, dx, rows, s);
+    if (e != hipSuccess) return MOE_EHIP;
+  }
+  if (w.defer) {
+    // every pass slot's weight gradients in one plan (a slot the device did
+    // not take has no rows), written once
+    e = launch_wgrad(d, slots, w.go_all, rows, f.slot_expert, w.d_h_all, w.x_sorted, w.d_out,
+                     w.act_all, dw_gate, dw_up, dw_down, 0, w.wgrad, s);
     if (e != hipSuccess) return MOE_EHIP;
   }
   return hip_status(launch_route_bwd(d, f.topk_idx, f.topk_gate, w.d_gate, d_logits, s));

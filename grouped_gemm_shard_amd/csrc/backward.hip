@@ -662,8 +662,13 @@ struct WgradPlan {
   int* meta;       // [0] chunks in use
 };
 
+// The groups are `nsets` sets of G (the passes of a layer call whose weight
+// gradients are taken together): set s's offsets are group_offsets[s (G+1)
+// ...] over rows s * row_stride + [0, max_rows) of the operands.  A set
+// with malformed offsets leaves every group empty.
 __global__ __launch_bounds__(1024) void wgrad_plan_kernel(WgradPlan W, const int* group_offsets,
                                                           const int* slot_expert, int G,
+                                                          int nsets, long long row_stride,
                                                           int lo_slot, int e_base, int e_res,
                                                           long long max_rows, int kc, int nc_ub) {
   __shared__ int ge[kMaxSlots], gr[kMaxSlots], g0[kMaxSlots];
@@ -672,13 +677,17 @@ __global__ __launch_bounds__(1024) void wgrad_plan_kernel(WgradPlan W, const int
   const int tid = threadIdx.x;
   if (tid == 0) bad = 0;
   __syncthreads();
+  const int Gs = G;
+  G = nsets * Gs;  // <= kMaxSlots (host)
   for (int g = tid; g < G; g += blockDim.x) {
-    const int a = group_offsets[g], b = group_offsets[g + 1];
+    const int set = g / Gs, gg = g - set * Gs;
+    const int* go = group_offsets + (size_t)set * (Gs + 1);
+    const int a = go[gg], b = go[gg + 1];
     if (a < 0 || b < a || b > max_rows) bad = 1;
-    const int e = slot_expert[lo_slot + g] - e_base;
+    const int e = slot_expert[lo_slot + gg] - e_base;
     ge[g] = (e >= 0 && e < e_res) ? e : -1;
     gr[g] = b - a;
-    g0[g] = a;
+    g0[g] = (int)(set * row_stride) + a;
   }
   __syncthreads();
   // a malformed offset sequence leaves every group empty, so the rows of
@@ -1171,7 +1180,7 @@ struct WgradScratch {
   size_t bytes;
 };
 
-WgradScratch carve_wgrad(const Dims& d, int64_t max_rows, char* base) {
+WgradScratch carve_wgrad(const Dims& d, int64_t max_rows, int groups, char* base) {
   const int e_res = d.S_res * d.El;
   const int kc = wgrad_kc(d, max_rows);
   const long long nc = wgrad_nc_ub(d, max_rows, kc);
@@ -1184,8 +1193,8 @@ WgradScratch carve_wgrad(const Dims& d, int64_t max_rows, char* base) {
     return p;
   };
   w.plan.grp_off = (int*)take((size_t)(e_res + 1) * 4);
-  w.plan.grp_row0 = (int*)take((size_t)d.G_res * 4);
-  w.plan.grp_len = (int*)take((size_t)d.G_res * 4);
+  w.plan.grp_row0 = (int*)take((size_t)groups * 4);
+  w.plan.grp_len = (int*)take((size_t)groups * 4);
   w.plan.rows = (int*)take((size_t)e_res * 4);
   w.plan.nch = (int*)take((size_t)e_res * 4);
   w.plan.pbase = (int*)take((size_t)e_res * 4);
@@ -1205,8 +1214,12 @@ size_t gmm_bwd_scratch_bytes(const Dims& d, int64_t max_rows) {
   const size_t el = d.bf16 ? 2 : 4;
   size_t b = 2 * a256((size_t)(d.G_res + 1) * 4) + 3 * a256((size_t)max_rows * d.F * el) +
              a256((size_t)max_rows * d.F * el);
-  if (d.bf16) b += carve_wgrad(d, max_rows, nullptr).bytes;
+  if (d.bf16) b += carve_wgrad(d, max_rows, d.G_res, nullptr).bytes;
   return b;
+}
+
+size_t wgrad_sets_scratch_bytes(const Dims& d, int sets, int64_t rows_per_set) {
+  return carve_wgrad(d, (int64_t)sets * rows_per_set, sets * d.G_res, nullptr).bytes;
 }
 
 hipError_t launch_combine_bwd(const Dims& d, const PassArgs& pa, const LayoutSet& ls,
@@ -1246,6 +1259,59 @@ hipError_t launch_route_bwd(const Dims& d, const int* idx, const float* gate,
   return hipGetLastError();
 }
 
+hipError_t launch_wgrad(const Dims& d, int sets, const int* group_offsets, int64_t rows,
+                        const int* slot_expert, const void* d_h, const void* x_sorted,
+                        const void* d_out, const void* act, float* dwg, float* dwu, float* dwd,
+                        int accumulate, void* scratch, hipStream_t s) {
+  // plan (rows and chunks per expert over every set's groups), then
+  // [dWg ; dWu] = [d_hg | d_hu]^T x_sorted and dWd = d_out^T act, each with
+  // the fixed-order sum of split experts' partials
+  const int e_res = d.S_res * d.El;
+  const int64_t total = (int64_t)sets * rows;
+  const WgradScratch wsc = carve_wgrad(d, total, sets * d.G_res, (char*)scratch);
+  const int kc = wgrad_kc(d, total);
+  const long long nc = wgrad_nc_ub(d, total, kc);
+  hipLaunchKernelGGL(wgrad_plan_kernel, dim3(1), dim3(1024), 0, s, wsc.plan, group_offsets,
+                     slot_expert, d.G_res, sets, (long long)rows, d.lo_slot, d.e_base, e_res,
+                     (long long)rows, kc, (int)nc);
+  WgradParams W;
+  W.Pm = (const uint16_t*)d_h;
+  W.Qm = (const uint16_t*)x_sorted;
+  W.C0 = dwg;
+  W.C1 = dwu;
+  W.part = wsc.part;
+  W.c_stride = (size_t)d.F * d.H;
+  W.I = 2 * d.F;
+  W.J = d.H;
+  W.i_split = d.F;
+  W.a_rows = (int)total;
+  W.plan = wsc.plan;
+  W.kc = kc;
+  W.slots = wgrad_slots(total, kc);
+  W.accumulate = accumulate;
+  W.ni_tiles = W.I / 128;
+  W.nj_tiles = W.J / 128;
+  WgradParams V = W;
+  V.Pm = (const uint16_t*)d_out;
+  V.Qm = (const uint16_t*)act;
+  V.C0 = V.C1 = dwd;
+  V.I = d.H;
+  V.J = d.F;
+  V.i_split = d.H;
+  V.ni_tiles = V.I / 128;
+  V.nj_tiles = V.J / 128;
+  for (const WgradParams* q : {&W, &V}) {
+    hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)(nc * q->ni_tiles * q->nj_tiles)),
+                       dim3(256), 0, s, *q);
+    // an expert is split only when it has more than kc rows
+    if (kc >= total) continue;
+    const long long ij4 = ((long long)q->I * q->J / 4 + 255) / 256;
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)ij4, (unsigned)e_res), dim3(256), 0, s,
+                       *q);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   const int e_res = d.S_res * d.El;
   const long long rows = a.max_rows;
@@ -1261,6 +1327,11 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   ws += a256((size_t)rows * d.F * el);
   void* d_a = ws;
   ws += a256((size_t)rows * d.F * el);
+  // a layer call that takes the weight gradients of all its passes at the
+  // end keeps each pass's group offsets, d_h and act rows in its own buffers
+  if (a.go_out != nullptr) go = a.go_out;
+  if (a.d_h_ext != nullptr) d_h = a.d_h_ext;
+  if (a.act_ext != nullptr) act = a.act_ext;
   long long lim = (long long)d.T * d.k;
   if (rows < lim) lim = rows;
   hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(1024), 0, s, d.G_res, (int)lim, a.pa,
@@ -1383,49 +1454,10 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(dgrad_kernel<false>, dim3(whole_rounds(mt_ub * O.n_ntiles, nb_o)),
                        dim3(256), 0, sx, O);
   }
-  // weight gradients: plan (rows and chunks per expert), then
-  // [dWg ; dWu] = [d_hg | d_hu]^T x_sorted and dWd = d_out^T act, each with
-  // the fixed-order sum of split experts' partials
-  const WgradScratch wsc = carve_wgrad(d, rows, ws);
-  const int kc = wgrad_kc(d, rows);
-  const long long nc = wgrad_nc_ub(d, rows, kc);
-  hipLaunchKernelGGL(wgrad_plan_kernel, dim3(1), dim3(1024), 0, s, wsc.plan, go,
-                     a.slot_expert, d.G_res, d.lo_slot, d.e_base, e_res, (long long)rows, kc,
-                     (int)nc);
-  WgradParams W;
-  W.Pm = (const uint16_t*)d_h;
-  W.Qm = (const uint16_t*)a.x_sorted;
-  W.C0 = a.dwg;
-  W.C1 = a.dwu;
-  W.part = wsc.part;
-  W.c_stride = (size_t)d.F * d.H;
-  W.I = 2 * d.F;
-  W.J = d.H;
-  W.i_split = d.F;
-  W.a_rows = (int)rows;
-  W.plan = wsc.plan;
-  W.kc = kc;
-  W.slots = wgrad_slots(rows, kc);
-  W.accumulate = a.accumulate;
-  W.ni_tiles = W.I / 128;
-  W.nj_tiles = W.J / 128;
-  WgradParams V = W;
-  V.Pm = (const uint16_t*)a.d_out;
-  V.Qm = (const uint16_t*)act;
-  V.C0 = V.C1 = a.dwd;
-  V.I = d.H;
-  V.J = d.F;
-  V.i_split = d.H;
-  V.ni_tiles = V.I / 128;
-  V.nj_tiles = V.J / 128;
-  for (const WgradParams* q : {&W, &V}) {
-    hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)(nc * q->ni_tiles * q->nj_tiles)),
-                       dim3(256), 0, s, *q);
-    // an expert is split only when it has more than kc rows
-    if (kc >= rows) continue;
-    const long long ij4 = ((long long)q->I * q->J / 4 + 255) / 256;
-    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)ij4, (unsigned)e_res), dim3(256), 0, s,
-                       *q);
+  if (a.wgrad) {
+    const hipError_t e = launch_wgrad(d, 1, go, rows, a.slot_expert, d_h, a.x_sorted, a.d_out,
+                                      act, a.dwg, a.dwu, a.dwd, a.accumulate, ws, s);
+    if (e != hipSuccess) return e;
   }
   if (ss != nullptr) {
     // join even after a failed launch: the caller's stream must not run

@@ -379,9 +379,26 @@ struct GemmBwdArgs {
   int64_t max_rows;
   void* scratch;
   void* out_recompute;  // bf16: if set, expert outputs from the recomputed activation
+  // bf16, a layer call taking every pass's weight gradients at the end: the
+  // pass's group offsets, d_h [rows, 2F] and act [rows, F] go to these
+  // buffers instead of the scratch, and wgrad = 0 skips the pass's weight
+  // gradients (launch_wgrad over all passes follows)
+  int* go_out = nullptr;
+  void* d_h_ext = nullptr;
+  void* act_ext = nullptr;
+  int wgrad = 1;
 };
 size_t gmm_bwd_scratch_bytes(const Dims& d, int64_t max_rows);
 hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s);
+// bf16 weight gradients over `sets` row sets of `rows` rows each (set s's
+// group offsets at group_offsets + s (G_res + 1), its rows at s * rows of
+// d_h [., 2F], x_sorted [., H], d_out [., H] and act [., F]); at most
+// kMaxSlots groups in all.  Scratch: wgrad_sets_scratch_bytes.
+size_t wgrad_sets_scratch_bytes(const Dims& d, int sets, int64_t rows_per_set);
+hipError_t launch_wgrad(const Dims& d, int sets, const int* group_offsets, int64_t rows,
+                        const int* slot_expert, const void* d_h, const void* x_sorted,
+                        const void* d_out, const void* act, float* dwg, float* dwu, float* dwd,
+                        int accumulate, void* scratch, hipStream_t s);
 // Combine / permute backward of a pass; row_of_assign advances by
 // roa_stride per row_of_assign set of the pass's layout (as launch_combine).
 // what: bit 0 the rows g * dy into d_out, bit 1 the gate gradients (reads out).
