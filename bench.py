@@ -565,7 +565,14 @@ def main():
         broof.update(traffic=None, arith_intensity=round(bai, 1),
                      kernel="grouped-GEMM backward call (d_a, gate/up recompute, dx_sorted, "
                             "weight gradients; accumulating)")
+        # the layer call's grouped-GEMM work (16 N H F; the expert outputs it
+        # also recomputes for the gate gradients are not counted) over the
+        # whole call's time: its weight gradients are taken once over every
+        # pass's rows, not accumulated pass by pass
+        lt = bf["flops"] / t_layer_bwd / 1e12
         bwd = {"layer_call_us": round(t_layer_bwd * 1e6, 2),
+               "layer_call_gemm_tflops": round(lt, 2),
+               "layer_call_frac_mfma_peak": round(lt / peak_mm, 4),
                "train_step_us": round((ms / 1e3 + t_layer_bwd) * 1e6, 2),
                "us_per_layer": round(bf["t_step"] * 1e6, 2),
                "tokens_s": round(w.tokens / bf["t_step"], 1),

@@ -849,6 +849,9 @@ struct LayerBwdWs {
   void* act_all;
   int* go_all;
   void* wgrad;
+  void* wguT;   // bf16: transposed weights for the data-gradient products
+  void* wdT;
+  void* plain;  // their tile maps
   size_t bytes;
 };
 
@@ -880,6 +883,13 @@ LayerBwdWs carve_layer_bwd(const Dims& d, const LayoutSet& ls, int64_t rows, int
     w.act_all = take(sets * rows * d.F * es);
     w.go_all = (int*)take(sets * (d.G_res + 1) * 4);
     w.wgrad = take(wgrad_sets_scratch_bytes(d, slots, rows));
+  }
+  w.wguT = w.wdT = w.plain = nullptr;
+  if (d.bf16) {
+    const size_t hf = (size_t)d.S_res * d.El * d.H * d.F * es;
+    w.wguT = take(2 * hf);
+    w.wdT = take(hf);
+    w.plain = take(gmm_bwd_plain_scratch_bytes(d));
   }
   w.bytes = off;
   return w;
@@ -964,6 +974,14 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
   const long long tk = (long long)d.T * d.k;
   const int es = d.bf16 ? 2 : 4;
   const int slots = layer_pass_slots(ls);
+  // bf16: the weights transposed once per call, so that the data-gradient
+  // products run on the forward's second-GEMM kernel
+  bool transposed = false;
+  if (d.bf16) {
+    e = launch_transpose_weights(d, w_gate, w_up, w_down, w.wguT, w.wdT, s);
+    if (e != hipSuccess && e != hipErrorNotSupported) return MOE_EHIP;
+    transposed = e == hipSuccess;
+  }
   for (int b = 0; b < slots; ++b) {
     PassArgs pa;
     if (ls.ovf != nullptr) {
@@ -1022,6 +1040,11 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
     a.max_rows = rows;
     a.scratch = w.gmm;
     a.out_recompute = d.bf16 ? f.out[0] : nullptr;
+    if (transposed) {
+      a.wguT = w.wguT;
+      a.wdT = w.wdT;
+    }
+    a.plain_scratch = w.plain;
     if (w.defer) {
       a.go_out = w.go_all + set * (d.G_res + 1);
       a.d_h_ext = (char*)w.d_h_all + set * rows * 2 * d.F * es;

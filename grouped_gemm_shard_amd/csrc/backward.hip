@@ -1210,6 +1210,8 @@ WgradScratch carve_wgrad(const Dims& d, int64_t max_rows, int groups, char* base
 
 }  // namespace
 
+size_t gmm_bwd_plain_scratch_bytes(const Dims& d) { return 3 * gmm_scratch_bytes(d); }
+
 size_t gmm_bwd_scratch_bytes(const Dims& d, int64_t max_rows) {
   const size_t el = d.bf16 ? 2 : 4;
   size_t b = 2 * a256((size_t)(d.G_res + 1) * 4) + 3 * a256((size_t)max_rows * d.F * el) +
@@ -1312,6 +1314,56 @@ hipError_t launch_wgrad(const Dims& d, int sets, const int* group_offsets, int64
   return hipGetLastError();
 }
 
+// dst[e][c][col0 + r] = src[e][r][c] for e_res bf16 matrices of R x C
+// (multiples of 64), dst rows ld elements apart: 64 x 64 tiles through LDS,
+// 16-byte loads and stores.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src,
+                                                             uint16_t* __restrict__ dst, int R,
+                                                             int C, size_t src_stride,
+                                                             size_t dst_stride, int ld,
+                                                             int col0) {
+  __shared__ uint16_t tile[64][72];
+  const int e = blockIdx.z, r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const uint16_t* sp = src + (size_t)e * src_stride;
+  uint16_t* dp = dst + (size_t)e * dst_stride;
+  const int t = threadIdx.x, lr = t >> 3, lc = (t & 7) * 8;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint4 v = *(const uint4*)(sp + (size_t)(r0 + lr + 32 * h) * C + c0 + lc);
+    const uint16_t* pv = (const uint16_t*)&v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[lr + 32 * h][lc + i] = pv[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int oc = lr + 32 * h;  // output row = source column c0 + oc
+    uint4 v;
+    uint16_t* pv = (uint16_t*)&v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pv[i] = tile[lc + i][oc];
+    *(uint4*)(dp + (size_t)(c0 + oc) * ld + col0 + r0 + lc) = v;
+  }
+}
+
+hipError_t launch_transpose_weights(const Dims& d, const void* wg, const void* wu,
+                                    const void* wd, void* wguT, void* wdT, hipStream_t s) {
+  const int e_res = d.S_res * d.El;
+  if (!d.bf16 || d.H % 64 != 0 || d.F % 64 != 0) return hipErrorNotSupported;
+  const size_t hf = (size_t)d.H * d.F;
+  // Wg, Wu [F, H] -> columns [0, F) and [F, 2F) of WguT [H, 2F]
+  const dim3 g1(d.H / 64, d.F / 64, e_res);
+  hipLaunchKernelGGL(transpose_bf16_kernel, g1, dim3(256), 0, s, (const uint16_t*)wg,
+                     (uint16_t*)wguT, d.F, d.H, hf, 2 * hf, 2 * d.F, 0);
+  hipLaunchKernelGGL(transpose_bf16_kernel, g1, dim3(256), 0, s, (const uint16_t*)wu,
+                     (uint16_t*)wguT, d.F, d.H, hf, 2 * hf, 2 * d.F, d.F);
+  // Wd [H, F] -> WdT [F, H]
+  const dim3 g2(d.F / 64, d.H / 64, e_res);
+  hipLaunchKernelGGL(transpose_bf16_kernel, g2, dim3(256), 0, s, (const uint16_t*)wd,
+                     (uint16_t*)wdT, d.H, d.F, hf, hf, d.H, 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   const int e_res = d.S_res * d.El;
   const long long rows = a.max_rows;
@@ -1393,8 +1445,19 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   P.Nout = d.F;
   P.n_ntiles = d.F / kBN;
   P.round_blocks = nb_km;
-  hipLaunchKernelGGL(dgrad_kmajor_kernel, dim3(whole_rounds(mt_ub * P.n_ntiles, nb_km)),
-                     dim3(256), 0, s, P);
+  // with the layer call's transposed weights, the data-gradient products run
+  // on the forward's second-GEMM kernel (each with its own tile map)
+  char* plain_ws = (char*)a.plain_scratch;
+  const size_t plain_step = gmm_scratch_bytes(d);
+  hipError_t pe = hipErrorNotSupported;
+  if (a.wdT != nullptr)
+    pe = launch_gmm_plain(d, go, a.slot_expert, a.d_out, rows, a.wdT, (size_t)d.F * d.H, d.H,
+                          d.F, d_a, rows, plain_ws, s);
+  if (pe == hipErrorNotSupported)
+    hipLaunchKernelGGL(dgrad_kmajor_kernel, dim3(whole_rounds(mt_ub * P.n_ntiles, nb_km)),
+                       dim3(256), 0, s, P);
+  else if (pe != hipSuccess)
+    return pe;
   // gate and up products recomputed; SwiGLU backward and the activation
   DgradParams Q = P;
   Q.A = (const uint16_t*)a.x_sorted;
@@ -1436,9 +1499,23 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     sx = ss->s;
   }
-  hipLaunchKernelGGL(dgrad_kmajor_kernel, dim3(whole_rounds(mt_ub * X.n_ntiles, nb_km)),
-                     dim3(256), 0, sx, X);
-  if (a.out_recompute != nullptr) {
+  // (a failed launch from here on is reported after the join)
+  hipError_t side_err = hipSuccess;
+  pe = hipErrorNotSupported;
+  if (a.wguT != nullptr)
+    pe = launch_gmm_plain(d, go, a.slot_expert, d_h, rows, a.wguT, (size_t)d.H * 2 * d.F,
+                          2 * d.F, d.H, a.dx_sorted, rows, plain_ws + plain_step, sx);
+  if (pe == hipErrorNotSupported)
+    hipLaunchKernelGGL(dgrad_kmajor_kernel, dim3(whole_rounds(mt_ub * X.n_ntiles, nb_km)),
+                       dim3(256), 0, sx, X);
+  else if (pe != hipSuccess)
+    side_err = pe;
+  pe = hipErrorNotSupported;
+  if (a.out_recompute != nullptr && plain_ws != nullptr)
+    pe = launch_gmm_plain(d, go, a.slot_expert, act, rows, a.wd, (size_t)d.H * d.F, d.F, d.H,
+                          a.out_recompute, rows, plain_ws + 2 * plain_step, sx);
+  if (pe != hipSuccess && pe != hipErrorNotSupported) side_err = pe;
+  if (a.out_recompute != nullptr && pe == hipErrorNotSupported) {
     // the expert outputs from the recomputed activation: act Wd^T (K = F,
     // Wd [H, F] K-contiguous)
     DgradParams O = P;
@@ -1454,11 +1531,9 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(dgrad_kernel<false>, dim3(whole_rounds(mt_ub * O.n_ntiles, nb_o)),
                        dim3(256), 0, sx, O);
   }
-  if (a.wgrad) {
-    const hipError_t e = launch_wgrad(d, 1, go, rows, a.slot_expert, d_h, a.x_sorted, a.d_out,
-                                      act, a.dwg, a.dwu, a.dwd, a.accumulate, ws, s);
-    if (e != hipSuccess) return e;
-  }
+  if (a.wgrad && side_err == hipSuccess)
+    side_err = launch_wgrad(d, 1, go, rows, a.slot_expert, d_h, a.x_sorted, a.d_out, act, a.dwg,
+                            a.dwu, a.dwd, a.accumulate, ws, s);
   if (ss != nullptr) {
     // join even after a failed launch: the caller's stream must not run
     // ahead of the side stream's work
@@ -1466,6 +1541,7 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
     if (e == hipSuccess) e = hipStreamWaitEvent(s, ss->join, 0);
     if (e != hipSuccess) return e;
   }
+  if (side_err != hipSuccess) return side_err;
   return hipGetLastError();
 }
 

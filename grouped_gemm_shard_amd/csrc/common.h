@@ -316,6 +316,13 @@ struct GemmPass {
                           // tile_off is null, else two launches
 };
 size_t gmm_scratch_bytes(const Dims& d);
+// bf16 C = A B^T over one pass's groups with the forward's second-GEMM
+// kernel: A [rows, K] in row order, B [e_res][N][K], C [rows, N]; scratch of
+// gmm_scratch_bytes(d) for the tile map.  hipErrorNotSupported for fp32 or
+// when K is not a multiple of the kernel's reduction step or N of 256.
+hipError_t launch_gmm_plain(const Dims& d, const int* group_offsets, const int* slot_expert,
+                            const void* A, int64_t a_rows, const void* B, size_t b_stride, int K,
+                            int N, void* C, int64_t max_rows, void* scratch, hipStream_t s);
 size_t gmm_sync_bytes(const Dims& d);
 int gmm_sync_ints(const Dims& d);  // ints of gmm_sync_bytes the kernel expects at zero
 
@@ -387,8 +394,21 @@ struct GemmBwdArgs {
   void* d_h_ext = nullptr;
   void* act_ext = nullptr;
   int wgrad = 1;
+  // bf16, optional: transposed weights (launch_transpose_weights) and the
+  // scratch of gmm_bwd_plain_scratch_bytes; d_a and dx_sorted then run on
+  // the forward's second-GEMM kernel, and the expert outputs too when only
+  // plain_scratch is given
+  const void* wdT = nullptr;   // [e_res][F][H]
+  const void* wguT = nullptr;  // [e_res][H][2F]: Wg^T | Wu^T
+  void* plain_scratch = nullptr;
 };
 size_t gmm_bwd_scratch_bytes(const Dims& d, int64_t max_rows);
+size_t gmm_bwd_plain_scratch_bytes(const Dims& d);
+// WguT[e] = [Wg[e]^T | Wu[e]^T] ([H, 2F]) and WdT[e] = Wd[e]^T ([F, H]) for
+// the resident experts (bf16; H and F multiples of 64, else
+// hipErrorNotSupported).
+hipError_t launch_transpose_weights(const Dims& d, const void* wg, const void* wu,
+                                    const void* wd, void* wguT, void* wdT, hipStream_t s);
 hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s);
 // bf16 weight gradients over `sets` row sets of `rows` rows each (set s's
 // group offsets at group_offsets + s (G_res + 1), its rows at s * rows of

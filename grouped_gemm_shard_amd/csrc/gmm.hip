@@ -1107,6 +1107,72 @@ size_t gmm_scratch_bytes(const Dims& d) {
          ((size_t)tile_map_len(d) * 4 + 255) / 256 * 256 + gmm_sync_bytes(d);
 }
 
+// C = A B^T over the groups of one pass with the second GEMM's kernel
+// (the layer backward's data-gradient products): A [rows, K] read in row
+// order, B [e_res][N][K] per resident expert, C [rows, N].  group_offsets
+// holds the pass's G_res + 1 offsets (malformed offsets give no tiles).
+template <int BM, int BK, int NST, int NW, int NWN>
+hipError_t launch_plain(const Dims& d, const int* group_offsets, const int* slot_expert,
+                        const void* A, int64_t a_rows, const void* B, size_t b_stride, int K,
+                        int N, void* C, int64_t max_rows, void* scratch, hipStream_t s) {
+  if (K % BK != 0 || N % 256 != 0 || K <= 0 || N <= 0) return hipErrorNotSupported;
+  int* toff = (int*)scratch;
+  int* tgroup = (int*)((char*)scratch + ((size_t)(d.G_res + 1) * 4 + 255) / 256 * 256);
+  long long lim = (long long)d.T * d.k;
+  if (max_rows < lim) lim = max_rows;
+  const PassArgs pa = static_pass_args(0, d.L, 0, 0, d.L);
+  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, d.G_res, BM, (int)lim,
+                     group_offsets, toff, tgroup, nullptr, 0, pa, nullptr);
+  GemmParams p;
+  p.A = (const uint16_t*)A;
+  p.a_index = nullptr;
+  p.a_index_stride = 0;
+  p.a_div = 1;
+  p.a_rows = (int)a_rows;
+  p.B0 = (const uint16_t*)B;
+  p.B1 = nullptr;
+  p.b_stride = b_stride;
+  p.C = (uint16_t*)C;
+  p.group_offsets = group_offsets;
+  p.tile_off = toff;
+  p.tile_group = tgroup;
+  p.go_stride = 0;
+  p.tg_stride = 0;
+  p.slot_expert = slot_expert;
+  p.G = d.G_res;
+  p.K = K;
+  p.Nout = N;
+  p.lo_slot = d.lo_slot;
+  p.e_base = d.e_base;
+  p.e_res = d.S_res * d.El;
+  p.max_rows = max_rows;
+  p.n_ntiles = N / 256;
+  p.pa = pa;
+  p.mt_cap = tile_map_len(d);
+  p.err = nullptr;
+  p.spin_limit = gemm_wait_limit();
+  p.part = 0;
+  p.parts = 1;
+  const long long mt_ub = (max_rows + BM - 1) / BM + d.G_res;
+  const int nb = round_blocks() * resident_blocks<BM, BK, NST, NW, NWN>();
+  p.round_blocks = nb;
+  const long long g = (mt_ub * p.n_ntiles + nb - 1) / nb * nb;
+  hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, false, NW, NWN>), dim3((unsigned)g),
+                     dim3(64 * NW), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gmm_plain(const Dims& d, const int* group_offsets, const int* slot_expert,
+                            const void* A, int64_t a_rows, const void* B, size_t b_stride, int K,
+                            int N, void* C, int64_t max_rows, void* scratch, hipStream_t s) {
+  if (!d.bf16) return hipErrorNotSupported;
+  if (d.gemm_bm == 256)
+    return launch_plain<MOE_GEMM_BIG>(d, group_offsets, slot_expert, A, a_rows, B, b_stride, K,
+                                      N, C, max_rows, scratch, s);
+  return launch_plain<MOE_GEMM_SMALL>(d, group_offsets, slot_expert, A, a_rows, B, b_stride, K, N,
+                                      C, max_rows, scratch, s);
+}
+
 hipError_t launch_gmm(const Dims& d, const PassArgs& pa, const GemmPass& gp,
                       const int* slot_expert, const void* wg, const void* wu, const void* wd,
                       void* act, void* out, int64_t max_rows, void* scratch, hipStream_t s) {
