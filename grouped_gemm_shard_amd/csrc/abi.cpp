@@ -851,7 +851,6 @@ struct LayerBwdWs {
   void* wgrad;
   void* wguT;   // bf16: transposed weights for the data-gradient products
   void* wdT;
-  void* plain;  // their tile maps
   size_t bytes;
 };
 
@@ -884,12 +883,11 @@ LayerBwdWs carve_layer_bwd(const Dims& d, const LayoutSet& ls, int64_t rows, int
     w.go_all = (int*)take(sets * (d.G_res + 1) * 4);
     w.wgrad = take(wgrad_sets_scratch_bytes(d, slots, rows));
   }
-  w.wguT = w.wdT = w.plain = nullptr;
+  w.wguT = w.wdT = nullptr;
   if (d.bf16) {
     const size_t hf = (size_t)d.S_res * d.El * d.H * d.F * es;
     w.wguT = take(2 * hf);
     w.wdT = take(hf);
-    w.plain = take(gmm_bwd_plain_scratch_bytes(d));
   }
   w.bytes = off;
   return w;
@@ -1044,7 +1042,6 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
       a.wguT = w.wguT;
       a.wdT = w.wdT;
     }
-    a.plain_scratch = w.plain;
     if (w.defer) {
       a.go_out = w.go_all + set * (d.G_res + 1);
       a.d_h_ext = (char*)w.d_h_all + set * rows * 2 * d.F * es;

@@ -1210,13 +1210,17 @@ WgradScratch carve_wgrad(const Dims& d, int64_t max_rows, int groups, char* base
 
 }  // namespace
 
-size_t gmm_bwd_plain_scratch_bytes(const Dims& d) { return 3 * gmm_scratch_bytes(d); }
+// bf16: the tile maps of the launches on the forward's GEMM kernel (d_a,
+// recompute, dx_sorted, expert outputs: one each, as two of them may run at
+// once on two streams)
+constexpr int kBwdPlainMaps = 4;
 
 size_t gmm_bwd_scratch_bytes(const Dims& d, int64_t max_rows) {
   const size_t el = d.bf16 ? 2 : 4;
   size_t b = 2 * a256((size_t)(d.G_res + 1) * 4) + 3 * a256((size_t)max_rows * d.F * el) +
              a256((size_t)max_rows * d.F * el);
-  if (d.bf16) b += carve_wgrad(d, max_rows, d.G_res, nullptr).bytes;
+  if (d.bf16)
+    b += kBwdPlainMaps * gmm_scratch_bytes(d) + carve_wgrad(d, max_rows, d.G_res, nullptr).bytes;
   return b;
 }
 
@@ -1379,6 +1383,12 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   ws += a256((size_t)rows * d.F * el);
   void* d_a = ws;
   ws += a256((size_t)rows * d.F * el);
+  char* plain_ws = nullptr;
+  const size_t plain_step = d.bf16 ? gmm_scratch_bytes(d) : 0;
+  if (d.bf16) {
+    plain_ws = ws;
+    ws += kBwdPlainMaps * plain_step;
+  }
   // a layer call that takes the weight gradients of all its passes at the
   // end keeps each pass's group offsets, d_h and act rows in its own buffers
   if (a.go_out != nullptr) go = a.go_out;
@@ -1447,8 +1457,6 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   P.round_blocks = nb_km;
   // with the layer call's transposed weights, the data-gradient products run
   // on the forward's second-GEMM kernel (each with its own tile map)
-  char* plain_ws = (char*)a.plain_scratch;
-  const size_t plain_step = gmm_scratch_bytes(d);
   hipError_t pe = hipErrorNotSupported;
   if (a.wdT != nullptr)
     pe = launch_gmm_plain(d, go, a.slot_expert, a.d_out, rows, a.wdT, (size_t)d.F * d.H, d.H,
@@ -1472,8 +1480,13 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   Q.d_h = (uint16_t*)d_h;
   Q.act = (uint16_t*)act;
   Q.round_blocks = nb_sw;
-  hipLaunchKernelGGL(dgrad_kernel<true>, dim3(whole_rounds(mt_ub * Q.n_ntiles, nb_sw)),
-                     dim3(256), 0, s, Q);
+  pe = launch_gmm_swiglu_recompute(d, go, a.slot_expert, a.x_sorted, rows, a.wg, a.wu, d_a, d_h,
+                                   act, rows, plain_ws + 3 * plain_step, s);
+  if (pe == hipErrorNotSupported)
+    hipLaunchKernelGGL(dgrad_kernel<true>, dim3(whole_rounds(mt_ub * Q.n_ntiles, nb_sw)),
+                       dim3(256), 0, s, Q);
+  else if (pe != hipSuccess)
+    return pe;
   // dx_sorted = [d_hg | d_hu] [Wg ; Wu]  (K = 2F; Wg and Wu [F, H] stacked
   // along the reduction and read reduction-major)
   DgradParams X = P;
@@ -1511,7 +1524,7 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   else if (pe != hipSuccess)
     side_err = pe;
   pe = hipErrorNotSupported;
-  if (a.out_recompute != nullptr && plain_ws != nullptr)
+  if (a.out_recompute != nullptr)
     pe = launch_gmm_plain(d, go, a.slot_expert, act, rows, a.wd, (size_t)d.H * d.F, d.F, d.H,
                           a.out_recompute, rows, plain_ws + 2 * plain_step, sx);
   if (pe != hipSuccess && pe != hipErrorNotSupported) side_err = pe;

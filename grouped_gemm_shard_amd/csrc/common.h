@@ -323,6 +323,14 @@ size_t gmm_scratch_bytes(const Dims& d);
 hipError_t launch_gmm_plain(const Dims& d, const int* group_offsets, const int* slot_expert,
                             const void* A, int64_t a_rows, const void* B, size_t b_stride, int K,
                             int N, void* C, int64_t max_rows, void* scratch, hipStream_t s);
+// bf16: the backward's gate/up recompute on the forward's first-GEMM kernel
+// with the SwiGLU backward in its epilogue: act and d_h = (d_hg | d_hu)
+// [rows, 2F] of x_sorted [rows, H] and d_a [rows, F]; scratch as above.
+hipError_t launch_gmm_swiglu_recompute(const Dims& d, const int* group_offsets,
+                                       const int* slot_expert, const void* x_sorted,
+                                       int64_t a_rows, const void* wg, const void* wu,
+                                       const void* d_a, void* d_h, void* act, int64_t max_rows,
+                                       void* scratch, hipStream_t s);
 size_t gmm_sync_bytes(const Dims& d);
 int gmm_sync_ints(const Dims& d);  // ints of gmm_sync_bytes the kernel expects at zero
 
@@ -394,16 +402,13 @@ struct GemmBwdArgs {
   void* d_h_ext = nullptr;
   void* act_ext = nullptr;
   int wgrad = 1;
-  // bf16, optional: transposed weights (launch_transpose_weights) and the
-  // scratch of gmm_bwd_plain_scratch_bytes; d_a and dx_sorted then run on
-  // the forward's second-GEMM kernel, and the expert outputs too when only
-  // plain_scratch is given
+  // bf16, optional: transposed weights (launch_transpose_weights); d_a and
+  // dx_sorted then run on the forward's second-GEMM kernel (the gate/up
+  // recompute and the expert outputs always do)
   const void* wdT = nullptr;   // [e_res][F][H]
   const void* wguT = nullptr;  // [e_res][H][2F]: Wg^T | Wu^T
-  void* plain_scratch = nullptr;
 };
 size_t gmm_bwd_scratch_bytes(const Dims& d, int64_t max_rows);
-size_t gmm_bwd_plain_scratch_bytes(const Dims& d);
 // WguT[e] = [Wg[e]^T | Wu[e]^T] ([H, 2F]) and WdT[e] = Wd[e]^T ([F, H]) for
 // the resident experts (bf16; H and F multiples of 64, else
 // hipErrorNotSupported).

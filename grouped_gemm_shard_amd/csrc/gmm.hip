@@ -106,7 +106,26 @@ struct GemmParams {
   PassArgs pa;
   int* err;                // MOE_ERR_* bits are OR-ed in here (may be null)
   int spin_limit;          // fused kernel: sleeps before a wait gives up (< 0: at once)
+  // GEMM1 as the backward's recompute (two-launch kernel only): with d_h
+  // set, the epilogue reads d_a [rows, Nout] and writes the SwiGLU backward,
+  // d_h [rows, 2 Nout] = (d_hg | d_hu), with the activation in C
+  const uint16_t* d_a = nullptr;
+  uint16_t* d_h = nullptr;
 };
+
+// The SwiGLU backward of one output element from the gate and up
+// pre-activations and d_a: act = SiLU(g) u, d_hg = d_a u SiLU'(g), d_hu =
+// d_a SiLU(g), SiLU'(g) = s (1 + g (1 - s)) with s the logistic of g (the
+// forward's SiLU, hardware reciprocal).
+__device__ __forceinline__ void swiglu_bwd_store(const GemmParams& P, size_t r, int c, float gv,
+                                                 float uv) {
+  const float da = bf2f(P.d_a[r * P.Nout + c]);
+  const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
+  const float silu = gv * sg;
+  P.C[r * P.Nout + c] = f2bf(silu * uv);
+  P.d_h[r * 2 * P.Nout + c] = f2bf(da * uv * (sg * (1.0f + gv * (1.0f - sg))));
+  P.d_h[r * 2 * P.Nout + P.Nout + c] = f2bf(da * silu);
+}
 
 // Reports an error bit found by the device (one report per block).
 __device__ __forceinline__ void report(int* err, int bit) {
@@ -343,6 +362,22 @@ __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const 
   const int live = __builtin_amdgcn_readfirstlane(min(MI, max(0, (rows - wm * WM + 31) / 32)));
   live_dispatch<MI>(live, kloop);
 
+  if (SWIGLU && !COH && P.d_h != nullptr) {
+    // the backward's recompute: element by element, no LDS
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int lr = wm * WM + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+        if (lr >= rows) continue;
+#pragma unroll
+        for (int ni = 0; ni < NI / 2; ++ni)
+          swiglu_bwd_store(P, (size_t)(row0 + lr), nt * 128 + wn * (128 / NWN) + ni * 32 + (lane & 31),
+                           acc[mi][ni][q], acc[mi][ni + NI / 2][q]);
+      }
+    __syncthreads();  // as after the LDS epilogue: every wave is done with the ring
+    return;
+  }
   // Epilogue through LDS: the ring is free once every wave has read its last
   // stage, so the tile is written there in bf16 and then stored as whole
   // 16-byte row chunks (instead of 2-byte stores scattered over rows).
@@ -578,6 +613,24 @@ __device__ __forceinline__ void gmm_tile_pp(const GemmParams& P, char* smem, con
   }
   if (grp == 0) pp_barrier();
 
+  if (SWIGLU && P.d_h != nullptr) {
+    // the backward's recompute: element by element, no LDS (16x16 layout:
+    // register q of a lane holds row (lane/16)*4 + q, column lane%16)
+    const int wr0 = grp * 128 + wml * 64;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int lr = wr0 + mi * 16 + (lane >> 4) * 4 + q;
+        if (lr >= rows) continue;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+          swiglu_bwd_store(P, (size_t)(row0 + lr), nt * 128 + wn * 64 + ni * 16 + (lane & 15),
+                           acc[mi][ni][q], acc[mi][ni + 4][q]);
+      }
+    __syncthreads();
+    return;
+  }
   // Epilogue through LDS (the ring is free: every wave passed the last
   // barrier after its last reads), then whole 16-byte row chunks.
   // 16x16 accumulator layout: register q of a lane holds row
@@ -1114,8 +1167,11 @@ size_t gmm_scratch_bytes(const Dims& d) {
 template <int BM, int BK, int NST, int NW, int NWN>
 hipError_t launch_plain(const Dims& d, const int* group_offsets, const int* slot_expert,
                         const void* A, int64_t a_rows, const void* B, size_t b_stride, int K,
-                        int N, void* C, int64_t max_rows, void* scratch, hipStream_t s) {
-  if (K % BK != 0 || N % 256 != 0 || K <= 0 || N <= 0) return hipErrorNotSupported;
+                        int N, void* C, int64_t max_rows, void* scratch, hipStream_t s,
+                        const void* B1 = nullptr, const void* d_a = nullptr,
+                        void* d_h = nullptr) {
+  const bool sw = d_h != nullptr;  // the SwiGLU-backward recompute (B, B1: gate, up)
+  if (K % BK != 0 || N % (sw ? 128 : 256) != 0 || K <= 0 || N <= 0) return hipErrorNotSupported;
   int* toff = (int*)scratch;
   int* tgroup = (int*)((char*)scratch + ((size_t)(d.G_res + 1) * 4 + 255) / 256 * 256);
   long long lim = (long long)d.T * d.k;
@@ -1130,9 +1186,11 @@ hipError_t launch_plain(const Dims& d, const int* group_offsets, const int* slot
   p.a_div = 1;
   p.a_rows = (int)a_rows;
   p.B0 = (const uint16_t*)B;
-  p.B1 = nullptr;
+  p.B1 = (const uint16_t*)B1;
   p.b_stride = b_stride;
   p.C = (uint16_t*)C;
+  p.d_a = (const uint16_t*)d_a;
+  p.d_h = (uint16_t*)d_h;
   p.group_offsets = group_offsets;
   p.tile_off = toff;
   p.tile_group = tgroup;
@@ -1146,7 +1204,7 @@ hipError_t launch_plain(const Dims& d, const int* group_offsets, const int* slot
   p.e_base = d.e_base;
   p.e_res = d.S_res * d.El;
   p.max_rows = max_rows;
-  p.n_ntiles = N / 256;
+  p.n_ntiles = N / (sw ? 128 : 256);
   p.pa = pa;
   p.mt_cap = tile_map_len(d);
   p.err = nullptr;
@@ -1157,9 +1215,27 @@ hipError_t launch_plain(const Dims& d, const int* group_offsets, const int* slot
   const int nb = round_blocks() * resident_blocks<BM, BK, NST, NW, NWN>();
   p.round_blocks = nb;
   const long long g = (mt_ub * p.n_ntiles + nb - 1) / nb * nb;
-  hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, false, NW, NWN>), dim3((unsigned)g),
-                     dim3(64 * NW), 0, s, p);
+  if (sw)
+    hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, true, NW, NWN>), dim3((unsigned)g),
+                       dim3(64 * NW), 0, s, p);
+  else
+    hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, false, NW, NWN>), dim3((unsigned)g),
+                       dim3(64 * NW), 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t launch_gmm_swiglu_recompute(const Dims& d, const int* group_offsets,
+                                       const int* slot_expert, const void* x_sorted,
+                                       int64_t a_rows, const void* wg, const void* wu,
+                                       const void* d_a, void* d_h, void* act, int64_t max_rows,
+                                       void* scratch, hipStream_t s) {
+  if (!d.bf16) return hipErrorNotSupported;
+  const size_t fh = (size_t)d.F * d.H;
+  if (d.gemm_bm == 256)
+    return launch_plain<MOE_GEMM_BIG>(d, group_offsets, slot_expert, x_sorted, a_rows, wg, fh,
+                                      d.H, d.F, act, max_rows, scratch, s, wu, d_a, d_h);
+  return launch_plain<MOE_GEMM_SMALL>(d, group_offsets, slot_expert, x_sorted, a_rows, wg, fh, d.H,
+                                      d.F, act, max_rows, scratch, s, wu, d_a, d_h);
 }
 
 hipError_t launch_gmm_plain(const Dims& d, const int* group_offsets, const int* slot_expert,
