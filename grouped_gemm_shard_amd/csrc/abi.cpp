@@ -825,6 +825,17 @@ namespace {
 // gradients are written once instead of read and written once per pass
 // (the pages' scan carries them from chunk to chunk; holding every chunk's
 // rows at once is what a GPU with this much memory can afford).
+// Whether a bf16 layer backward transposes the resident weights once per
+// call so that its data-gradient products run on the forward's GEMM kernel:
+// only where the weights are small (at most 2 GiB), since the copy reads and
+// writes all of them whatever rows the experts get (on the Llama4-Maverick
+// shard, 2 GB of weights for 32k rows, it pays; on 32 or 256 resident
+// experts of the DeepSeek-V3 shapes with a few thousand rows it does not).
+bool transpose_weights(const Dims& d) {
+  const int64_t wbytes = (int64_t)d.S_res * d.El * d.H * d.F * 2 * 3;
+  return d.bf16 && wbytes <= ((int64_t)2 << 30);
+}
+
 bool defer_wgrad(const Dims& d, int slots, int64_t rows) {
   if (!d.bf16 || slots < 2 || (int64_t)slots * d.G_res > kMaxSlots) return false;
   const int64_t wide = d.H > 2 * d.F ? d.H : 2 * d.F;
@@ -884,7 +895,7 @@ LayerBwdWs carve_layer_bwd(const Dims& d, const LayoutSet& ls, int64_t rows, int
     w.wgrad = take(wgrad_sets_scratch_bytes(d, slots, rows));
   }
   w.wguT = w.wdT = nullptr;
-  if (d.bf16) {
+  if (transpose_weights(d)) {
     const size_t hf = (size_t)d.S_res * d.El * d.H * d.F * es;
     w.wguT = take(2 * hf);
     w.wdT = take(hf);
@@ -975,7 +986,7 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
   // bf16: the weights transposed once per call, so that the data-gradient
   // products run on the forward's second-GEMM kernel
   bool transposed = false;
-  if (d.bf16) {
+  if (transpose_weights(d)) {
     e = launch_transpose_weights(d, w_gate, w_up, w_down, w.wguT, w.wdT, s);
     if (e != hipSuccess && e != hipErrorNotSupported) return MOE_EHIP;
     transposed = e == hipSuccess;
