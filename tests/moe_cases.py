@@ -99,6 +99,18 @@ def check_close_grad(got, ref, what=""):
     return rel, mean
 
 
+def check_close_grad_per_expert(got, ref, what=""):
+    """check_close_grad on each expert's slice (axis 0) at that slice's own
+    scale: under skewed routing a cold expert's weight gradient can be orders
+    of magnitude below the hottest expert's, and the whole tensor's scale
+    would let a wrong cold-expert slice (one left at zero, say) pass."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    for e in range(ref.shape[0]):
+        check_close_grad(got[e], ref[e], f"{what} expert {e}")
+
+
 class LazyExperts:
     """w[e] -> float64 host copy of one resident expert's matrix, fetched on
     demand so that full-size weights never sit on the host all at once."""

@@ -7,7 +7,8 @@ selects; weight gradients overwritten on the first pass and accumulated
 after), and compares dx, d_logits, d_gate and the three weight gradients
 with the float64 oracle's backward of the same layer (oracle.layer_bwd) on
 the same seeded inputs and upstream gradient, to the layer's tolerance taken
-relative to each gradient's scale (check_close_grad).
+relative to each gradient's scale (check_close_grad), and for the weight
+gradients also expert by expert at each expert's own scale.
 The pass choice is compared bit-exactly.
 
 Cases: the fp32 path; the benchmark's mid-sized layer at full size (its
@@ -23,7 +24,8 @@ import torch
 
 import oracle
 import workloads
-from moe_cases import MEDIUM, binding_problem, check_close_grad, host, oracle_problem, say
+from moe_cases import (MEDIUM, binding_problem, check_close_grad, check_close_grad_per_expert,
+                        host, oracle_problem, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -105,6 +107,8 @@ def compare(w, mode):
         assert np.all(np.isfinite(got[name])), name
         rel, mean = check_close_grad(got[name], ref[name], f"{w.name} {name}")
         say(f"  {name:9s} max-rel {rel:.2e} mean/max {mean:.2e}")
+        if name.startswith("dw_"):
+            check_close_grad_per_expert(got[name], ref[name], f"{w.name} {name}")
 
 
 # factor 0.5: every shard's distinct tokens exceed the cap, so LAYER runs
@@ -152,6 +156,8 @@ def compare_layer(w, mode):
         assert np.all(np.isfinite(got[name])), name
         rel, mean = check_close_grad(got[name], ref[name], f"{w.name} {name}")
         say(f"  {name:9s} max-rel {rel:.2e} mean/max {mean:.2e}")
+        if name.startswith("dw_"):
+            check_close_grad_per_expert(got[name], ref[name], f"{w.name} {name}")
     # no atomics anywhere: a second call gives the same bits
     again = run(inp["x"], inp["logits"], *inp["weights"], dy)
     torch.cuda.synchronize()

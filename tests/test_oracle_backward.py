@@ -262,3 +262,19 @@ def test_bf16_storage_stays_within_the_layer_tolerance():
         assert 0 < err < 2e-2, (name, err)
     # dx is stored in bf16
     np.testing.assert_array_equal(b["dx"], r(b["dx"]))
+
+
+def test_per_expert_tolerance_catches_a_zeroed_cold_expert():
+    """The weight-gradient check of the GPU tests, expert by expert: a cold
+    expert's slice 1e4 times below the hot one's, left at zero by a faulty
+    kernel, passes the whole-tensor bound but fails the per-expert one."""
+    import pytest
+    from moe_cases import check_close_grad, check_close_grad_per_expert
+    rng = np.random.default_rng(3)
+    ref = np.stack([rng.standard_normal((8, 8)), 1e-4 * rng.standard_normal((8, 8))])
+    got = ref.copy()
+    got[1] = 0.0
+    check_close_grad(got, ref)
+    with pytest.raises(AssertionError):
+        check_close_grad_per_expert(got, ref)
+    check_close_grad_per_expert(ref * (1 + 1e-4), ref)
