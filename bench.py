@@ -59,11 +59,11 @@ PEAK_HBM_GBS = 8000.0
 # is reported as null.
 GEMM_TRAFFIC = {
     "maverick_shard": {
-        "gmm_src_sha256": "a3ef9fdd0ed55c6134f80e5945d8fe2e7e92e0cc06b38d889691823a0cb7d162",
-        "bytes_per_layer": 31358998472},
+        "gmm_src_sha256": "26ecee9a76e49b4486f441e31af53503060077866554c9d17a942d864911dbee",
+        "bytes_per_layer": 31428590069},
     "mid_bf16": {
-        "gmm_src_sha256": "a3ef9fdd0ed55c6134f80e5945d8fe2e7e92e0cc06b38d889691823a0cb7d162",
-        "bytes_per_layer": 270736657},
+        "gmm_src_sha256": "26ecee9a76e49b4486f441e31af53503060077866554c9d17a942d864911dbee",
+        "bytes_per_layer": 264802973},
 }
 
 
@@ -476,6 +476,9 @@ def main():
                     help="skip timing the backward of the layer's passes")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run the calibration copy of 1 GiB (reference for HBM counters)")
+    ap.add_argument("--layer-backward-only", action="store_true",
+                    help="time only the whole-layer backward call (one untimed call, then "
+                         "--steps timed ones) and print its mean duration; for profiling")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs one expert-parallel shard per "
@@ -487,6 +490,13 @@ def main():
     torch.cuda.set_device(0)
     log(f"[bench] workload {w.name}: generating inputs")
     inp = workloads.make_inputs(w, device="cuda")
+    if args.layer_backward_only:
+        brun = g.LayerBackwardRunner(p, g.MODE_LAYER)
+        dy = workloads.make_dy(w, device="cuda")
+        t = time_calls(lambda: brun(inp["x"], inp["logits"], *inp["weights"], dy), args.steps)
+        print(json.dumps({"workload": w.name, "layer_backward_calls": args.steps,
+                          "layer_call_us": round(t * 1e6, 2)}), flush=True)
+        return
     run = g.LayerRunner(p, g.MODE_LAYER)
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):

@@ -825,17 +825,6 @@ namespace {
 // gradients are written once instead of read and written once per pass
 // (the pages' scan carries them from chunk to chunk; holding every chunk's
 // rows at once is what a GPU with this much memory can afford).
-// Whether a bf16 layer backward transposes the resident weights once per
-// call so that its data-gradient products run on the forward's GEMM kernel:
-// only where the weights are small (at most 2 GiB), since the copy reads and
-// writes all of them whatever rows the experts get (on the Llama4-Maverick
-// shard, 2 GB of weights for 32k rows, it pays; on 32 or 256 resident
-// experts of the DeepSeek-V3 shapes with a few thousand rows it does not).
-bool transpose_weights(const Dims& d) {
-  const int64_t wbytes = (int64_t)d.S_res * d.El * d.H * d.F * 2 * 3;
-  return d.bf16 && wbytes <= ((int64_t)2 << 30);
-}
-
 bool defer_wgrad(const Dims& d, int slots, int64_t rows) {
   if (!d.bf16 || slots < 2 || (int64_t)slots * d.G_res > kMaxSlots) return false;
   const int64_t wide = d.H > 2 * d.F ? d.H : 2 * d.F;
@@ -860,8 +849,6 @@ struct LayerBwdWs {
   void* act_all;
   int* go_all;
   void* wgrad;
-  void* wguT;   // bf16: transposed weights for the data-gradient products
-  void* wdT;
   size_t bytes;
 };
 
@@ -893,12 +880,6 @@ LayerBwdWs carve_layer_bwd(const Dims& d, const LayoutSet& ls, int64_t rows, int
     w.act_all = take(sets * rows * d.F * es);
     w.go_all = (int*)take(sets * (d.G_res + 1) * 4);
     w.wgrad = take(wgrad_sets_scratch_bytes(d, slots, rows));
-  }
-  w.wguT = w.wdT = nullptr;
-  if (transpose_weights(d)) {
-    const size_t hf = (size_t)d.S_res * d.El * d.H * d.F * es;
-    w.wguT = take(2 * hf);
-    w.wdT = take(hf);
   }
   w.bytes = off;
   return w;
@@ -983,14 +964,6 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
   const long long tk = (long long)d.T * d.k;
   const int es = d.bf16 ? 2 : 4;
   const int slots = layer_pass_slots(ls);
-  // bf16: the weights transposed once per call, so that the data-gradient
-  // products run on the forward's second-GEMM kernel
-  bool transposed = false;
-  if (transpose_weights(d)) {
-    e = launch_transpose_weights(d, w_gate, w_up, w_down, w.wguT, w.wdT, s);
-    if (e != hipSuccess && e != hipErrorNotSupported) return MOE_EHIP;
-    transposed = e == hipSuccess;
-  }
   for (int b = 0; b < slots; ++b) {
     PassArgs pa;
     if (ls.ovf != nullptr) {
@@ -1049,10 +1022,6 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
     a.max_rows = rows;
     a.scratch = w.gmm;
     a.out_recompute = d.bf16 ? f.out[0] : nullptr;
-    if (transposed) {
-      a.wguT = w.wguT;
-      a.wdT = w.wdT;
-    }
     if (w.defer) {
       a.go_out = w.go_all + set * (d.G_res + 1);
       a.d_h_ext = (char*)w.d_h_all + set * rows * 2 * d.F * es;

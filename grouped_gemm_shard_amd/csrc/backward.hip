@@ -21,7 +21,11 @@
 //    and Wg/Wu in the d_a and dx GEMMs, both operands of the weight
 //    gradients), its rows are staged in LDS as they are and the MFMA
 //    fragments are read with gfx950's LDS transpose read, so no transposed
-//    copy is ever made;
+//    copy is ever made.  With 256-row tiles (H >= 2048) d_a, dx_sorted, the
+//    gate/up recompute and the layer call's expert outputs run on the
+//    forward's grouped-GEMM kernel (gmm.hip: its reduction-major-B mode for
+//    d_a and dx, the SwiGLU backward in its first GEMM's epilogue for the
+//    recompute); the kernels here cover the other shapes;
 //  * permute backward: dx_t = the sum of dx_sorted over the token's rows,
 //    one wave per token;
 //  * gate backward into the logits, one wave per token.
@@ -1318,56 +1322,6 @@ hipError_t launch_wgrad(const Dims& d, int sets, const int* group_offsets, int64
   return hipGetLastError();
 }
 
-// dst[e][c][col0 + r] = src[e][r][c] for e_res bf16 matrices of R x C
-// (multiples of 64), dst rows ld elements apart: 64 x 64 tiles through LDS,
-// 16-byte loads and stores.
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src,
-                                                             uint16_t* __restrict__ dst, int R,
-                                                             int C, size_t src_stride,
-                                                             size_t dst_stride, int ld,
-                                                             int col0) {
-  __shared__ uint16_t tile[64][72];
-  const int e = blockIdx.z, r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const uint16_t* sp = src + (size_t)e * src_stride;
-  uint16_t* dp = dst + (size_t)e * dst_stride;
-  const int t = threadIdx.x, lr = t >> 3, lc = (t & 7) * 8;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint4 v = *(const uint4*)(sp + (size_t)(r0 + lr + 32 * h) * C + c0 + lc);
-    const uint16_t* pv = (const uint16_t*)&v;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tile[lr + 32 * h][lc + i] = pv[i];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int oc = lr + 32 * h;  // output row = source column c0 + oc
-    uint4 v;
-    uint16_t* pv = (uint16_t*)&v;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pv[i] = tile[lc + i][oc];
-    *(uint4*)(dp + (size_t)(c0 + oc) * ld + col0 + r0 + lc) = v;
-  }
-}
-
-hipError_t launch_transpose_weights(const Dims& d, const void* wg, const void* wu,
-                                    const void* wd, void* wguT, void* wdT, hipStream_t s) {
-  const int e_res = d.S_res * d.El;
-  if (!d.bf16 || d.H % 64 != 0 || d.F % 64 != 0) return hipErrorNotSupported;
-  const size_t hf = (size_t)d.H * d.F;
-  // Wg, Wu [F, H] -> columns [0, F) and [F, 2F) of WguT [H, 2F]
-  const dim3 g1(d.H / 64, d.F / 64, e_res);
-  hipLaunchKernelGGL(transpose_bf16_kernel, g1, dim3(256), 0, s, (const uint16_t*)wg,
-                     (uint16_t*)wguT, d.F, d.H, hf, 2 * hf, 2 * d.F, 0);
-  hipLaunchKernelGGL(transpose_bf16_kernel, g1, dim3(256), 0, s, (const uint16_t*)wu,
-                     (uint16_t*)wguT, d.F, d.H, hf, 2 * hf, 2 * d.F, d.F);
-  // Wd [H, F] -> WdT [F, H]
-  const dim3 g2(d.F / 64, d.H / 64, e_res);
-  hipLaunchKernelGGL(transpose_bf16_kernel, g2, dim3(256), 0, s, (const uint16_t*)wd,
-                     (uint16_t*)wdT, d.H, d.F, hf, hf, d.H, 0);
-  return hipGetLastError();
-}
-
 hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   const int e_res = d.S_res * d.El;
   const long long rows = a.max_rows;
@@ -1455,12 +1409,11 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   P.Nout = d.F;
   P.n_ntiles = d.F / kBN;
   P.round_blocks = nb_km;
-  // with the layer call's transposed weights, the data-gradient products run
-  // on the forward's second-GEMM kernel (each with its own tile map)
-  hipError_t pe = hipErrorNotSupported;
-  if (a.wdT != nullptr)
-    pe = launch_gmm_plain(d, go, a.slot_expert, a.d_out, rows, a.wdT, (size_t)d.F * d.H, d.H,
-                          d.F, d_a, rows, plain_ws, s);
+  // with 256-row tiles the data-gradient products run on the forward's
+  // kernel reading the weights as stored, reduction-major (each launch with
+  // its own tile map); d_a = d_out Wd
+  hipError_t pe = launch_gmm_plain_kmajor(d, go, a.slot_expert, a.d_out, rows, a.wd, a.wd, d.H,
+                                          (size_t)d.H * d.F, d.H, d.F, d_a, rows, plain_ws, s);
   if (pe == hipErrorNotSupported)
     hipLaunchKernelGGL(dgrad_kmajor_kernel, dim3(whole_rounds(mt_ub * P.n_ntiles, nb_km)),
                        dim3(256), 0, s, P);
@@ -1514,10 +1467,11 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   }
   // (a failed launch from here on is reported after the join)
   hipError_t side_err = hipSuccess;
-  pe = hipErrorNotSupported;
-  if (a.wguT != nullptr)
-    pe = launch_gmm_plain(d, go, a.slot_expert, d_h, rows, a.wguT, (size_t)d.H * 2 * d.F,
-                          2 * d.F, d.H, a.dx_sorted, rows, plain_ws + plain_step, sx);
+  // dx_sorted = d_hg Wg + d_hu Wu: Wg then Wu [F, H] as stored are the
+  // reduction's first and second F rows
+  pe = launch_gmm_plain_kmajor(d, go, a.slot_expert, d_h, rows, a.wg, a.wu, d.F,
+                               (size_t)d.F * d.H, 2 * d.F, d.H, a.dx_sorted, rows,
+                               plain_ws + plain_step, sx);
   if (pe == hipErrorNotSupported)
     hipLaunchKernelGGL(dgrad_kmajor_kernel, dim3(whole_rounds(mt_ub * X.n_ntiles, nb_km)),
                        dim3(256), 0, sx, X);

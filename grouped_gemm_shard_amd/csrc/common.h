@@ -323,6 +323,15 @@ size_t gmm_scratch_bytes(const Dims& d);
 hipError_t launch_gmm_plain(const Dims& d, const int* group_offsets, const int* slot_expert,
                             const void* A, int64_t a_rows, const void* B, size_t b_stride, int K,
                             int N, void* C, int64_t max_rows, void* scratch, hipStream_t s);
+// bf16 with 256-row tiles: C = A B over one pass's groups on the forward's
+// 256-row kernel with B stored reduction-major: rows [0, k_split) of the
+// reduction from B0 [e_res][k_split][N] (experts b_stride apart), the rest
+// from B1 [e_res][K - k_split][N]; hipErrorNotSupported otherwise.
+hipError_t launch_gmm_plain_kmajor(const Dims& d, const int* group_offsets,
+                                   const int* slot_expert, const void* A, int64_t a_rows,
+                                   const void* B0, const void* B1, int k_split, size_t b_stride,
+                                   int K, int N, void* C, int64_t max_rows, void* scratch,
+                                   hipStream_t s);
 // bf16: the backward's gate/up recompute on the forward's first-GEMM kernel
 // with the SwiGLU backward in its epilogue: act and d_h = (d_hg | d_hu)
 // [rows, 2F] of x_sorted [rows, H] and d_a [rows, F]; scratch as above.
@@ -402,18 +411,8 @@ struct GemmBwdArgs {
   void* d_h_ext = nullptr;
   void* act_ext = nullptr;
   int wgrad = 1;
-  // bf16, optional: transposed weights (launch_transpose_weights); d_a and
-  // dx_sorted then run on the forward's second-GEMM kernel (the gate/up
-  // recompute and the expert outputs always do)
-  const void* wdT = nullptr;   // [e_res][F][H]
-  const void* wguT = nullptr;  // [e_res][H][2F]: Wg^T | Wu^T
 };
 size_t gmm_bwd_scratch_bytes(const Dims& d, int64_t max_rows);
-// WguT[e] = [Wg[e]^T | Wu[e]^T] ([H, 2F]) and WdT[e] = Wd[e]^T ([F, H]) for
-// the resident experts (bf16; H and F multiples of 64, else
-// hipErrorNotSupported).
-hipError_t launch_transpose_weights(const Dims& d, const void* wg, const void* wu,
-                                    const void* wd, void* wguT, void* wdT, hipStream_t s);
 hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s);
 // bf16 weight gradients over `sets` row sets of `rows` rows each (set s's
 // group offsets at group_offsets + s (G_res + 1), its rows at s * rows of

@@ -111,6 +111,9 @@ struct GemmParams {
   // d_h [rows, 2 Nout] = (d_hg | d_hu), with the activation in C
   const uint16_t* d_a = nullptr;
   uint16_t* d_h = nullptr;
+  // reduction-major B (the 256-row loop's BKM mode): B0 [e_res][k_split][Nout]
+  // holds rows k < k_split, B1 [e_res][K - k_split][Nout] the rest
+  int k_split = 0;
 };
 
 // The SwiGLU backward of one output element from the gate and up
@@ -175,6 +178,38 @@ __device__ __forceinline__ void pp_barrier() {
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 as inline asm (the builtin would make the compiler
+// wait for the ring's in-flight LDS-direct loads first): within each
+// 16-lane group, output lane 4a+b receives element b of the 8-byte runs
+// that lanes a, a+4, a+8 and a+12 address.  Pending until tie_wait.
+template <int OFF>
+__device__ __forceinline__ void lds_read_tr(v4i16& r, unsigned addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+}
+
+// Waits for every LDS read of the wave; the 16 registers are tied to the
+// wait so that no use of them is placed before it.
+__device__ __forceinline__ void tie_wait(v4i16 (&r)[16]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]),
+                 "+v"(r[6]), "+v"(r[7]), "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]),
+                 "+v"(r[12]), "+v"(r[13]), "+v"(r[14]), "+v"(r[15]));
+}
+
+__device__ __forceinline__ bf16x8 join_halves(const v4i16& lo, const v4i16& hi) {
+  bf16x8 v;
+  __builtin_memcpy(&v, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&v) + 8, &hi, 8);
+  return v;
+}
+
+// 16-byte chunk permutation of a 256-byte LDS row of a reduction-major B
+// quarter: the transpose reads of 4 consecutive rows at one column land on
+// disjoint 64-byte bank windows.
+__device__ __forceinline__ int kswz(int row) { return (row & 3) << 2; }
 
 // Starts the loads of K step `step` into its ring stage: each wave-wide
 // load fills RPI consecutive rows (1 KB) of the stage.
@@ -468,9 +503,14 @@ __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const 
 // epilogue pairs them in registers.  GEMM2's wave takes 128 output columns
 // from one B quarter.  A rows past the group read as zero; a wave whose 64
 // rows are all past the group skips its reads and MFMAs.
-template <bool SWIGLU>
+// BKM: B is stored reduction-major ([e][K][Nout], the backward's weights as
+// they are), plain GEMM only.  A B quarter then holds 64 reduction rows of
+// the quarter's 128 output columns (256 bytes each, chunks permuted by
+// kswz), and the B fragments come from two transpose reads each.
+template <bool SWIGLU, bool BKM = false>
 __device__ __forceinline__ void gmm_tile_pp(const GemmParams& P, char* smem, const int* aidx,
                                             int row0, int rows, int nt, int e) {
+  static_assert(!(SWIGLU && BKM), "reduction-major B for the plain GEMM only");
   constexpr int BK = 64, RB = BK * 2, CPR = BK / 8, RPI = 1024 / RB;  // 8 rows per load
   constexpr int QS = 128 * RB;       // bytes per quarter
   constexpr int LQ = 128 / RPI / 4;  // loads per wave per quarter (4)
@@ -484,7 +524,9 @@ __device__ __forceinline__ void gmm_tile_pp(const GemmParams& P, char* smem, con
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(P.A, (unsigned)P.a_rows * K * 2);
   __amdgpu_buffer_rsrc_t rb0, rb1;
-  if (SWIGLU) {
+  if (BKM) {
+    rb0 = rb1 = make_rsrc(P.B0, 0);  // per quarter in issue_bk
+  } else if (SWIGLU) {
     rb0 = make_rsrc(P.B0 + (size_t)e * P.b_stride + (size_t)nt * 128 * K, 128u * K * 2);
     rb1 = make_rsrc(P.B1 + (size_t)e * P.b_stride + (size_t)nt * 128 * K, 128u * K * 2);
   } else {
@@ -527,6 +569,38 @@ __device__ __forceinline__ void gmm_tile_pp(const GemmParams& P, char* smem, con
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + (i * 4 + wig) * RPI * RB), 16,
                                                b_off0 + i * b_step, kb, 0, 0);
   };
+  // BKM: load i of wave wig fills quarter rows 4 (4i + wig) + lane/16, 16
+  // chunks of 16 bytes each; the quarter's rows are reduction rows 64 s ..
+  // 64 s + 63 of step s, from B0 below k_split and B1 above
+  int bk_off[LQ];
+#pragma unroll
+  for (int i = 0; i < LQ; ++i) {
+    const int r = (i * 4 + wig) * 4 + (lane >> 4);
+    bk_off[i] = r * P.Nout * 2 + (((lane & 15) ^ kswz(r)) << 4);
+  }
+  auto issue_bk = [&](int q, int half) {
+    if (q >= NQ) return;
+    char* st = smem + (q % 10) * QS;
+    const int k0 = (q >> 2) * BK;
+    const bool lo = k0 < P.k_split;
+    // B0's experts are b_stride apart; B1's (K - k_split) x Nout
+    const uint16_t* base = (lo ? P.B0 + (size_t)e * P.b_stride
+                               : P.B1 + (size_t)e * (size_t)(K - P.k_split) * P.Nout) +
+                           (size_t)nt * 256 + half * 128;
+    const int kr = lo ? k0 : k0 - P.k_split;
+    const int krows = lo ? P.k_split : K - P.k_split;
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(base, (unsigned)((krows - 1) * P.Nout * 2 + 256));
+#pragma unroll
+    for (int i = 0; i < LQ; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + (i * 4 + wig) * 1024), 16,
+                                               bk_off[i], kr * P.Nout * 2, 0, 0);
+  };
+  // BKM fragment reads: lane j of 16-lane group g addresses row 8g + j/4
+  // (+4 for the second read) and columns 4 (j%4) .. of the 16-column tile
+  const int tj = lane & 15;
+  const unsigned tk_base = (8 * (lane >> 4) + (tj >> 2)) * 256 + (tj & 1) * 8 + (((tj & 3) >> 1) << 4);
+  const int tk_sw = (tj >> 2) << 2;  // kswz of the lane's rows
   // fragment rows within their quarters (16x16x32: lane reads row lane%16)
   int ar[MI], br[NI];
 #pragma unroll
@@ -547,14 +621,21 @@ __device__ __forceinline__ void gmm_tile_pp(const GemmParams& P, char* smem, con
   // prologue: steps 0 and 1; group 0 its A quarters and B rows 0-127,
   // group 1 its A quarters and B rows 128-255
   if (grp == 0) {
-    issue_a(0); issue_b(2, rb0); issue_a(4); issue_b(6, rb0);
+    issue_a(0);
+    if (BKM) issue_bk(2, 0); else issue_b(2, rb0);
+    issue_a(4);
+    if (BKM) issue_bk(6, 0); else issue_b(6, rb0);
   } else {
-    issue_a(1); issue_b(3, rb1); issue_a(5); issue_b(7, rb1);
+    issue_a(1);
+    if (BKM) issue_bk(3, 1); else issue_b(3, rb1);
+    issue_a(5);
+    if (BKM) issue_bk(7, 1); else issue_b(7, rb1);
   }
   vm_wait<0>();
   pp_barrier();
   if (grp == 1) pp_barrier();
-  bf16x8 a[2][MI], b[2][NI];
+  bf16x8 a[2][MI], b[2][BKM ? 1 : NI];
+  v4i16 bt[2][BKM ? NI : 1][2];  // BKM: the two 4-row halves of each B fragment
   for (int kt = 0; kt < KT; ++kt) {
     const char* sa = smem + ((4 * kt + grp) % 10) * QS;
     const char* sb0 = smem + ((4 * kt + 2) % 10) * QS;
@@ -565,11 +646,13 @@ __device__ __forceinline__ void gmm_tile_pp(const GemmParams& P, char* smem, con
     // B rows 0-127 of step kt+2), then the step's fragments
     const int q0 = 4 * kt + 7 + 2 * grp, q1 = q0 + 1;
     if (grp == 0) {
-      if (q0 >= NQ_PRO) issue_b(q0, rb1);
+      if (q0 >= NQ_PRO) {
+        if (BKM) issue_bk(q0, 1); else issue_b(q0, rb1);
+      }
       issue_a(q1);
     } else {
       issue_a(q0);
-      issue_b(q1, rb0);
+      if (BKM) issue_bk(q1, 0); else issue_b(q1, rb0);
     }
     if (live) {
 #pragma unroll
@@ -578,10 +661,34 @@ __device__ __forceinline__ void gmm_tile_pp(const GemmParams& P, char* smem, con
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
           a[ks][mi] = *(const bf16x8*)(sa + ar[mi] * RB + ((kc ^ swz<BK>(ar[mi])) << 4));
+        if constexpr (!BKM) {
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const char* sb = SWIGLU ? (ni < 4 ? sb0 : sb1) : sbw;
-          b[ks][ni] = *(const bf16x8*)(sb + br[ni] * RB + ((kc ^ swz<BK>(br[ni])) << 4));
+          for (int ni = 0; ni < NI; ++ni) {
+            const char* sb = SWIGLU ? (ni < 4 ? sb0 : sb1) : sbw;
+            b[ks][ni] = *(const bf16x8*)(sb + br[ni] * RB + ((kc ^ swz<BK>(br[ni])) << 4));
+          }
+        }
+      }
+      if constexpr (BKM) {
+        // rows 32 ks + 8g .. +7 of column 16 ni + lane%16: two transpose
+        // reads of 4 rows each, per slice and n-tile
+        const unsigned sbw_a =
+            (unsigned)(size_t)(const __attribute__((address_space(3))) char*)sbw + tk_base;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            // chunk 2 ni + (j%4)/2 of the lane's rows, permuted by kswz
+            const unsigned ad = sbw_a + ((((2 * ni) ^ tk_sw)) << 4);
+            if (ks == 0) {
+              lds_read_tr<0>(bt[ks][ni][0], ad);
+              lds_read_tr<1024>(bt[ks][ni][1], ad);
+            } else {
+              lds_read_tr<8192>(bt[ks][ni][0], ad);
+              lds_read_tr<9216>(bt[ks][ni][1], ad);
+            }
+          }
+          tie_wait(*reinterpret_cast<v4i16(*)[16]>(&bt[ks][0][0]));
         }
       }
     }
@@ -600,9 +707,12 @@ __device__ __forceinline__ void gmm_tile_pp(const GemmParams& P, char* smem, con
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][mi], b[ks][ni], acc[mi][ni], 0, 0, 0);
+          for (int ni = 0; ni < NI; ++ni) {
+            bf16x8 bv;
+            if constexpr (BKM) bv = join_halves(bt[ks][ni][0], bt[ks][ni][1]);
+            else bv = b[ks][ni];
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][mi], bv, acc[mi][ni], 0, 0, 0);
+          }
     }
     if (grp == 0) {
       // quarters up to 4kt+7 landed; its newest (4kt+8) may stay in flight
@@ -672,11 +782,13 @@ __device__ __forceinline__ void gmm_tile_pp(const GemmParams& P, char* smem, con
   }
 }
 
-template <int BM, int BK, int NST, bool SWIGLU, int NW, int NWN>
+template <int BM, int BK, int NST, bool SWIGLU, int NW, int NWN, bool BKM = false>
 __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   // one ring for either tile shape the kernel may run; 256-row tiles run
-  // the two-group loop over its 160 KB ring of quarters
-  constexpr bool HAS_REM = BM > kRemBM;
+  // the two-group loop over its 160 KB ring of quarters (with reduction-major
+  // B every tile does, short ones too)
+  static_assert(!BKM || BM == 256, "reduction-major B in the 256-row loop only");
+  constexpr bool HAS_REM = BM > kRemBM && !BKM;
   constexpr int RING = BM == 256 ? kPpRing : NST * (BM + BNB) * BK * 2;
   static_assert(BM != 256 || NW == 8, "the 256-row loop runs 8 waves");
   static_assert(!HAS_REM || shape_waves(MOE_GEMM_REM) == NW, "REM runs in the same block");
@@ -734,7 +846,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   if (HAS_REM && rows <= kRemBM)
     gmm_tile<MOE_GEMM_REM, SWIGLU>(P, smem, aidx, row0, rows, nt, e);
   else if constexpr (BM == 256)
-    gmm_tile_pp<SWIGLU>(P, smem, aidx, row0, rows, nt, e);
+    gmm_tile_pp<SWIGLU, BKM>(P, smem, aidx, row0, rows, nt, e);
   else
     gmm_tile<BM, BK, NST, NW, NWN, SWIGLU>(P, smem, aidx, row0, rows, nt, e);
 }
@@ -1169,9 +1281,12 @@ hipError_t launch_plain(const Dims& d, const int* group_offsets, const int* slot
                         const void* A, int64_t a_rows, const void* B, size_t b_stride, int K,
                         int N, void* C, int64_t max_rows, void* scratch, hipStream_t s,
                         const void* B1 = nullptr, const void* d_a = nullptr,
-                        void* d_h = nullptr) {
+                        void* d_h = nullptr, int k_split = 0) {
   const bool sw = d_h != nullptr;  // the SwiGLU-backward recompute (B, B1: gate, up)
+  // k_split > 0: B reduction-major, rows [0, k_split) from B, the rest from B1
+  const bool bkm = k_split > 0;
   if (K % BK != 0 || N % (sw ? 128 : 256) != 0 || K <= 0 || N <= 0) return hipErrorNotSupported;
+  if (bkm && (BM != 256 || sw || k_split % BK != 0 || k_split > K)) return hipErrorNotSupported;
   int* toff = (int*)scratch;
   int* tgroup = (int*)((char*)scratch + ((size_t)(d.G_res + 1) * 4 + 255) / 256 * 256);
   long long lim = (long long)d.T * d.k;
@@ -1191,6 +1306,7 @@ hipError_t launch_plain(const Dims& d, const int* group_offsets, const int* slot
   p.C = (uint16_t*)C;
   p.d_a = (const uint16_t*)d_a;
   p.d_h = (uint16_t*)d_h;
+  p.k_split = k_split;
   p.group_offsets = group_offsets;
   p.tile_off = toff;
   p.tile_group = tgroup;
@@ -1218,10 +1334,27 @@ hipError_t launch_plain(const Dims& d, const int* group_offsets, const int* slot
   if (sw)
     hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, true, NW, NWN>), dim3((unsigned)g),
                        dim3(64 * NW), 0, s, p);
-  else
+  else if constexpr (BM == 256) {
+    if (bkm)
+      hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, false, NW, NWN, true>), dim3((unsigned)g),
+                         dim3(64 * NW), 0, s, p);
+    else
+      hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, false, NW, NWN>), dim3((unsigned)g),
+                         dim3(64 * NW), 0, s, p);
+  } else
     hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, false, NW, NWN>), dim3((unsigned)g),
                        dim3(64 * NW), 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t launch_gmm_plain_kmajor(const Dims& d, const int* group_offsets,
+                                   const int* slot_expert, const void* A, int64_t a_rows,
+                                   const void* B0, const void* B1, int k_split, size_t b_stride,
+                                   int K, int N, void* C, int64_t max_rows, void* scratch,
+                                   hipStream_t s) {
+  if (!d.bf16 || d.gemm_bm != 256) return hipErrorNotSupported;
+  return launch_plain<MOE_GEMM_BIG>(d, group_offsets, slot_expert, A, a_rows, B0, b_stride, K, N,
+                                    C, max_rows, scratch, s, B1, nullptr, nullptr, k_split);
 }
 
 hipError_t launch_gmm_swiglu_recompute(const Dims& d, const int* group_offsets,

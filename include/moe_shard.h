@@ -393,15 +393,13 @@ int moe_layer_bwd_workspace_bytes(const moe_problem* p, int32_t mode, size_t* by
  * slots (and every operand offset within 31 bits) the weight gradients are
  * not carried from pass to pass: each pass keeps its rows in the workspace
  * and the gradients of all passes are one reduction after the last pass,
- * written once (the same sum in another order).  Where the resident bf16
- * weights take at most 2 GiB they are also transposed into the workspace
- * once per call for the data-gradient products.  Outputs:
+ * written once (the same sum in another order).  Outputs:
  *   dx [T,H] (activation dtype; 0 for a token with no resident row),
  *   d_logits [T,E] float32 (only chosen logits are nonzero),
  *   dw_gate, dw_up [E_res,F,H], dw_down [E_res,H,F] float32, overwritten
  *   (the sum over every pass).
  * Pointers 16-byte aligned; ws holds moe_layer_bwd_workspace_bytes(p, mode)
- * (which includes those per-pass rows and transposed weights). */
+ * (which includes those per-pass rows). */
 int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float* logits,
                   const void* w_gate, const void* w_up, const void* w_down, const void* dy,
                   void* dx, float* d_logits, float* dw_gate, float* dw_up, float* dw_down,
