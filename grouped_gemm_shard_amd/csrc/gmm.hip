@@ -52,7 +52,15 @@ namespace {
 
 constexpr int BNB = 256;  // weight rows per tile
 typedef int v4i __attribute__((ext_vector_type(4)));
-constexpr int GM = 8;     // m-tiles per band of the tile order
+#ifndef MOE_GEMM_GM
+#define MOE_GEMM_GM 8
+#endif
+constexpr int GM = MOE_GEMM_GM;  // m-tiles per band of the tile order
+// Bands of the tile order aligned to groups (1) or cut through the whole
+// run of m-tiles (0).
+#ifndef MOE_GEMM_GBAND
+#define MOE_GEMM_GBAND 1
+#endif
 
 // Tile shapes <BM, BK, stages, waves, waves along N>: BIG for long
 // reductions, SMALL for the rest, and REM, the 128-row shape a BIG kernel
@@ -822,6 +830,27 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   const int x = bid & 7, slot = (bid - rbase) >> 3;
   const int L = rbase + (x * rs >> 3) + slot;
   if (L >= rbase + ((x + 1) * rs >> 3)) return;
+#if MOE_GEMM_GBAND
+  // The part's tiles go group by group, each group's m-tiles in bands of up
+  // to GM, n-tile by n-tile: the tiles an XCD runs together are a few
+  // m-tiles of one expert by many n-tiles (or of the next expert), so an
+  // expert's rows are streamed by few XCDs and every weight panel by one.
+  // A group's tiles start at its first m-tile times the n-tiles per m-tile,
+  // so the group of tile L is that of m-tile L / n_ntiles.
+  const int nn = P.n_ntiles;
+  const int q = m0 + L / nn;
+  const int g = tile_group[q];
+  if (g < 0 || g >= P.G) return;
+  const int ga = max(tile_off[g], m0) - m0;            // group's first m-tile in the part
+  const int gv = min(tile_off[g + 1], m0 + mx) - m0 - ga;  // its m-tiles in the part
+  if (gv <= 0) return;
+  const int gr = L - ga * nn;
+  const int band = gr / (GM * nn);
+  const int gm = min(GM, gv - band * GM);
+  const int r = gr - band * GM * nn;
+  const int nt = r / gm;
+  const int m = m0 + ga + band * GM + (r - nt * gm);
+#else
   // The part's tiles go in bands of up to GM m-tiles, n-tile by n-tile, so
   // neighbouring tiles cover a few m-tiles by a few n-tiles and share both
   // operand panels in an XCD's L2.
@@ -832,6 +861,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
   const int m = m0 + band * GM + (r - nt * gm);
   const int g = tile_group[m];
   if (g < 0 || g >= P.G) return;
+#endif
   const int ml = m - tile_off[g];
   const int gend = group_offsets[g + 1];
   const int row0 = group_offsets[g] + ml * BM;
