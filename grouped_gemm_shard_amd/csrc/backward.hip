@@ -780,6 +780,7 @@ struct WgradParams {
   int kc, ni_tiles, nj_tiles;
   long long slots;      // partial slots in part
   int accumulate;
+  int round_blocks;     // 256 x 256 tiles: blocks per round (xcd_unit)
 };
 
 constexpr int kWMaxGroups = 1024;  // groups of one expert kept in LDS
@@ -994,6 +995,313 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradParams P) {
   wgrad_tile(P, smem, gl);
 }
 
+// ---- weight gradients on 256 x 256 tiles (long reductions, H >= 2048) ----
+//
+// The forward's two-group loop with both operands reduction-major: 8 waves
+// in two groups of four (one wave of each per SIMD) take turns reading
+// fragments and multiplying.  A K step is 64 reduction rows; its operands
+// are four 16 KB quarters in a ring of ten (the whole LDS): P columns i0 ..
+// i0+127 (read by group 0), i0+128 .. i0+255 (group 1), Q columns j0 ..
+// j0+127 and j0+128 .. j0+255 (both groups).  Each quarter holds the step's
+// 64 rows of its 128 columns (256-byte rows, 16-byte chunks permuted by
+// row), and every MFMA fragment comes from two LDS transpose reads.  The
+// issue and wait schedule is the forward's: group 0 issues quarters 4j+7 and
+// 4j+8 in its read phase of step j, group 1 quarters 4j+9 and 4j+10.
+//
+// The rows of a step are gathered: reduction position p of the chunk is
+// row grp_row0[g] + (p - start of g) of the expert's groups in order.  Each
+// wave keeps a window of up to 64 groups in registers (lane l: group wb+l,
+// its first row, first position and length) and walks it with uniform
+// reads of single lanes, so issuing a step's loads waits on no memory
+// access; the window is refilled (rarely: more than 64 groups) by plain
+// loads, which only make the ring's later waits stronger, since vector
+// memory loads complete in issue order.
+constexpr int kWpQ = 16384;         // bytes per quarter
+constexpr int kWpRing = 10 * kWpQ;  // the whole LDS
+constexpr int kWpStride = 256 + 16;  // floats per row of the epilogue's half tile
+
+template <int OFF>
+__device__ __forceinline__ void lds_tr(v4i16& r, unsigned addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+}
+
+// Waits for every LDS read of the wave, with 16 fragment registers tied to
+// the wait so that no use of them is placed before it.
+__device__ __forceinline__ void tie16(v4i16* r) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]),
+                 "+v"(r[6]), "+v"(r[7]), "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]),
+                 "+v"(r[12]), "+v"(r[13]), "+v"(r[14]), "+v"(r[15]));
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lgkm_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier that no instruction is scheduled across.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void wgrad_tile_pp(const WgradParams& P, char* smem) {
+  constexpr int BK = 64, LQ = 4, NQ_PRO = 8, MI = 4, NI = 8;
+  const int tiles = P.ni_tiles * P.nj_tiles;
+  const int L = xcd_unit(P.round_blocks, P.plan.meta[0] * tiles);
+  if (L < 0) return;
+  const int u = L / tiles, t = L - u * tiles;
+  const int e = P.plan.order_e[u];
+  if (e < 0) return;
+  const int ci = P.plan.order_i[u];
+  const int it = t / P.nj_tiles, jt = t - it * P.nj_tiles;
+  const int i0 = it * 256, j0 = jt * 256;
+  const int R = P.plan.rows[e], nch = P.plan.nch[e];
+  const int k0 = ci * P.kc, k1 = min(R, k0 + P.kc);
+  const int KT = k1 > k0 ? (k1 - k0 + BK - 1) / BK : 0;
+  const int NQ = 4 * KT;
+  const int g_lo = P.plan.grp_off[e];
+  const int ng = P.plan.grp_off[e + 1] - g_lo;
+  const bool direct = nch == 1;
+  const long long slot = direct ? 0 : (long long)P.plan.pbase[e] + ci;
+  if (!direct && (P.plan.pbase[e] < 0 || slot >= P.slots)) return;
+  if (direct && P.accumulate && KT == 0) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = w >> 2, wig = w & 3;
+  const int wml = wig >> 1, wn = wig & 1;
+  const __amdgpu_buffer_rsrc_t rp = raw_rsrc(P.Pm, (unsigned)P.a_rows * P.I * 2);
+  const __amdgpu_buffer_rsrc_t rq = raw_rsrc(P.Qm, (unsigned)P.a_rows * P.J * 2);
+
+  // the group window: lane l holds group wb + l as the end of its positions
+  // and its first row minus its first position (lanes past the expert's
+  // groups: length 0)
+  int wb = 0, cseg = 0, cpos = 0;  // cpos: first position of group cseg
+  int s_end = 0, s_rbase = 0;
+  auto load_window = [&](int base, int base_pos) {
+    wb = base;
+    const int c = base + lane;
+    const int ln = c < ng ? P.plan.grp_len[g_lo + c] : 0;
+    const int r0 = c < ng ? P.plan.grp_row0[g_lo + c] : 0;
+    int x = ln;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    s_end = base_pos + x;
+    s_rbase = r0 - (s_end - ln);
+  };
+  load_window(0, 0);
+  // rows of the chunk's step s for this lane's LQ loads (-1: past the
+  // chunk); steps are asked for in nondecreasing order.  Load i of the lane
+  // covers position 16 i + rr0 of the step.
+  const int rr0 = 4 * wig + (lane >> 4);
+  auto rows_of = [&](int s, int (&row)[LQ]) {
+#pragma unroll
+    for (int i = 0; i < LQ; ++i) row[i] = -1;
+    const int lo = k0 + s * BK, hi = min(lo + BK, k1);
+    // a walk past the window left group cseg behind: refill from it
+    if (cseg < wb) load_window(cseg, cpos);
+    // first group that ends after lo
+    while (cseg < ng) {
+      const int en = __builtin_amdgcn_readlane(s_end, cseg - wb);
+      if (en > lo) break;
+      ++cseg;
+      cpos = en;
+      if (cseg - wb == 64 && cseg < ng) load_window(cseg, en);
+    }
+    int c = cseg;
+    while (c < ng) {
+      if (c - wb == 64) load_window(c, __builtin_amdgcn_readlane(s_end, 63));
+      const int l = c - wb;
+      const int en = __builtin_amdgcn_readlane(s_end, l);
+      const int rb = __builtin_amdgcn_readlane(s_rbase, l);
+#pragma unroll
+      for (int i = 0; i < LQ; ++i) {
+        const int p = lo + 16 * i + rr0;
+        if (row[i] < 0 && p < en && p < hi) row[i] = rb + p;
+      }
+      if (en >= hi) break;
+      ++c;
+    }
+  };
+  // quarter q = 4 step + part: P columns (parts 0, 1) or Q columns (2, 3)
+  const int pch = lane & 15;
+  auto issue_q = [&](int q, const int (&row)[LQ]) {
+    if (q >= NQ) return;
+    char* st = smem + (q % 10) * kWpQ;
+    const int part = q & 3;
+    const bool isp = part < 2;
+    const int rowb = (isp ? P.I : P.J) * 2;
+    const int colb = (isp ? i0 : j0) * 2 + (part & 1) * 256;
+#pragma unroll
+    for (int i = 0; i < LQ; ++i) {
+      const int off = row[i] >= 0 ? row[i] * rowb + colb + ((pch ^ wswz(rr0)) << 4)
+                                  : (int)0x80000000;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isp ? rp : rq,
+                                               (lds_void*)(st + (i * 4 + wig) * 1024), 16, off,
+                                               0, 0, 0);
+    }
+  };
+  // fragment reads: lane j of 16-lane group g addresses row 8g + j/4 (+4 for
+  // the second read) and columns 4 (j%4) .. of its 16-column tile
+  const int tj = lane & 15;
+  const unsigned tk_base =
+      (8 * (lane >> 4) + (tj >> 2)) * 256 + (tj & 1) * 8 + (((tj & 3) >> 1) << 4);
+  const int tk_sw = (tj >> 2) << 2;
+  const unsigned lds0 = lds_addr(smem);
+
+  floatx4 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[mi][ni][q] = 0.0f;
+
+  // prologue: steps 0 and 1 (group 0 its P quarters and Q columns 0-127,
+  // group 1 its P quarters and Q columns 128-255)
+  int rows[LQ];
+  rows_of(0, rows);
+  issue_q(grp, rows);
+  issue_q(2 + grp, rows);
+  if (KT > 1) {
+    rows_of(1, rows);
+    issue_q(4 + grp, rows);
+    issue_q(6 + grp, rows);
+  }
+  vm_wait_n<0>();
+  phase_barrier();
+  if (grp == 1) phase_barrier();
+  v4i16 at[2][MI][2], bt[2][NI][2];
+  for (int kt = 0; kt < KT; ++kt) {
+    const unsigned sa = lds0 + ((4 * kt + grp) % 10) * kWpQ + tk_base;
+    const unsigned sb = lds0 + ((4 * kt + 2 + wn) % 10) * kWpQ + tk_base;
+    // read phase: this group's two quarters (group 0: Q columns 128-255 of
+    // step kt+1 and its P quarter of step kt+2; group 1: its P quarter and
+    // Q columns 0-127 of step kt+2), then the step's fragments
+    const int q0 = 4 * kt + 7 + 2 * grp, q1 = q0 + 1;
+    if (grp == 0) {
+      if (q0 >= NQ_PRO && q0 < NQ) {
+        rows_of(kt + 1, rows);
+        issue_q(q0, rows);
+      }
+      if (q1 < NQ) {
+        rows_of(kt + 2, rows);
+        issue_q(q1, rows);
+      }
+    } else if (q0 < NQ) {
+      rows_of(kt + 2, rows);
+      issue_q(q0, rows);
+      issue_q(q1, rows);
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const unsigned ad = sa + (((2 * (4 * wml + mi)) ^ tk_sw) << 4);
+      lds_tr<0>(at[0][mi][0], ad);
+      lds_tr<1024>(at[0][mi][1], ad);
+      lds_tr<8192>(at[1][mi][0], ad);
+      lds_tr<9216>(at[1][mi][1], ad);
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const unsigned ad = sb + (((2 * ni) ^ tk_sw) << 4);
+      lds_tr<0>(bt[0][ni][0], ad);
+      lds_tr<1024>(bt[0][ni][1], ad);
+      lds_tr<8192>(bt[1][ni][0], ad);
+      lds_tr<9216>(bt[1][ni][1], ad);
+    }
+    tie16(&at[0][0][0]);
+    tie16(&bt[0][0][0]);
+    tie16(&bt[1][0][0]);
+    if (grp == 1) {
+      // quarters up to 4kt+6 landed; its two newest may stay in flight
+      if (q1 < NQ) vm_wait_n<2 * LQ>();
+      else if (q0 < NQ) vm_wait_n<LQ>();
+      else vm_wait_n<0>();
+    }
+    lgkm_wait_all();
+    phase_barrier();
+    // multiply phase
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const bf16x8 av = join8(at[ks][mi][0], at[ks][mi][1]);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              av, join8(bt[ks][ni][0], bt[ks][ni][1]), acc[mi][ni], 0, 0, 0);
+      }
+    if (grp == 0) {
+      // quarters up to 4kt+7 landed; its newest (4kt+8) may stay in flight
+      if (q1 >= NQ_PRO && q1 < NQ) vm_wait_n<LQ>();
+      else vm_wait_n<0>();
+    }
+    phase_barrier();
+  }
+  if (grp == 0) phase_barrier();
+
+  // Epilogue: the tile leaves through LDS in two halves of 128 rows (group
+  // h's), each thread then reading, adding and storing 16-byte runs of
+  // rows.  A single-chunk expert writes its gradient (adding the old values
+  // when accumulating), a split expert's chunk its partial.
+  float* part = direct ? nullptr : P.part + (size_t)slot * P.I * P.J;
+  auto out_ptr = [&](int i, int j) {
+    if (!direct) return part + (size_t)i * P.J + j;
+    if (i < P.i_split) return P.C0 + (size_t)e * P.c_stride + (size_t)i * P.J + j;
+    return P.C1 + (size_t)e * P.c_stride + (size_t)(i - P.i_split) * P.J + j;
+  };
+  const bool rmw = direct && P.accumulate;
+  float* tile = (float*)smem;
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (grp == h) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = wml * 64 + mi * 16 + (lane >> 4) * 4 + q;
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+            tile[r * kWpStride + wn * 128 + ni * 16 + (lane & 15)] = acc[mi][ni][q];
+        }
+    }
+    __syncthreads();
+    float4 old[16];
+    if (rmw) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m)
+        old[m] = *(const float4*)out_ptr(i0 + h * 128 + m * 8 + (tid >> 6), j0 + (tid & 63) * 4);
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int r = m * 8 + (tid >> 6), c = (tid & 63) * 4;
+      float4 v = *(const float4*)(tile + r * kWpStride + c);
+      if (rmw) {
+        v.x += old[m].x;
+        v.y += old[m].y;
+        v.z += old[m].z;
+        v.w += old[m].w;
+      }
+      *(float4*)out_ptr(i0 + h * 128 + r, j0 + c) = v;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void wgrad_pp_kernel(WgradParams P) {
+  static_assert(128 * kWpStride * 4 <= kWpRing, "the epilogue's half tile fits the ring");
+  __shared__ __attribute__((aligned(1024))) char smem[kWpRing];
+  wgrad_tile_pp(P, smem);
+}
+
 // dW[e] (+)= the sum of a split expert's partials, in chunk order.
 __global__ __launch_bounds__(256) void wgrad_reduce_kernel(WgradParams P) {
   const int e = blockIdx.y;
@@ -1030,6 +1338,11 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(WgradParams P) {
 // most floor(2 max_rows / Kc) partials.  (Measured on the mid-sized layer's
 // backward, 16384 rows: 256 slots, i.e. chunks of 2048 rows, beat 64, 128,
 // 512, 1024 and 2048 slots by 3-30%: fewer partial gradients to write and add.)
+// Weight gradients of long reductions on the 256 x 256 two-group loop (1)
+// or on 128 x 128 tiles (0).
+#ifndef MOE_WGRAD_PP
+#define MOE_WGRAD_PP 1
+#endif
 #ifndef MOE_WGRAD_TILES
 #define MOE_WGRAD_TILES 256
 #endif
@@ -1150,7 +1463,7 @@ inline size_t a256(size_t b) { return (b + 255) / 256 * 256; }
 // units rounded down to a multiple of 8 (the XCDs) times the workgroups of
 // the kernel that fit on one, cached per device and kernel.
 int bwd_round_blocks(const void* kernel, int threads, int which) {
-  static int cache[64][4] = {};
+  static int cache[64][8] = {};
   static std::mutex mu;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -1299,6 +1612,7 @@ hipError_t launch_wgrad(const Dims& d, int sets, const int* group_offsets, int64
   W.kc = kc;
   W.slots = wgrad_slots(total, kc);
   W.accumulate = accumulate;
+  W.round_blocks = 0;
   W.ni_tiles = W.I / 128;
   W.nj_tiles = W.J / 128;
   WgradParams V = W;
@@ -1310,9 +1624,25 @@ hipError_t launch_wgrad(const Dims& d, int sets, const int* group_offsets, int64
   V.i_split = d.H;
   V.ni_tiles = V.I / 128;
   V.nj_tiles = V.J / 128;
+  // long reductions (H >= 2048, both dimensions whole 256-column tiles): the
+  // two-group loop on 256 x 256 tiles
+  const bool pp = MOE_WGRAD_PP && d.bf16 && d.H >= 2048 && d.H % 256 == 0 && d.F % 256 == 0;
+  if (pp) {
+    const int nb = bwd_round_blocks(reinterpret_cast<const void*>(wgrad_pp_kernel), 512, 4);
+    for (WgradParams* q : {&W, &V}) {
+      q->ni_tiles = q->I / 256;
+      q->nj_tiles = q->J / 256;
+      q->round_blocks = nb;
+    }
+  }
   for (const WgradParams* q : {&W, &V}) {
-    hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)(nc * q->ni_tiles * q->nj_tiles)),
-                       dim3(256), 0, s, *q);
+    if (pp)
+      hipLaunchKernelGGL(wgrad_pp_kernel,
+                         dim3(whole_rounds(nc * q->ni_tiles * q->nj_tiles, q->round_blocks)),
+                         dim3(512), 0, s, *q);
+    else
+      hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)(nc * q->ni_tiles * q->nj_tiles)),
+                         dim3(256), 0, s, *q);
     // an expert is split only when it has more than kc rows
     if (kc >= total) continue;
     const long long ij4 = ((long long)q->I * q->J / 4 + 255) / 256;
