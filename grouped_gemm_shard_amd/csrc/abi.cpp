@@ -849,6 +849,8 @@ struct LayerBwdWs {
   void* act_all;
   int* go_all;
   void* wgrad;
+  float* row_gate;  // bf16: each row's gate (the gated mode of launch_gmm_bwd)
+  float* dg_part;   // bf16: the rows' gate-gradient parts [rows, F/32]
   size_t bytes;
 };
 
@@ -873,6 +875,11 @@ LayerBwdWs carve_layer_bwd(const Dims& d, const LayoutSet& ls, int64_t rows, int
   w.dxs = take((size_t)rows * d.H * es);
   w.d_gate = (float*)take((size_t)d.T * d.k * 4);
   w.gmm = take(gmm_bwd_scratch_bytes(d, rows));
+  w.row_gate = w.dg_part = nullptr;
+  if (d.bf16) {
+    w.row_gate = (float*)take((size_t)rows * 4);
+    w.dg_part = (float*)take((size_t)rows * (d.F / 32) * 4);
+  }
   w.d_h_all = w.act_all = w.wgrad = nullptr;
   w.go_all = nullptr;
   if (w.defer) {
@@ -981,9 +988,10 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
     e = launch_gather_rows(lb.meta, kLayoutMeta, lb.sorted_assign, tk, d.k, x, xs_b, d.H * es,
                            d.T, rows, pa, s);
     if (e != hipSuccess) return MOE_EHIP;
-    // bf16: the rows g*dy need no expert output, and the grouped-GEMM
-    // backward recomputes the activation anyway, so it also returns the
-    // expert outputs (act Wd^T) and the gate gradients come after it; fp32
+    // bf16: the rows go ungated (dy) with each row's gate, d_a = dy Wd is
+    // ungated, and the grouped-GEMM backward's recompute applies the gate
+    // and returns the gate gradients in parts, <dy Wd, act> = <dy, act Wd^T>
+    // = <dy, expert output>, so no expert output is recomputed; fp32
     // recomputes the forward first
     if (!d.bf16) {
       GemmPass gp;
@@ -1002,7 +1010,7 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
       if (e != hipSuccess) return MOE_EHIP;
     }
     e = launch_combine_bwd(d, pa, ls, dy, f.out[0], lb.row_of_assign, tk, f.topk_gate, dout_b,
-                           w.d_gate, rows, d.bf16 ? 1 : 3, s);
+                           w.d_gate, rows, d.bf16 ? 1 | 4 : 3, s, w.row_gate, nullptr);
     if (e != hipSuccess) return MOE_EHIP;
     GemmBwdArgs a;
     a.x_sorted = xs_b;
@@ -1021,7 +1029,9 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
     a.accumulate = b > 0;
     a.max_rows = rows;
     a.scratch = w.gmm;
-    a.out_recompute = d.bf16 ? f.out[0] : nullptr;
+    a.out_recompute = nullptr;
+    a.row_gate = w.row_gate;
+    a.dg_part = w.dg_part;
     if (w.defer) {
       a.go_out = w.go_all + set * (d.G_res + 1);
       a.d_h_ext = (char*)w.d_h_all + set * rows * 2 * d.F * es;
@@ -1031,8 +1041,8 @@ int moe_layer_bwd(const moe_problem* p, int32_t mode, const void* x, const float
     e = launch_gmm_bwd(d, a, s);
     if (e != hipSuccess) return MOE_EHIP;
     if (d.bf16) {
-      e = launch_combine_bwd(d, pa, ls, dy, f.out[0], lb.row_of_assign, tk, f.topk_gate, nullptr,
-                             w.d_gate, rows, 2, s);
+      e = launch_combine_bwd(d, pa, ls, dy, nullptr, lb.row_of_assign, tk, f.topk_gate, nullptr,
+                             w.d_gate, rows, 2 | 8, s, nullptr, w.dg_part);
       if (e != hipSuccess) return MOE_EHIP;
     }
     e = launch_permute_bwd(d, pa, ls, w.dxs, lb.row_of_assign, tk, dx, rows, s);

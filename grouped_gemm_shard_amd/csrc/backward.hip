@@ -76,14 +76,18 @@ struct Vec {
 
 // ---- combine backward ------------------------------------------------------
 
-// what: bit 0 writes the rows g * dy, bit 1 the gate gradients <dy, out>.
+// what: bit 0 writes the rows g * dy, bit 1 the gate gradients <dy, out>;
+// bit 2 makes the rows dy ungated and writes each row's gate to row_gate;
+// bit 3 takes the gate gradient of a row as the sum of its F/32 parts
+// dg_part [r, .] (= <dy Wd, act>, the same quantity) instead of reading out.
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(Dims d, PassArgs pa, LayoutSet ls,
                                                           const void* dy, const void* out,
                                                           const int* roa, long long roa_stride,
                                                           const float* gate, void* d_out,
                                                           float* d_gate, long long max_rows,
-                                                          int what) {
+                                                          int what, float* row_gate,
+                                                          const float* dg_part) {
   const PassInfo pi = resolve_pass(pa);
   if (!pi.active) return;
   roa += (size_t)layout_set_of(ls, pi.j) * roa_stride;
@@ -92,29 +96,37 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(Dims d, PassArgs pa, L
   const int t = pass_token(d, pi, i);
   const int lane = threadIdx.x & 63;
   constexpr int N = Vec<BF16>::N;
-  const bool rows = what & 1, dots = what & 2;
+  const bool ungated = what & 4, parts = what & 8;
+  const bool rows = what & 1, dots = (what & 2) && !parts;
+  const int nparts = d.F / 32;
   for (int j = 0; j < d.k; ++j) {
     const int r = roa[(size_t)t * d.k + j];
     float dot = 0.0f;
     if (r >= 0 && r < max_rows) {
       const float g = gate[(size_t)t * d.k + j];
-      for (int c = lane * N; c < d.H; c += 64 * N) {
-        Vec<BF16> a;
-        a.load(dy, (size_t)t * d.H + c);
-        if (dots) {
-          Vec<BF16> o;
-          o.load(out, (size_t)r * d.H + c);
+      if (rows && ungated && lane == 0) row_gate[r] = g;
+      if (parts && (what & 2))
+        for (int b = lane; b < nparts; b += 64) dot += dg_part[(size_t)r * nparts + b];
+      if (rows || dots)
+        for (int c = lane * N; c < d.H; c += 64 * N) {
+          Vec<BF16> a;
+          a.load(dy, (size_t)t * d.H + c);
+          if (dots) {
+            Vec<BF16> o;
+            o.load(out, (size_t)r * d.H + c);
 #pragma unroll
-          for (int q = 0; q < N; ++q) dot = fmaf(a.v[q], o.v[q], dot);
-        }
-        if (rows) {
+            for (int q = 0; q < N; ++q) dot = fmaf(a.v[q], o.v[q], dot);
+          }
+          if (rows) {
+            if (!ungated) {
 #pragma unroll
-          for (int q = 0; q < N; ++q) a.v[q] *= g;
-          a.store(d_out, (size_t)r * d.H + c);
+              for (int q = 0; q < N; ++q) a.v[q] *= g;
+            }
+            a.store(d_out, (size_t)r * d.H + c);
+          }
         }
-      }
     }
-    if (dots) {
+    if (what & 2) {
       dot = wave_sum(dot);
       if (lane == 0) d_gate[(size_t)t * d.k + j] = dot;
     }
@@ -1016,6 +1028,9 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradParams P) {
 // access; the window is refilled (rarely: more than 64 groups) by plain
 // loads, which only make the ring's later waits stronger, since vector
 // memory loads complete in issue order.
+#ifndef MOE_WGRAD_BAND
+#define MOE_WGRAD_BAND 4
+#endif
 constexpr int kWpQ = 16384;         // bytes per quarter
 constexpr int kWpRing = 10 * kWpQ;  // the whole LDS
 constexpr int kWpStride = 256 + 16;  // floats per row of the epilogue's half tile
@@ -1057,7 +1072,14 @@ __device__ __forceinline__ void wgrad_tile_pp(const WgradParams& P, char* smem) 
   const int e = P.plan.order_e[u];
   if (e < 0) return;
   const int ci = P.plan.order_i[u];
-  const int it = t / P.nj_tiles, jt = t - it * P.nj_tiles;
+  // a chunk's tiles go in bands of up to WB tile rows, column by column:
+  // the 32 tiles an XCD runs together then share a few row panels of P and
+  // a few column panels of Q in its L2
+  constexpr int WB = MOE_WGRAD_BAND;
+  const int band = t / (WB * P.nj_tiles);
+  const int bh = min(WB, P.ni_tiles - band * WB);
+  const int tr = t - band * WB * P.nj_tiles;
+  const int jt = tr / bh, it = band * WB + (tr - jt * bh);
   const int i0 = it * 256, j0 = jt * 256;
   const int R = P.plan.rows[e], nch = P.plan.nch[e];
   const int k0 = ci * P.kc, k1 = min(R, k0 + P.kc);
@@ -1548,16 +1570,19 @@ size_t wgrad_sets_scratch_bytes(const Dims& d, int sets, int64_t rows_per_set) {
 hipError_t launch_combine_bwd(const Dims& d, const PassArgs& pa, const LayoutSet& ls,
                               const void* dy, const void* out, const int* roa,
                               long long roa_stride, const float* gate, void* d_out,
-                              float* d_gate, int64_t max_rows, int what, hipStream_t s) {
+                              float* d_gate, int64_t max_rows, int what, hipStream_t s,
+                              float* row_gate, const float* dg_part) {
   // a pass of a layer call covers at most its window; the single pass L
   const int ntok = (d.T / d.L) * (pa.ovf != nullptr ? d.L : pa.lw);
   const dim3 grid((ntok + 3) / 4);
   if (d.bf16)
     hipLaunchKernelGGL(combine_bwd_kernel<true>, grid, dim3(256), 0, s, d, pa, ls, dy, out, roa,
-                       roa_stride, gate, d_out, d_gate, (long long)max_rows, what);
+                       roa_stride, gate, d_out, d_gate, (long long)max_rows, what, row_gate,
+                       dg_part);
   else
     hipLaunchKernelGGL(combine_bwd_kernel<false>, grid, dim3(256), 0, s, d, pa, ls, dy, out, roa,
-                       roa_stride, gate, d_out, d_gate, (long long)max_rows, what);
+                       roa_stride, gate, d_out, d_gate, (long long)max_rows, what, row_gate,
+                       dg_part);
   return hipGetLastError();
 }
 
@@ -1764,12 +1789,13 @@ hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s) {
   Q.act = (uint16_t*)act;
   Q.round_blocks = nb_sw;
   pe = launch_gmm_swiglu_recompute(d, go, a.slot_expert, a.x_sorted, rows, a.wg, a.wu, d_a, d_h,
-                                   act, rows, plain_ws + 3 * plain_step, s);
-  if (pe == hipErrorNotSupported)
+                                   act, rows, plain_ws + 3 * plain_step, s, a.row_gate,
+                                   a.dg_part);
+  if (pe == hipErrorNotSupported && a.row_gate == nullptr)
     hipLaunchKernelGGL(dgrad_kernel<true>, dim3(whole_rounds(mt_ub * Q.n_ntiles, nb_sw)),
                        dim3(256), 0, s, Q);
   else if (pe != hipSuccess)
-    return pe;
+    return pe;  // (the gated mode runs on the forward's kernel only)
   // dx_sorted = [d_hg | d_hu] [Wg ; Wu]  (K = 2F; Wg and Wu [F, H] stacked
   // along the reduction and read reduction-major)
   DgradParams X = P;

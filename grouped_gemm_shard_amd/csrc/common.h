@@ -339,7 +339,8 @@ hipError_t launch_gmm_swiglu_recompute(const Dims& d, const int* group_offsets,
                                        const int* slot_expert, const void* x_sorted,
                                        int64_t a_rows, const void* wg, const void* wu,
                                        const void* d_a, void* d_h, void* act, int64_t max_rows,
-                                       void* scratch, hipStream_t s);
+                                       void* scratch, hipStream_t s,
+                                       const float* row_gate = nullptr, float* dg_part = nullptr);
 size_t gmm_sync_bytes(const Dims& d);
 int gmm_sync_ints(const Dims& d);  // ints of gmm_sync_bytes the kernel expects at zero
 
@@ -411,6 +412,12 @@ struct GemmBwdArgs {
   void* d_h_ext = nullptr;
   void* act_ext = nullptr;
   int wgrad = 1;
+  // bf16, the layer call's gated mode: d_out holds the ungated rows dy (so
+  // d_a = dy Wd is ungated), row_gate [rows] each row's gate; the recompute
+  // applies the gate, stores gate * act as the activation (dWd = dy^T
+  // (gate act)) and writes the gate-gradient parts dg_part [rows, F/32]
+  const float* row_gate = nullptr;
+  float* dg_part = nullptr;
 };
 size_t gmm_bwd_scratch_bytes(const Dims& d, int64_t max_rows);
 hipError_t launch_gmm_bwd(const Dims& d, const GemmBwdArgs& a, hipStream_t s);
@@ -425,11 +432,15 @@ hipError_t launch_wgrad(const Dims& d, int sets, const int* group_offsets, int64
                         int accumulate, void* scratch, hipStream_t s);
 // Combine / permute backward of a pass; row_of_assign advances by
 // roa_stride per row_of_assign set of the pass's layout (as launch_combine).
-// what: bit 0 the rows g * dy into d_out, bit 1 the gate gradients (reads out).
+// what: bit 0 the rows g * dy into d_out, bit 1 the gate gradients <dy, out>
+// (reads out); bit 2 (with bit 0) the rows dy ungated and each row's gate
+// into row_gate; bit 3 (with bit 1) the gate gradients as the sum of the
+// row's parts dg_part [rows, F/32] instead of reading out.
 hipError_t launch_combine_bwd(const Dims& d, const PassArgs& pa, const LayoutSet& ls,
                               const void* dy, const void* out, const int* roa,
                               long long roa_stride, const float* gate, void* d_out,
-                              float* d_gate, int64_t max_rows, int what, hipStream_t s);
+                              float* d_gate, int64_t max_rows, int what, hipStream_t s,
+                              float* row_gate = nullptr, const float* dg_part = nullptr);
 hipError_t launch_permute_bwd(const Dims& d, const PassArgs& pa, const LayoutSet& ls,
                               const void* dxs, const int* roa, long long roa_stride, void* dx,
                               int64_t max_rows, hipStream_t s);

@@ -122,20 +122,33 @@ struct GemmParams {
   // reduction-major B (the 256-row loop's BKM mode): B0 [e_res][k_split][Nout]
   // holds rows k < k_split, B1 [e_res][K - k_split][Nout] the rest
   int k_split = 0;
+  // the recompute with ungated d_a (the layer backward): d_a holds u = dy Wd
+  // for each row, the row's gate is row_gate[r]; the SwiGLU backward takes
+  // d_a = gate * u, C receives gate * act, and dg_part[r * (Nout / 32) + b]
+  // the sum over act columns 32 b .. 32 b + 31 of u * act (the row's gate
+  // gradient in parts)
+  const float* row_gate = nullptr;
+  float* dg_part = nullptr;
 };
 
 // The SwiGLU backward of one output element from the gate and up
 // pre-activations and d_a: act = SiLU(g) u, d_hg = d_a u SiLU'(g), d_hu =
 // d_a SiLU(g), SiLU'(g) = s (1 + g (1 - s)) with s the logistic of g (the
 // forward's SiLU, hardware reciprocal).
-__device__ __forceinline__ void swiglu_bwd_store(const GemmParams& P, size_t r, int c, float gv,
-                                                 float uv) {
-  const float da = bf2f(P.d_a[r * P.Nout + c]);
+// With the row's gate rg (1 when d_a is already gated) d_a = rg * (stored
+// d_a) and C receives rg * act; returns (stored d_a) * act, act as stored in
+// bf16, the element's term of the row's gate gradient.
+__device__ __forceinline__ float swiglu_bwd_store(const GemmParams& P, size_t r, int c, float gv,
+                                                  float uv, float rg) {
+  const float u = bf2f(P.d_a[r * P.Nout + c]);
+  const float da = u * rg;
   const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
   const float silu = gv * sg;
-  P.C[r * P.Nout + c] = f2bf(silu * uv);
+  const float act = silu * uv;
+  P.C[r * P.Nout + c] = f2bf(act * rg);
   P.d_h[r * 2 * P.Nout + c] = f2bf(da * uv * (sg * (1.0f + gv * (1.0f - sg))));
   P.d_h[r * 2 * P.Nout + P.Nout + c] = f2bf(da * silu);
+  return u * bf2f(f2bf(act));
 }
 
 // Reports an error bit found by the device (one report per block).
@@ -406,17 +419,32 @@ __device__ __forceinline__ void gmm_tile(const GemmParams& P, char* smem, const 
   live_dispatch<MI>(live, kloop);
 
   if (SWIGLU && !COH && P.d_h != nullptr) {
-    // the backward's recompute: element by element, no LDS
+    // the backward's recompute: element by element, no LDS (32x32 layout:
+    // register q of a lane holds row (q/4)*8 + (lane/32)*4 + q%4, column
+    // lane%32; each ni is one 32-column block of the gate-gradient parts)
+    const bool gated = P.row_gate != nullptr;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int lr = wm * WM + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-        if (lr >= rows) continue;
+        const bool ok = lr < rows;
+        const float rg = gated && ok ? P.row_gate[row0 + lr] : 1.0f;
 #pragma unroll
-        for (int ni = 0; ni < NI / 2; ++ni)
-          swiglu_bwd_store(P, (size_t)(row0 + lr), nt * 128 + wn * (128 / NWN) + ni * 32 + (lane & 31),
-                           acc[mi][ni][q], acc[mi][ni + NI / 2][q]);
+        for (int ni = 0; ni < NI / 2; ++ni) {
+          const int c0 = nt * 128 + wn * (128 / NWN) + ni * 32;
+          float t = 0.0f;
+          if (ok)
+            t = swiglu_bwd_store(P, (size_t)(row0 + lr), c0 + (lane & 31), acc[mi][ni][q],
+                                 acc[mi][ni + NI / 2][q], rg);
+          if (gated) {
+            // the 32 lanes of a row (wave-uniform branch: every lane shuffles)
+#pragma unroll
+            for (int o = 16; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+            if (ok && (lane & 31) == 0)
+              P.dg_part[(size_t)(row0 + lr) * (P.Nout / 32) + c0 / 32] = t;
+          }
+        }
       }
     __syncthreads();  // as after the LDS epilogue: every wave is done with the ring
     return;
@@ -734,17 +762,37 @@ __device__ __forceinline__ void gmm_tile_pp(const GemmParams& P, char* smem, con
   if (SWIGLU && P.d_h != nullptr) {
     // the backward's recompute: element by element, no LDS (16x16 layout:
     // register q of a lane holds row (lane/16)*4 + q, column lane%16)
+    // (each pair of ni is one 32-column block of the gate-gradient parts)
     const int wr0 = grp * 128 + wml * 64;
+    const bool gated = P.row_gate != nullptr;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int lr = wr0 + mi * 16 + (lane >> 4) * 4 + q;
-        if (lr >= rows) continue;
+        const bool ok = lr < rows;
+        const float rg = gated && ok ? P.row_gate[row0 + lr] : 1.0f;
+        float t[2] = {0.0f, 0.0f};
+        if (ok) {
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          swiglu_bwd_store(P, (size_t)(row0 + lr), nt * 128 + wn * 64 + ni * 16 + (lane & 15),
-                           acc[mi][ni][q], acc[mi][ni + 4][q]);
+          for (int ni = 0; ni < 4; ++ni)
+            t[ni >> 1] += swiglu_bwd_store(P, (size_t)(row0 + lr),
+                                           nt * 128 + wn * 64 + ni * 16 + (lane & 15),
+                                           acc[mi][ni][q], acc[mi][ni + 4][q], rg);
+        }
+        if (gated) {
+          // the 16 lanes of a row (wave-uniform branch: every lane shuffles)
+#pragma unroll
+          for (int o = 8; o >= 1; o >>= 1) {
+            t[0] += __shfl_xor(t[0], o);
+            t[1] += __shfl_xor(t[1], o);
+          }
+          if (ok && (lane & 15) == 0) {
+            float* pr = P.dg_part + (size_t)(row0 + lr) * (P.Nout / 32) + (nt * 128 + wn * 64) / 32;
+            pr[0] = t[0];
+            pr[1] = t[1];
+          }
+        }
       }
     __syncthreads();
     return;
@@ -1311,7 +1359,8 @@ hipError_t launch_plain(const Dims& d, const int* group_offsets, const int* slot
                         const void* A, int64_t a_rows, const void* B, size_t b_stride, int K,
                         int N, void* C, int64_t max_rows, void* scratch, hipStream_t s,
                         const void* B1 = nullptr, const void* d_a = nullptr,
-                        void* d_h = nullptr, int k_split = 0) {
+                        void* d_h = nullptr, int k_split = 0, const float* row_gate = nullptr,
+                        float* dg_part = nullptr) {
   const bool sw = d_h != nullptr;  // the SwiGLU-backward recompute (B, B1: gate, up)
   // k_split > 0: B reduction-major, rows [0, k_split) from B, the rest from B1
   const bool bkm = k_split > 0;
@@ -1337,6 +1386,8 @@ hipError_t launch_plain(const Dims& d, const int* group_offsets, const int* slot
   p.d_a = (const uint16_t*)d_a;
   p.d_h = (uint16_t*)d_h;
   p.k_split = k_split;
+  p.row_gate = row_gate;
+  p.dg_part = dg_part;
   p.group_offsets = group_offsets;
   p.tile_off = toff;
   p.tile_group = tgroup;
@@ -1391,14 +1442,17 @@ hipError_t launch_gmm_swiglu_recompute(const Dims& d, const int* group_offsets,
                                        const int* slot_expert, const void* x_sorted,
                                        int64_t a_rows, const void* wg, const void* wu,
                                        const void* d_a, void* d_h, void* act, int64_t max_rows,
-                                       void* scratch, hipStream_t s) {
+                                       void* scratch, hipStream_t s, const float* row_gate,
+                                       float* dg_part) {
   if (!d.bf16) return hipErrorNotSupported;
   const size_t fh = (size_t)d.F * d.H;
   if (d.gemm_bm == 256)
     return launch_plain<MOE_GEMM_BIG>(d, group_offsets, slot_expert, x_sorted, a_rows, wg, fh,
-                                      d.H, d.F, act, max_rows, scratch, s, wu, d_a, d_h);
+                                      d.H, d.F, act, max_rows, scratch, s, wu, d_a, d_h, 0,
+                                      row_gate, dg_part);
   return launch_plain<MOE_GEMM_SMALL>(d, group_offsets, slot_expert, x_sorted, a_rows, wg, fh, d.H,
-                                      d.F, act, max_rows, scratch, s, wu, d_a, d_h);
+                                      d.F, act, max_rows, scratch, s, wu, d_a, d_h, 0, row_gate,
+                                      dg_part);
 }
 
 hipError_t launch_gmm_plain(const Dims& d, const int* group_offsets, const int* slot_expert,
