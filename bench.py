@@ -59,11 +59,11 @@ PEAK_HBM_GBS = 8000.0
 # is reported as null.
 GEMM_TRAFFIC = {
     "maverick_shard": {
-        "gmm_src_sha256": "26ecee9a76e49b4486f441e31af53503060077866554c9d17a942d864911dbee",
-        "bytes_per_layer": 31428590069},
+        "gmm_src_sha256": "fdfe9c7ffa6bf1b143cf41677242c983a6760a16c2bdf65929917322154ff197",
+        "bytes_per_layer": 28870910278},
     "mid_bf16": {
-        "gmm_src_sha256": "26ecee9a76e49b4486f441e31af53503060077866554c9d17a942d864911dbee",
-        "bytes_per_layer": 264802973},
+        "gmm_src_sha256": "fdfe9c7ffa6bf1b143cf41677242c983a6760a16c2bdf65929917322154ff197",
+        "bytes_per_layer": 267318021},
 }
 
 
@@ -335,6 +335,18 @@ def backward_figures(p, w, inp, info, reps):
                 flops=flops, rows=n_rows, gemm_bytes=w_bytes + row_bytes + dw_bytes)
 
 
+def run_calib_copy():
+    """The calibration copy of 1 GiB, 3 times: the reference that HBM
+    counters of the same run are scaled by."""
+    log("[bench] calibration copy: moe_calib_copy of 1 GiB, 3 times")
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        g.calib_copy(src, dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def measured_peaks(reps=10):
     """What this machine reaches outside the layer, as context for the fractions
     of the spec peaks: the library's own calibration kernels
@@ -494,6 +506,8 @@ def main():
         brun = g.LayerBackwardRunner(p, g.MODE_LAYER)
         dy = workloads.make_dy(w, device="cuda")
         t = time_calls(lambda: brun(inp["x"], inp["logits"], *inp["weights"], dy), args.steps)
+        if args.calib_copy:
+            run_calib_copy()
         print(json.dumps({"workload": w.name, "layer_backward_calls": args.steps,
                           "layer_call_us": round(t * 1e6, 2)}), flush=True)
         return
@@ -583,10 +597,11 @@ def main():
         broof.update(traffic=None, arith_intensity=round(bai, 1),
                      kernel="grouped-GEMM backward call (d_a, gate/up recompute, dx_sorted, "
                             "weight gradients; accumulating)")
-        # the layer call's grouped-GEMM work (16 N H F; the expert outputs it
-        # also recomputes for the gate gradients are not counted) over the
-        # whole call's time: its weight gradients are taken once over every
-        # pass's rows, not accumulated pass by pass
+        # the layer call's grouped-GEMM work (16 N H F: d_a, the gate/up
+        # recompute, dx_sorted and the weight gradients; bf16 takes the gate
+        # gradients from the recompute's epilogue) over the whole call's
+        # time: its weight gradients are taken once over every pass's rows,
+        # not accumulated pass by pass
         lt = bf["flops"] / t_layer_bwd / 1e12
         bwd = {"layer_call_us": round(t_layer_bwd * 1e6, 2),
                "layer_call_gemm_tflops": round(lt, 2),
@@ -602,13 +617,7 @@ def main():
                "roofline": broof}
 
     if args.calib_copy:
-        log("[bench] calibration copy: moe_calib_copy of 1 GiB, 3 times")
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            g.calib_copy(src, dst)
-        torch.cuda.synchronize()
-        del src, dst
+        run_calib_copy()
 
     log("[bench] measured peaks (calibration copy and MFMA loop, vendor dense GEMM)")
     peaks = measured_peaks()
