@@ -388,8 +388,12 @@ int moe_layer_bwd_workspace_bytes(const moe_problem* p, int32_t mode, size_t* by
  * layouts are recomputed from x and logits, and the device takes the same
  * passes as the forward (LAYER: the capped pass or the dropless chunk
  * batches, from the flag, with no host synchronisation).  Per pass:
- * x_sorted and the expert outputs recomputed, then the combine, grouped
- * GEMM and permute backward of that pass.  In bf16 with two or more pass
+ * x_sorted recomputed (and in fp32 the expert outputs), then the combine,
+ * grouped GEMM and permute backward of that pass; in bf16 the gate
+ * gradients <dy, expert output> are taken as <dy Wd, act> in the grouped
+ * GEMM's recompute, so no expert output is recomputed (the bf16 rounding
+ * points differ from the step calls': dy Wd and gate * act are rounded
+ * instead of gate * dy and the expert output).  In bf16 with two or more pass
  * slots (and every operand offset within 31 bits) the weight gradients are
  * not carried from pass to pass: each pass keeps its rows in the workspace
  * and the gradients of all passes are one reduction after the last pass,
