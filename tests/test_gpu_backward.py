@@ -186,3 +186,18 @@ def test_layer_backward_modes(which, mode):
 @pytest.mark.slow
 def test_layer_backward_mid_full_size():
     compare_layer(workloads.CONFIGS["mid_bf16"], 0)
+
+
+# 65 chunk passes of one chunk each (the 0.02x buffer holds 333 rows, a
+# chunk 256): in the layer call an expert's weight gradients span 65 groups,
+# one per pass, more than the 64 that the 256 x 256 weight-gradient kernel
+# keeps in its register window, and the hottest experts are cut into chunks
+# whose partials are added in chunk order.
+MANY_PASSES = W("bwd_many_passes", tokens=8320, seq_len=8320, hidden=2048, ffn=256,
+                num_experts=8, top_k=2, num_shards=1, res_lo=0, res_hi=1, factor=0.02,
+                num_chunks=65, zipf=1.1)
+
+
+@pytest.mark.slow
+def test_layer_backward_many_passes():
+    compare_layer(MANY_PASSES, 0)
