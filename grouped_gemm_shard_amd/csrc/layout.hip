@@ -450,6 +450,7 @@ __device__ __forceinline__ void wave_copy_row_deep(char* __restrict__ dst,
 constexpr int kOneLaunchElems = 4096;  // most elements of a pass
 constexpr int kOneLaunchOwn = 64;      // most elements per workgroup
 constexpr int kOneLaunchBlocks = 256;  // workgroups aimed for
+constexpr int kOneLaunchPrefetch = 16384;  // longest row loaded before the layout
 
 __global__ __launch_bounds__(1024) void permute_one_launch_kernel(
     Dims d, LayoutSet ls, const int* __restrict__ soa, LayoutBuffers lb,
@@ -469,15 +470,62 @@ __global__ __launch_bounds__(1024) void permute_one_launch_kernel(
   const int e_hi = min(g.nelem, e_lo + per_block);
   const int G = d.G_res, k = d.k, lane = lane_id(), w = threadIdx.x >> 6;
   const int nb = key_bits(G);
+  // Every slot key the wave needs, read first: the keys of its counting
+  // rounds, in wave 0 those of the workgroup's own elements, and that of
+  // the wave's own first element (vector loads complete in issue order, so
+  // a key read after the row prefetch below would wait for the rows).  The
+  // loads are unconditional, element 0's slot standing in for lanes past
+  // the elements, so that they issue back to back and are waited for once.
+  constexpr int RND = kOneLaunchElems / 1024;
+  auto key_of = [&](int e, bool in, int& t) {
+    const int ec = in ? e : 0;
+    const int tt = elem_token(d, g, ec);  // (garbage when the pass is empty: unused)
+    t = in ? tt : 0;
+    const int v = soa[(size_t)t * k + (in ? ec % k : 0)];
+    return slot_key(d, v) | ((int)in - 1);  // -1 past the elements, no branch
+  };
+  int kr[RND], tr;
+#pragma unroll
+  for (int r = 0; r < RND; ++r) {
+    const int e = w * 64 + r * 1024 + lane;
+    kr[r] = key_of(e, e < g.nelem, tr);
+  }
+  int to;
+  const int ko = key_of(e_lo + lane, w == 0 && e_lo + lane < e_hi, to);
+  int tw;
+  const bool res_w = key_of(e_lo + w, w < e_hi - e_lo, tw) >= 0;
+  // every key landed on every path (s_waitcnt vmcnt(0): the encoding's
+  // expcnt and lgkmcnt fields at their maxima), so that no later use of a
+  // key waits on the row loads below
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // Each wave's first own element: its source row is known before the
+  // layout, so a resident element's row (at most kOneLaunchPrefetch bytes)
+  // is loaded into registers now and lands while the workgroup recounts
+  // and places the keys; it is stored once its position is known.
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  constexpr int PF = kOneLaunchPrefetch / 1024;
+  v4i pf[PF];
+  const bool pf_on = row_bytes <= kOneLaunchPrefetch && w < e_hi - e_lo;
+  const bool pf_load = pf_on && res_w;
+  if (pf_on) {
+    const char* src = x + (size_t)tw * row_bytes;
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int o = u * 1024 + lane * 16;
+      pf[u] = pf_load && o < row_bytes ? *(const v4i*)(src + o) : v4i{0, 0, 0, 0};
+    }
+  }
   for (int q = threadIdx.x; q < G; q += 1024) tot[q] = bef[q] = 0;
   __syncthreads();
   // the waves take rounds of 64 elements in turn; per round and key the
   // highest peer adds the key's lanes (and those before e_lo)
-  for (int base = w * 64; base < g.nelem; base += 1024) {
+#pragma unroll
+  for (int r = 0; r < RND; ++r) {
+    const int base = w * 64 + r * 1024;
+    if (base >= g.nelem) break;  // wave-uniform
     const int e = base + lane;
     const bool in = e < g.nelem;
-    int ks = -1;
-    if (in) ks = slot_key(d, slot_at(d, soa + (size_t)elem_token(d, g, e) * k, 0, e % k));
+    const int ks = kr[r];
     const unsigned long long peers = wave_peers(ks, ks >= 0, nb);
     const unsigned long long early = __ballot(in && e < e_lo);
     if (ks >= 0 && (peers >> lane) == 1ull) {
@@ -492,14 +540,10 @@ __global__ __launch_bounds__(1024) void permute_one_launch_kernel(
   if (w == 0) {
     int* roa = lb.row_of_assign + (size_t)layout_set_of(ls, 0) * ((size_t)d.T * k);
     int* sa = lb.sorted_assign + layout_row_base(d, ls, 0);
-    for (int base = e_lo; base < e_hi; base += 64) {
-      const int e = base + lane;
+    {  // the workgroup's own elements (at most 64: one round)
+      const int e = e_lo + lane;
       const bool in = e < e_hi;
-      int ks = -1, t = 0;
-      if (in) {
-        t = elem_token(d, g, e);
-        ks = slot_key(d, slot_at(d, soa + (size_t)t * k, 0, e % k));
-      }
+      const int ks = ko, t = to;
       const int r = wave_rank_step(ks, nb, bef);
       int pos = -1;
       if (ks >= 0 && r < kept_l[ks]) pos = go_l[ks] + r;
@@ -513,7 +557,20 @@ __global__ __launch_bounds__(1024) void permute_one_launch_kernel(
     }
   }
   __syncthreads();
-  for (int i = w; i < e_hi - e_lo; i += 16) {
+  int i = w;
+  if (pf_on) {
+    const int pos = pos_l[i];
+    if (pos >= 0 && pos < max_rows) {
+      char* dst = x_sorted + (size_t)pos * row_bytes;
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int o = u * 1024 + lane * 16;
+        if (o < row_bytes) *(v4i*)(dst + o) = pf[u];
+      }
+    }
+    i += 16;
+  }
+  for (; i < e_hi - e_lo; i += 16) {
     const int pos = pos_l[i];
     if (pos < 0 || pos >= max_rows) continue;
     wave_copy_row_deep(x_sorted + (size_t)pos * row_bytes, x + (size_t)tok_l[i] * row_bytes,
