@@ -60,10 +60,10 @@ PEAK_HBM_GBS = 8000.0
 GEMM_TRAFFIC = {
     "maverick_shard": {
         "gmm_src_sha256": "fdfe9c7ffa6bf1b143cf41677242c983a6760a16c2bdf65929917322154ff197",
-        "bytes_per_layer": 28870910278},
+        "bytes_per_layer": 28933922469},
     "mid_bf16": {
         "gmm_src_sha256": "fdfe9c7ffa6bf1b143cf41677242c983a6760a16c2bdf65929917322154ff197",
-        "bytes_per_layer": 267318021},
+        "bytes_per_layer": 267226130},
 }
 
 
