@@ -315,3 +315,41 @@ def test_repeat_is_bitwise_deterministic(g):
     y2 = run(inp["x"], inp["logits"], *inp["weights"]).clone()
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+# Rows of exactly 16 KB and of 17 KB (bf16, H = 8192 and 8704) through the
+# step API's permute: passes of at most 4096 elements take the one-launch
+# permute, whose waves load a row of up to 16 KB before the layout and copy
+# longer rows after it.
+@pytest.mark.parametrize("hidden", [8192, 8704])
+def test_permute_long_rows(g, hidden):
+    w = workloads.Workload(f"long_rows_{hidden}", tokens=512, seq_len=256, hidden=hidden,
+                           ffn=128, num_experts=8, top_k=2, num_shards=4, res_lo=1, res_hi=3,
+                           factor=1.0, num_chunks=2, zipf=1.0)
+    p, op = binding_problem(w), oracle_problem(w)
+    inp = workloads.make_inputs(w, device="cuda")
+    x_host = host(inp["x"])
+    idx, _ = gpu_route(g, p, inp["logits"])
+    cnt = gpu_count(g, p, idx)
+    o_idx, _ = oracle.route(inp["logits"].cpu().numpy(), w.top_k, w.gate)
+    want = oracle_count(op, o_idx)
+    torch.cuda.synchronize()
+    assert np.array_equal(ints(cnt["slot_of_assign"]), want["slot_of_assign"])
+    slot_np = want["slot_of_assign"].reshape(w.tokens, w.top_k)
+    cap = oracle.capacity(op)
+    ws = torch.empty(g.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    for (n, c, capped) in _passes(w):
+        say(f"[permute] H={hidden} n={n} c={c} capped={capped}")
+        rows, _ = g.pass_max_rows(p, n, capped)
+        go, roa, sa = i32(p.g_res + 1, -7), i32(w.tokens * w.top_k, -7), i32(rows, -7)
+        xs = torch.full((rows, w.hidden), 7.0, dtype=p.dtype, device="cuda")
+        g.moe_permute(p, n, c, capped, inp["x"], cnt["slot_of_assign"], go, roa, sa, None, None,
+                      None, None, xs, ws)
+        toks = oracle.pass_tokens(op, n, c)
+        lay = oracle.pass_layout(op, slot_np, toks, cap if capped else None)
+        torch.cuda.synchronize()
+        N = lay["num_rows"]
+        assert np.array_equal(ints(go), lay["group_offsets"])
+        assert np.array_equal(ints(sa)[:N], lay["sorted_assign"])
+        assert np.array_equal(host(xs[:N]), oracle.permute(x_host, lay["sorted_assign"], w.top_k))
+        assert bool((xs[N:] == 7.0).all())   # rows past the pass untouched
