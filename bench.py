@@ -55,25 +55,27 @@ PEAK_HBM_GBS = 8000.0
 # call), from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by
 # what the counters read for the calibration copy of 1 GiB (FETCH_SIZE
 # x1.99997, WRITE_SIZE x1.0).  It holds only for the kernel source it was
-# measured on (sha256 of gmm.hip) and that workload; otherwise the traffic
-# is reported as null.
+# measured on (sha256 of gmm.hip), that workload and the layer's chunks per
+# pass; otherwise the traffic is reported as null.
 GEMM_TRAFFIC = {
     "maverick_shard": {
-        "gmm_src_sha256": "fdfe9c7ffa6bf1b143cf41677242c983a6760a16c2bdf65929917322154ff197",
-        "bytes_per_layer": 28933922469},
+        "gmm_src_sha256": "ba4c08344c6d87c122f9950375da211687f229f1dc4d8e176249b88330557135",
+        "chunks_per_pass": 2,
+        "bytes_per_layer": 20966336534},
     "mid_bf16": {
-        "gmm_src_sha256": "fdfe9c7ffa6bf1b143cf41677242c983a6760a16c2bdf65929917322154ff197",
-        "bytes_per_layer": 267226130},
+        "gmm_src_sha256": "ba4c08344c6d87c122f9950375da211687f229f1dc4d8e176249b88330557135",
+        "chunks_per_pass": 4,
+        "bytes_per_layer": 265615727},
 }
 
 
-def recorded_gemm_traffic(workload):
+def recorded_gemm_traffic(workload, chunks_per_pass):
     import hashlib
     src = os.path.join(ROOT, "grouped_gemm_shard_amd", "csrc", "gmm.hip")
     with open(src, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
     rec = GEMM_TRAFFIC.get(workload)
-    if rec is None or sha != rec["gmm_src_sha256"]:
+    if rec is None or sha != rec["gmm_src_sha256"] or chunks_per_pass != rec["chunks_per_pass"]:
         return None
     return rec["bytes_per_layer"]
 
@@ -171,30 +173,14 @@ def time_calls(fn, reps):
 
 def gemm_layer_schedule(p, inp, cnt, bufs, reps):
     """Duration (s) of the grouped GEMMs of every pass on the layer's own
-    schedule: with two or more passes the layer alternates them between the
-    caller's stream and a second stream (fork and join by events), so one
-    pass's last tiles overlap the next pass's first ones.  The same GEMM
+    schedule, the passes in order on the caller's stream: the same GEMM
     calls are replayed that way (without the layer's layout and combine
-    launches) and timed between the fork and the join on the caller's
-    stream, so the figure is a span of the layer step, never longer than it."""
-    main = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
-    if len(bufs) < 2:
-        # one pass runs on the caller's stream alone, with no fork or join
-        return time_calls(lambda: run_gmm(p, inp, cnt, bufs[0]), reps)
-
-    def span():
-        fork = torch.cuda.Event()
-        fork.record(main)
-        side.wait_event(fork)
-        for i, b in enumerate(bufs):
-            with torch.cuda.stream(main if i % 2 == 0 else side):
-                run_gmm(p, inp, cnt, b)
-        join = torch.cuda.Event()
-        join.record(side)
-        main.wait_event(join)
-
-    return time_calls(span, reps)
+    launches) and timed as one span, so the figure is a span of the layer
+    step, never longer than it."""
+    def serial():
+        for b in bufs:
+            run_gmm(p, inp, cnt, b)
+    return time_calls(serial, reps)
 
 
 def kernel_figures(p, w, inp, info, reps):
@@ -566,13 +552,14 @@ def main():
     else:
         roof = dict(bound="hbm", achieved=round(gemm_gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(gemm_gbs / PEAK_HBM_GBS, 4), traffic=None)
-    roof["traffic"] = recorded_gemm_traffic(w.name)
+    roof["traffic"] = recorded_gemm_traffic(w.name, g.layer_chunks_per_pass(p, g.MODE_LAYER))
     # 128-row tiles (hidden < 2048) run GEMM1 and GEMM2 as one launch
+    sched = "the layer's schedule (passes in order on the caller's stream)"
     roof["kernel"] = ("grouped SwiGLU GEMM of every pass of the layer (" +
                       ("GEMM1 and GEMM2 in one launch" if w.hidden < 2048
                        else "GEMM1 and GEMM2 launches") +
-                      " per pass, with the step call's tile schedule), timed as one span on "
-                      "the layer's two-stream schedule")
+                      " per pass, with the step call's tile schedule), timed as one span on " +
+                      sched)
 
     bwd = None
     if not args.no_backward:
@@ -656,8 +643,7 @@ def main():
                                          if w.bf16 else None),
                  "gbs": round(gemm_gbs, 1), "arith_intensity": round(ai, 1),
                  "us_per_layer": round(kf["t_gmm_sched"] * 1e6, 2),
-                 "schedule": "every pass's GEMM calls replayed on the layer's two-stream "
-                             "schedule, one span",
+                 "schedule": "every pass's GEMM calls replayed on " + sched + ", one span",
                  "passes": kf["passes"], "rows": kf["rows"],
                  "serial_calls": {"us_per_layer": round(kf["t_gmm"] * 1e6, 2),
                                   "tflops": round(gemm_tflops_serial, 2),

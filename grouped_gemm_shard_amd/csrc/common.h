@@ -308,7 +308,6 @@ struct GemmPass {
   const int* tile_off;
   const int* tile_group;
   int go_stride, tg_stride;
-  bool split_ok;          // long-F passes may split their m-tiles over the side stream
   int* err;               // MOE_ERR_* bits of the GEMM are OR-ed into *err (may be null)
   int* sync;              // bf16: counters of the one-launch GEMM1+GEMM2 kernel
                           // (gmm_sync_bytes), zeroed by an earlier launch of the

@@ -108,7 +108,6 @@ struct GemmParams {
   int G, K, Nout, lo_slot, e_base, e_res, n_ntiles;
   int round_blocks;        // blocks per round of the tile order (a multiple of 8):
                            // the blocks resident on the chip at once
-  int part, parts;         // this launch covers m-tiles [M*part/parts, M*(part+1)/parts)
   int mt_cap;              // fused kernel: m-tiles its completion flags can hold
   long long max_rows;
   PassArgs pa;
@@ -859,9 +858,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gmm_bf16_kernel(GemmParams P) {
     if (blockIdx.x == 0) report(P.err, MOE_ERR_BAD_OFFSETS);
     return;
   }
-  // this launch's part of the m-tiles
-  const int m0 = (int)(((long long)total_mt * P.part) / P.parts);
-  const int mx = (int)(((long long)total_mt * (P.part + 1)) / P.parts) - m0;
+  const int m0 = 0, mx = total_mt;  // the launch's m-tiles
   const int total = mx * P.n_ntiles;
   // Blocks go round-robin over the 8 XCDs (block b to XCD b % 8).  Each
   // round of round_blocks blocks covers that many consecutive tiles of the
@@ -1251,8 +1248,6 @@ hipError_t launch_bf16(const Dims& d, const PassArgs& pa, const GemmPass& gp, co
   p1.mt_cap = p2.mt_cap = tile_map_len(d);
   p1.err = p2.err = gp.err;
   p1.spin_limit = p2.spin_limit = gemm_wait_limit();
-  p1.part = p2.part = 0;
-  p1.parts = p2.parts = 1;
 
   if (gsync != nullptr && (MOE_GEMM_FUSE & (BM == 256 ? 2 : 1))) {
     // both GEMMs in one launch (its counters and flags were zeroed before)
@@ -1265,41 +1260,20 @@ hipError_t launch_bf16(const Dims& d, const PassArgs& pa, const GemmPass& gp, co
     return hipGetLastError();
   }
 
-  // GEMM2 of a set of m-tiles needs only GEMM1 of the same m-tiles, so with
-  // long GEMM2 reductions (F >= 4096) the m-tiles run as two independent
-  // GEMM1 -> GEMM2 chains, one on the caller's stream and one on the side
-  // stream: the long last round of one half's GEMM2 overlaps the other
-  // half's work instead of idling the chip.  (Measured on MI355X: 8% faster
-  // on the Llama4-Maverick-shaped shard; with short GEMM2 reductions the
-  // second queue costs more than it saves.)
-  SideStream* ss = gp.split_ok && d.F >= 4096 ? side_stream() : nullptr;
-  const int parts = ss ? 2 : 1;
-  const long long mt_part = (mt_ub + parts - 1) / parts + 1;
+  // (Splitting the m-tiles into two GEMM1 -> GEMM2 chains on two streams,
+  // so that one half's last GEMM2 round overlaps the other half's work,
+  // measured 2-4% slower on the Llama4-Maverick-shaped shard in every mode
+  // once the layer's passes hold two chunks: both halves stream the weights
+  // of the experts they share.)
+  const long long mt = mt_ub + 1;
   const int nb = round_blocks() * resident_blocks<BM, BK, NST, NW, NWN>();
   p1.round_blocks = p2.round_blocks = nb;
-  const long long g1 = (mt_part * p1.n_ntiles + nb - 1) / nb * nb;
-  const long long g2 = (mt_part * p2.n_ntiles + nb - 1) / nb * nb;
-  std::unique_lock<std::mutex> lock(side_mutex(), std::defer_lock);
-  if (parts == 2) {
-    lock.lock();
-    hipError_t e = hipEventRecord(ss->fork, s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
-    if (e != hipSuccess) return e;
-  }
-  for (int part = 0; part < parts; ++part) {
-    hipStream_t st = part == 0 ? s : ss->s;
-    p1.part = p2.part = part;
-    p1.parts = p2.parts = parts;
-    hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, true, NW, NWN>), dim3((unsigned)g1),
-                       dim3(64 * NW), 0, st, p1);
-    hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, false, NW, NWN>), dim3((unsigned)g2),
-                       dim3(64 * NW), 0, st, p2);
-  }
-  if (parts == 2) {
-    hipError_t e = hipEventRecord(ss->join, ss->s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(s, ss->join, 0);
-    if (e != hipSuccess) return e;
-  }
+  const long long g1 = (mt * p1.n_ntiles + nb - 1) / nb * nb;
+  const long long g2 = (mt * p2.n_ntiles + nb - 1) / nb * nb;
+  hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, true, NW, NWN>), dim3((unsigned)g1),
+                     dim3(64 * NW), 0, s, p1);
+  hipLaunchKernelGGL((gmm_bf16_kernel<BM, BK, NST, false, NW, NWN>), dim3((unsigned)g2),
+                     dim3(64 * NW), 0, s, p2);
   return hipGetLastError();
 }
 
@@ -1406,8 +1380,6 @@ hipError_t launch_plain(const Dims& d, const int* group_offsets, const int* slot
   p.mt_cap = tile_map_len(d);
   p.err = nullptr;
   p.spin_limit = gemm_wait_limit();
-  p.part = 0;
-  p.parts = 1;
   const long long mt_ub = (max_rows + BM - 1) / BM + d.G_res;
   const int nb = round_blocks() * resident_blocks<BM, BK, NST, NW, NWN>();
   p.round_blocks = nb;

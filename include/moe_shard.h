@@ -25,12 +25,12 @@
  *    aligned), sized by moe_workspace_bytes / moe_layer_workspace_bytes.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work: nothing synchronises the host, so integer outputs are
- *    valid once the stream reaches them.  moe_layer_dropless_chunked puts
- *    part of its work on the side stream (with two or more passes, or a
- *    single pass with F >= 4096), forked from `stream` and joined back to it
- *    by events inside the call, so everything is complete when `stream`
- *    reaches the point after the call.  Concurrent calls on one device serialise
- *    only that enqueue (a mutex), not their GPU work.
+ *    valid once the stream reaches them.  moe_gmm_swiglu_bwd and moe_layer_bwd
+ *    put part of their work (dx_sorted) on the side stream, forked from
+ *    `stream` and joined back to it by events inside the call, so everything
+ *    is complete when `stream` reaches the point after the call.  Concurrent
+ *    calls on one device serialise only that enqueue (a mutex), not their
+ *    GPU work.
  *  - Errors: a negative moe_status, returned after validating every argument
  *    on the host and before any launch.  A failed launch returns MOE_EHIP.
  *    The library never truncates silently: too small a buffer is
@@ -152,12 +152,15 @@ int moe_layer_workspace_bytes(const moe_problem* p, int32_t mode, size_t* bytes)
 
 /* Chunks of the dropless fallback that moe_layer_dropless_chunked runs as
  * one pass in `mode`: the most consecutive chunks whose worst-case rows fit
- * the buffers the call is sized for, so running them together never needs
- * more memory than the capped buffer ([FALLBACK] How: the fallback keeps
- * each chunk's worst case within the capped buffer, so the layer's peak
- * HBM stays that of the capped layer).  The
- * tokens of the chunks are disjoint and every grouped-GEMM row is computed
- * on its own, so y is the same as chunk by chunk.  1 = one chunk per pass. */
+ * the buffers the call is sized for.  Those hold the rows of the capped
+ * buffer ([FALLBACK] How: the fallback keeps each chunk's worst case within
+ * the capped buffer, so the layer's peak HBM stays that of the capped
+ * layer), or twice those where that leaves two or more passes: a pass
+ * streams every resident expert's weights once, so twice the chunks per
+ * pass halve that traffic, for a constant factor of two on the pass
+ * buffers.  The passes run in order on the caller's stream.  The tokens of
+ * the chunks are disjoint and every grouped-GEMM row is computed on its
+ * own, so y is the same as chunk by chunk.  1 = one chunk per pass. */
 int moe_layer_chunks_per_pass(const moe_problem* p, int32_t mode, int32_t* chunks);
 
 /* ---- the hot path -------------------------------------------------------- */

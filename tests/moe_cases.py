@@ -38,8 +38,7 @@ MEDIUM = {
     # most 128 rows runs as a 128-row tile)
     "maverick_mid": CONFIGS["maverick_shard"].scaled(name="maverick_mid", tokens=2048,
                                                      seq_len=512, hidden=2048, ffn=1024),
-    # F >= 4096: the grouped GEMM splits each pass into two stream-parallel
-    # halves of m-tiles
+    # F >= 4096: long GEMM2 reductions
     "maverick_wide": CONFIGS["maverick_shard"].scaled(name="maverick_wide", tokens=1024,
                                                       seq_len=256, hidden=256, ffn=4096),
 }

@@ -152,32 +152,51 @@ def test_layer_workspace_grows_with_uncapped_modes():
 def test_fallback_chunks_per_pass_stay_within_the_capped_buffer():
     g = _binding()
     # One resident shard (Llama4-Maverick shard): a chunk's worst case already
-    # equals the capped buffer, so the chunks run one at a time.
+    # equals the capped buffer, which would leave 8 passes of one chunk, so
+    # the pass buffers hold twice that and the passes two chunks each.
     mav = problem(tokens=32768, seq_len=8192, hidden=5120, ffn=8192, num_experts=128, top_k=1,
                   num_shards=16, res_lo=0, res_hi=1, factor=2.0, num_chunks=8, gate="sigmoid")
-    assert g.layer_chunks_per_pass(mav, g.MODE_LAYER) == 1
+    assert g.layer_chunks_per_pass(mav, g.MODE_LAYER) == 2
     # All 8 virtual shards resident (mid layer): the buffer of 8 x 3072 rows
     # holds every assignment (16384 rows), so the 4 chunks run together.
     mid = problem()
     assert g.layer_chunks_per_pass(mid, g.MODE_LAYER) == 4
-    # FORCE_CHUNKED is sized for one chunk only.
-    assert g.layer_chunks_per_pass(mid, g.MODE_FORCE_CHUNKED) == 1
+    # FORCE_CHUNKED is sized for one chunk, doubled for its 4 passes.
+    assert g.layer_chunks_per_pass(mid, g.MODE_FORCE_CHUNKED) == 2
     # dedup + redundancy over 16 resident shards: rows and dedup rows of all
     # 8 chunks (65536 each) fit the capped bounds.
     ded = problem(tokens=8192, seq_len=8192, hidden=7168, ffn=2048, num_experts=256, top_k=8,
                   num_shards=16, res_lo=0, res_hi=16, factor=2.0, num_chunks=8, dedup=True,
                   slots_per_shard=2, num_replicas=2)
     assert g.layer_chunks_per_pass(ded, g.MODE_LAYER) == 8
-    # DeepSeek-V3 shard, 1 of 8 resident: cap 8192 = one chunk's worst case.
+    # DeepSeek-V3 shard, 1 of 8 resident: cap 8192 = one chunk's worst case,
+    # doubled for the fallback's passes.
     ds = problem(tokens=4096, seq_len=4096, hidden=7168, ffn=2048, num_experts=256, top_k=8,
                  num_shards=8, res_lo=0, res_hi=1, factor=2.0, num_chunks=4)
-    assert g.layer_chunks_per_pass(ds, g.MODE_LAYER) == 1
+    assert g.layer_chunks_per_pass(ds, g.MODE_LAYER) == 2
+    # the chunks of a pass divide num_chunks here
     for p, n in ((mav, 8), (mid, 4), (ded, 8), (ds, 4)):
         q = g.layer_chunks_per_pass(p, g.MODE_LAYER)
-        rows_q, drows_q = g.pass_max_rows(p, n // q, 0) if n % q == 0 else (None, None)
+        assert n % q == 0
+        rows_q, drows_q = g.pass_max_rows(p, n // q, 0)
         r1, u1 = g.pass_max_rows(p, 1, 1)
         rc, uc = g.pass_max_rows(p, n, 0)
-        assert rows_q <= max(r1, rc) and drows_q <= max(u1, uc)
+        # one pass: within the capped buffer; passes of a multi-pass call:
+        # within twice it
+        k = 1 if q == n else 2
+        assert rows_q <= k * max(r1, rc) and drows_q <= k * max(u1, uc)
+
+
+def test_two_chunk_passes_hold_twice_the_capped_rows():
+    # the Maverick shard's passes of two chunks: twice the rows of the capped
+    # buffer (a chunk's worst case equals it)
+    g = _binding()
+    mav = problem(tokens=32768, seq_len=8192, hidden=5120, ffn=8192, num_experts=128, top_k=1,
+                  num_shards=16, res_lo=0, res_hi=1, factor=2.0, num_chunks=8, gate="sigmoid")
+    rows1, _ = g.pass_max_rows(mav, 1, 1)
+    rows8, _ = g.pass_max_rows(mav, 8, 0)
+    rows4, _ = g.pass_max_rows(mav, 4, 0)
+    assert rows4 == 2 * max(rows1, rows8)
 
 
 def test_backward_entry_points_validate_on_the_host():

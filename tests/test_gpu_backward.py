@@ -188,16 +188,20 @@ def test_layer_backward_mid_full_size():
     compare_layer(workloads.CONFIGS["mid_bf16"], 0)
 
 
-# 65 chunk passes of one chunk each (the 0.02x buffer holds 333 rows, a
-# chunk 256): in the layer call an expert's weight gradients span 65 groups,
-# one per pass, more than the 64 that the 256 x 256 weight-gradient kernel
-# keeps in its register window, and the hottest experts are cut into chunks
-# whose partials are added in chunk order.
+# 130 chunks in 65 passes of two (the 0.009x buffer holds 150 rows, a chunk
+# 128, so passes of two chunks fit twice the buffer): in the layer call an
+# expert's weight gradients span 65 groups, one per pass, more than the 64
+# that the 256 x 256 weight-gradient kernel keeps in its register window, and
+# the hottest experts are cut into chunks whose partials are added in chunk
+# order.
 MANY_PASSES = W("bwd_many_passes", tokens=8320, seq_len=8320, hidden=2048, ffn=256,
-                num_experts=8, top_k=2, num_shards=1, res_lo=0, res_hi=1, factor=0.02,
-                num_chunks=65, zipf=1.1)
+                num_experts=8, top_k=2, num_shards=1, res_lo=0, res_hi=1, factor=0.009,
+                num_chunks=130, zipf=1.1)
 
 
 @pytest.mark.slow
 def test_layer_backward_many_passes():
+    import grouped_gemm_shard_amd as g
+    p = binding_problem(MANY_PASSES)
+    assert MANY_PASSES.num_chunks // g.layer_chunks_per_pass(p, g.MODE_LAYER) == 65
     compare_layer(MANY_PASSES, 0)

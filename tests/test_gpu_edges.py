@@ -6,7 +6,7 @@ The cases sit at the edges the method allows: every token choosing every
 expert (k = E), one expert per shard with only some shards resident, a
 fallback whose chunks hold one position of each sequence, a single token,
 heavy capped drops, more resident slots than the fused layout holds, 256-row
-GEMM tiles with the long-F split, and the fp32 path with dedup and redundant
+GEMM tiles with F >= 4096, and the fp32 path with dedup and redundant
 slots.  The grouped GEMM is also given malformed group offsets (both tile
 heights): it must compute nothing, and the same workspace must then serve a
 well-formed call.
@@ -47,8 +47,7 @@ EDGES = {
     "many_slots": W("many_slots", tokens=512, seq_len=256, hidden=256, ffn=128,
                     num_experts=256, top_k=4, num_shards=2, res_lo=0, res_hi=2, factor=1.0,
                     num_chunks=2, zipf=0.8),
-    # 256-row GEMM tiles (H >= 2048) with F >= 4096: a single pass splits its
-    # m-tiles over two streams, the chunked mode runs its passes on two
+    # 256-row GEMM tiles (H >= 2048) with F >= 4096, single and chunked passes
     "big_tiles_split": W("big_tiles_split", tokens=256, seq_len=128, hidden=2048, ffn=4096,
                          num_experts=16, top_k=2, num_shards=4, res_lo=0, res_hi=4, factor=2.0,
                          num_chunks=2, zipf=0.5),

@@ -1,11 +1,9 @@
 """The layer captured in a HIP graph (torch.cuda.graph) and replayed.
 
 The layer call only enqueues work (no host synchronisation, no allocation,
-no memset), so it can be captured.  Multi-pass calls fork half their passes
-onto the library's side stream and join them back inside the call, and a
-single long-F pass splits its GEMM the same way; the capture must follow
-those fork/join edges.  Every replay, with other eager work on the device
-between replays, must give y and info bitwise equal to the eager call.
+no memset), so it can be captured, its passes in order on the caller's
+stream.  Every replay, with other eager work on the device between
+replays, must give y and info bitwise equal to the eager call.
 """
 
 import pytest
@@ -17,11 +15,11 @@ from moe_cases import SMALL_CASES, binding_problem, say
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    ("mid_bf16", "LAYER"),            # one pass, no side stream
-    ("mid_bf16", "FORCE_CHUNKED"),    # four passes on two streams
-    ("maverick_small", "LAYER"),      # eight pass slots chosen on the device
-    ("dedup_small", "FORCE_CHUNKED"),  # dedup gather, eight passes
-    ("maverick_wide", "FORCE_DROPLESS"),  # one pass, F = 4096: GEMM split
+    ("mid_bf16", "LAYER"),            # one pass
+    ("mid_bf16", "FORCE_CHUNKED"),    # passes of two chunks
+    ("maverick_small", "LAYER"),      # pass slots chosen on the device
+    ("dedup_small", "FORCE_CHUNKED"),  # dedup gather, several passes
+    ("maverick_wide", "FORCE_DROPLESS"),  # one pass, F = 4096
 ]
 
 
@@ -35,8 +33,7 @@ def test_layer_graph_replay(name, mode_name):
     args = (inp["x"], inp["logits"], *inp["weights"])
     say(f"[graph] {name} {mode_name}")
     run = g.LayerRunner(p, mode)
-    # eager reference (also creates the side stream and caches launch
-    # shapes before the capture)
+    # eager reference (also caches launch shapes before the capture)
     y_ref = run(*args).clone()
     info_ref = run.info.clone()
     torch.cuda.synchronize()
