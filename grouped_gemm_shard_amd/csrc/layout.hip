@@ -444,10 +444,12 @@ __device__ __forceinline__ void wave_copy_row_deep(char* __restrict__ dst,
 // 16 waves, one row per wave at a time.  Workgroup 0 also writes the scan's
 // results (group offsets, kept rows, tile schedule, row count).  The
 // recount costs every workgroup a read of the pass's slots (L2-resident),
-// which is why the path is kept to small passes (measured on MI355X: 19.7
-// us against 26.9 us for the three-launch path at 4096 elements of 10 KB
-// rows; at 16384 elements the recount makes it twice as slow).
-constexpr int kOneLaunchElems = 4096;  // most elements of a pass
+// which is why the path is kept to passes of at most 8192 elements
+// (measured on MI355X with 10 KB rows: 19.7 us against 26.9 us for the
+// three-launch path at 4096 elements, 37 us against 40 us at 8192; at 16384
+// elements the recount makes it twice as slow, and 512 workgroups of 16
+// elements instead of 256 of 32 were 13% slower at 8192).
+constexpr int kOneLaunchElems = 8192;  // most elements of a pass
 constexpr int kOneLaunchOwn = 64;      // most elements per workgroup
 constexpr int kOneLaunchBlocks = 256;  // workgroups aimed for
 constexpr int kOneLaunchPrefetch = 16384;  // longest row loaded before the layout

@@ -318,7 +318,7 @@ def test_repeat_is_bitwise_deterministic(g):
 
 
 # Rows of exactly 16 KB and of 17 KB (bf16, H = 8192 and 8704) through the
-# step API's permute: passes of at most 4096 elements take the one-launch
+# step API's permute: passes of at most 8192 elements take the one-launch
 # permute, whose waves load a row of up to 16 KB before the layout and copy
 # longer rows after it.
 @pytest.mark.parametrize("hidden", [8192, 8704])
@@ -350,6 +350,47 @@ def test_permute_long_rows(g, hidden):
         torch.cuda.synchronize()
         N = lay["num_rows"]
         assert np.array_equal(ints(go), lay["group_offsets"])
+        assert np.array_equal(ints(sa)[:N], lay["sorted_assign"])
+        assert np.array_equal(host(xs[:N]), oracle.permute(x_host, lay["sorted_assign"], w.top_k))
+        assert bool((xs[N:] == 7.0).all())   # rows past the pass untouched
+
+
+# The one-launch permute at its largest passes: 4097-8192 elements give each
+# workgroup 32 elements, two rows per wave (the first loaded before the
+# layout, the second copied after it), with a ragged last workgroup; the
+# Maverick-shaped rows of 10 KB and rows of 17 KB, whose every row is copied
+# after the layout.
+@pytest.mark.parametrize("tokens,hidden,res_lo,res_hi",
+                         [(4096, 1024, 0, 4), (3000, 5120, 1, 3), (2500, 8704, 0, 4)])
+def test_permute_one_launch_large(g, tokens, hidden, res_lo, res_hi):
+    w = workloads.Workload(f"perm_large_{tokens}_{hidden}", tokens=tokens, seq_len=tokens,
+                           hidden=hidden, ffn=128, num_experts=16, top_k=2, num_shards=4,
+                           res_lo=res_lo, res_hi=res_hi, factor=1.0, num_chunks=1, zipf=1.0)
+    p, op = binding_problem(w), oracle_problem(w)
+    inp = workloads.make_inputs(w, device="cuda")
+    x_host = host(inp["x"])
+    idx, _ = gpu_route(g, p, inp["logits"])
+    cnt = gpu_count(g, p, idx)
+    o_idx, _ = oracle.route(inp["logits"].cpu().numpy(), w.top_k, w.gate)
+    want = oracle_count(op, o_idx)
+    torch.cuda.synchronize()
+    assert np.array_equal(ints(cnt["slot_of_assign"]), want["slot_of_assign"])
+    slot_np = want["slot_of_assign"].reshape(w.tokens, w.top_k)
+    cap = oracle.capacity(op)
+    ws = torch.empty(g.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    for (n, c, capped) in _passes(w):
+        say(f"[permute large] T={tokens} H={hidden} n={n} c={c} capped={capped}")
+        rows, _ = g.pass_max_rows(p, n, capped)
+        go, roa, sa = i32(p.g_res + 1, -7), i32(w.tokens * w.top_k, -7), i32(rows, -7)
+        xs = torch.full((rows, w.hidden), 7.0, dtype=p.dtype, device="cuda")
+        g.moe_permute(p, n, c, capped, inp["x"], cnt["slot_of_assign"], go, roa, sa, None, None,
+                      None, None, xs, ws)
+        toks = oracle.pass_tokens(op, n, c)
+        lay = oracle.pass_layout(op, slot_np, toks, cap if capped else None)
+        torch.cuda.synchronize()
+        N = lay["num_rows"]
+        assert np.array_equal(ints(go), lay["group_offsets"])
+        assert np.array_equal(ints(roa), lay["row_of_assign"].reshape(-1))
         assert np.array_equal(ints(sa)[:N], lay["sorted_assign"])
         assert np.array_equal(host(xs[:N]), oracle.permute(x_host, lay["sorted_assign"], w.top_k))
         assert bool((xs[N:] == 7.0).all())   # rows past the pass untouched
