@@ -282,6 +282,13 @@ __device__ __forceinline__ int xcd_unit(int nb, int total) {
 // 64-byte bank windows.
 __device__ __forceinline__ int wswz(int row) { return (row & 3) << 2; }
 
+// The same for the two-group weight-gradient loop, whose transpose reads
+// take 32 bytes from each of rows 8g + k (k < 4) for the read's 16-lane
+// groups g: row bit 3 also moves odd groups to the other 32-byte half of
+// each 64-byte window, so a read's 512 bytes cover each of the 64 banks
+// exactly twice (with bits 0-1 alone, all four groups shared 32 banks).
+__device__ __forceinline__ int ppswz(int row) { return ((row & 3) << 2) | ((row >> 2) & 2); }
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
@@ -1163,7 +1170,7 @@ __device__ __forceinline__ void wgrad_tile_pp(const WgradParams& P, char* smem) 
     const int colb = (isp ? i0 : j0) * 2 + (part & 1) * 256;
 #pragma unroll
     for (int i = 0; i < LQ; ++i) {
-      const int off = row[i] >= 0 ? row[i] * rowb + colb + ((pch ^ wswz(rr0)) << 4)
+      const int off = row[i] >= 0 ? row[i] * rowb + colb + ((pch ^ ppswz(rr0)) << 4)
                                   : (int)0x80000000;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(isp ? rp : rq,
                                                (lds_void*)(st + (i * 4 + wig) * 1024), 16, off,
@@ -1175,7 +1182,7 @@ __device__ __forceinline__ void wgrad_tile_pp(const WgradParams& P, char* smem) 
   const int tj = lane & 15;
   const unsigned tk_base =
       (8 * (lane >> 4) + (tj >> 2)) * 256 + (tj & 1) * 8 + (((tj & 3) >> 1) << 4);
-  const int tk_sw = (tj >> 2) << 2;
+  const int tk_sw = ((tj >> 2) << 2) | (((lane >> 4) & 1) << 1);  // ppswz of the lane's rows
   const unsigned lds0 = lds_addr(smem);
 
   floatx4 acc[MI][NI];

@@ -227,9 +227,13 @@ __device__ __forceinline__ bf16x8 join_halves(const v4i16& lo, const v4i16& hi) 
 }
 
 // 16-byte chunk permutation of a 256-byte LDS row of a reduction-major B
-// quarter: the transpose reads of 4 consecutive rows at one column land on
-// disjoint 64-byte bank windows.
-__device__ __forceinline__ int kswz(int row) { return (row & 3) << 2; }
+// quarter.  A transpose read takes 32 bytes from each of 16 rows, 8g + k
+// (k < 4) for its 16-lane groups g; rows 256 bytes apart share their banks
+// (64 banks of 4 bytes).  Row bits 0-1 move the 4 rows of a group to
+// disjoint 64-byte windows, and row bit 3 (g odd) to the other 32-byte half
+// of each window, so the 512 bytes of a read cover every bank exactly twice
+// (with bits 0-1 alone, groups 0-3 shared 32 banks: twice the cycles).
+__device__ __forceinline__ int kswz(int row) { return ((row & 3) << 2) | ((row >> 2) & 2); }
 
 // Starts the loads of K step `step` into its ring stage: each wave-wide
 // load fills RPI consecutive rows (1 KB) of the stage.
@@ -635,7 +639,7 @@ __device__ __forceinline__ void gmm_tile_pp(const GemmParams& P, char* smem, con
   // (+4 for the second read) and columns 4 (j%4) .. of the 16-column tile
   const int tj = lane & 15;
   const unsigned tk_base = (8 * (lane >> 4) + (tj >> 2)) * 256 + (tj & 1) * 8 + (((tj & 3) >> 1) << 4);
-  const int tk_sw = (tj >> 2) << 2;  // kswz of the lane's rows
+  const int tk_sw = ((tj >> 2) << 2) | (((lane >> 4) & 1) << 1);  // kswz of the lane's rows
   // fragment rows within their quarters (16x16x32: lane reads row lane%16)
   int ar[MI], br[NI];
 #pragma unroll
