@@ -441,19 +441,24 @@ __device__ __forceinline__ void wave_copy_row_deep(char* __restrict__ dst,
 // elements: the rows per slot; over the elements before its own: their
 // bases), runs the slot scan in LDS, ranks and places its own `per_block`
 // elements (one wave, on top of those bases) and copies their rows with its
-// 16 waves, one row per wave at a time.  Workgroup 0 also writes the scan's
+// 16 waves, a wave's first rows loaded before the layout.  Workgroup 0 also writes the scan's
 // results (group offsets, kept rows, tile schedule, row count).  The
 // recount costs every workgroup a read of the pass's slots (L2-resident),
 // which is why the path is kept to passes of at most 8192 elements
 // (measured on MI355X with 10 KB rows: 19.7 us against 26.9 us for the
-// three-launch path at 4096 elements, 37 us against 40 us at 8192; at 16384
+// three-launch path at 4096 elements, 35 us against 39 us at 8192 with one
+// row a wave loaded ahead; at 16384
 // elements the recount makes it twice as slow, and 512 workgroups of 16
 // elements instead of 256 of 32 were 13% slower at 8192).
 constexpr int kOneLaunchElems = 8192;  // most elements of a pass
 constexpr int kOneLaunchOwn = 64;      // most elements per workgroup
 constexpr int kOneLaunchBlocks = 256;  // workgroups aimed for
-constexpr int kOneLaunchPrefetch = 16384;  // longest row loaded before the layout
 
+// PF: 1 KB slices (16 bytes a lane) of the longest row a wave loads before
+// the layout; NR: rows a wave loads then (its elements w and w + 16).  Two
+// rows of up to 10 KB or one of up to 16 KB keep a wave within the 128
+// registers of a 1024-thread workgroup.
+template <int PF, int NR>
 __global__ __launch_bounds__(1024) void permute_one_launch_kernel(
     Dims d, LayoutSet ls, const int* __restrict__ soa, LayoutBuffers lb,
     const char* __restrict__ x, char* __restrict__ x_sorted, int row_bytes, long long max_rows,
@@ -494,27 +499,33 @@ __global__ __launch_bounds__(1024) void permute_one_launch_kernel(
   }
   int to;
   const int ko = key_of(e_lo + lane, w == 0 && e_lo + lane < e_hi, to);
-  int tw;
-  const bool res_w = key_of(e_lo + w, w < e_hi - e_lo, tw) >= 0;
+  int tw[NR];
+  bool res_w[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    res_w[r] = key_of(e_lo + w + 16 * r, w + 16 * r < e_hi - e_lo, tw[r]) >= 0;
   // every key landed on every path (s_waitcnt vmcnt(0): the encoding's
   // expcnt and lgkmcnt fields at their maxima), so that no later use of a
   // key waits on the row loads below
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  // Each wave's first own element: its source row is known before the
-  // layout, so a resident element's row (at most kOneLaunchPrefetch bytes)
-  // is loaded into registers now and lands while the workgroup recounts
-  // and places the keys; it is stored once its position is known.
+  // Each wave's first NR own elements: their source rows are known before
+  // the layout, so a resident element's row (at most PF KB) is loaded into
+  // registers now and lands while the workgroup recounts and places the
+  // keys; it is stored once its position is known.
   typedef int v4i __attribute__((ext_vector_type(4)));
-  constexpr int PF = kOneLaunchPrefetch / 1024;
-  v4i pf[PF];
-  const bool pf_on = row_bytes <= kOneLaunchPrefetch && w < e_hi - e_lo;
-  const bool pf_load = pf_on && res_w;
-  if (pf_on) {
-    const char* src = x + (size_t)tw * row_bytes;
+  v4i pf[NR][PF];
+  const bool pf_fit = row_bytes <= PF * 1024;
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int o = u * 1024 + lane * 16;
-      pf[u] = pf_load && o < row_bytes ? *(const v4i*)(src + o) : v4i{0, 0, 0, 0};
+  for (int r = 0; r < NR; ++r) {
+    const bool pf_on = pf_fit && w + 16 * r < e_hi - e_lo;
+    const bool pf_load = pf_on && res_w[r];
+    if (pf_on) {
+      const char* src = x + (size_t)tw[r] * row_bytes;
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int o = u * 1024 + lane * 16;
+        pf[r][u] = pf_load && o < row_bytes ? *(const v4i*)(src + o) : v4i{0, 0, 0, 0};
+      }
     }
   }
   for (int q = threadIdx.x; q < G; q += 1024) tot[q] = bef[q] = 0;
@@ -560,17 +571,20 @@ __global__ __launch_bounds__(1024) void permute_one_launch_kernel(
   }
   __syncthreads();
   int i = w;
-  if (pf_on) {
-    const int pos = pos_l[i];
-    if (pos >= 0 && pos < max_rows) {
-      char* dst = x_sorted + (size_t)pos * row_bytes;
 #pragma unroll
-      for (int u = 0; u < PF; ++u) {
-        const int o = u * 1024 + lane * 16;
-        if (o < row_bytes) *(v4i*)(dst + o) = pf[u];
+  for (int r = 0; r < NR; ++r) {
+    if (pf_fit && i < e_hi - e_lo) {
+      const int pos = pos_l[i];
+      if (pos >= 0 && pos < max_rows) {
+        char* dst = x_sorted + (size_t)pos * row_bytes;
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          const int o = u * 1024 + lane * 16;
+          if (o < row_bytes) *(v4i*)(dst + o) = pf[r][u];
+        }
       }
+      i += 16;
     }
-    i += 16;
   }
   for (; i < e_hi - e_lo; i += 16) {
     const int pos = pos_l[i];
@@ -699,8 +713,14 @@ hipError_t launch_permute_one(const Dims& d, const LayoutSet& ls, const int* soa
   per = per < 16 ? 16 : (per + 15) / 16 * 16;
   if (per > kOneLaunchOwn) return hipErrorNotSupported;
   const int nb = nelem > 0 ? (nelem + per - 1) / per : 1;
-  hipLaunchKernelGGL(permute_one_launch_kernel, dim3(nb), dim3(1024), 0, s, d, ls, soa, lb,
-                     (const char*)x, (char*)x_sorted, row_bytes, (long long)max_rows, per);
+  if (row_bytes <= 10240 && per > 16)
+    hipLaunchKernelGGL((permute_one_launch_kernel<10, 2>), dim3(nb), dim3(1024), 0, s, d, ls,
+                       soa, lb, (const char*)x, (char*)x_sorted, row_bytes, (long long)max_rows,
+                       per);
+  else
+    hipLaunchKernelGGL((permute_one_launch_kernel<16, 1>), dim3(nb), dim3(1024), 0, s, d, ls,
+                       soa, lb, (const char*)x, (char*)x_sorted, row_bytes, (long long)max_rows,
+                       per);
   return hipGetLastError();
 }
 

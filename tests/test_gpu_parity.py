@@ -356,12 +356,13 @@ def test_permute_long_rows(g, hidden):
 
 
 # The one-launch permute at its largest passes: 4097-8192 elements give each
-# workgroup 32 elements, two rows per wave (the first loaded before the
-# layout, the second copied after it), with a ragged last workgroup; the
-# Maverick-shaped rows of 10 KB and rows of 17 KB, whose every row is copied
-# after the layout.
+# workgroup 32 elements, two rows per wave, with a ragged last workgroup.
+# Rows of up to 10 KB (2 KB, and the Maverick-shaped 10 KB) are both loaded
+# before the layout; rows of 14 KB load the first before it and copy the
+# second after it; rows of 17 KB are all copied after it.
 @pytest.mark.parametrize("tokens,hidden,res_lo,res_hi",
-                         [(4096, 1024, 0, 4), (3000, 5120, 1, 3), (2500, 8704, 0, 4)])
+                         [(4096, 1024, 0, 4), (3000, 5120, 1, 3), (3000, 7168, 0, 4),
+                          (2500, 8704, 0, 4)])
 def test_permute_one_launch_large(g, tokens, hidden, res_lo, res_hi):
     w = workloads.Workload(f"perm_large_{tokens}_{hidden}", tokens=tokens, seq_len=tokens,
                            hidden=hidden, ffn=128, num_experts=16, top_k=2, num_shards=4,
