@@ -59,13 +59,13 @@ PEAK_HBM_GBS = 8000.0
 # pass; otherwise the traffic is reported as null.
 GEMM_TRAFFIC = {
     "maverick_shard": {
-        "gmm_src_sha256": "ba4c08344c6d87c122f9950375da211687f229f1dc4d8e176249b88330557135",
+        "gmm_src_sha256": "2ee25cb014df7ce9608d68cb2f1860a7ebc712b43414fe8a5cbc49868e412a2f",
         "chunks_per_pass": 2,
-        "bytes_per_layer": 20966336534},
+        "bytes_per_layer": 20883169063},
     "mid_bf16": {
-        "gmm_src_sha256": "ba4c08344c6d87c122f9950375da211687f229f1dc4d8e176249b88330557135",
+        "gmm_src_sha256": "2ee25cb014df7ce9608d68cb2f1860a7ebc712b43414fe8a5cbc49868e412a2f",
         "chunks_per_pass": 4,
-        "bytes_per_layer": 265615727},
+        "bytes_per_layer": 268087767},
 }
 
 
